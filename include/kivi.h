@@ -1,0 +1,207 @@
+/*
+ * kivi.h - C ABI of the KIVI hot path on AMD Instinct MI355X (gfx950).
+ *
+ * KIVI keeps the attention KV cache of a decoder in low-bit integer codes:
+ *   - keys are quantized per channel: the G consecutive tokens of one channel
+ *     form a group with its own scale and zero-point
+ *     (page "KIVI: Asymmetric 2-Bit KV Cache Quantization Guide", section
+ *     "The Three Structural Innovations of KIVI", item 1; page "KV cache
+ *     quantization with KIVI INT2 setup guide", section "KIVI: Per-Channel Key,
+ *     Per-Token Value Quantization Explained", defaults G=32, R=128);
+ *   - values are quantized per token: the G consecutive channels of one token
+ *     form a group (same pages, item 2 / same section);
+ *   - the newest R tokens stay unquantized in a residual window; when the
+ *     window is full it is quantized and packed as a whole ("Asymmetric 2-Bit"
+ *     guide, item 3 "The Streaming Residual FP16 Window");
+ *   - decode attention reads the packed codes and dequantizes them on the fly
+ *     ("Asymmetric 2-Bit" guide, section "Production Serving and vLLM
+ *     Deployment Trade-offs"; page "KV-Cache Quantization: I Ran the
+ *     Experiments", section "Where it still breaks", item 3).
+ *
+ * Quantizer of one group x_0..x_{G-1} (b bits, qmax = 2^b - 1), in binary32
+ * with round-to-nearest-even on every operation ("Asymmetric 2-Bit" guide,
+ * "Step 1" and "Step 2"; zero-point kept as a float, see the design notes):
+ *     mn = min x_j,  mx = max x_j,  s = (mx - mn) / qmax
+ *     c_j = clamp(rne((x_j - mn) / s), 0, qmax)      (all c_j = 0 when s == 0)
+ *     S = fp16(s), Z = fp16(mn)   (a zero S or Z is stored as +0, bits 0x0000)
+ *     dequantized value  x^_j = c_j * S + Z
+ *
+ * ------------------------------------------------------------------------
+ * Packed layout (all arrays are per cache = one attention layer).
+ *   B = batch, H = KV heads, D = head_dim, G = group_size, R = residual_length,
+ *   cap = max_tokens rounded up to a multiple of R, NB = cap / G blocks,
+ *   bk = k_bits, bv = v_bits, Pk = 32 / bk and Pv = 32 / bv codes per word.
+ * A "unit" is one (batch b, kv head h) pair, unit index u = b * H + h.
+ * Token t of a unit lies in block g = t / G at row j = t % G.
+ *
+ * Word bit order ("split-half"): code number i (0 <= i < P) of a 32-bit word
+ * occupies bits [o, o + bits) with o = bits * (i / 2) + 16 * (i % 2): even
+ * codes fill the low half-word, odd codes the high half-word, each half in
+ * increasing order.  Masking a word with 0x00030003 (2-bit) or 0x000F000F
+ * (4-bit) after a shift therefore yields two codes, one per 16-bit lane.
+ *
+ * Codes are packed along the axis that the attention contraction runs over
+ * (channels for q.K, tokens for p.V), not along the quantization group:
+ *   k_codes  uint32 [B*H][cap][D / Pk]     word w of token t holds channels
+ *                                          w*Pk .. w*Pk + Pk - 1
+ *   k_scale  fp16   [B*H][NB][D]           one {S} per (block, channel)
+ *   k_zero   fp16   [B*H][NB][D]           one {Z} per (block, channel)
+ *   v_codes  uint32 [B*H][NB][D][G / Pv]   word w of (block g, channel d)
+ *                                          holds rows w*Pv .. w*Pv + Pv - 1
+ *   v_scale  fp16   [B*H][NB][D / G][G]    one {S} per (token, channel group)
+ *   v_zero   fp16   [B*H][NB][D / G][G]
+ *   k_resid, v_resid  kv_dtype [B*H][R][D] residual window, slot i holds the
+ *                                          token n_quant + i
+ * Tokens [0, n_quant) are packed, tokens [n_quant, n_quant + n_resid) are in
+ * the residual window.  Entries beyond those are unspecified.
+ *
+ * ------------------------------------------------------------------------
+ * Conventions for every entry point.
+ *   - All device memory is owned by the caller (cache buffer, inputs, q, out,
+ *     workspace) and must stay alive until the stream work that uses it has
+ *     finished.  The library never allocates or frees device memory and never
+ *     creates streams; it owns only the host-side kivi_cache struct.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ *     Calls enqueue work and return without synchronizing.  Host-side counters
+ *     (n_quant, n_resid) advance at enqueue time, so all calls on one cache
+ *     must be issued in order on one stream.  A cache handle is not
+ *     thread-safe.
+ *   - Argument errors are detected before anything is enqueued; the call then
+ *     returns the error and leaves the cache unchanged.  A failed kernel
+ *     launch returns KIVI_ERR_HIP and poisons the handle (later calls return
+ *     KIVI_ERR_HIP).  Device faults surface at the caller's next
+ *     synchronization.  kivi_last_error_message() gives a thread-local text.
+ *   - Inputs must be finite and within +-65504 (the fp16 range of S and Z);
+ *     results for other inputs are unspecified.
+ */
+#ifndef KIVI_H_
+#define KIVI_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct kivi_cache kivi_cache; /* opaque host handle, one per layer */
+
+typedef enum {
+  KIVI_OK = 0,
+  KIVI_ERR_INVALID_ARG = 1,      /* null pointer, malformed config or size */
+  KIVI_ERR_UNSUPPORTED = 2,      /* valid, but not built (e.g. head_dim != 128) */
+  KIVI_ERR_CAPACITY = 3,         /* more tokens than max_tokens */
+  KIVI_ERR_BUFFER_TOO_SMALL = 4, /* cache buffer or workspace too small */
+  KIVI_ERR_EMPTY = 5,            /* decode on a cache that holds no token */
+  KIVI_ERR_HIP = 6               /* a HIP call failed; handle is poisoned */
+} kivi_status;
+
+typedef enum { KIVI_F16 = 0, KIVI_BF16 = 1, KIVI_F32 = 2 } kivi_dtype;
+
+/* Quantization config: the knobs k_bits, v_bits, group_size and
+ * residual_length of page "KV-Cache Quantization: I Ran the Experiments",
+ * section "Component 4 - Serving architecture & manifests". */
+typedef struct {
+  int32_t batch;           /* B >= 1 */
+  int32_t num_kv_heads;    /* H >= 1 */
+  int32_t head_dim;        /* D; multiple of group_size. Kernels: 128 */
+  int32_t max_tokens;      /* per-sequence capacity T_max >= 1 */
+  int32_t k_bits;          /* 2 or 4 */
+  int32_t v_bits;          /* 2 or 4 */
+  int32_t group_size;      /* G. Kernels: 32 */
+  int32_t residual_length; /* R; positive multiple of G, at most 1024 */
+  int32_t kv_dtype;        /* kivi_dtype: KIVI_F16 or KIVI_BF16 (inputs,
+                              residual window and q) */
+} kivi_config;
+
+/* Device pointers into the cache buffer plus the host counters. */
+typedef struct {
+  int32_t n_quant;   /* tokens packed; a multiple of R */
+  int32_t n_resid;   /* tokens in the residual window, 0..R */
+  int32_t capacity;  /* cap: max_tokens rounded up to a multiple of R */
+  int32_t num_blocks;/* NB = cap / G */
+  uint32_t *k_codes, *v_codes;
+  uint16_t *k_scale, *k_zero, *v_scale, *v_zero; /* fp16 bit patterns */
+  void *k_resid, *v_resid;                        /* kv_dtype */
+} kivi_cache_view;
+
+/* Bytes of device memory the cache for `cfg` needs (all arrays above, each
+ * 256-byte aligned).  Pure arithmetic; no device is touched. */
+kivi_status kivi_cache_bytes(const kivi_config* cfg, size_t* bytes);
+
+/* Creates an empty cache (n_quant = n_resid = 0) over the caller's device
+ * buffer `dev_buf` of `dev_bytes` bytes (>= kivi_cache_bytes, 256-byte
+ * aligned).  The buffer content is not read or written here.  On success
+ * *out receives a handle the caller frees with kivi_cache_destroy. */
+kivi_status kivi_cache_create(const kivi_config* cfg, void* dev_buf,
+                              size_t dev_bytes, kivi_cache** out);
+
+/* Frees the host handle.  Does not synchronize and does not touch the
+ * device buffer.  NULL is accepted. */
+kivi_status kivi_cache_destroy(kivi_cache* cache);
+
+/* Forgets every token (n_quant = n_resid = 0) without touching device
+ * memory, so the buffer can be refilled. */
+kivi_status kivi_cache_reset(kivi_cache* cache);
+
+/* Appends n_tokens tokens per sequence.  k and v are device arrays of
+ * kv_dtype laid out [B][H][n_tokens][D] (page "KIVI: Asymmetric 2-Bit KV Cache
+ * Quantization Guide", "Step 1", tensor layout [batch, heads, seq_len,
+ * head_dim]).  The result is, bit for bit, that of n_tokens single-token
+ * appends, each of which first packs the residual window if it holds R
+ * tokens and then stores the token in the window ("Step 3" and item 3 of
+ * "The Three Structural Innovations of KIVI").  Afterwards
+ * 1 <= n_resid <= R (for n_tokens >= 1) and n_quant % R == 0.
+ * Full windows inside the input are packed straight from k/v.
+ * Errors: INVALID_ARG (null cache/k/v, n_tokens < 0), CAPACITY (total would
+ * exceed max_tokens), HIP.  n_tokens == 0 is a no-op. */
+kivi_status kivi_append(kivi_cache* cache, const void* k, const void* v,
+                        int32_t n_tokens, void* stream);
+
+/* Packs the residual window if it holds exactly R tokens (n_quant += R,
+ * n_resid = 0); otherwise does nothing and returns KIVI_OK. */
+kivi_status kivi_flush_residual(kivi_cache* cache, void* stream);
+
+/* Workspace bytes kivi_decode_attn needs for num_q_heads query heads at any
+ * fill level of this cache.  Pure arithmetic. */
+kivi_status kivi_decode_attn_workspace_bytes(const kivi_cache* cache,
+                                             int32_t num_q_heads,
+                                             size_t* bytes);
+
+/* One decode step of attention for every sequence:
+ *   out[b][j] = sum_t softmax_t(softmax_scale * q[b][j] . k^_t) v^_t
+ * over the T = n_quant + n_resid cached tokens of kv head h = j / (Hq / H)
+ * (consecutive query heads share a kv head), where k^ and v^ are the
+ * dequantized codes for packed tokens and the stored kv_dtype values for
+ * window tokens.  q is a device array of kv_dtype [B][Hq][D]; out is a
+ * device array of out_dtype (KIVI_F32, KIVI_F16 or KIVI_BF16) [B][Hq][D].
+ * The token axis is split across workgroups and the per-split partial
+ * softmax states are merged exactly (log-sum-exp) in a second kernel; the
+ * workspace holds those partials.
+ * Errors: INVALID_ARG (nulls, Hq not a positive multiple of H, bad dtype),
+ * EMPTY (T == 0), BUFFER_TOO_SMALL (ws_bytes below the workspace query),
+ * HIP. */
+kivi_status kivi_decode_attn(const kivi_cache* cache, const void* q,
+                             int32_t num_q_heads, float softmax_scale,
+                             void* out, int32_t out_dtype, void* workspace,
+                             size_t ws_bytes, void* stream);
+
+/* Fixes the number of token splits used by kivi_decode_attn (0 restores the
+ * automatic choice).  The value is clamped to [1, blocks + 1]. For tests of
+ * split invariance and for tuning. */
+kivi_status kivi_set_decode_splits(kivi_cache* cache, int32_t n_split);
+
+/* Fills *view with the device pointers and counters of the cache. */
+kivi_status kivi_cache_get_view(const kivi_cache* cache, kivi_cache_view* view);
+
+/* Static text for a status code. */
+const char* kivi_status_string(kivi_status status);
+
+/* Thread-local detail for the last non-OK status returned on this thread. */
+const char* kivi_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KIVI_H_ */

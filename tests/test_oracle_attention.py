@@ -1,0 +1,107 @@
+"""Pins of the oracle's decode attention (CPU only).
+
+Decode attention reads every cached key and value for each new token (page
+"KV-Cache Quantization: I Ran the Experiments", "Component 1"; paper
+abstract "KIVI: A Tuning-Free Asymmetric 2bit Quantization for KV Cache").
+The pages never write the formula out; it is the textbook scaled dot-product
+softmax attention, which is what the special cases below compare against.
+"""
+import numpy as np
+import pytest
+
+from tests.grid_inputs import attention_fp64, from_bits, grid_kv, to_bits
+
+SCALE = 1.0 / np.sqrt(128.0)
+
+
+def _rand(rng, shape, dtype):
+    x = rng.standard_normal(shape) * 1.5
+    if dtype == "f16":
+        return x.astype(np.float16).astype(np.float64)
+    f = x.astype(np.float32)
+    return ((f.view(np.uint32) & 0xFFFF0000).view(np.float32)).astype(np.float64)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_window_only_is_plain_attention(oracle_mod, dtype):
+    # T <= R: nothing is packed, the result is plain softmax attention on the
+    # stored values.
+    rng = np.random.default_rng(1)
+    B, H, Hq, D, T = 2, 2, 4, 128, 100
+    K, V = _rand(rng, (B, H, T, D), dtype), _rand(rng, (B, H, T, D), dtype)
+    q = _rand(rng, (B, Hq, D), dtype)
+    c = oracle_mod.OracleCache(B, H, D, T, 2, 2, 32, 128, 0 if dtype == "f16" else 1)
+    c.append(to_bits(K, dtype), to_bits(V, dtype))
+    assert c.n_quant == 0
+    out = c.decode_attn(to_bits(q, dtype), SCALE)
+    ref = attention_fp64(q, K, V, SCALE, Hq // H)
+    assert np.max(np.abs(out - ref)) < 1e-12
+
+
+@pytest.mark.parametrize("kb,vb,dtype,gq", [(2, 2, "f16", 1), (2, 2, "f16", 4),
+                                            (4, 4, "bf16", 4), (2, 4, "f16", 2)])
+def test_grid_exact_cache_is_plain_attention(oracle_mod, kb, vb, dtype, gq):
+    # Grid-exact groups dequantize to their inputs, so attention over the
+    # packed cache equals plain attention on the raw tensors.  A wrong code
+    # index, a transposed operand, a wrong kv-head mapping or a dropped
+    # zero-point term would each break the equality.
+    B, H, D, T, R = 2, 2, 128, 3 * 64 + 45, 64
+    K, V = grid_kv(B, H, T, D, k_bits=kb, v_bits=vb, seed=kb * 7 + gq)
+    rng = np.random.default_rng(gq)
+    q = _rand(rng, (B, H * gq, D), dtype)
+    c = oracle_mod.OracleCache(B, H, D, T, kb, vb, 32, R, 0 if dtype == "f16" else 1)
+    c.append(to_bits(K, dtype), to_bits(V, dtype))
+    assert (c.n_quant, c.n_resid) == (192, 45)
+    out = c.decode_attn(to_bits(q, dtype), SCALE)
+    ref = attention_fp64(q, from_bits(to_bits(K, dtype), dtype),
+                         from_bits(to_bits(V, dtype), dtype), SCALE, gq)
+    assert np.max(np.abs(out - ref)) < 1e-11
+
+
+def test_single_token_returns_its_value(oracle_mod):
+    rng = np.random.default_rng(2)
+    K, V = _rand(rng, (1, 1, 1, 128), "f16"), _rand(rng, (1, 1, 1, 128), "f16")
+    q = _rand(rng, (1, 3, 128), "f16")
+    c = oracle_mod.OracleCache(1, 1, 128, 10, 2, 2, 32, 128)
+    c.append(to_bits(K, "f16"), to_bits(V, "f16"))
+    out = c.decode_attn(to_bits(q, "f16"), SCALE)
+    for j in range(3):
+        assert np.array_equal(out[0, j], V[0, 0, 0])
+
+
+def test_zero_query_averages_values(oracle_mod):
+    # q = 0 gives equal weights: the mean of the (exactly dequantized) rows.
+    B, H, D, T = 1, 1, 128, 300
+    K, V = grid_kv(B, H, T, D, seed=5)
+    c = oracle_mod.OracleCache(B, H, D, T, 2, 2, 32, 128)
+    c.append(to_bits(K, "f16"), to_bits(V, "f16"))
+    out = c.decode_attn(np.zeros((1, 1, D), np.uint16), SCALE)
+    assert np.max(np.abs(out[0, 0] - V[0, 0].astype(np.float64).mean(0))) < 1e-13
+
+
+def test_four_bits_closer_than_two_bits(oracle_mod):
+    # More bits per code give a smaller attention error against the
+    # unquantized result (page "KV-Cache Quantization: I Ran the
+    # Experiments", Figure 4: every scheme's 4-bit error is below its 2-bit
+    # error), and neither is bit-identical.
+    from kv_cache_bit_kivi_amd.inputs import bits16, make_layer, small
+    w = small("t", 2, 2, 8, 1024)
+    x = make_layer(w, seed=0, n_new=0)
+    ref = attention_fp64(x.q.double().numpy(), x.k.double().numpy(),
+                         x.v.double().numpy(), SCALE, 4)
+    err = {}
+    for bits in (2, 4):
+        c = oracle_mod.OracleCache(2, 2, 128, 1024, bits, bits, 32, 128)
+        c.append(bits16(x.k), bits16(x.v))
+        out = c.decode_attn(bits16(x.q), SCALE)
+        err[bits] = np.sqrt(np.mean((out - ref) ** 2))
+    assert 0 < err[4] < err[2]
+
+
+def test_errors(oracle_mod):
+    c = oracle_mod.OracleCache(1, 2, 64, 10, 2, 2, 32, 32)
+    with pytest.raises(ValueError):
+        c.decode_attn(np.zeros((1, 2, 64), np.uint16), SCALE)  # empty
+    c.append(np.zeros((1, 2, 1, 64), np.uint16), np.zeros((1, 2, 1, 64), np.uint16))
+    with pytest.raises(ValueError):
+        c.decode_attn(np.zeros((1, 3, 64), np.uint16), SCALE)  # 3 % 2 != 0
