@@ -1,0 +1,433 @@
+// kivi_api.cpp - host state machine and C ABI (include/kivi.h).
+//
+// The cache is one attention layer: packed codes and metadata for tokens
+// [0, n_quant) plus an unquantized residual window for [n_quant, T).  The
+// window policy follows page "KIVI: Asymmetric 2-Bit KV Cache Quantization
+// Guide", item 3 of "The Three Structural Innovations of KIVI" and "Step 3":
+// new tokens enter the full-precision window, and a full window is grouped
+// and packed before the next token enters (whole-window flush, so the window
+// holds 1..R tokens after any append).  Appending n tokens at once produces
+// exactly the state of n single appends; full windows inside the input are
+// packed straight from the caller's buffer.
+//
+// Every entry point validates its arguments before enqueuing anything; the
+// counters advance at enqueue time.  A failed launch poisons the handle.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "../../include/kivi.h"
+#include "kivi_internal.h"
+
+struct kivi_cache {
+  kivi_config cfg;
+  int cap;  // token capacity per unit (max_tokens rounded up to R)
+  int nb;   // blocks per unit
+  int n_quant;
+  int n_resid;
+  int forced_splits;
+  int cu_count;  // queried on first decode
+  bool poisoned;
+  uint32_t* k_codes;
+  uint16_t* k_scale;
+  uint16_t* k_zero;
+  uint32_t* v_codes;
+  uint16_t* v_scale;
+  uint16_t* v_zero;
+  uint16_t* k_resid;
+  uint16_t* v_resid;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kivi_status fail(kivi_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+kivi_status fail(kivi_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  size_t off[8];  // k_codes, k_scale, k_zero, v_codes, v_scale, v_zero, k_resid, v_resid
+  size_t total;
+  int cap, nb;
+};
+
+kivi_status check_config(const kivi_config* c) {
+  if (!c) return fail(KIVI_ERR_INVALID_ARG, "config is NULL");
+  if (c->batch < 1 || c->num_kv_heads < 1 || c->head_dim < 1 || c->max_tokens < 1)
+    return fail(KIVI_ERR_INVALID_ARG, "batch, num_kv_heads, head_dim and max_tokens must be >= 1");
+  if ((c->k_bits != 2 && c->k_bits != 4) || (c->v_bits != 2 && c->v_bits != 4))
+    return fail(KIVI_ERR_INVALID_ARG, "k_bits and v_bits must be 2 or 4 (got %d, %d)", c->k_bits,
+                c->v_bits);
+  if (c->group_size < 2 || c->head_dim % c->group_size != 0)
+    return fail(KIVI_ERR_INVALID_ARG, "head_dim (%d) must be a multiple of group_size (%d)",
+                c->head_dim, c->group_size);
+  if (c->residual_length < c->group_size || c->residual_length % c->group_size != 0 ||
+      c->residual_length > 1024)
+    return fail(KIVI_ERR_INVALID_ARG,
+                "residual_length (%d) must be a positive multiple of group_size, at most 1024",
+                c->residual_length);
+  if (c->kv_dtype != KIVI_F16 && c->kv_dtype != KIVI_BF16)
+    return fail(KIVI_ERR_INVALID_ARG, "kv_dtype must be KIVI_F16 or KIVI_BF16");
+  if (c->head_dim != kivi::kHeadDim || c->group_size != kivi::kGroup)
+    return fail(KIVI_ERR_UNSUPPORTED, "kernels are built for head_dim %d and group_size %d",
+                kivi::kHeadDim, kivi::kGroup);
+  if ((long long)c->batch * c->num_kv_heads > 65535)
+    return fail(KIVI_ERR_UNSUPPORTED, "batch * num_kv_heads must be at most 65535");
+  if ((long long)c->max_tokens + c->residual_length > (1LL << 30))
+    return fail(KIVI_ERR_UNSUPPORTED, "max_tokens too large");
+  return KIVI_OK;
+}
+
+Layout layout_of(const kivi_config* c) {
+  Layout L;
+  const size_t U = (size_t)c->batch * c->num_kv_heads;
+  const size_t D = c->head_dim, G = c->group_size, R = c->residual_length;
+  L.cap = (int)(((size_t)c->max_tokens + R - 1) / R * R);
+  L.nb = (int)(L.cap / G);
+  const size_t sizes[8] = {
+      U * L.cap * (D * c->k_bits / 32) * 4,  // k_codes
+      U * L.nb * D * 2,                      // k_scale
+      U * L.nb * D * 2,                      // k_zero
+      U * L.nb * D * (G * c->v_bits / 32) * 4,  // v_codes
+      U * L.nb * D * 2,                      // v_scale ([block][D/G][G] = D per block)
+      U * L.nb * D * 2,                      // v_zero
+      U * R * D * 2,                         // k_resid
+      U * R * D * 2,                         // v_resid
+  };
+  size_t o = 0;
+  for (int i = 0; i < 8; ++i) {
+    L.off[i] = o;
+    o = align_up(o + sizes[i]);
+  }
+  L.total = o;
+  return L;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+kivi::PackArgs base_pack_args(const kivi_cache* c) {
+  kivi::PackArgs a{};
+  a.k_codes = c->k_codes;
+  a.k_scale = c->k_scale;
+  a.k_zero = c->k_zero;
+  a.v_codes = c->v_codes;
+  a.v_scale = c->v_scale;
+  a.v_zero = c->v_zero;
+  a.k_resid = c->k_resid;
+  a.v_resid = c->v_resid;
+  a.cap = c->cap;
+  a.nb = c->nb;
+  a.R = c->cfg.residual_length;
+  a.units = c->cfg.batch * c->cfg.num_kv_heads;
+  return a;
+}
+
+kivi_status hip_fail(kivi_cache* c, hipError_t e, const char* what) {
+  if (c) c->poisoned = true;
+  return fail(KIVI_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Packs the full window (R tokens) into positions n_quant .. n_quant + R - 1.
+kivi_status flush_window(kivi_cache* c, hipStream_t s) {
+  kivi::PackArgs a = base_pack_args(c);
+  const int R = c->cfg.residual_length, D = c->cfg.head_dim;
+  a.k_src = c->k_resid;
+  a.v_src = c->v_resid;
+  a.src_unit_stride = (long long)R * D;
+  a.src_tok0 = 0;
+  a.nblk = R / c->cfg.group_size;
+  a.dst_blk0 = c->n_quant / c->cfg.group_size;
+  a.r_count = 0;
+  hipError_t e = kivi::launch_pack(a, c->cfg.k_bits, c->cfg.v_bits, c->cfg.kv_dtype, s);
+  if (e != hipSuccess) return hip_fail(c, e, "pack (window flush) launch");
+  c->n_quant += R;
+  c->n_resid = 0;
+  return KIVI_OK;
+}
+
+// Copies input tokens [tok0, tok0 + n) of every unit into window slots
+// [n_resid, n_resid + n).
+kivi_status copy_to_window(kivi_cache* c, const uint16_t* k, const uint16_t* v,
+                           long long unit_stride, int tok0, int n, hipStream_t s) {
+  kivi::PackArgs a = base_pack_args(c);
+  a.rk_src = k;
+  a.rv_src = v;
+  a.r_src_unit_stride = unit_stride;
+  a.r_src_tok0 = tok0;
+  a.r_count = n;
+  a.r_dst_slot0 = c->n_resid;
+  hipError_t e = kivi::launch_resid_copy(a, c->cfg.kv_dtype, s);
+  if (e != hipSuccess) return hip_fail(c, e, "window copy launch");
+  c->n_resid += n;
+  return KIVI_OK;
+}
+
+size_t workspace_bytes_for(const kivi_cache* c, int hq, int n_split) {
+  return (size_t)c->cfg.batch * hq * n_split * (c->cfg.head_dim + 2) * sizeof(float);
+}
+
+int max_items(const kivi_cache* c) {
+  return c->cap / c->cfg.group_size + c->cfg.residual_length / c->cfg.group_size;
+}
+
+}  // namespace
+
+extern "C" {
+
+kivi_status kivi_cache_bytes(const kivi_config* cfg, size_t* bytes) {
+  kivi_status s = check_config(cfg);
+  if (s != KIVI_OK) return s;
+  if (!bytes) return fail(KIVI_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = layout_of(cfg).total;
+  return KIVI_OK;
+}
+
+kivi_status kivi_cache_create(const kivi_config* cfg, void* dev_buf, size_t dev_bytes,
+                              kivi_cache** out) {
+  kivi_status s = check_config(cfg);
+  if (s != KIVI_OK) return s;
+  if (!dev_buf || !out) return fail(KIVI_ERR_INVALID_ARG, "dev_buf and out must not be NULL");
+  if (reinterpret_cast<uintptr_t>(dev_buf) % kAlign)
+    return fail(KIVI_ERR_INVALID_ARG, "dev_buf must be 256-byte aligned");
+  const Layout L = layout_of(cfg);
+  if (dev_bytes < L.total)
+    return fail(KIVI_ERR_BUFFER_TOO_SMALL, "cache needs %zu bytes, got %zu", L.total, dev_bytes);
+  kivi_cache* c = new (std::nothrow) kivi_cache();
+  if (!c) return fail(KIVI_ERR_INVALID_ARG, "host allocation failed");
+  c->cfg = *cfg;
+  c->cap = L.cap;
+  c->nb = L.nb;
+  char* base = static_cast<char*>(dev_buf);
+  c->k_codes = reinterpret_cast<uint32_t*>(base + L.off[0]);
+  c->k_scale = reinterpret_cast<uint16_t*>(base + L.off[1]);
+  c->k_zero = reinterpret_cast<uint16_t*>(base + L.off[2]);
+  c->v_codes = reinterpret_cast<uint32_t*>(base + L.off[3]);
+  c->v_scale = reinterpret_cast<uint16_t*>(base + L.off[4]);
+  c->v_zero = reinterpret_cast<uint16_t*>(base + L.off[5]);
+  c->k_resid = reinterpret_cast<uint16_t*>(base + L.off[6]);
+  c->v_resid = reinterpret_cast<uint16_t*>(base + L.off[7]);
+  *out = c;
+  return KIVI_OK;
+}
+
+kivi_status kivi_cache_destroy(kivi_cache* cache) {
+  delete cache;
+  return KIVI_OK;
+}
+
+kivi_status kivi_cache_reset(kivi_cache* cache) {
+  if (!cache) return fail(KIVI_ERR_INVALID_ARG, "cache is NULL");
+  if (cache->poisoned) return fail(KIVI_ERR_HIP, "cache handle is poisoned by an earlier HIP error");
+  cache->n_quant = 0;
+  cache->n_resid = 0;
+  return KIVI_OK;
+}
+
+kivi_status kivi_append(kivi_cache* c, const void* k, const void* v, int32_t n_tokens,
+                        void* stream) {
+  if (!c) return fail(KIVI_ERR_INVALID_ARG, "cache is NULL");
+  if (c->poisoned) return fail(KIVI_ERR_HIP, "cache handle is poisoned by an earlier HIP error");
+  if (n_tokens < 0) return fail(KIVI_ERR_INVALID_ARG, "n_tokens must be >= 0");
+  if (n_tokens == 0) return KIVI_OK;
+  if (!k || !v) return fail(KIVI_ERR_INVALID_ARG, "k and v must not be NULL");
+  if (!aligned16(k) || !aligned16(v)) return fail(KIVI_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
+  if ((long long)c->n_quant + c->n_resid + n_tokens > c->cfg.max_tokens)
+    return fail(KIVI_ERR_CAPACITY, "appending %d tokens to %d exceeds max_tokens %d", n_tokens,
+                c->n_quant + c->n_resid, c->cfg.max_tokens);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint16_t* kk = static_cast<const uint16_t*>(k);
+  const uint16_t* vv = static_cast<const uint16_t*>(v);
+  const int R = c->cfg.residual_length, G = c->cfg.group_size, D = c->cfg.head_dim;
+  const long long stride = (long long)n_tokens * D;
+  kivi_status st;
+
+  // A full window is packed before the next token enters it.
+  if (c->n_resid == R) {
+    if ((st = flush_window(c, s)) != KIVI_OK) return st;
+  }
+  int pos = 0;
+  if (c->n_resid > 0 && c->n_resid + n_tokens > R) {
+    // top the window up, then pack it: more tokens follow
+    const int fill = R - c->n_resid;
+    if ((st = copy_to_window(c, kk, vv, stride, 0, fill, s)) != KIVI_OK) return st;
+    if ((st = flush_window(c, s)) != KIVI_OK) return st;
+    pos = fill;
+  }
+  const int rem = n_tokens - pos;
+  if (c->n_resid == 0) {
+    // empty window: every full window but the last goes straight to the
+    // packed store; the last 1..R tokens enter the window (same launch)
+    const int keep = (rem - 1) % R + 1;
+    const int npack = rem - keep;
+    kivi::PackArgs a = base_pack_args(c);
+    a.k_src = kk;
+    a.v_src = vv;
+    a.src_unit_stride = stride;
+    a.src_tok0 = pos;
+    a.nblk = npack / G;
+    a.dst_blk0 = c->n_quant / G;
+    a.rk_src = kk;
+    a.rv_src = vv;
+    a.r_src_unit_stride = stride;
+    a.r_src_tok0 = pos + npack;
+    a.r_count = keep;
+    a.r_dst_slot0 = 0;
+    hipError_t e = kivi::launch_pack(a, c->cfg.k_bits, c->cfg.v_bits, c->cfg.kv_dtype, s);
+    if (e != hipSuccess) return hip_fail(c, e, "pack launch");
+    c->n_quant += npack;
+    c->n_resid = keep;
+  } else {
+    if ((st = copy_to_window(c, kk, vv, stride, pos, rem, s)) != KIVI_OK) return st;
+  }
+  return KIVI_OK;
+}
+
+kivi_status kivi_flush_residual(kivi_cache* c, void* stream) {
+  if (!c) return fail(KIVI_ERR_INVALID_ARG, "cache is NULL");
+  if (c->poisoned) return fail(KIVI_ERR_HIP, "cache handle is poisoned by an earlier HIP error");
+  if (c->n_resid != c->cfg.residual_length) return KIVI_OK;
+  return flush_window(c, static_cast<hipStream_t>(stream));
+}
+
+kivi_status kivi_decode_attn_workspace_bytes(const kivi_cache* c, int32_t num_q_heads,
+                                             size_t* bytes) {
+  if (!c || !bytes) return fail(KIVI_ERR_INVALID_ARG, "cache and bytes must not be NULL");
+  if (num_q_heads < 1 || num_q_heads % c->cfg.num_kv_heads)
+    return fail(KIVI_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                num_q_heads, c->cfg.num_kv_heads);
+  *bytes = workspace_bytes_for(c, num_q_heads, std::min(kivi::kMaxSplits, max_items(c)));
+  return KIVI_OK;
+}
+
+kivi_status kivi_decode_attn(const kivi_cache* cc, const void* q, int32_t num_q_heads,
+                             float softmax_scale, void* out, int32_t out_dtype, void* workspace,
+                             size_t ws_bytes, void* stream) {
+  kivi_cache* c = const_cast<kivi_cache*>(cc);
+  if (!c) return fail(KIVI_ERR_INVALID_ARG, "cache is NULL");
+  if (c->poisoned) return fail(KIVI_ERR_HIP, "cache handle is poisoned by an earlier HIP error");
+  if (!q || !out || !workspace) return fail(KIVI_ERR_INVALID_ARG, "q, out and workspace must not be NULL");
+  if (num_q_heads < 1 || num_q_heads % c->cfg.num_kv_heads)
+    return fail(KIVI_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                num_q_heads, c->cfg.num_kv_heads);
+  if (out_dtype != KIVI_F16 && out_dtype != KIVI_BF16 && out_dtype != KIVI_F32)
+    return fail(KIVI_ERR_INVALID_ARG, "bad out_dtype %d", out_dtype);
+  const int gq = num_q_heads / c->cfg.num_kv_heads;
+  if (gq != 1 && gq != 2 && gq != 4 && gq != 8)
+    return fail(KIVI_ERR_UNSUPPORTED, "query heads per kv head must be 1, 2, 4 or 8 (got %d)", gq);
+  const int T = c->n_quant + c->n_resid;
+  if (T < 1) return fail(KIVI_ERR_EMPTY, "decode on an empty cache");
+  size_t need = 0;
+  kivi_decode_attn_workspace_bytes(c, num_q_heads, &need);
+  if (ws_bytes < need)
+    return fail(KIVI_ERR_BUFFER_TOO_SMALL, "workspace needs %zu bytes, got %zu", need, ws_bytes);
+
+  if (c->cu_count == 0) {
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess || cus < 1) return hip_fail(c, e, "querying the compute-unit count");
+    c->cu_count = cus;
+  }
+
+  const int G = c->cfg.group_size;
+  const int units = c->cfg.batch * c->cfg.num_kv_heads;
+  const int n_items = c->n_quant / G + (c->n_resid + G - 1) / G;
+  int n_split;
+  if (c->forced_splits > 0) {
+    n_split = c->forced_splits;
+  } else {
+    const int target = 4 * c->cu_count;  // workgroups to keep every CU busy
+    n_split = (target + units - 1) / units;
+  }
+  n_split = std::max(1, std::min({n_split, n_items, kivi::kMaxSplits}));
+  const int per = (n_items + n_split - 1) / n_split;
+  n_split = (n_items + per - 1) / per;
+
+  kivi::DecodeArgs a{};
+  a.k_codes = c->k_codes;
+  a.k_scale = c->k_scale;
+  a.k_zero = c->k_zero;
+  a.v_codes = c->v_codes;
+  a.v_scale = c->v_scale;
+  a.v_zero = c->v_zero;
+  a.k_resid = c->k_resid;
+  a.v_resid = c->v_resid;
+  a.q = static_cast<const uint16_t*>(q);
+  a.out = out;
+  a.partial = static_cast<float*>(workspace);
+  a.B = c->cfg.batch;
+  a.H = c->cfg.num_kv_heads;
+  a.Hq = num_q_heads;
+  a.gq = gq;
+  a.cap = c->cap;
+  a.nb = c->nb;
+  a.R = c->cfg.residual_length;
+  a.n_quant = c->n_quant;
+  a.n_resid = c->n_resid;
+  a.n_split = n_split;
+  a.items_per_split = per;
+  a.qscale = softmax_scale * 1.4426950408889634f;  // log2(e): base-2 softmax
+  hipError_t e = kivi::launch_decode(a, c->cfg.k_bits, c->cfg.v_bits, c->cfg.kv_dtype, out_dtype,
+                                     static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(c, e, "decode launch");
+  return KIVI_OK;
+}
+
+kivi_status kivi_set_decode_splits(kivi_cache* c, int32_t n_split) {
+  if (!c) return fail(KIVI_ERR_INVALID_ARG, "cache is NULL");
+  if (n_split < 0) return fail(KIVI_ERR_INVALID_ARG, "n_split must be >= 0");
+  c->forced_splits = n_split;
+  return KIVI_OK;
+}
+
+kivi_status kivi_cache_get_view(const kivi_cache* c, kivi_cache_view* v) {
+  if (!c || !v) return fail(KIVI_ERR_INVALID_ARG, "cache and view must not be NULL");
+  v->n_quant = c->n_quant;
+  v->n_resid = c->n_resid;
+  v->capacity = c->cap;
+  v->num_blocks = c->nb;
+  v->k_codes = c->k_codes;
+  v->v_codes = c->v_codes;
+  v->k_scale = c->k_scale;
+  v->k_zero = c->k_zero;
+  v->v_scale = c->v_scale;
+  v->v_zero = c->v_zero;
+  v->k_resid = c->k_resid;
+  v->v_resid = c->v_resid;
+  return KIVI_OK;
+}
+
+const char* kivi_status_string(kivi_status s) {
+  switch (s) {
+    case KIVI_OK: return "KIVI_OK";
+    case KIVI_ERR_INVALID_ARG: return "KIVI_ERR_INVALID_ARG";
+    case KIVI_ERR_UNSUPPORTED: return "KIVI_ERR_UNSUPPORTED";
+    case KIVI_ERR_CAPACITY: return "KIVI_ERR_CAPACITY";
+    case KIVI_ERR_BUFFER_TOO_SMALL: return "KIVI_ERR_BUFFER_TOO_SMALL";
+    case KIVI_ERR_EMPTY: return "KIVI_ERR_EMPTY";
+    case KIVI_ERR_HIP: return "KIVI_ERR_HIP";
+  }
+  return "unknown kivi_status";
+}
+
+const char* kivi_last_error_message(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

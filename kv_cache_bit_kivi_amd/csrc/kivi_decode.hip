@@ -1,0 +1,281 @@
+// kivi_decode.hip - split-K decode attention over the packed cache plus the
+// residual window, and the cross-split merge.
+//
+// Method: decode attention must read the whole cache for every new token,
+// so it is bound by memory traffic, and the dequantization has to happen
+// inside the attention kernel for the smaller cache to pay off (page
+// "KV-Cache Quantization: I Ran the Experiments", "Component 1" and "Where it
+// still breaks" item 3; page "KIVI: Asymmetric 2-Bit KV Cache Quantization
+// Guide", "Production Serving and vLLM Deployment Trade-offs").  Dequantized
+// value = code * scale + zero ("Step 2" of the same guide, floating zero).
+//
+// Work split: grid (n_split, B * H).  A workgroup owns one (batch, kv head)
+// unit and a contiguous range of work items: packed blocks of 32 tokens
+// first, then 32-token chunks of the residual window.  It serves all gq query
+// heads of that kv head, keeps an online softmax in base 2 (q is pre-scaled
+// by softmax_scale * log2 e) and writes (m, l, o[D]) per query head and
+// split.  The merge kernel combines the splits exactly:
+//   M = max m_s,  out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+#include <hip/hip_bf16.h>
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include "kivi_internal.h"
+
+namespace kivi {
+namespace {
+
+constexpr int G = kGroup;
+constexpr int D = kHeadDim;
+
+template <bool BF16>
+__device__ __forceinline__ float to_f32(uint16_t h) {
+  if constexpr (BF16) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+  } else {
+    return __half2float(__ushort_as_half(h));
+  }
+}
+
+__device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
+
+template <int BITS>
+__device__ __forceinline__ uint32_t code_at(uint32_t word, int i) {
+  return (word >> (BITS * (i >> 1) + 16 * (i & 1))) & ((1u << BITS) - 1u);
+}
+
+// ---------------------------------------------------------------------------
+// Reference-structured VALU kernel: every element is dequantized in fp32 and
+// both products run on the vector ALUs.
+template <int KB, int VB, bool BF16, int GQ>
+__global__ __launch_bounds__(256) void decode_split_valu(DecodeArgs a) {
+  constexpr int PK = 32 / KB, KW = D / PK;
+  constexpr int PV = 32 / VB, VW = G / PV;
+
+  __shared__ float qs[GQ][D];
+  __shared__ float kS[D], kZ[D];
+  __shared__ float vS[4 * G], vZ[4 * G];  // [m][row]
+  __shared__ float sc[GQ][G];             // scores, then probabilities
+  __shared__ float st_m[GQ], st_l[GQ], st_a[GQ];
+  __shared__ float ored[GQ][D];
+
+  const int tid = threadIdx.x;
+  const int split = blockIdx.x;
+  const long long u = blockIdx.y;
+  const int b = static_cast<int>(u / a.H), h = static_cast<int>(u % a.H);
+
+  for (int i = tid; i < GQ * D; i += 256) {
+    const int j = i / D, d = i % D;
+    qs[j][d] = to_f32<BF16>(a.q[((long long)b * a.Hq + h * GQ + j) * D + d]) * a.qscale;
+  }
+  if (tid < GQ) {
+    st_m[tid] = -INFINITY;
+    st_l[tid] = 0.0f;
+  }
+  float o[GQ];
+#pragma unroll
+  for (int j = 0; j < GQ; ++j) o[j] = 0.0f;
+
+  const int nqb = a.n_quant / G;
+  const int n_items = nqb + (a.n_resid + G - 1) / G;
+  const int i0 = split * a.items_per_split;
+  const int i1 = min(n_items, i0 + a.items_per_split);
+  __syncthreads();
+
+  for (int it = i0; it < i1; ++it) {
+    const bool packed = it < nqb;
+    const int rc = it - nqb;  // window chunk index when !packed
+    const int ntok = packed ? G : min(G, a.n_resid - rc * G);
+    if (packed) {
+      const long long mk = (u * a.nb + it) * D;  // key meta [block][d]
+      const long long mv = (u * a.nb + it) * D;  // value meta [block][m][row], 4*32 = D entries
+      if (tid < D) {
+        kS[tid] = h2f(a.k_scale[mk + tid]);
+        vS[tid] = h2f(a.v_scale[mv + tid]);
+      } else {
+        kZ[tid - D] = h2f(a.k_zero[mk + tid - D]);
+        vZ[tid - D] = h2f(a.v_zero[mv + tid - D]);
+      }
+    }
+    __syncthreads();
+
+    // ---- scores: token t = tid / 8, channels 16*sl .. 16*sl+15
+    {
+      const int t = tid >> 3, sl = tid & 7;
+      float acc[GQ];
+#pragma unroll
+      for (int j = 0; j < GQ; ++j) acc[j] = 0.0f;
+      if (t < ntok) {
+        if (packed) {
+          const uint32_t* kw = a.k_codes + (u * a.cap + (long long)it * G + t) * KW;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int d = sl * 16 + i;
+            const uint32_t c = code_at<KB>(kw[d / PK], d % PK);
+            const float kh = fmaf(static_cast<float>(c), kS[d], kZ[d]);
+#pragma unroll
+            for (int j = 0; j < GQ; ++j) acc[j] = fmaf(qs[j][d], kh, acc[j]);
+          }
+        } else {
+          const uint16_t* kr = a.k_resid + (u * a.R + rc * G + t) * D + sl * 16;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float kh = to_f32<BF16>(kr[i]);
+#pragma unroll
+            for (int j = 0; j < GQ; ++j) acc[j] = fmaf(qs[j][sl * 16 + i], kh, acc[j]);
+          }
+        }
+      }
+#pragma unroll
+      for (int off = 1; off < 8; off <<= 1) {
+#pragma unroll
+        for (int j = 0; j < GQ; ++j) acc[j] += __shfl_xor(acc[j], off);
+      }
+      if (sl == 0) {
+#pragma unroll
+        for (int j = 0; j < GQ; ++j) sc[j][t] = (t < ntok) ? acc[j] : -INFINITY;
+      }
+    }
+    __syncthreads();
+
+    // ---- online softmax update, one wave per head
+    {
+      const int wave = tid >> 6, lane = tid & 63;
+      for (int j = wave; j < GQ; j += 4) {
+        const float s = lane < G ? sc[j][lane] : -INFINITY;
+        float mx = s;
+        for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+        const float m_old = st_m[j];
+        const float m_new = fmaxf(m_old, mx);
+        const float p = (s == -INFINITY) ? 0.0f : exp2f(s - m_new);
+        float ps = p;
+        for (int off = 32; off > 0; off >>= 1) ps += __shfl_xor(ps, off);
+        if (lane < G) sc[j][lane] = p;
+        if (lane == 0) {
+          const float alpha = (m_old == -INFINITY) ? 0.0f : exp2f(m_old - m_new);
+          st_l[j] = st_l[j] * alpha + ps;
+          st_m[j] = m_new;
+          st_a[j] = alpha;
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- values: channel d = tid % 128, rows 16*half .. 16*half+15
+    {
+      const int d = tid & (D - 1), half = tid >> 7, m = d / G;
+#pragma unroll
+      for (int j = 0; j < GQ; ++j) o[j] *= st_a[j];
+      if (packed) {
+        const uint32_t* vw = a.v_codes + ((u * a.nb + it) * D + d) * VW;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = half * 16 + i;
+          const uint32_t c = code_at<VB>(vw[row / PV], row % PV);
+          const float vh = fmaf(static_cast<float>(c), vS[m * G + row], vZ[m * G + row]);
+#pragma unroll
+          for (int j = 0; j < GQ; ++j) o[j] = fmaf(sc[j][row], vh, o[j]);
+        }
+      } else {
+        for (int i = 0; i < 16; ++i) {
+          const int row = half * 16 + i;
+          if (row < ntok) {
+            const float vh = to_f32<BF16>(a.v_resid[(u * a.R + rc * G + row) * D + d]);
+#pragma unroll
+            for (int j = 0; j < GQ; ++j) o[j] = fmaf(sc[j][row], vh, o[j]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if (tid >= D) {
+#pragma unroll
+    for (int j = 0; j < GQ; ++j) ored[j][tid - D] = o[j];
+  }
+  __syncthreads();
+  if (tid < D) {
+#pragma unroll
+    for (int j = 0; j < GQ; ++j) {
+      float* P = a.partial + (((long long)b * a.Hq + h * GQ + j) * a.n_split + split) * (D + 2);
+      P[2 + tid] = o[j] + ored[j][tid];
+      if (tid == 0) {
+        P[0] = st_m[j];
+        P[1] = st_l[j];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of the per-split partial softmax states; one workgroup per (b, j).
+template <int OUT>
+__global__ __launch_bounds__(D) void decode_merge(DecodeArgs a) {
+  const long long bj = blockIdx.x;
+  const int d = threadIdx.x;
+  const float* P = a.partial + bj * a.n_split * (D + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, P[s * (D + 2)]);
+  float L = 0.0f, O = 0.0f;
+  for (int s = 0; s < a.n_split; ++s) {
+    const float ms = P[s * (D + 2)];
+    if (ms == -INFINITY) continue;  // a split that saw no token
+    const float w = exp2f(ms - M);
+    L = fmaf(w, P[s * (D + 2) + 1], L);
+    O = fmaf(w, P[s * (D + 2) + 2 + d], O);
+  }
+  const float r = O / L;
+  if constexpr (OUT == 2) {
+    static_cast<float*>(a.out)[bj * D + d] = r;
+  } else if constexpr (OUT == 1) {
+    static_cast<__hip_bfloat16*>(a.out)[bj * D + d] = __float2bfloat16(r);
+  } else {
+    static_cast<__half*>(a.out)[bj * D + d] = __float2half_rn(r);
+  }
+}
+
+template <int KB, int VB, bool BF16, int GQ>
+hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
+  dim3 grid(a.n_split, a.B * a.H);
+  hipLaunchKernelGGL((decode_split_valu<KB, VB, BF16, GQ>), grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int KB, int VB, bool BF16>
+hipError_t launch_split_gq(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.gq) {
+    case 1: return launch_split<KB, VB, BF16, 1>(a, stream);
+    case 2: return launch_split<KB, VB, BF16, 2>(a, stream);
+    case 4: return launch_split<KB, VB, BF16, 4>(a, stream);
+    case 8: return launch_split<KB, VB, BF16, 8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, int k_bits, int v_bits, int kv_dtype,
+                         int out_dtype, hipStream_t stream) {
+  const bool bf = kv_dtype == 1;
+  hipError_t e = hipErrorInvalidValue;
+#define KIVI_SPLIT_CASE(KB, VB)                                                   \
+  if (k_bits == KB && v_bits == VB)                                               \
+    e = bf ? launch_split_gq<KB, VB, true>(a, stream) : launch_split_gq<KB, VB, false>(a, stream);
+  KIVI_SPLIT_CASE(2, 2)
+  KIVI_SPLIT_CASE(2, 4)
+  KIVI_SPLIT_CASE(4, 2)
+  KIVI_SPLIT_CASE(4, 4)
+#undef KIVI_SPLIT_CASE
+  if (e != hipSuccess) return e;
+  dim3 grid(a.B * a.Hq);
+  switch (out_dtype) {
+    case 0: hipLaunchKernelGGL(decode_merge<0>, grid, dim3(D), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL(decode_merge<1>, grid, dim3(D), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(decode_merge<2>, grid, dim3(D), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kivi

@@ -1,0 +1,74 @@
+// kivi_internal.h - argument blocks and kernel launchers shared by the host
+// state machine (kivi_api.cpp) and the HIP kernels (*.hip).  Not installed.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace kivi {
+
+constexpr int kGroup = 32;       // G: tokens per key group, channels per value group
+constexpr int kHeadDim = 128;    // D handled by the kernels
+constexpr int kMaxSplits = 256;  // upper bound on decode token splits
+
+// One launch of the pack kernel: quantize + bit-pack `nblk` blocks of G
+// tokens per unit, and copy `r_count` tokens per unit into the window.
+struct PackArgs {
+  // tokens to pack: unit u, token i is at src + u * src_unit_stride + i * D
+  const uint16_t* k_src;
+  const uint16_t* v_src;
+  long long src_unit_stride;  // elements
+  int src_tok0;               // first source token to pack
+  int nblk;                   // blocks of G tokens to pack per unit
+  int dst_blk0;               // destination block index (n_quant / G)
+  // tokens to copy into the residual window (0 when r_count == 0)
+  const uint16_t* rk_src;
+  const uint16_t* rv_src;
+  long long r_src_unit_stride;
+  int r_src_tok0;
+  int r_count;
+  int r_dst_slot0;
+  // cache arrays
+  uint32_t* k_codes;
+  uint16_t* k_scale;
+  uint16_t* k_zero;
+  uint32_t* v_codes;
+  uint16_t* v_scale;
+  uint16_t* v_zero;
+  uint16_t* k_resid;
+  uint16_t* v_resid;
+  int cap;    // token capacity per unit
+  int nb;     // blocks per unit (cap / G)
+  int R;      // window length
+  int units;  // B * H
+};
+
+// One decode-attention launch (split kernel + merge kernel).
+struct DecodeArgs {
+  const uint32_t* k_codes;
+  const uint16_t* k_scale;
+  const uint16_t* k_zero;
+  const uint32_t* v_codes;
+  const uint16_t* v_scale;
+  const uint16_t* v_zero;
+  const uint16_t* k_resid;
+  const uint16_t* v_resid;
+  const uint16_t* q;   // [B][Hq][D] kv dtype
+  void* out;           // [B][Hq][D] out dtype
+  float* partial;      // [B][Hq][n_split][D + 2] fp32 (m, l, o[D])
+  int B, H, Hq, gq;
+  int cap, nb, R;
+  int n_quant, n_resid;
+  int n_split;
+  int items_per_split;  // work items (packed blocks, then window chunks) per split
+  float qscale;         // softmax_scale * log2(e): scores in base-2 units
+};
+
+// dtype codes: 0 fp16, 1 bf16, 2 fp32 (matches kivi_dtype)
+hipError_t launch_pack(const PackArgs& a, int k_bits, int v_bits, int kv_dtype,
+                       hipStream_t stream);
+hipError_t launch_resid_copy(const PackArgs& a, int kv_dtype, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int k_bits, int v_bits, int kv_dtype,
+                         int out_dtype, hipStream_t stream);
+
+}  // namespace kivi

@@ -1,0 +1,266 @@
+"""ctypes binding of libkivi.so (include/kivi.h), same names as the C ABI.
+
+This module only marshals arguments: every step of the KIVI hot path runs in
+the HIP kernels of libkivi.so.  torch is used for device memory and streams
+in the convenience class KiviCache.  There is no fallback: if libkivi.so is
+missing or cannot be loaded, importing the binding raises.
+"""
+import ctypes
+import os
+
+# torch is imported before libkivi.so is loaded so that the process holds one
+# HIP runtime: torch bundles its own libamdhip64 (same soname), and loading
+# libkivi.so first would pull in a second copy from /opt/rocm.
+import torch  # noqa: F401
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkivi.so")
+
+KIVI_OK = 0
+KIVI_ERR_INVALID_ARG = 1
+KIVI_ERR_UNSUPPORTED = 2
+KIVI_ERR_CAPACITY = 3
+KIVI_ERR_BUFFER_TOO_SMALL = 4
+KIVI_ERR_EMPTY = 5
+KIVI_ERR_HIP = 6
+
+KIVI_F16, KIVI_BF16, KIVI_F32 = 0, 1, 2
+
+EXPORTED = (
+    "kivi_cache_bytes", "kivi_cache_create", "kivi_cache_destroy", "kivi_cache_reset",
+    "kivi_append", "kivi_flush_residual", "kivi_decode_attn_workspace_bytes",
+    "kivi_decode_attn", "kivi_set_decode_splits", "kivi_cache_get_view",
+    "kivi_status_string", "kivi_last_error_message",
+)
+
+
+class kivi_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "num_kv_heads", "head_dim", "max_tokens", "k_bits", "v_bits",
+        "group_size", "residual_length", "kv_dtype")]
+
+
+class kivi_cache_view(ctypes.Structure):
+    _fields_ = [
+        ("n_quant", ctypes.c_int32), ("n_resid", ctypes.c_int32),
+        ("capacity", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+        ("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p), ("k_zero", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p), ("v_zero", ctypes.c_void_p),
+        ("k_resid", ctypes.c_void_p), ("v_resid", ctypes.c_void_p),
+    ]
+
+
+class KiviError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{status_name(status)}: {message}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                          "(hipcc --offload-arch=gfx950); there is no CPU fallback")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    cfgp = ctypes.POINTER(kivi_config)
+    sig = {
+        "kivi_cache_bytes": ([cfgp, ctypes.POINTER(sz)], i32),
+        "kivi_cache_create": ([cfgp, vp, sz, ctypes.POINTER(vp)], i32),
+        "kivi_cache_destroy": ([vp], i32),
+        "kivi_cache_reset": ([vp], i32),
+        "kivi_append": ([vp, vp, vp, i32, vp], i32),
+        "kivi_flush_residual": ([vp, vp], i32),
+        "kivi_decode_attn_workspace_bytes": ([vp, i32, ctypes.POINTER(sz)], i32),
+        "kivi_decode_attn": ([vp, vp, i32, ctypes.c_float, vp, i32, vp, sz, vp], i32),
+        "kivi_set_decode_splits": ([vp, i32], i32),
+        "kivi_cache_get_view": ([vp, ctypes.POINTER(kivi_cache_view)], i32),
+        "kivi_status_string": ([i32], ctypes.c_char_p),
+        "kivi_last_error_message": ([], ctypes.c_char_p),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = res
+    return L
+
+
+lib = _load()
+
+
+def status_name(s):
+    return lib.kivi_status_string(s).decode()
+
+
+def last_error_message():
+    return lib.kivi_last_error_message().decode()
+
+
+def _check(status):
+    if status != KIVI_OK:
+        raise KiviError(status, last_error_message())
+
+
+# ----------------------------------------------------------- raw C entry points
+
+def kivi_cache_bytes(cfg):
+    n = ctypes.c_size_t()
+    _check(lib.kivi_cache_bytes(ctypes.byref(cfg), ctypes.byref(n)))
+    return n.value
+
+
+def kivi_cache_create(cfg, dev_ptr, dev_bytes):
+    h = ctypes.c_void_p()
+    _check(lib.kivi_cache_create(ctypes.byref(cfg), ctypes.c_void_p(dev_ptr), dev_bytes,
+                                 ctypes.byref(h)))
+    return h
+
+
+def kivi_cache_destroy(h):
+    _check(lib.kivi_cache_destroy(h))
+
+
+def kivi_cache_reset(h):
+    _check(lib.kivi_cache_reset(h))
+
+
+def kivi_append(h, k_ptr, v_ptr, n_tokens, stream):
+    _check(lib.kivi_append(h, ctypes.c_void_p(k_ptr), ctypes.c_void_p(v_ptr), n_tokens,
+                           ctypes.c_void_p(stream)))
+
+
+def kivi_flush_residual(h, stream):
+    _check(lib.kivi_flush_residual(h, ctypes.c_void_p(stream)))
+
+
+def kivi_decode_attn_workspace_bytes(h, num_q_heads):
+    n = ctypes.c_size_t()
+    _check(lib.kivi_decode_attn_workspace_bytes(h, num_q_heads, ctypes.byref(n)))
+    return n.value
+
+
+def kivi_decode_attn(h, q_ptr, num_q_heads, softmax_scale, out_ptr, out_dtype, ws_ptr,
+                     ws_bytes, stream):
+    _check(lib.kivi_decode_attn(h, ctypes.c_void_p(q_ptr), num_q_heads,
+                                float(softmax_scale), ctypes.c_void_p(out_ptr), out_dtype,
+                                ctypes.c_void_p(ws_ptr), ws_bytes, ctypes.c_void_p(stream)))
+
+
+def kivi_set_decode_splits(h, n_split):
+    _check(lib.kivi_set_decode_splits(h, n_split))
+
+
+def kivi_cache_get_view(h):
+    v = kivi_cache_view()
+    _check(lib.kivi_cache_get_view(h, ctypes.byref(v)))
+    return v
+
+
+# ------------------------------------------------------------ torch convenience
+
+class KiviCache:
+    """One layer's KIVI cache in a torch-allocated device buffer.
+
+    Tensors passed in must be contiguous device tensors: k, v [B][H][n][D] in
+    the cache's kv dtype, q [B][Hq][D].  Work is enqueued on the current torch
+    stream unless a stream is given."""
+
+    def __init__(self, batch, num_kv_heads, max_tokens, head_dim=128, k_bits=2, v_bits=2,
+                 group_size=32, residual_length=128, dtype=None, device="cuda"):
+        import torch
+        self.torch = torch
+        dtype = torch.float16 if dtype is None else dtype
+        kv = {torch.float16: KIVI_F16, torch.bfloat16: KIVI_BF16}[dtype]
+        self.cfg = kivi_config(batch, num_kv_heads, head_dim, max_tokens, k_bits, v_bits,
+                               group_size, residual_length, kv)
+        self.dtype = dtype
+        self.nbytes = kivi_cache_bytes(self.cfg)
+        self.buffer = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+        self.handle = kivi_cache_create(self.cfg, self.buffer.data_ptr(), self.nbytes)
+        self.device = self.buffer.device
+        self._ws = None
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and lib is not None:
+            lib.kivi_cache_destroy(h)
+            self.handle = None
+
+    def _stream(self, stream):
+        return (self.torch.cuda.current_stream(self.device) if stream is None else stream).cuda_stream
+
+    def _check_kv(self, t, n):
+        c = self.cfg
+        assert t.is_contiguous() and t.dtype == self.dtype and t.device == self.device
+        assert tuple(t.shape) == (c.batch, c.num_kv_heads, n, c.head_dim), t.shape
+
+    def append(self, k, v, stream=None):
+        n = k.shape[2]
+        self._check_kv(k, n)
+        self._check_kv(v, n)
+        kivi_append(self.handle, k.data_ptr(), v.data_ptr(), n, self._stream(stream))
+
+    def flush(self, stream=None):
+        kivi_flush_residual(self.handle, self._stream(stream))
+
+    def reset(self):
+        kivi_cache_reset(self.handle)
+
+    def set_splits(self, n_split):
+        kivi_set_decode_splits(self.handle, n_split)
+
+    def workspace(self, num_q_heads):
+        n = kivi_decode_attn_workspace_bytes(self.handle, num_q_heads)
+        if self._ws is None or self._ws.numel() < n:
+            self._ws = self.torch.empty(max(n, 4), dtype=self.torch.uint8, device=self.device)
+        return self._ws
+
+    def decode_attn(self, q, softmax_scale, out=None, out_dtype=None, stream=None):
+        torch = self.torch
+        c = self.cfg
+        assert q.is_contiguous() and q.dtype == self.dtype and q.device == self.device
+        B, Hq, D = q.shape
+        assert B == c.batch and D == c.head_dim
+        out_dtype = torch.float32 if out_dtype is None else out_dtype
+        if out is None:
+            out = torch.empty(B, Hq, D, dtype=out_dtype, device=self.device)
+        od = {torch.float16: KIVI_F16, torch.bfloat16: KIVI_BF16, torch.float32: KIVI_F32}[out.dtype]
+        ws = self.workspace(Hq)
+        kivi_decode_attn(self.handle, q.data_ptr(), Hq, softmax_scale, out.data_ptr(), od,
+                         ws.data_ptr(), ws.numel(), self._stream(stream))
+        return out
+
+    def view(self):
+        return kivi_cache_get_view(self.handle)
+
+    @property
+    def n_quant(self):
+        return self.view().n_quant
+
+    @property
+    def n_resid(self):
+        return self.view().n_resid
+
+    def arrays(self):
+        """Device tensors aliasing the packed-layout arrays (flat)."""
+        torch = self.torch
+        v = self.view()
+        c = self.cfg
+        U = c.batch * c.num_kv_heads
+        cap, nb, D, G, R = v.capacity, v.num_blocks, c.head_dim, c.group_size, c.residual_length
+        base = self.buffer.data_ptr()
+
+        def sub(ptr, n, dt, esize):
+            off = ptr - base
+            return self.buffer[off:off + n * esize].view(dt)
+
+        return {
+            "k_codes": sub(v.k_codes, U * cap * D * c.k_bits // 32, torch.int32, 4),
+            "k_scale": sub(v.k_scale, U * nb * D, torch.int16, 2),
+            "k_zero": sub(v.k_zero, U * nb * D, torch.int16, 2),
+            "v_codes": sub(v.v_codes, U * nb * D * G * c.v_bits // 32, torch.int32, 4),
+            "v_scale": sub(v.v_scale, U * nb * D, torch.int16, 2),
+            "v_zero": sub(v.v_zero, U * nb * D, torch.int16, 2),
+            "k_resid": sub(v.k_resid, U * R * D, torch.int16, 2),
+            "v_resid": sub(v.v_resid, U * R * D, torch.int16, 2),
+        }

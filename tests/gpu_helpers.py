@@ -1,0 +1,78 @@
+"""Helpers for the GPU parity tests: run the HIP library and the oracle on the
+same seeded inputs and compare the valid regions of the packed layout."""
+import numpy as np
+
+import oracle
+from kv_cache_bit_kivi_amd.inputs import bits16
+
+ARRAYS = ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_resid", "v_resid")
+
+
+def gpu_arrays(cache, units=None):
+    """Host copies of the GPU cache arrays, shaped per unit; optionally only
+    the listed units (copied one by one to keep host memory small)."""
+    import torch
+    c = cache.cfg
+    U = c.batch * c.num_kv_heads
+    out = {}
+    for name, t in cache.arrays().items():
+        t = t.view(U, -1)
+        if units is not None:
+            t = t[torch.as_tensor(units, device=t.device)]
+        a = t.cpu().numpy()
+        out[name] = a.view(np.uint32) if "codes" in name else a.view(np.uint16)
+    return out
+
+
+def oracle_arrays(ref):
+    U = ref.B * ref.H
+    return {n: a.reshape(U, -1) for n, a in ref.arrays().items()}
+
+
+def valid_slices(n_quant, n_resid, cap, nb, D=128, G=32):
+    """Selectors of the valid region of each per-unit flat array: packed
+    tokens [0, n_quant) and window slots [0, n_resid)."""
+    nblk = n_quant // G
+    return {
+        "k_codes": lambda a: a[:, : n_quant * (a.shape[1] // cap)],
+        "k_scale": lambda a: a[:, : nblk * D],
+        "k_zero": lambda a: a[:, : nblk * D],
+        "v_codes": lambda a: a[:, : nblk * (a.shape[1] // nb)],
+        "v_scale": lambda a: a[:, : nblk * D],
+        "v_zero": lambda a: a[:, : nblk * D],
+        "k_resid": lambda a: a[:, : n_resid * D],
+        "v_resid": lambda a: a[:, : n_resid * D],
+    }
+
+
+def assert_cache_equal(got, want, n_quant, n_resid, cap, nb):
+    sl = valid_slices(n_quant, n_resid, cap, nb)
+    for name in ARRAYS:
+        a, b = sl[name](got[name]), sl[name](want[name])
+        assert a.shape == b.shape, (name, a.shape, b.shape)
+        if not np.array_equal(a, b):
+            bad = np.argwhere(a != b)
+            u, i = bad[0]
+            raise AssertionError(f"{name}: {len(bad)} mismatches, first at unit {u} index {i}: "
+                                 f"gpu {a[u, i]:#x} oracle {b[u, i]:#x}")
+
+
+def oracle_for(x_k, x_v, w, max_tokens, n_tokens=None):
+    """Oracle cache of a workload's layer over all units (small sizes)."""
+    ref = oracle.OracleCache(w.batch, w.kv_heads, w.head_dim, max_tokens, w.k_bits, w.v_bits,
+                             w.group_size, w.residual_length,
+                             oracle.BF16 if "bfloat" in str(w.dtype) else oracle.F16)
+    kb, vb = bits16(x_k), bits16(x_v)
+    if n_tokens is not None:
+        kb, vb = kb[:, :, :n_tokens], vb[:, :, :n_tokens]
+    ref.append(kb, vb)
+    return ref
+
+
+def unit_oracle(k_unit, v_unit, w, max_tokens, dtype_code):
+    """Oracle cache of one (batch, kv head) unit; k_unit/v_unit are host
+    uint16 arrays [T][D]."""
+    ref = oracle.OracleCache(1, 1, w.head_dim, max_tokens, w.k_bits, w.v_bits, w.group_size,
+                             w.residual_length, dtype_code)
+    ref.append(k_unit[None, None], v_unit[None, None])
+    return ref

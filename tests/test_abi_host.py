@@ -1,0 +1,132 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/kivi.h declares, and rejects bad arguments before enqueuing anything
+(these paths return before any HIP call, so fake device addresses are fine)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from kv_cache_bit_kivi_amd import kivi
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "kivi.h")
+FAKE_DEV = 0x7F0000000000  # never dereferenced by these calls
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kivi_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(kivi.lib, n), n
+    assert sorted(kivi.EXPORTED) == names
+
+
+def cfg(**kw):
+    base = dict(batch=2, num_kv_heads=2, head_dim=128, max_tokens=300, k_bits=2, v_bits=2,
+                group_size=32, residual_length=128, kv_dtype=kivi.KIVI_F16)
+    base.update(kw)
+    return kivi.kivi_config(*[base[f] for f, _ in kivi.kivi_config._fields_])
+
+
+def status_of(fn, *a):
+    try:
+        fn(*a)
+    except kivi.KiviError as e:
+        return e.status
+    return kivi.KIVI_OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k_bits=3), kivi.KIVI_ERR_INVALID_ARG),
+    (dict(v_bits=8), kivi.KIVI_ERR_INVALID_ARG),
+    (dict(batch=0), kivi.KIVI_ERR_INVALID_ARG),
+    (dict(max_tokens=0), kivi.KIVI_ERR_INVALID_ARG),
+    (dict(residual_length=100), kivi.KIVI_ERR_INVALID_ARG),
+    (dict(residual_length=2048), kivi.KIVI_ERR_INVALID_ARG),
+    (dict(head_dim=100), kivi.KIVI_ERR_INVALID_ARG),
+    (dict(kv_dtype=kivi.KIVI_F32), kivi.KIVI_ERR_INVALID_ARG),
+    (dict(head_dim=64), kivi.KIVI_ERR_UNSUPPORTED),
+    (dict(group_size=64, residual_length=128), kivi.KIVI_ERR_UNSUPPORTED),
+    (dict(batch=300, num_kv_heads=300), kivi.KIVI_ERR_UNSUPPORTED),
+    (dict(), kivi.KIVI_OK),
+    (dict(k_bits=4, v_bits=2, kv_dtype=kivi.KIVI_BF16, residual_length=32), kivi.KIVI_OK),
+])
+def test_config_validation(kw, status):
+    assert status_of(kivi.kivi_cache_bytes, cfg(**kw)) == status
+    if status != kivi.KIVI_OK:
+        assert kivi.last_error_message()
+
+
+def test_cache_bytes_closed_form():
+    # codes: bits per element; metadata: two fp16 per group of 32; window: fp16
+    c = cfg(batch=8, num_kv_heads=32, max_tokens=4097)
+    cap = 4224  # 4097 rounded up to a multiple of 128
+    U, D = 256, 128
+    expect = (U * cap * D * 2 // 8 * 2  # k and v codes
+              + 4 * U * (cap // 32) * D * 2  # k/v scale and zero
+              + 2 * U * 128 * D * 2)  # windows
+    assert kivi.kivi_cache_bytes(c) == expect  # every array is a multiple of 256 B
+
+
+def _make(c=None, nbytes=None):
+    c = c or cfg()
+    n = kivi.kivi_cache_bytes(c)
+    return kivi.kivi_cache_create(c, FAKE_DEV, n if nbytes is None else nbytes)
+
+
+def test_create_errors():
+    c = cfg()
+    n = kivi.kivi_cache_bytes(c)
+    assert status_of(kivi.kivi_cache_create, c, FAKE_DEV, n - 1) == kivi.KIVI_ERR_BUFFER_TOO_SMALL
+    assert status_of(kivi.kivi_cache_create, c, FAKE_DEV + 16, n) == kivi.KIVI_ERR_INVALID_ARG
+    assert status_of(kivi.kivi_cache_create, c, 0, n) == kivi.KIVI_ERR_INVALID_ARG
+    h = _make(c)
+    v = kivi.kivi_cache_get_view(h)
+    assert (v.n_quant, v.n_resid, v.capacity, v.num_blocks) == (0, 0, 384, 12)
+    assert v.k_codes == FAKE_DEV
+    kivi.kivi_cache_destroy(h)
+
+
+def test_append_and_decode_errors_leave_state():
+    h = _make()
+    A, S = kivi.kivi_append, kivi.KIVI_OK
+    assert status_of(A, h, 0, FAKE_DEV, 5, 0) == kivi.KIVI_ERR_INVALID_ARG
+    assert status_of(A, h, FAKE_DEV + 2, FAKE_DEV, 5, 0) == kivi.KIVI_ERR_INVALID_ARG
+    assert status_of(A, h, FAKE_DEV, FAKE_DEV, -1, 0) == kivi.KIVI_ERR_INVALID_ARG
+    assert status_of(A, h, FAKE_DEV, FAKE_DEV, 301, 0) == kivi.KIVI_ERR_CAPACITY
+    assert status_of(A, h, FAKE_DEV, FAKE_DEV, 0, 0) == S  # no-op
+    v = kivi.kivi_cache_get_view(h)
+    assert (v.n_quant, v.n_resid) == (0, 0)
+    ws = kivi.kivi_decode_attn_workspace_bytes(h, 4)
+    # 2 batch * 4 q heads * min(256, 384/32 + 128/32 = 16) splits * 130 floats
+    assert ws == 2 * 4 * 16 * 130 * 4
+    D = kivi.kivi_decode_attn
+    assert status_of(D, h, FAKE_DEV, 4, 0.1, FAKE_DEV, kivi.KIVI_F32, FAKE_DEV, ws, 0) == kivi.KIVI_ERR_EMPTY
+    assert status_of(D, h, FAKE_DEV, 3, 0.1, FAKE_DEV, kivi.KIVI_F32, FAKE_DEV, ws, 0) == kivi.KIVI_ERR_INVALID_ARG
+    assert status_of(D, h, FAKE_DEV, 4, 0.1, FAKE_DEV, 7, FAKE_DEV, ws, 0) == kivi.KIVI_ERR_INVALID_ARG
+    assert status_of(D, h, FAKE_DEV, 6, 0.1, FAKE_DEV, kivi.KIVI_F32, FAKE_DEV, ws, 0) == kivi.KIVI_ERR_UNSUPPORTED
+    assert status_of(D, h, 0, 4, 0.1, FAKE_DEV, kivi.KIVI_F32, FAKE_DEV, ws, 0) == kivi.KIVI_ERR_INVALID_ARG
+    assert status_of(kivi.kivi_flush_residual, h, 0) == S  # window not full: no-op
+    assert status_of(kivi.kivi_set_decode_splits, h, -1) == kivi.KIVI_ERR_INVALID_ARG
+    kivi.kivi_cache_reset(h)
+    kivi.kivi_cache_destroy(h)
+
+
+def test_status_strings():
+    for s in range(7):
+        assert kivi.status_name(s).startswith("KIVI_")
+    assert kivi.lib.kivi_status_string(99) == b"unknown kivi_status"
+    assert kivi.lib.kivi_cache_destroy(None) == 0
+
+
+def test_null_handles():
+    n = ctypes.c_size_t()
+    assert kivi.lib.kivi_cache_bytes(None, ctypes.byref(n)) == kivi.KIVI_ERR_INVALID_ARG
+    assert kivi.lib.kivi_append(None, None, None, 1, None) == kivi.KIVI_ERR_INVALID_ARG
+    assert kivi.lib.kivi_cache_get_view(None, None) == kivi.KIVI_ERR_INVALID_ARG

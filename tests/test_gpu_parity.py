@@ -1,0 +1,203 @@
+"""GPU parity of the HIP path against the CPU oracle on the same seeded
+inputs: packed codes, metadata and window bit-exact; attention within 2e-3
+max abs error (fp32 output).  Sizes span several blocks and ragged tails."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_cache_bit_kivi_amd import kivi
+from kv_cache_bit_kivi_amd.inputs import bits16, make_layer, small
+from tests.gpu_helpers import assert_cache_equal, gpu_arrays, oracle_arrays, oracle_for
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+TOL = 2e-3
+
+#        name              B  H  Hq  T     kb vb dtype           R
+CASES = [("c0",            1, 1, 1, 1024, 2, 2, torch.float16, 128),
+         ("mha_ragged",    2, 3, 3, 300, 2, 2, torch.float16, 128),
+         ("gqa4_bf16_4b",  2, 2, 8, 333, 4, 4, torch.bfloat16, 128),
+         ("k2v4",          1, 2, 4, 257, 2, 4, torch.float16, 128),
+         ("k4v2_r32",      2, 1, 8, 200, 4, 2, torch.float16, 32),
+         ("gq8",           1, 2, 16, 700, 2, 2, torch.float16, 128),
+         ("T1",            1, 1, 2, 1, 2, 2, torch.float16, 128),
+         ("T32",           1, 1, 1, 32, 2, 2, torch.float16, 128),
+         ("T128_fullwin",  1, 2, 2, 128, 2, 2, torch.float16, 128),
+         ("T129",          1, 2, 2, 129, 2, 2, torch.bfloat16, 128)]
+IDS = [c[0] for c in CASES]
+
+
+def _setup(case, seed=0, extra=1):
+    name, B, H, Hq, T, kb, vb, dt, R = case
+    w = small(name, B, H, Hq, T, kb, vb, dt, residual_length=R)
+    x = make_layer(w, seed=seed, n_new=extra)
+    return w, x
+
+
+def _gpu_cache(w, max_tokens):
+    return kivi.KiviCache(w.batch, w.kv_heads, max_tokens, k_bits=w.k_bits, v_bits=w.v_bits,
+                          residual_length=w.residual_length, dtype=w.dtype, device=DEV)
+
+
+def _dev(t, lo, hi):
+    return t[:, :, lo:hi].contiguous().to(DEV)
+
+
+def _compare(cache, ref):
+    torch.cuda.synchronize()
+    v = cache.view()
+    assert (v.n_quant, v.n_resid) == (ref.n_quant, ref.n_resid)
+    assert_cache_equal(gpu_arrays(cache), oracle_arrays(ref), ref.n_quant, ref.n_resid,
+                       ref.capacity, ref.num_blocks)
+
+
+@pytest.mark.parametrize("case", CASES, ids=IDS)
+def test_prefix_pack_bitexact(case):
+    w, x = _setup(case)
+    T = w.tokens
+    print(f"case {case[0]}: prefix append T={T}", flush=True)
+    cache = _gpu_cache(w, T + 1)
+    cache.append(_dev(x.k, 0, T), _dev(x.v, 0, T))
+    _compare(cache, oracle_for(x.k, x.v, w, T + 1, n_tokens=T))
+
+
+@pytest.mark.parametrize("case", CASES[:6], ids=IDS[:6])
+def test_append_paths_bitexact(case):
+    # token-by-token, ragged chunks and an explicit flush on the GPU all give
+    # the oracle's bulk result
+    w, x = _setup(case, seed=1, extra=0)
+    T, R = w.tokens, w.residual_length
+    ref = oracle_for(x.k, x.v, w, T, n_tokens=T)
+    rng = np.random.default_rng(T)
+    for mode in ("single", "chunks", "flush"):
+        print(f"case {case[0]}: append mode {mode}", flush=True)
+        cache = _gpu_cache(w, T)
+        p = 0
+        while p < T:
+            if mode == "single":
+                n = 1
+            elif mode == "chunks":
+                n = int(rng.integers(1, 2 * R + 40))
+            else:
+                n = R if p + R <= T else T - p
+            n = min(n, T - p)
+            cache.append(_dev(x.k, p, p + n), _dev(x.v, p, p + n))
+            p += n
+            if mode == "flush":
+                cache.flush()
+        if mode == "flush" and T % R == 0:
+            # the final window was packed by the explicit flush; the oracle
+            # packs it too when flushed
+            ref_f = oracle_for(x.k, x.v, w, T, n_tokens=T)
+            ref_f.flush()
+            _compare(cache, ref_f)
+        else:
+            _compare(cache, ref)
+
+
+@pytest.mark.parametrize("case", CASES, ids=IDS)
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.float16])
+def test_decode_parity(case, out_dtype):
+    # prefix + one decode token (which flushes a full window), then attention
+    w, x = _setup(case, seed=2)
+    T = w.tokens
+    print(f"case {case[0]}: decode out {out_dtype}", flush=True)
+    cache = _gpu_cache(w, T + 1)
+    cache.append(_dev(x.k, 0, T), _dev(x.v, 0, T))
+    cache.append(_dev(x.k, T, T + 1), _dev(x.v, T, T + 1))
+    scale = 1.0 / np.sqrt(w.head_dim)
+    out = cache.decode_attn(x.q.contiguous().to(DEV), scale, out_dtype=out_dtype)
+    ref = oracle_for(x.k, x.v, w, T + 1)
+    _compare(cache, ref)
+    o_ref = ref.decode_attn(bits16(x.q), scale)
+    got = out.float().cpu().numpy().astype(np.float64)
+    tol = TOL if out_dtype == torch.float32 else TOL + np.abs(o_ref) * 2.0 ** -11
+    err = np.abs(got - o_ref)
+    assert np.all(err <= tol), f"max abs error {err.max():.3e}"
+
+
+@pytest.mark.parametrize("case", [CASES[0], CASES[2], CASES[5]], ids=[IDS[0], IDS[2], IDS[5]])
+def test_split_invariance_and_determinism(case):
+    w, x = _setup(case, seed=3)
+    T = w.tokens
+    cache = _gpu_cache(w, T + 1)
+    cache.append(_dev(x.k, 0, T + 1), _dev(x.v, 0, T + 1))
+    q = x.q.contiguous().to(DEV)
+    scale = 1.0 / np.sqrt(w.head_dim)
+    n_items = cache.n_quant // 32 + (cache.n_resid + 31) // 32
+    outs = {}
+    for ns in (1, 2, 7, n_items, 0):
+        print(f"case {case[0]}: n_split {ns}", flush=True)
+        cache.set_splits(ns)
+        outs[ns] = cache.decode_attn(q, scale).cpu().numpy()
+    for ns, o in outs.items():
+        assert np.max(np.abs(o - outs[1])) < 1e-5, ns
+    again = cache.decode_attn(q, scale).cpu().numpy()
+    assert np.array_equal(again, outs[0])
+
+
+def test_empty_and_errors_gpu():
+    w, x = _setup(CASES[1])
+    cache = _gpu_cache(w, 10)
+    q = x.q.contiguous().to(DEV)
+    with pytest.raises(kivi.KiviError) as e:
+        cache.decode_attn(q, 0.1)
+    assert e.value.status == kivi.KIVI_ERR_EMPTY
+    cache.append(_dev(x.k, 0, 10), _dev(x.v, 0, 10))
+    with pytest.raises(kivi.KiviError) as e:
+        cache.append(_dev(x.k, 0, 1), _dev(x.v, 0, 1))
+    assert e.value.status == kivi.KIVI_ERR_CAPACITY
+    assert (cache.n_quant, cache.n_resid) == (0, 10)
+
+
+def _hard_triples(bits, count, seed):
+    # binary16 triples (min, max, x) where multiplying by a rounded reciprocal
+    # gives another code than the division; the kernel's fast path must fall
+    # back to the exact division on them
+    rng = np.random.default_rng(seed)
+    qmax = np.float32((1 << bits) - 1)
+    n = 4_000_000
+    a = (rng.standard_normal(n) * rng.uniform(0.1, 30, n)).astype(np.float16).astype(np.float32)
+    b = (rng.standard_normal(n) * rng.uniform(0.1, 30, n)).astype(np.float16).astype(np.float32)
+    mn, mx = np.minimum(a, b), np.maximum(a, b)
+    u = rng.uniform(0, 1, n).astype(np.float32)
+    x = np.clip((mn + (mx - mn) * u).astype(np.float16).astype(np.float32), mn, mx)
+    with np.errstate(all="ignore"):
+        s = ((mx - mn) / qmax).astype(np.float32)
+        d = (x - mn).astype(np.float32)
+        recip = np.rint((d * (np.float32(1) / s).astype(np.float32)).astype(np.float32))
+        div = np.rint((d / s).astype(np.float32))
+    idx = np.nonzero((s > 0) & (recip != div))[0][:count]
+    return mn[idx], mx[idx], x[idx]
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_quantizer_hard_cases_bitexact(bits):
+    mn, mx, xv = _hard_triples(bits, 128, 17 + bits)
+    n = mn.size
+    # keys: channel d of block 0 holds [mn, mx, x, x, ...] over its 32 tokens;
+    # values: token t's channel group m holds [mn, mx, x, ...] over 32 channels
+    T = 32
+    K = np.empty((T, 128), np.float32)
+    V = np.empty((T, 128), np.float32)
+    for d in range(128):
+        i = d % n
+        K[:, d] = xv[i]
+        K[0, d], K[1, d] = mn[i], mx[i]
+    for t in range(T):
+        for m in range(4):
+            i = (t * 4 + m) % n
+            V[t, m * 32:(m + 1) * 32] = xv[i]
+            V[t, m * 32], V[t, m * 32 + 1] = mn[i], mx[i]
+    k = torch.from_numpy(K.astype(np.float16))[None, None]
+    v = torch.from_numpy(V.astype(np.float16))[None, None]
+    kk = torch.cat([k, k[:, :, :1]], 2)  # one more token flushes the block
+    vv = torch.cat([v, v[:, :, :1]], 2)
+    w = small("hard", 1, 1, 1, T + 1, bits, bits, torch.float16, residual_length=32)
+    cache = _gpu_cache(w, T + 1)
+    cache.append(kk.contiguous().to(DEV), vv.contiguous().to(DEV))
+    ref = oracle.OracleCache(1, 1, 128, T + 1, bits, bits, 32, 32)
+    ref.append(bits16(kk), bits16(vv))
+    assert ref.n_quant == 32
+    _compare(cache, ref)
