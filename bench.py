@@ -1,0 +1,256 @@
+"""Benchmark of the KIVI hot path on one MI355X.
+
+One step = one pass of the whole hot path over one layer's synthetic batch:
+  1. bulk append of the T-token prefix: quantize + bit-pack every full
+     window straight from the input, copy the last R tokens to the window
+     (one pack launch);
+  2. append of the decode token: the full window is packed (flush) and the
+     token enters the window (two launches);
+  3. split-K decode attention over the packed cache plus the window, and the
+     cross-split merge (two launches).
+The cache is reset (host counters only) at the start of each step.
+
+Default workload: Llama-2-7B-shaped MHA layer, batch 8, 32 heads, T = 4096,
+2-bit, G = 32, R = 128, fp16 (--workload c1).  `value` is the step's
+algorithmic bytes (fp16 K/V read by the pack, codes + scale/zero + window
+written and read back, q, out) divided by the step time, in GB/s.
+
+Prints one JSON line.  Inputs are resident in HBM before timing starts.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_GBPS = 8000.0  # MI355X HBM3E
+METRIC = "fused 2-bit dequant decode-attn effective HBM GB/s + % peak; pack GB/s"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="c1", choices=["c0", "c1", "c2", "c3", "c4"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cold-iters", type=int, default=20,
+                   help="decode-only iterations with the last-level cache scrubbed")
+    return p.parse_args()
+
+
+# ------------------------------------------------------------ byte accounting
+
+def algorithmic_bytes(w):
+    """Bytes the method must move per step, per phase (whole batch).
+    Codes: bits/8 per element; scale + zero: 4 bytes per group of G."""
+    U = w.batch * w.kv_heads
+    D, G, R, T = w.head_dim, w.group_size, w.residual_length, w.tokens
+    e = 2  # fp16 / bf16
+    r = (T - 1) % R + 1
+    nq = T - r
+    codes = lambda n: n * D * (w.k_bits + w.v_bits) // 8
+    meta = lambda n: (n // G) * D * 4 + n * (D // G) * 4
+    pack = 2 * T * D * e + codes(nq) + meta(nq) + 2 * r * D * e
+    flush = 2 * R * D * e + codes(R) + meta(R) + 2 * (2 * D * e)  # + the appended token
+    nq2, r2 = nq + R, 1
+    decode = codes(nq2) + meta(nq2) + 2 * r2 * D * e + w.gq * D * e + w.gq * D * 4
+    return {"pack": U * pack, "flush_append": U * flush, "decode": U * decode}
+
+
+def traffic_from_profile(kernel_src):
+    """HBM bytes per pack launch measured by rocprofv3 counters, if the summary
+    under profiles/ was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "pack_c1_counters.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    src = open(kernel_src, "rb").read()
+    if kv.get("kernel_source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------- GPU run
+
+def run(args):
+    import numpy as np
+    import torch
+
+    from kv_cache_bit_kivi_amd import kivi
+    from kv_cache_bit_kivi_amd.inputs import WORKLOADS, make_layer
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    T = w.tokens
+    scale = 1.0 / np.sqrt(w.head_dim)
+    layers = []
+    for layer in range(w.layers):
+        x = make_layer(w, seed=layer, device=dev, n_new=1)
+        layers.append(dict(
+            kp=x.k[:, :, :T].contiguous(), vp=x.v[:, :, :T].contiguous(),
+            kn=x.k[:, :, T:].contiguous(), vn=x.v[:, :, T:].contiguous(), q=x.q,
+            cache=kivi.KiviCache(w.batch, w.kv_heads, T + 1, k_bits=w.k_bits, v_bits=w.v_bits,
+                                 group_size=w.group_size, residual_length=w.residual_length,
+                                 dtype=w.dtype, device=dev),
+            out=torch.empty(w.batch, w.q_heads, w.head_dim, dtype=torch.float32, device=dev)))
+        del x
+    for L in layers:
+        L["cache"].workspace(w.q_heads)  # allocate before timing
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        # ev: four HIP events bracketing the phases of layer 0
+        for i, L in enumerate(layers):
+            rec = (lambda n: ev[n].record(stream)) if (ev is not None and i == 0) else (lambda n: None)
+            c = L["cache"]
+            c.reset()
+            rec(0)
+            c.append(L["kp"], L["vp"])
+            rec(1)
+            c.append(L["kn"], L["vn"])
+            rec(2)
+            c.decode_attn(L["q"], scale, out=L["out"])
+            rec(3)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps between two synchronizations
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+
+    # per-phase durations from HIP events on the launch stream (same steps,
+    # separate pass so the timed loop above carries no event overhead)
+    phase = {"pack": [], "flush_append": [], "decode": []}
+    for _ in range(args.steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        step(ev)
+        torch.cuda.synchronize()
+        phase["pack"].append(ev[0].elapsed_time(ev[1]) * 1e-3)
+        phase["flush_append"].append(ev[1].elapsed_time(ev[2]) * 1e-3)
+        phase["decode"].append(ev[2].elapsed_time(ev[3]) * 1e-3)
+
+    # decode alone with the 256 MB last-level cache scrubbed before each call
+    scrub = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cold = []
+    L0 = layers[0]
+    for _ in range(args.cold_iters):
+        scrub.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        L0["cache"].decode_attn(L0["q"], scale, out=L0["out"])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1) * 1e-3)
+    del scrub
+    return w, wall, phase, cold, layers
+
+
+def cpu_baseline(w, layers):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    whole batch rows of the first layer (prefix + decode token appended, then
+    decode attention for every query head of the sampled units)."""
+    import numpy as np
+
+    import oracle
+    from kv_cache_bit_kivi_amd.inputs import bits16
+
+    L = layers[0]
+    # rows of the batch so that the sample is about 10-30 s of CPU work
+    rows = {"c0": 1, "c1": 8, "c2": 1, "c3": 4, "c4": 1}[w.name]
+    units_per_row = w.kv_heads
+    if w.name in ("c2", "c4"):
+        units_per_row = {"c2": 4, "c4": 1}[w.name]  # first kv heads of row 0
+    k = bits16(L["kp"][:rows, :units_per_row])
+    v = bits16(L["vp"][:rows, :units_per_row])
+    kn = bits16(L["kn"][:rows, :units_per_row])
+    vn = bits16(L["vn"][:rows, :units_per_row])
+    q = bits16(L["q"][:rows, : units_per_row * w.gq])
+    dt = oracle.BF16 if "bfloat" in str(w.dtype) else oracle.F16
+    t0 = time.perf_counter()
+    ref = oracle.OracleCache(rows, units_per_row, w.head_dim, w.tokens + 1, w.k_bits, w.v_bits,
+                             w.group_size, w.residual_length, dt)
+    ref.append(k, v)
+    ref.append(kn, vn)
+    ref.decode_attn(q, 1.0 / np.sqrt(w.head_dim))
+    t = time.perf_counter() - t0
+    frac = rows * units_per_row / (w.batch * w.kv_heads)
+    b = sum(algorithmic_bytes(w).values()) * frac
+    return {"value": b / t / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{rows} of {w.batch} sequences x {units_per_row} of {w.kv_heads} kv heads, "
+                      f"one step of layer 0 (prefix pack, decode-token append, decode attention); "
+                      f"{t:.1f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the KIVI hot path "
+              "shards by (batch, kv head) with no exchange, so N GPUs run N independent "
+              "copies of this single-GPU measurement", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+
+    w, wall, phase, cold, layers = run(args)
+    ab = algorithmic_bytes(w)
+    layers_n = w.layers
+    step_bytes = sum(ab.values()) * layers_n
+    med = {k: float(np.median(v)) for k, v in phase.items()}
+    pack_gbps = ab["pack"] / med["pack"] / 1e9
+    src = os.path.join(ROOT, "kv_cache_bit_kivi_amd", "csrc", "kivi_pack.hip")
+    traffic = traffic_from_profile(src) if w.name == "c1" else None
+    phases = {}
+    for k in ("pack", "flush_append", "decode"):
+        g = ab[k] / med[k] / 1e9
+        phases[k] = {"bytes": ab[k], "us": med[k] * 1e6, "gbps": g, "frac": g / PEAK_GBPS}
+    cold_med = float(np.median(cold))
+    phases["decode_cold_llc"] = {"bytes": ab["decode"], "us": cold_med * 1e6,
+                                 "gbps": ab["decode"] / cold_med / 1e9,
+                                 "frac": ab["decode"] / cold_med / 1e9 / PEAK_GBPS}
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, layers)
+    res = {
+        "metric": METRIC,
+        "value": step_bytes / wall / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.description}", "batch": w.batch,
+                   "kv_heads": w.kv_heads, "q_heads": w.q_heads, "head_dim": w.head_dim,
+                   "tokens": w.tokens, "k_bits": w.k_bits, "v_bits": w.v_bits,
+                   "group_size": w.group_size, "residual_length": w.residual_length,
+                   "kv_dtype": str(w.dtype).replace("torch.", ""), "layers": w.layers},
+        "roofline": {"bound": "hbm", "kernel": "pack (prefix bulk append)",
+                     "achieved": pack_gbps, "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": pack_gbps / PEAK_GBPS, "traffic": traffic},
+        "cpu_baseline": cpu,
+        "phases": phases,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

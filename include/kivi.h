@@ -46,8 +46,9 @@
  *                                          w*Pk .. w*Pk + Pk - 1
  *   k_scale  fp16   [B*H][NB][D]           one {S} per (block, channel)
  *   k_zero   fp16   [B*H][NB][D]           one {Z} per (block, channel)
- *   v_codes  uint32 [B*H][NB][D][G / Pv]   word w of (block g, channel d)
- *                                          holds rows w*Pv .. w*Pv + Pv - 1
+ *   v_codes  uint32 [B*H][NB][G / Pv][D]   word w of (block g, channel d)
+ *                                          holds rows w*Pv .. w*Pv + Pv - 1;
+ *                                          the D words of one w are adjacent
  *   v_scale  fp16   [B*H][NB][D / G][G]    one {S} per (token, channel group)
  *   v_zero   fp16   [B*H][NB][D / G][G]
  *   k_resid, v_resid  kv_dtype [B*H][R][D] residual window, slot i holds the

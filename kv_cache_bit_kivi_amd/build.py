@@ -25,6 +25,7 @@ COMMON = [
 UNITS = {
     "kivi_pack.hip": ["-ffp-contract=off"],
     "kivi_decode.hip": [],
+    "kivi_decode_mfma.hip": [],
     "kivi_api.cpp": ["-x", "hip"],
 }
 

@@ -349,17 +349,34 @@ kivi_status kivi_decode_attn(const kivi_cache* cc, const void* q, int32_t num_q_
 
   const int G = c->cfg.group_size;
   const int units = c->cfg.batch * c->cfg.num_kv_heads;
-  const int n_items = c->n_quant / G + (c->n_resid + G - 1) / G;
-  int n_split;
-  if (c->forced_splits > 0) {
-    n_split = c->forced_splits;
+  const int nqg = c->n_quant / G;
+  const bool use_mfma = gq == 4;
+  int n_split, per = 0, n_split_packed = 0, gps = 0;
+  if (use_mfma) {
+    // one wave per split; one round of as many waves as fit in LDS on every
+    // CU, each split a multiple of 4 groups; the window gets one extra split
+    if (nqg > 0) {
+      const int waves_per_cu =
+          std::max(1, kivi::kLdsPerCu / kivi::mfma_wave_lds_bytes(c->cfg.k_bits, c->cfg.v_bits));
+      int want = c->forced_splits > 0 ? c->forced_splits
+                                      : (waves_per_cu * c->cu_count + units - 1) / units;
+      want = std::max(1, std::min({want, (nqg + 3) / 4, kivi::kMaxSplits - 1}));
+      gps = ((nqg + want - 1) / want + 3) / 4 * 4;
+      n_split_packed = (nqg + gps - 1) / gps;
+    }
+    n_split = n_split_packed + (c->n_resid > 0 ? 1 : 0);
   } else {
-    const int target = 4 * c->cu_count;  // workgroups to keep every CU busy
-    n_split = (target + units - 1) / units;
+    const int n_items = nqg + (c->n_resid + G - 1) / G;
+    if (c->forced_splits > 0) {
+      n_split = c->forced_splits;
+    } else {
+      const int target = 4 * c->cu_count;  // workgroups to keep every CU busy
+      n_split = (target + units - 1) / units;
+    }
+    n_split = std::max(1, std::min({n_split, n_items, kivi::kMaxSplits}));
+    per = (n_items + n_split - 1) / n_split;
+    n_split = (n_items + per - 1) / per;
   }
-  n_split = std::max(1, std::min({n_split, n_items, kivi::kMaxSplits}));
-  const int per = (n_items + n_split - 1) / n_split;
-  n_split = (n_items + per - 1) / per;
 
   kivi::DecodeArgs a{};
   a.k_codes = c->k_codes;
@@ -384,9 +401,11 @@ kivi_status kivi_decode_attn(const kivi_cache* cc, const void* q, int32_t num_q_
   a.n_resid = c->n_resid;
   a.n_split = n_split;
   a.items_per_split = per;
+  a.n_split_packed = n_split_packed;
+  a.groups_per_split = gps;
   a.qscale = softmax_scale * 1.4426950408889634f;  // log2(e): base-2 softmax
   hipError_t e = kivi::launch_decode(a, c->cfg.k_bits, c->cfg.v_bits, c->cfg.kv_dtype, out_dtype,
-                                     static_cast<hipStream_t>(stream));
+                                     use_mfma, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(c, e, "decode launch");
   return KIVI_OK;
 }

@@ -167,11 +167,11 @@ __global__ __launch_bounds__(256) void decode_split_valu(DecodeArgs a) {
 #pragma unroll
       for (int j = 0; j < GQ; ++j) o[j] *= st_a[j];
       if (packed) {
-        const uint32_t* vw = a.v_codes + ((u * a.nb + it) * D + d) * VW;
+        const uint32_t* vw = a.v_codes + (u * a.nb + it) * VW * D + d;  // word w at vw[w * D]
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int row = half * 16 + i;
-          const uint32_t c = code_at<VB>(vw[row / PV], row % PV);
+          const uint32_t c = code_at<VB>(vw[(row / PV) * D], row % PV);
           const float vh = fmaf(static_cast<float>(c), vS[m * G + row], vZ[m * G + row]);
 #pragma unroll
           for (int j = 0; j < GQ; ++j) o[j] = fmaf(sc[j][row], vh, o[j]);
@@ -256,9 +256,12 @@ hipError_t launch_split_gq(const DecodeArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, int k_bits, int v_bits, int kv_dtype,
-                         int out_dtype, hipStream_t stream) {
+                         int out_dtype, bool use_mfma, hipStream_t stream) {
   const bool bf = kv_dtype == 1;
   hipError_t e = hipErrorInvalidValue;
+  if (use_mfma) {
+    e = launch_decode_mfma_gq4(a, k_bits, v_bits, kv_dtype, stream);
+  } else {
 #define KIVI_SPLIT_CASE(KB, VB)                                                   \
   if (k_bits == KB && v_bits == VB)                                               \
     e = bf ? launch_split_gq<KB, VB, true>(a, stream) : launch_split_gq<KB, VB, false>(a, stream);
@@ -267,6 +270,7 @@ hipError_t launch_decode(const DecodeArgs& a, int k_bits, int v_bits, int kv_dty
   KIVI_SPLIT_CASE(4, 2)
   KIVI_SPLIT_CASE(4, 4)
 #undef KIVI_SPLIT_CASE
+  }
   if (e != hipSuccess) return e;
   dim3 grid(a.B * a.Hq);
   switch (out_dtype) {

@@ -1,0 +1,586 @@
+// kivi_decode_mfma.hip - decode attention for 4 query heads per kv head
+// (grouped-query attention), with both contractions on the matrix cores.
+//
+// Method: split-K decode attention over the packed cache (dequantized value =
+// code * scale + zero, page "KIVI: Asymmetric 2-Bit KV Cache Quantization
+// Guide", "Step 2"), fused with the dequantization as the pages require for
+// the memory saving to turn into speed (page "KV-Cache Quantization: I Ran the
+// Experiments", "Where it still breaks", item 3).
+//
+// One wave per (unit, split).  The scales are folded into the dense operand
+// of each product so that the codes themselves feed the matrix cores:
+//   q . k^_t   = sum_d (q_d S_gd) c_td + sum_d q_d Z_gd         (key group g)
+//   sum_t p_t v^_t,d = sum_t (p_t S_tm) c_td + sum_t p_t Z_tm   (value group m)
+// Codes enter v_mfma_f32_16x16x32_f16 as fp16 subnormals c * 2^-24 (exact),
+// extracted from the split-half words with one shift and one mask per pair.
+// The folded operands q*S and p*S are carried as fp16 hi + lo pairs (two
+// MFMAs), which keeps them within 2^-22 relative; the zero-point term of the keys
+// (one dot product per group and head) runs on the vector ALUs.
+//
+// Key side: four consecutive 32-token groups at once, block-diagonal: A rows
+// are 4 tokens of each of the 4 groups, B columns are the 4 heads x 4 groups,
+// so each lane builds distinct q*S values; the 16 diagonal lanes hold the
+// scores.  Value side, per group: A = codes of 16 channels x 32 tokens, B
+// columns = 4 heads x 4 channel groups m (p*S differs per m); each output
+// lane keeps the column of its own channel group.
+//
+// The residual window (at most R tokens, stored in kv dtype) is handled by an
+// extra wave per unit on the vector ALUs in fp32.
+#include <hip/hip_bf16.h>
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include "kivi_internal.h"
+
+namespace kivi {
+namespace {
+
+constexpr int G = kGroup;
+constexpr int D = kHeadDim;
+constexpr int GQ = 4;
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <bool BF16>
+__device__ __forceinline__ float to_f32(uint16_t h) {
+  if constexpr (BF16) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+  } else {
+    return __half2float(__ushort_as_half(h));
+  }
+}
+
+__device__ __forceinline__ f32x4 mfma(const half8_t& a, const half8_t& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ half8_t as_h8(const u32x4& v) { return __builtin_bit_cast(half8_t, v); }
+
+__device__ __forceinline__ float lo_half(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xffffu)));
+}
+__device__ __forceinline__ float hi_half(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+}
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// Two binary32 values to an fp16 pair, each rounded to nearest-even (one
+// v_cvt_pk_f16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pk_rne(float x0, float x1) {
+  const half2_t h = {static_cast<_Float16>(x0), static_cast<_Float16>(x1)};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// x - (fp16 half `sel` of h), one v_fma_mix_f32 (the half is read as fp16).
+template <int SEL>
+__device__ __forceinline__ float minus_half(uint32_t h, float x) {
+  float r;
+  if constexpr (SEL == 0) {
+    asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x));
+  } else {
+    asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x));
+  }
+  return r;
+}
+
+// x * (fp16 half `sel` of h), one v_fma_mix_f32 (exact product, one rounding).
+template <int SEL>
+__device__ __forceinline__ float times_half(float x, uint32_t h) {
+  float r;
+  if constexpr (SEL == 0) {
+    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[0,0,0] op_sel_hi:[0,1,0]" : "=v"(r) : "v"(x), "v"(h));
+  } else {
+    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "=v"(r) : "v"(x), "v"(h));
+  }
+  return r;
+}
+
+// (x0, x1) -> fp16 pairs hi (nearest) and lo (nearest of the exact remainder
+// x - hi): hi + lo = x within 2^-22 relative.  |x| must stay below 65504.
+__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  hi = pk_rne(x0, x1);
+  lo = pk_rne(minus_half<0>(hi, x0), minus_half<1>(hi, x1));
+}
+
+// Code extraction.  Two codes of a split-half word sit at bits [s, s+b) and
+// [16+s, 16+s+b); masking the word (or the word shifted right by 8) in place
+// leaves them as fp16 subnormals c * 2^(t-24), t = 0, 2, 4, 6 (2-bit) or
+// t = 0, 4 (4-bit), exactly.  The dense operand of the product carries the
+// compensating 2^(F-t) (F = 6 for 2-bit, 4 for 4-bit), so every product is
+// c * x * 2^(F-24) and results are rescaled by 2^(24-F) once.
+template <int BITS>
+struct CodeScale {
+  static constexpr int F = BITS == 2 ? 6 : 4;
+  // log2 of the factor for pair e' (codes 2e', 2e'+1 of an 8-code run)
+  static constexpr int lf(int ep) { return BITS == 2 ? F - 2 * ep : F - 4 * (ep & 1); }
+};
+
+// 8 codes (one run of 8 consecutive entries: positions 8*hb .. 8*hb+7 of
+// word x) as four fp16 pairs c * 2^(t-24).
+template <int BITS>
+__device__ __forceinline__ half8_t codes8(uint32_t x, bool high_byte) {
+  u32x4 r;
+  if constexpr (BITS == 2) {
+    const uint32_t y = high_byte ? (x >> 8) : x;
+    r[0] = y & 0x00030003u;
+    r[1] = y & 0x000C000Cu;
+    r[2] = y & 0x00300030u;
+    r[3] = y & 0x00C000C0u;
+  } else {
+    const uint32_t y = x >> 8;
+    r[0] = x & 0x000F000Fu;
+    r[1] = x & 0x00F000F0u;
+    r[2] = y & 0x000F000Fu;
+    r[3] = y & 0x00F000F0u;
+  }
+  return as_h8(r);
+}
+
+__device__ __forceinline__ float xor_max(float v, int m) { return fmaxf(v, __shfl_xor(v, m)); }
+__device__ __forceinline__ float xor_sum(float v, int m) { return v + __shfl_xor(v, m); }
+
+// ---------------------------------------------------------------------------
+// Residual window on the vector ALUs (one wave, fp32), written as the last
+// split of the unit.
+template <bool BF16>
+__device__ void window_wave(const DecodeArgs& a, long long u, int b, int kvh, int split,
+                            float (*qsh)[D], float (*psh)[G]) {
+  const int lane = threadIdx.x;
+  for (int i = lane; i < GQ * D; i += 64) {
+    qsh[i / D][i % D] =
+        to_f32<BF16>(a.q[((long long)b * a.Hq + kvh * GQ + i / D) * D + i % D]) * a.qscale;
+  }
+  __syncthreads();
+  float m[GQ], l[GQ], o[GQ][2];
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.0f;
+    o[h][0] = o[h][1] = 0.0f;
+  }
+  const int half = lane >> 5;
+  for (int c0 = 0; c0 < a.n_resid; c0 += G) {
+    const int t = c0 + (lane & 31);
+    const bool live = t < a.n_resid;
+    float acc[GQ] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (live) {
+      const uint16_t* kr = a.k_resid + (u * a.R + t) * D + 64 * half;
+      for (int d0 = 0; d0 < 64; d0 += 8) {
+        const uint4 kv = *reinterpret_cast<const uint4*>(kr + d0);
+        const uint32_t ww[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float kx = to_f32<BF16>(static_cast<uint16_t>(ww[i >> 1] >> (16 * (i & 1))));
+#pragma unroll
+          for (int h = 0; h < GQ; ++h) acc[h] = fmaf(qsh[h][64 * half + d0 + i], kx, acc[h]);
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+      float s = acc[h] + __shfl_xor(acc[h], 32);
+      s = live ? s : -INFINITY;
+      float mx = s;
+      for (int off = 16; off > 0; off >>= 1) mx = xor_max(mx, off);
+      const float m_new = fmaxf(m[h], mx);
+      const float alpha = (m[h] == -INFINITY) ? 0.0f : exp2f(m[h] - m_new);
+      const float p = live ? exp2f(s - m_new) : 0.0f;
+      float ps = p;
+      for (int off = 16; off > 0; off >>= 1) ps = xor_sum(ps, off);
+      l[h] = l[h] * alpha + ps;
+      m[h] = m_new;
+      o[h][0] *= alpha;
+      o[h][1] *= alpha;
+      if (lane < G) psh[h][lane] = p;
+    }
+    __syncthreads();
+    const int n = min(G, a.n_resid - c0);
+    for (int tt = 0; tt < n; ++tt) {
+      const uint32_t vv = *reinterpret_cast<const uint32_t*>(a.v_resid + (u * a.R + c0 + tt) * D + 2 * lane);
+      const float v0 = to_f32<BF16>(static_cast<uint16_t>(vv & 0xffffu));
+      const float v1 = to_f32<BF16>(static_cast<uint16_t>(vv >> 16));
+#pragma unroll
+      for (int h = 0; h < GQ; ++h) {
+        o[h][0] = fmaf(psh[h][tt], v0, o[h][0]);
+        o[h][1] = fmaf(psh[h][tt], v1, o[h][1]);
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+    float* P = a.partial + (((long long)b * a.Hq + kvh * GQ + h) * a.n_split + split) * (D + 2);
+    P[2 + 2 * lane] = o[h][0];
+    P[3 + 2 * lane] = o[h][1];
+    if (lane == 0) {
+      P[0] = m[h];
+      P[1] = l[h];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// LDS stage of one step (4 consecutive packed groups of one unit), filled by
+// direct global->LDS loads (64 lanes x 16 bytes = 1 KiB per instruction):
+//   K codes  4 groups x 32 rows x D*KB/8 bytes (token-major rows); each group
+//            padded by 64 bytes so the 4 groups fall on different banks
+//   K scale  4 x D fp16, K zero 4 x D fp16
+//   V codes  4 groups x (G/PV words) x D words
+//   V scale  4 x 4 x G fp16, V zero likewise
+template <int KB, int VB>
+struct Stage {
+  static constexpr int kRow = D * KB / 8;              // bytes per key row
+  static constexpr int kGroup = G * kRow;              // 1 or 2 KiB
+  static constexpr int kGroupPad = kGroup + 64;
+  static constexpr int kCodes = 4 * kGroupPad;
+  static constexpr int kMeta = 4 * D * 2;              // 1 KiB
+  static constexpr int vGroup = (G * VB / 32) * D * 4; // 1 or 2 KiB
+  static constexpr int vCodes = 4 * vGroup;
+  static constexpr int vMeta = 4 * D * 2;              // 1 KiB
+  static constexpr int offKS = kCodes, offKZ = offKS + kMeta;
+  static constexpr int offVC = offKZ + kMeta;
+  static constexpr int offVS = offVC + vCodes, offVZ = offVS + vMeta;
+  static constexpr int bytes = offVZ + vMeta;
+  static constexpr int loads = (4 * kGroup + 4 * kMeta + vCodes) / 1024;  // DMA instructions
+};
+static_assert(2 * Stage<2, 2>::bytes + 4 * GQ * G * 4 == mfma_wave_lds_bytes(2, 2), "lds");
+static_assert(2 * Stage<4, 4>::bytes + 4 * GQ * G * 4 == mfma_wave_lds_bytes(4, 4), "lds");
+static_assert(2 * Stage<2, 4>::bytes + 4 * GQ * G * 4 == mfma_wave_lds_bytes(2, 4), "lds");
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef const __attribute__((address_space(1))) void glb_void_t;
+
+__device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
+  // address-space conversions need C-style casts
+  __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)lds_dst, 16, 0, 0);
+}
+
+// Issues the loads of groups [g0, g0 + ns) into `dst`.  Every call issues
+// Stage::loads instructions; slots of missing groups re-read the last valid
+// group so that every address stays inside the cache.
+template <int KB, int VB>
+__device__ __forceinline__ void issue_stage(const DecodeArgs& a, long long u, int g0, int ns,
+                                            uint8_t* dst) {
+  using S = Stage<KB, VB>;
+  const int lane = threadIdx.x;
+  const int glast = g0 + ns - 1;
+  const uint8_t* kc = reinterpret_cast<const uint8_t*>(a.k_codes) + (u * a.cap) * (long long)S::kRow;
+#pragma unroll
+  for (int gi = 0; gi < 4; ++gi) {
+    const long long g = min(g0 + gi, glast);
+#pragma unroll
+    for (int j = 0; j < S::kGroup / 1024; ++j)
+      dma16(kc + g * S::kGroup + j * 1024 + lane * 16, dst + gi * S::kGroupPad + j * 1024);
+  }
+  {
+    // per-group metadata, 256 bytes per group for each of the four arrays
+    const int g = min(g0 + (lane >> 4), glast);
+    const long long km = (u * a.nb + g) * D * 2 + (lane & 15) * 16;  // bytes
+    dma16(reinterpret_cast<const uint8_t*>(a.k_scale) + km, dst + S::offKS);
+    dma16(reinterpret_cast<const uint8_t*>(a.k_zero) + km, dst + S::offKZ);
+    dma16(reinterpret_cast<const uint8_t*>(a.v_scale) + km, dst + S::offVS);
+    dma16(reinterpret_cast<const uint8_t*>(a.v_zero) + km, dst + S::offVZ);
+  }
+  const uint8_t* vc = reinterpret_cast<const uint8_t*>(a.v_codes) + (u * a.nb) * (long long)S::vGroup;
+#pragma unroll
+  for (int gi = 0; gi < 4; ++gi) {
+    const long long g = min(g0 + gi, glast);
+#pragma unroll
+    for (int j = 0; j < S::vGroup / 1024; ++j)
+      dma16(vc + g * S::vGroup + j * 1024 + lane * 16, dst + S::offVC + gi * S::vGroup + j * 1024);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N == 0 || N == 12 || N == 16 || N == 20, "stage sizes");
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Orders LDS traffic inside the (single-wave) workgroup without waiting for
+// the stage loads still in flight: LDS operations of one wave execute in
+// order, so completing this wave's own LDS operations is enough.
+// (__syncthreads would also wait for every outstanding global load.)
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+template <int KB, int VB, bool BF16>
+__global__ __launch_bounds__(64) void decode_mfma_gq4(DecodeArgs a) {
+  // one wave per workgroup: the in-loop synchronisation relies on it
+  using S = Stage<KB, VB>;
+  using KS = CodeScale<KB>;
+  using VS = CodeScale<VB>;
+  constexpr int KL = KB;                    // key words per lane (32 channels)
+  constexpr int VW = G * VB / 32;           // value words per (group, channel)
+  __shared__ __align__(16) uint8_t smem[2 * S::bytes + 4 * GQ * G * 4];
+  float (*pl)[GQ][G] = reinterpret_cast<float (*)[GQ][G]>(smem + 2 * S::bytes);  // [stream][head][row]
+
+  const int lane = threadIdx.x;
+  const int lc = lane & 15, lk = lane >> 4;
+  const int split = blockIdx.x;
+  const long long u = blockIdx.y;
+  const int b = static_cast<int>(u / a.H), kvh = static_cast<int>(u % a.H);
+
+  if (split >= a.n_split_packed) {
+    window_wave<BF16>(a, u, b, kvh, split, reinterpret_cast<float (*)[D]>(smem), pl[0]);
+    return;
+  }
+
+  const int nqg = a.n_quant / G;
+  const int gb = split * a.groups_per_split;
+  const int ge = min(nqg, gb + a.groups_per_split);
+  const int n_steps = (ge - gb + 3) / 4;
+  if (n_steps > 0) issue_stage<KB, VB>(a, u, gb, min(4, ge - gb), smem);
+
+  const int hq = lc >> 2;  // head of this lane's B / C columns
+  // q' = q * softmax_scale * log2(e) for head hq, channels 32*lk .. 32*lk+31,
+  // times the code-position factor 2^lf of the key codes it multiplies
+  float qf[32];
+  {
+    const uint16_t* qp = a.q + ((long long)b * a.Hq + kvh * GQ + hq) * D + 32 * lk;
+#pragma unroll
+    for (int i = 0; i < 32; i += 8) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qp + i);
+      const uint32_t ww[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int ep = (j >> 1);  // pair index inside the run of 8 channels
+        qf[i + j] = to_f32<BF16>(static_cast<uint16_t>(ww[j >> 1] >> (16 * (j & 1)))) * a.qscale *
+                    static_cast<float>(1 << KS::lf(ep));
+      }
+    }
+  }
+  constexpr float k_unscale = static_cast<float>(1 << (24 - KS::F));  // product -> score
+  constexpr float v_unscale = static_cast<float>(1 << (24 - VS::F));  // product -> output
+
+  const bool diag = (lc & 3) == lk;  // lane holds scores / outputs (stream or m = lk)
+  float m_run = -INFINITY;           // running max of head hq (base 2)
+  float lcls[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // sum of scaled p, per pair class e'
+  float zcls[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // sum of scaled p * Z, per pair class e'
+  f32x4 o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (int step = 0; step < n_steps; ++step) {
+    const int g0 = gb + 4 * step;
+    const int ns = min(4, ge - g0);
+    uint8_t* cur = smem + (step & 1) * S::bytes;
+    if (step + 1 < n_steps) {
+      issue_stage<KB, VB>(a, u, g0 + 4, min(4, ge - g0 - 4), smem + ((step + 1) & 1) * S::bytes);
+      wait_vm<S::loads>();  // this step's stage has landed, the next is in flight
+    } else {
+      wait_vm<0>();
+    }
+    wave_lds_sync();
+
+    // ------------------------------------------------------------- key side
+    const int ga = lc >> 2;  // stream of this lane's A row
+    const int gc = lc & 3;   // stream of this lane's B column
+    const u32x4* sBp = reinterpret_cast<const u32x4*>(cur + S::offKS + gc * D * 2 + 64 * lk);
+    const u32x4* zBp = reinterpret_cast<const u32x4*>(cur + S::offKZ + gc * D * 2 + 64 * lk);
+    // B = q' * S (hi, lo) for head hq and group g0 + gc; zero-point term
+    // sum_d q'_d Z_d of the same (head, group) on the vector ALUs
+    half8_t bh[4], bl[4];
+    float bcls[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // per pair class: q' carries 2^lf(e)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 sB = sBp[c], zB = zBp[c];
+      u32x4 h4, l4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float q0 = qf[8 * c + 2 * e], q1 = qf[8 * c + 2 * e + 1];
+        uint32_t hi, lo;
+        split_pair(times_half<0>(q0, sB[e]), times_half<1>(q1, sB[e]), hi, lo);
+        h4[e] = hi;
+        l4[e] = lo;
+        bcls[e] = fmaf(q0, lo_half(zB[e]), bcls[e]);
+        bcls[e] = fmaf(q1, hi_half(zB[e]), bcls[e]);
+      }
+      bh[c] = as_h8(h4);
+      bl[c] = as_h8(l4);
+    }
+    float bias = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bias = fmaf(bcls[e], 1.0f / static_cast<float>(1 << KS::lf(e)), bias);
+    bias = xor_sum(bias, 16);
+    bias = xor_sum(bias, 32);  // all 128 channels: head hq, group g0 + (lc & 3)
+    // scores of 8 steps x 4 rows; row 4*ga + r = token 4*s + r of stream ga
+    const uint8_t* krow = cur + ga * S::kGroupPad + (lc & 3) * S::kRow + 4 * KL * lk;
+    uint32_t kw[8][KL];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      if constexpr (KL == 2) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(krow + 4 * s * S::kRow);
+        kw[s][0] = v[0];
+        kw[s][1] = v[1];
+      } else {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(krow + 4 * s * S::kRow);
+#pragma unroll
+        for (int i = 0; i < KL; ++i) kw[s][i] = v[i];
+      }
+    }
+    // 8 independent accumulators; consecutive MFMAs never depend on each other
+    f32x4 sc[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) sc[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      half8_t ak[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        ak[s] = (KB == 2) ? codes8<2>(kw[s][c >> 1], c & 1) : codes8<4>(kw[s][c & (KL - 1)], false);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) sc[s] = mfma(ak[s], bh[c], sc[s]);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) sc[s] = mfma(ak[s], bl[c], sc[s]);
+    }
+    // ------------------------------------------------------------- softmax
+    const bool live = diag && lk < ns;  // this lane's stream is lk
+    float mx = -INFINITY;
+    if (live) {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          sc[s][r] = fmaf(sc[s][r], k_unscale, bias);
+          mx = fmaxf(mx, sc[s][r]);
+        }
+      }
+    }
+    mx = xor_max(mx, 1);
+    mx = xor_max(mx, 2);
+    mx = xor_max(mx, 16);
+    mx = xor_max(mx, 32);  // max over the 4 streams and 32 rows of head hq
+    const float m_new = fmaxf(m_run, mx);
+    if (__any(m_new > m_run)) {
+      const float alpha = (m_run == -INFINITY) ? 0.0f : fast_exp2(m_run - m_new);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] *= alpha;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        zcls[e] *= alpha;
+        lcls[e] *= alpha;
+      }
+      m_run = m_new;
+    }
+    if (live) {
+      // p scaled by the value-code factor of its row position: row t sits in
+      // pair class e'(t) = (t mod 8) / 2 of its run of 8
+      float mc[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mc[e] = m_run - static_cast<float>(VS::lf(e));
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        f32x4 p;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int ep = 2 * (s & 1) + (r >> 1);
+          p[r] = fast_exp2(sc[s][r] - mc[ep]);
+          lcls[ep] += p[r];
+        }
+        *reinterpret_cast<f32x4*>(&pl[lk][hq][4 * s]) = p;
+      }
+    }
+    wave_lds_sync();
+    // ------------------------------------------------------------- value side
+    const int mcol = lc & 3;  // channel group of this lane's B column
+    for (int gs = 0; gs < ns; ++gs) {
+      const int w = (VB == 2) ? (lk >> 1) : lk;
+      const u32x4* vp = reinterpret_cast<const u32x4*>(cur + S::offVC + gs * S::vGroup + (w * D + 8 * lc) * 4);
+      const u32x4 v0 = vp[0], v1 = vp[1];
+      const int vmo = ((gs * 4 + mcol) * G + 8 * lk) * 2;
+      const u32x4 vs = *reinterpret_cast<const u32x4*>(cur + S::offVS + vmo);
+      const u32x4 vz = *reinterpret_cast<const u32x4*>(cur + S::offVZ + vmo);
+      const f32x4 p0 = *reinterpret_cast<const f32x4*>(&pl[gs][hq][8 * lk]);
+      const f32x4 p1 = *reinterpret_cast<const f32x4*>(&pl[gs][hq][8 * lk + 4]);
+      const float p[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+      u32x4 h4, l4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint32_t hi, lo;
+        split_pair(times_half<0>(p[2 * e], vs[e]), times_half<1>(p[2 * e + 1], vs[e]), hi, lo);
+        h4[e] = hi;
+        l4[e] = lo;
+        zcls[e] = fmaf(p[2 * e], lo_half(vz[e]), zcls[e]);
+        zcls[e] = fmaf(p[2 * e + 1], hi_half(vz[e]), zcls[e]);
+      }
+      const half8_t bph = as_h8(h4), bpl = as_h8(l4);
+      const uint32_t vc[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      half8_t av[8];
+#pragma unroll
+      for (int be = 0; be < 8; ++be)
+        av[be] = (VB == 2) ? codes8<2>(vc[be], lk & 1) : codes8<4>(vc[be], false);
+#pragma unroll
+      for (int be = 0; be < 8; ++be) o[be] = mfma(av[be], bph, o[be]);
+#pragma unroll
+      for (int be = 0; be < 8; ++be) o[be] = mfma(av[be], bpl, o[be]);
+    }
+    wave_lds_sync();  // the stage and pl are rewritten by the next steps
+  }
+
+  // ------------------------------------------------------------- partials
+  float l = 0.0f, z = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float f = 1.0f / static_cast<float>(1 << VS::lf(e));
+    l = fmaf(lcls[e], f, l);
+    z = fmaf(zcls[e], f, z);
+  }
+  l = xor_sum(l, 1);
+  l = xor_sum(l, 2);
+  l = xor_sum(l, 16);
+  l = xor_sum(l, 32);
+  z = xor_sum(z, 16);
+  z = xor_sum(z, 32);  // sum over the 4 row chunks: head hq, channel group lc & 3
+  float* P = a.partial + (((long long)b * a.Hq + kvh * GQ + hq) * a.n_split + split) * (D + 2);
+  if (lk == 0 && (lc & 3) == 0) {
+    P[0] = m_run;
+    P[1] = l;
+  }
+  if (diag) {
+    // rows 4*lk + r of channel block be = channel 32*lk + 8*r + be
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      f32x4 x0, x1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x0[i] = fmaf(o[i][r], v_unscale, z);
+        x1[i] = fmaf(o[4 + i][r], v_unscale, z);
+      }
+      *reinterpret_cast<f32x4*>(P + 2 + 32 * lk + 8 * r) = x0;
+      *reinterpret_cast<f32x4*>(P + 2 + 32 * lk + 8 * r + 4) = x1;
+    }
+  }
+}
+
+template <int KB, int VB, bool BF16>
+hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
+  dim3 grid(a.n_split, a.B * a.H);
+  hipLaunchKernelGGL((decode_mfma_gq4<KB, VB, BF16>), grid, dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma_gq4(const DecodeArgs& a, int k_bits, int v_bits, int kv_dtype,
+                                  hipStream_t stream) {
+  const bool bf = kv_dtype == 1;
+#define KIVI_MFMA_CASE(KB, VB) \
+  if (k_bits == KB && v_bits == VB) return bf ? launch_t<KB, VB, true>(a, stream) : launch_t<KB, VB, false>(a, stream);
+  KIVI_MFMA_CASE(2, 2)
+  KIVI_MFMA_CASE(2, 4)
+  KIVI_MFMA_CASE(4, 2)
+  KIVI_MFMA_CASE(4, 4)
+#undef KIVI_MFMA_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kivi

@@ -60,15 +60,30 @@ struct DecodeArgs {
   int cap, nb, R;
   int n_quant, n_resid;
   int n_split;
-  int items_per_split;  // work items (packed blocks, then window chunks) per split
+  int items_per_split;  // vector kernel: work items (blocks, then window chunks) per split
+  int n_split_packed;   // matrix kernel: splits over packed groups (window split follows)
+  int groups_per_split; // matrix kernel: packed groups per split, a multiple of 4
   float qscale;         // softmax_scale * log2(e): scores in base-2 units
 };
+
+// LDS bytes of one wave of the matrix-core decode kernel: two stages of 4
+// packed groups (codes + scale/zero of keys and values) plus the 4 x 4 x 32
+// fp32 probabilities.  Bounds the number of resident waves per CU.
+constexpr int mfma_wave_lds_bytes(int k_bits, int v_bits) {
+  return 2 * (4 * (kGroup * kHeadDim * k_bits / 8 + 64) + 4 * kHeadDim * 2 * 4 +
+              4 * kGroup * v_bits / 32 * kHeadDim * 4) +
+         4 * 4 * kGroup * 4;
+}
+constexpr int kLdsPerCu = 160 * 1024;  // MI355X (gfx950)
 
 // dtype codes: 0 fp16, 1 bf16, 2 fp32 (matches kivi_dtype)
 hipError_t launch_pack(const PackArgs& a, int k_bits, int v_bits, int kv_dtype,
                        hipStream_t stream);
 hipError_t launch_resid_copy(const PackArgs& a, int kv_dtype, hipStream_t stream);
+// use_mfma selects the matrix-core kernel (4 query heads per kv head).
 hipError_t launch_decode(const DecodeArgs& a, int k_bits, int v_bits, int kv_dtype,
-                         int out_dtype, hipStream_t stream);
+                         int out_dtype, bool use_mfma, hipStream_t stream);
+hipError_t launch_decode_mfma_gq4(const DecodeArgs& a, int k_bits, int v_bits, int kv_dtype,
+                                  hipStream_t stream);
 
 }  // namespace kivi

@@ -179,9 +179,10 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
     a.k_codes[(u * a.cap + (long long)gblk * G + t) * KW + w] = word;
   }
 
-  // ---- value code words: channel d, word w holds rows w*PV .. w*PV+PV-1
+  // ---- value code words: channel d, word w holds rows w*PV .. w*PV+PV-1;
+  // word-major, so consecutive threads write consecutive channels
   for (int wi = tid; wi < D * VW; wi += 256) {
-    const int d = wi / VW, w = wi % VW;
+    const int w = wi / D, d = wi % D;
     const int m = d / G;
     uint32_t word = 0;
 #pragma unroll
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
       const uint32_t c = quant_code<QV>(to_f32<BF16>(vt[t * RS + d]), vmn[si], vsc[si], vrc[si]);
       word |= c << code_shift<VB>(i);
     }
-    a.v_codes[((u * a.nb + gblk) * D + d) * VW + w] = word;
+    a.v_codes[((u * a.nb + gblk) * VW + w) * D + d] = word;
   }
 }
 

@@ -223,13 +223,14 @@ static void pack_window_unit(oracle_cache* c, size_t u) {
         c->k_codes[(u * c->cap + t) * kw + w] = word;
       }
     }
-    /* value words: channel d of block g, word w holds rows w*Pv .. w*Pv+Pv-1 */
-    for (int d = 0; d < D; ++d) {
-      for (size_t w = 0; w < vw; ++w) {
+    /* value words: word w of channel d in block g holds rows w*Pv ..
+     * w*Pv+Pv-1; the D words of one w are stored next to each other */
+    for (size_t w = 0; w < vw; ++w) {
+      for (int d = 0; d < D; ++d) {
         uint32_t word = 0;
         for (int i = 0; i < Pv; ++i)
           word |= (uint32_t)vc[(w * Pv + i) * D + d] << code_bit_offset(i, c->vb);
-        c->v_codes[((u * c->nb + g) * D + d) * vw + w] = word;
+        c->v_codes[((u * c->nb + g) * vw + w) * D + d] = word;
       }
     }
   }
@@ -287,7 +288,7 @@ static double value_hat(const oracle_cache* c, size_t u, int t, int d) {
   const size_t vw = v_words_per_channel(c);
   const int Pv = 32 / c->vb, G = c->G;
   const int g = t / G, j = t % G;
-  uint32_t word = c->v_codes[((u * c->nb + g) * c->D + d) * vw + j / Pv];
+  uint32_t word = c->v_codes[((u * c->nb + g) * vw + j / Pv) * c->D + d];
   int code = (word >> code_bit_offset(j % Pv, c->vb)) & ((1 << c->vb) - 1);
   size_t mi = ((u * c->nb + g) * (c->D / G) + d / G) * G + j;
   return oracle_dequant(code, c->v_scale[mi], c->v_zero[mi]);

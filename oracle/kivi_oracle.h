@@ -58,7 +58,7 @@ typedef struct {
   uint32_t* k_codes; /* [B*H][cap][D*kb/32] */
   uint16_t* k_scale; /* [B*H][nb][D] */
   uint16_t* k_zero;  /* [B*H][nb][D] */
-  uint32_t* v_codes; /* [B*H][nb][D][G*vb/32] */
+  uint32_t* v_codes; /* [B*H][nb][G*vb/32][D] */
   uint16_t* v_scale; /* [B*H][nb][D/G][G] */
   uint16_t* v_zero;  /* [B*H][nb][D/G][G] */
   uint16_t* k_resid; /* [B*H][R][D] */

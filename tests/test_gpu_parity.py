@@ -24,7 +24,14 @@ CASES = [("c0",            1, 1, 1, 1024, 2, 2, torch.float16, 128),
          ("T1",            1, 1, 2, 1, 2, 2, torch.float16, 128),
          ("T32",           1, 1, 1, 32, 2, 2, torch.float16, 128),
          ("T128_fullwin",  1, 2, 2, 128, 2, 2, torch.float16, 128),
-         ("T129",          1, 2, 2, 129, 2, 2, torch.bfloat16, 128)]
+         ("T129",          1, 2, 2, 129, 2, 2, torch.bfloat16, 128),
+         # 4 query heads per kv head: the matrix-core kernel
+         ("gq4_f16",       2, 2, 8, 1000, 2, 2, torch.float16, 128),
+         ("gq4_k2v4",      1, 2, 8, 700, 2, 4, torch.float16, 128),
+         ("gq4_k4v2_r32",  1, 1, 4, 333, 4, 2, torch.float16, 32),
+         ("gq4_window",    1, 2, 8, 100, 2, 2, torch.bfloat16, 128),
+         ("gq4_T129",      2, 1, 4, 129, 2, 2, torch.float16, 128),
+         ("gq4_long",      1, 1, 4, 4096, 2, 2, torch.float16, 128)]
 IDS = [c[0] for c in CASES]
 
 
@@ -117,7 +124,11 @@ def test_decode_parity(case, out_dtype):
     assert np.all(err <= tol), f"max abs error {err.max():.3e}"
 
 
-@pytest.mark.parametrize("case", [CASES[0], CASES[2], CASES[5]], ids=[IDS[0], IDS[2], IDS[5]])
+SPLIT_CASES = [c for c in CASES if c[0] in ("c0", "gqa4_bf16_4b", "gq8", "gq4_f16", "gq4_k4v2_r32",
+                                             "gq4_long")]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
 def test_split_invariance_and_determinism(case):
     w, x = _setup(case, seed=3)
     T = w.tokens
@@ -131,8 +142,16 @@ def test_split_invariance_and_determinism(case):
         print(f"case {case[0]}: n_split {ns}", flush=True)
         cache.set_splits(ns)
         outs[ns] = cache.decode_attn(q, scale).cpu().numpy()
+    # fp32 vector path: only summation order changes (1e-5).  Matrix path
+    # (4 query heads per kv head): q*S and p*S are rounded to fp16 hi + lo
+    # (2^-22 relative each) relative to each split's own maximum, so changing
+    # the split count moves scores by up to 2^-22 * sum_d |c q' S| (about
+    # 3e-5 on these inputs) and outputs by that times max |v| (about 30).
+    tol = 1e-4 if w.gq == 4 else 1e-5
     for ns, o in outs.items():
-        assert np.max(np.abs(o - outs[1])) < 1e-5, ns
+        d = np.max(np.abs(o - outs[1]))
+        print(f"case {case[0]}: n_split {ns} vs 1: max abs diff {d:.2e}", flush=True)
+        assert d < tol, (ns, d)
     again = cache.decode_attn(q, scale).cpu().numpy()
     assert np.array_equal(again, outs[0])
 

@@ -39,11 +39,11 @@ def test_layout_2bit_hand_words(oracle_mod):
     for t in range(32):
         assert kc[t].tolist() == [expect[t % 4]] * 2, t
     # Values: word w of (block 0, channel d) holds rows 16w..16w+15 with the
-    # same order; the value group of token t over channels gives codes
+    # same order, stored word-major ([word][channel]); the value group of token t over channels gives codes
     # (t + d) mod 4 as well, so channel d shows the token-d word pattern.
-    vc = c.array("v_codes").reshape(-1, 32, 2)[0]  # [channel][word]
+    vc = c.array("v_codes").reshape(-1, 2, 32)[0]  # [word][channel]
     for d in range(32):
-        assert vc[d].tolist() == [expect[d % 4]] * 2, d
+        assert vc[:, d].tolist() == [expect[d % 4]] * 2, d
     assert set(c.array("k_scale")[:32].tolist()) == {0x3C00}
     assert set(c.array("k_zero")[:32].tolist()) == {0}
     assert set(c.array("v_scale")[:32].tolist()) == {0x3C00}
@@ -63,9 +63,9 @@ def test_layout_4bit_hand_words(oracle_mod):
     assert kc[0].tolist() == [0x75316420, 0xFDB9ECA8, 0x75316420, 0xFDB9ECA8]
     # token 8: codes (8 + d) mod 16 -> word 0 holds 8..15, word 1 holds 0..7
     assert kc[8].tolist() == [0xFDB9ECA8, 0x75316420, 0xFDB9ECA8, 0x75316420]
-    vc = c.array("v_codes").reshape(-1, 32, 4)[0]
-    assert vc[0].tolist() == [0x75316420, 0xFDB9ECA8, 0x75316420, 0xFDB9ECA8]
-    assert vc[8].tolist() == [0xFDB9ECA8, 0x75316420, 0xFDB9ECA8, 0x75316420]
+    vc = c.array("v_codes").reshape(-1, 4, 32)[0]  # [word][channel]
+    assert vc[:, 0].tolist() == [0x75316420, 0xFDB9ECA8, 0x75316420, 0xFDB9ECA8]
+    assert vc[:, 8].tolist() == [0xFDB9ECA8, 0x75316420, 0xFDB9ECA8, 0x75316420]
 
 
 def _random_bits(rng, shape):
