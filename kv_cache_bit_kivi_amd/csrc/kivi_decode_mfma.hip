@@ -140,6 +140,39 @@ __device__ __forceinline__ half8_t codes8(uint32_t x, bool high_byte) {
   return as_h8(r);
 }
 
+// Cross-lane exchanges on the vector ALUs (no LDS round trip):
+//   lane ^ 1, lane ^ 2 : DPP quad permutations
+//   lane ^ 16          : v_permlane16_swap (rows 0<->1, 2<->3)
+//   lane ^ 32          : v_permlane32_swap (halves)
+// Each returns the value of the partner lane combined with the own value.
+template <int M>
+__device__ __forceinline__ float partner(float v) {
+  const uint32_t x = __float_as_uint(v);
+  if constexpr (M == 1) {
+    return __uint_as_float(__builtin_amdgcn_update_dpp(0u, x, 0xB1, 0xF, 0xF, false));  // [1,0,3,2]
+  } else if constexpr (M == 2) {
+    return __uint_as_float(__builtin_amdgcn_update_dpp(0u, x, 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
+  } else {
+    static_assert(M == 16 || M == 32, "exchange");
+    return 0.0f;
+  }
+}
+// reduce over lanes l ^ 16 / l ^ 32: after the swap the two results hold
+// (own, partner) in some order on every lane, so op(r0, r1) is the pair op
+template <int M>
+__device__ __forceinline__ float swap_max(float v) {
+  const uint32_t x = __float_as_uint(v);
+  auto r = (M == 16) ? __builtin_amdgcn_permlane16_swap(x, x, false, false)
+                     : __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+template <int M>
+__device__ __forceinline__ float swap_sum(float v) {
+  const uint32_t x = __float_as_uint(v);
+  auto r = (M == 16) ? __builtin_amdgcn_permlane16_swap(x, x, false, false)
+                     : __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 __device__ __forceinline__ float xor_max(float v, int m) { return fmaxf(v, __shfl_xor(v, m)); }
 __device__ __forceinline__ float xor_sum(float v, int m) { return v + __shfl_xor(v, m); }
 
@@ -224,32 +257,36 @@ __device__ void window_wave(const DecodeArgs& a, long long u, int b, int kvh, in
 }
 
 // ---------------------------------------------------------------------------
-// LDS stage of one step (4 consecutive packed groups of one unit), filled by
-// direct global->LDS loads (64 lanes x 16 bytes = 1 KiB per instruction):
+// LDS stages of one step (4 consecutive packed groups of one unit), filled
+// by direct global->LDS loads (64 lanes x 16 bytes = 1 KiB per instruction).
+// Key stage (double-buffered):
 //   K codes  4 groups x 32 rows x D*KB/8 bytes (token-major rows); each group
 //            padded by 64 bytes so the 4 groups fall on different banks
 //   K scale  4 x D fp16, K zero 4 x D fp16
+// Value stage (single-buffered, refilled right after the value side of the
+// previous step):
 //   V codes  4 groups x (G/PV words) x D words
 //   V scale  4 x 4 x G fp16, V zero likewise
+// The probabilities of a step (4 x 4 x 32 fp32) reuse the key-code area of
+// the current key stage, whose codes are consumed before the softmax.
 template <int KB, int VB>
 struct Stage {
   static constexpr int kRow = D * KB / 8;              // bytes per key row
   static constexpr int kGroup = G * kRow;              // 1 or 2 KiB
   static constexpr int kGroupPad = kGroup + 64;
-  static constexpr int kCodes = 4 * kGroupPad;
-  static constexpr int kMeta = 4 * D * 2;              // 1 KiB
+  static constexpr int offKS = 4 * kGroupPad, offKZ = offKS + 4 * D * 2;
+  static constexpr int kBytes = offKZ + 4 * D * 2;
   static constexpr int vGroup = (G * VB / 32) * D * 4; // 1 or 2 KiB
-  static constexpr int vCodes = 4 * vGroup;
-  static constexpr int vMeta = 4 * D * 2;              // 1 KiB
-  static constexpr int offKS = kCodes, offKZ = offKS + kMeta;
-  static constexpr int offVC = offKZ + kMeta;
-  static constexpr int offVS = offVC + vCodes, offVZ = offVS + vMeta;
-  static constexpr int bytes = offVZ + vMeta;
-  static constexpr int loads = (4 * kGroup + 4 * kMeta + vCodes) / 1024;  // DMA instructions
+  static constexpr int offVS = 4 * vGroup, offVZ = offVS + 4 * D * 2;
+  static constexpr int vBytes = offVZ + 4 * D * 2;
+  static constexpr int bytes = 2 * kBytes + vBytes;    // LDS per wave
+  static constexpr int kLoads = (4 * kGroup + 2 * 4 * D * 2) / 1024;  // DMA instructions
+  static constexpr int vLoads = (4 * vGroup + 2 * 4 * D * 2) / 1024;
+  static_assert(4 * kGroup >= GQ * GQ * G * 4, "probabilities fit in the key-code area");
 };
-static_assert(2 * Stage<2, 2>::bytes + 4 * GQ * G * 4 == mfma_wave_lds_bytes(2, 2), "lds");
-static_assert(2 * Stage<4, 4>::bytes + 4 * GQ * G * 4 == mfma_wave_lds_bytes(4, 4), "lds");
-static_assert(2 * Stage<2, 4>::bytes + 4 * GQ * G * 4 == mfma_wave_lds_bytes(2, 4), "lds");
+static_assert(Stage<2, 2>::bytes == mfma_wave_lds_bytes(2, 2), "lds");
+static_assert(Stage<4, 4>::bytes == mfma_wave_lds_bytes(4, 4), "lds");
+static_assert(Stage<2, 4>::bytes == mfma_wave_lds_bytes(2, 4), "lds");
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef const __attribute__((address_space(1))) void glb_void_t;
@@ -259,12 +296,11 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
   __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)lds_dst, 16, 0, 0);
 }
 
-// Issues the loads of groups [g0, g0 + ns) into `dst`.  Every call issues
-// Stage::loads instructions; slots of missing groups re-read the last valid
-// group so that every address stays inside the cache.
+// Key stage of groups [g0, g0 + ns): Stage::kLoads instructions; slots of
+// missing groups re-read the last valid group (addresses stay inside).
 template <int KB, int VB>
-__device__ __forceinline__ void issue_stage(const DecodeArgs& a, long long u, int g0, int ns,
-                                            uint8_t* dst) {
+__device__ __forceinline__ void issue_kstage(const DecodeArgs& a, long long u, int g0, int ns,
+                                             uint8_t* dst) {
   using S = Stage<KB, VB>;
   const int lane = threadIdx.x;
   const int glast = g0 + ns - 1;
@@ -276,32 +312,38 @@ __device__ __forceinline__ void issue_stage(const DecodeArgs& a, long long u, in
     for (int j = 0; j < S::kGroup / 1024; ++j)
       dma16(kc + g * S::kGroup + j * 1024 + lane * 16, dst + gi * S::kGroupPad + j * 1024);
   }
-  {
-    // per-group metadata, 256 bytes per group for each of the four arrays
-    const int g = min(g0 + (lane >> 4), glast);
-    const long long km = (u * a.nb + g) * D * 2 + (lane & 15) * 16;  // bytes
-    dma16(reinterpret_cast<const uint8_t*>(a.k_scale) + km, dst + S::offKS);
-    dma16(reinterpret_cast<const uint8_t*>(a.k_zero) + km, dst + S::offKZ);
-    dma16(reinterpret_cast<const uint8_t*>(a.v_scale) + km, dst + S::offVS);
-    dma16(reinterpret_cast<const uint8_t*>(a.v_zero) + km, dst + S::offVZ);
-  }
+  const int g = min(g0 + (lane >> 4), glast);  // 256 bytes per group and array
+  const long long km = (u * a.nb + g) * D * 2 + (lane & 15) * 16;
+  dma16(reinterpret_cast<const uint8_t*>(a.k_scale) + km, dst + S::offKS);
+  dma16(reinterpret_cast<const uint8_t*>(a.k_zero) + km, dst + S::offKZ);
+}
+
+// Value stage of groups [g0, g0 + ns): Stage::vLoads instructions.
+template <int KB, int VB>
+__device__ __forceinline__ void issue_vstage(const DecodeArgs& a, long long u, int g0, int ns,
+                                             uint8_t* dst) {
+  using S = Stage<KB, VB>;
+  const int lane = threadIdx.x;
+  const int glast = g0 + ns - 1;
   const uint8_t* vc = reinterpret_cast<const uint8_t*>(a.v_codes) + (u * a.nb) * (long long)S::vGroup;
 #pragma unroll
   for (int gi = 0; gi < 4; ++gi) {
     const long long g = min(g0 + gi, glast);
 #pragma unroll
     for (int j = 0; j < S::vGroup / 1024; ++j)
-      dma16(vc + g * S::vGroup + j * 1024 + lane * 16, dst + S::offVC + gi * S::vGroup + j * 1024);
+      dma16(vc + g * S::vGroup + j * 1024 + lane * 16, dst + gi * S::vGroup + j * 1024);
   }
+  const int g = min(g0 + (lane >> 4), glast);
+  const long long vm = (u * a.nb + g) * D * 2 + (lane & 15) * 16;
+  dma16(reinterpret_cast<const uint8_t*>(a.v_scale) + vm, dst + S::offVS);
+  dma16(reinterpret_cast<const uint8_t*>(a.v_zero) + vm, dst + S::offVZ);
 }
 
+// Waits until at most N vector-memory operations of this wave are in flight
+// (loads complete in issue order).
 template <int N>
 __device__ __forceinline__ void wait_vm() {
-  static_assert(N == 0 || N == 12 || N == 16 || N == 20, "stage sizes");
-  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-  else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -319,9 +361,8 @@ __global__ __launch_bounds__(64) void decode_mfma_gq4(DecodeArgs a) {
   using KS = CodeScale<KB>;
   using VS = CodeScale<VB>;
   constexpr int KL = KB;                    // key words per lane (32 channels)
-  constexpr int VW = G * VB / 32;           // value words per (group, channel)
-  __shared__ __align__(16) uint8_t smem[2 * S::bytes + 4 * GQ * G * 4];
-  float (*pl)[GQ][G] = reinterpret_cast<float (*)[GQ][G]>(smem + 2 * S::bytes);  // [stream][head][row]
+  __shared__ __align__(16) uint8_t smem[S::bytes];
+  uint8_t* const vstage = smem + 2 * S::kBytes;
 
   const int lane = threadIdx.x;
   const int lc = lane & 15, lk = lane >> 4;
@@ -330,7 +371,8 @@ __global__ __launch_bounds__(64) void decode_mfma_gq4(DecodeArgs a) {
   const int b = static_cast<int>(u / a.H), kvh = static_cast<int>(u % a.H);
 
   if (split >= a.n_split_packed) {
-    window_wave<BF16>(a, u, b, kvh, split, reinterpret_cast<float (*)[D]>(smem), pl[0]);
+    window_wave<BF16>(a, u, b, kvh, split, reinterpret_cast<float (*)[D]>(smem),
+                      reinterpret_cast<float (*)[G]>(smem + GQ * D * 4));
     return;
   }
 
@@ -338,7 +380,10 @@ __global__ __launch_bounds__(64) void decode_mfma_gq4(DecodeArgs a) {
   const int gb = split * a.groups_per_split;
   const int ge = min(nqg, gb + a.groups_per_split);
   const int n_steps = (ge - gb + 3) / 4;
-  if (n_steps > 0) issue_stage<KB, VB>(a, u, gb, min(4, ge - gb), smem);
+  if (n_steps > 0) {
+    issue_kstage<KB, VB>(a, u, gb, min(4, ge - gb), smem);
+    issue_vstage<KB, VB>(a, u, gb, min(4, ge - gb), vstage);
+  }
 
   const int hq = lc >> 2;  // head of this lane's B / C columns
   // q' = q * softmax_scale * log2(e) for head hq, channels 32*lk .. 32*lk+31,
@@ -372,12 +417,14 @@ __global__ __launch_bounds__(64) void decode_mfma_gq4(DecodeArgs a) {
   for (int step = 0; step < n_steps; ++step) {
     const int g0 = gb + 4 * step;
     const int ns = min(4, ge - g0);
-    uint8_t* cur = smem + (step & 1) * S::bytes;
-    if (step + 1 < n_steps) {
-      issue_stage<KB, VB>(a, u, g0 + 4, min(4, ge - g0 - 4), smem + ((step + 1) & 1) * S::bytes);
-      wait_vm<S::loads>();  // this step's stage has landed, the next is in flight
+    uint8_t* cur = smem + (step & 1) * S::kBytes;
+    const bool more = step + 1 < n_steps;
+    // in flight, oldest first: K(step), V(step) [, K(step+1)]
+    if (more) {
+      issue_kstage<KB, VB>(a, u, g0 + 4, min(4, ge - g0 - 4), smem + ((step + 1) & 1) * S::kBytes);
+      wait_vm<S::vLoads + S::kLoads>();
     } else {
-      wait_vm<0>();
+      wait_vm<S::vLoads>();
     }
     wave_lds_sync();
 
@@ -386,6 +433,20 @@ __global__ __launch_bounds__(64) void decode_mfma_gq4(DecodeArgs a) {
     const int gc = lc & 3;   // stream of this lane's B column
     const u32x4* sBp = reinterpret_cast<const u32x4*>(cur + S::offKS + gc * D * 2 + 64 * lk);
     const u32x4* zBp = reinterpret_cast<const u32x4*>(cur + S::offKZ + gc * D * 2 + 64 * lk);
+    const uint8_t* krow = cur + ga * S::kGroupPad + (lc & 3) * S::kRow + 4 * KL * lk;
+    uint32_t kw[8][KL];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      if constexpr (KL == 2) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(krow + 4 * s * S::kRow);
+        kw[s][0] = v[0];
+        kw[s][1] = v[1];
+      } else {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(krow + 4 * s * S::kRow);
+#pragma unroll
+        for (int i = 0; i < KL; ++i) kw[s][i] = v[i];
+      }
+    }
     // B = q' * S (hi, lo) for head hq and group g0 + gc; zero-point term
     // sum_d q'_d Z_d of the same (head, group) on the vector ALUs
     half8_t bh[4], bl[4];
@@ -410,27 +471,14 @@ __global__ __launch_bounds__(64) void decode_mfma_gq4(DecodeArgs a) {
     float bias = 0.0f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) bias = fmaf(bcls[e], 1.0f / static_cast<float>(1 << KS::lf(e)), bias);
-    bias = xor_sum(bias, 16);
-    bias = xor_sum(bias, 32);  // all 128 channels: head hq, group g0 + (lc & 3)
-    // scores of 8 steps x 4 rows; row 4*ga + r = token 4*s + r of stream ga
-    const uint8_t* krow = cur + ga * S::kGroupPad + (lc & 3) * S::kRow + 4 * KL * lk;
-    uint32_t kw[8][KL];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      if constexpr (KL == 2) {
-        const u32x2 v = *reinterpret_cast<const u32x2*>(krow + 4 * s * S::kRow);
-        kw[s][0] = v[0];
-        kw[s][1] = v[1];
-      } else {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(krow + 4 * s * S::kRow);
-#pragma unroll
-        for (int i = 0; i < KL; ++i) kw[s][i] = v[i];
-      }
-    }
-    // 8 independent accumulators; consecutive MFMAs never depend on each other
+    bias = swap_sum<16>(bias);
+    bias = swap_sum<32>(bias);  // all 128 channels: head hq, group g0 + (lc & 3)
+    // accumulators start at the zero-point term, in product units
+    const float b0 = bias * (1.0f / k_unscale);
+    const f32x4 binit = f32x4{b0, b0, b0, b0};
+    // scores of 8 steps x 4 rows; row 4*ga + r = token 4*s + r of stream ga;
+    // 8 independent accumulators so consecutive MFMAs never depend
     f32x4 sc[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) sc[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       half8_t ak[8];
@@ -438,7 +486,7 @@ __global__ __launch_bounds__(64) void decode_mfma_gq4(DecodeArgs a) {
       for (int s = 0; s < 8; ++s)
         ak[s] = (KB == 2) ? codes8<2>(kw[s][c >> 1], c & 1) : codes8<4>(kw[s][c & (KL - 1)], false);
 #pragma unroll
-      for (int s = 0; s < 8; ++s) sc[s] = mfma(ak[s], bh[c], sc[s]);
+      for (int s = 0; s < 8; ++s) sc[s] = mfma(ak[s], bh[c], c == 0 ? binit : sc[s]);
 #pragma unroll
       for (int s = 0; s < 8; ++s) sc[s] = mfma(ak[s], bl[c], sc[s]);
     }
@@ -447,18 +495,13 @@ __global__ __launch_bounds__(64) void decode_mfma_gq4(DecodeArgs a) {
     float mx = -INFINITY;
     if (live) {
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          sc[s][r] = fmaf(sc[s][r], k_unscale, bias);
-          mx = fmaxf(mx, sc[s][r]);
-        }
-      }
+      for (int s = 0; s < 8; ++s) mx = fmaxf(mx, fmaxf(fmaxf(sc[s][0], sc[s][1]), fmaxf(sc[s][2], sc[s][3])));
+      mx *= k_unscale;
     }
-    mx = xor_max(mx, 1);
-    mx = xor_max(mx, 2);
-    mx = xor_max(mx, 16);
-    mx = xor_max(mx, 32);  // max over the 4 streams and 32 rows of head hq
+    mx = fmaxf(mx, partner<1>(mx));
+    mx = fmaxf(mx, partner<2>(mx));
+    mx = swap_max<16>(mx);
+    mx = swap_max<32>(mx);  // max over the 4 streams and 32 rows of head hq
     const float m_new = fmaxf(m_run, mx);
     if (__any(m_new > m_run)) {
       const float alpha = (m_run == -INFINITY) ? 0.0f : fast_exp2(m_run - m_new);
@@ -471,34 +514,42 @@ __global__ __launch_bounds__(64) void decode_mfma_gq4(DecodeArgs a) {
       }
       m_run = m_new;
     }
+    float(*pl)[GQ][G] = reinterpret_cast<float (*)[GQ][G]>(cur);  // [stream][head][row]
+    wave_lds_sync();  // key codes of this stage fully read before pl overwrites them
     if (live) {
       // p scaled by the value-code factor of its row position: row t sits in
       // pair class e'(t) = (t mod 8) / 2 of its run of 8
-      float mc[4];
+      float nmc[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) mc[e] = m_run - static_cast<float>(VS::lf(e));
+      for (int e = 0; e < 4; ++e) nmc[e] = static_cast<float>(VS::lf(e)) - m_run;
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         f32x4 p;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int ep = 2 * (s & 1) + (r >> 1);
-          p[r] = fast_exp2(sc[s][r] - mc[ep]);
+          p[r] = fast_exp2(fmaf(sc[s][r], k_unscale, nmc[ep]));
           lcls[ep] += p[r];
         }
         *reinterpret_cast<f32x4*>(&pl[lk][hq][4 * s]) = p;
       }
+    }
+    // the value stage of this step was issued before K(step+1)
+    if (more) {
+      wait_vm<S::kLoads>();
+    } else {
+      wait_vm<0>();
     }
     wave_lds_sync();
     // ------------------------------------------------------------- value side
     const int mcol = lc & 3;  // channel group of this lane's B column
     for (int gs = 0; gs < ns; ++gs) {
       const int w = (VB == 2) ? (lk >> 1) : lk;
-      const u32x4* vp = reinterpret_cast<const u32x4*>(cur + S::offVC + gs * S::vGroup + (w * D + 8 * lc) * 4);
+      const u32x4* vp = reinterpret_cast<const u32x4*>(vstage + gs * S::vGroup + (w * D + 8 * lc) * 4);
       const u32x4 v0 = vp[0], v1 = vp[1];
       const int vmo = ((gs * 4 + mcol) * G + 8 * lk) * 2;
-      const u32x4 vs = *reinterpret_cast<const u32x4*>(cur + S::offVS + vmo);
-      const u32x4 vz = *reinterpret_cast<const u32x4*>(cur + S::offVZ + vmo);
+      const u32x4 vs = *reinterpret_cast<const u32x4*>(vstage + S::offVS + vmo);
+      const u32x4 vz = *reinterpret_cast<const u32x4*>(vstage + S::offVZ + vmo);
       const f32x4 p0 = *reinterpret_cast<const f32x4*>(&pl[gs][hq][8 * lk]);
       const f32x4 p1 = *reinterpret_cast<const f32x4*>(&pl[gs][hq][8 * lk + 4]);
       const float p[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
@@ -523,7 +574,8 @@ __global__ __launch_bounds__(64) void decode_mfma_gq4(DecodeArgs a) {
 #pragma unroll
       for (int be = 0; be < 8; ++be) o[be] = mfma(av[be], bpl, o[be]);
     }
-    wave_lds_sync();  // the stage and pl are rewritten by the next steps
+    wave_lds_sync();  // value stage and pl fully read
+    if (more) issue_vstage<KB, VB>(a, u, g0 + 4, min(4, ge - g0 - 4), vstage);
   }
 
   // ------------------------------------------------------------- partials
@@ -534,12 +586,12 @@ __global__ __launch_bounds__(64) void decode_mfma_gq4(DecodeArgs a) {
     l = fmaf(lcls[e], f, l);
     z = fmaf(zcls[e], f, z);
   }
-  l = xor_sum(l, 1);
-  l = xor_sum(l, 2);
-  l = xor_sum(l, 16);
-  l = xor_sum(l, 32);
-  z = xor_sum(z, 16);
-  z = xor_sum(z, 32);  // sum over the 4 row chunks: head hq, channel group lc & 3
+  l = l + partner<1>(l);
+  l = l + partner<2>(l);
+  l = swap_sum<16>(l);
+  l = swap_sum<32>(l);
+  z = swap_sum<16>(z);
+  z = swap_sum<32>(z);  // sum over the 4 row chunks: head hq, channel group lc & 3
   float* P = a.partial + (((long long)b * a.Hq + kvh * GQ + hq) * a.n_split + split) * (D + 2);
   if (lk == 0 && (lc & 3) == 0) {
     P[0] = m_run;

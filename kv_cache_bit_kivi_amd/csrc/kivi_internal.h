@@ -66,13 +66,12 @@ struct DecodeArgs {
   float qscale;         // softmax_scale * log2(e): scores in base-2 units
 };
 
-// LDS bytes of one wave of the matrix-core decode kernel: two stages of 4
-// packed groups (codes + scale/zero of keys and values) plus the 4 x 4 x 32
-// fp32 probabilities.  Bounds the number of resident waves per CU.
+// LDS bytes of one wave of the matrix-core decode kernel: two key stages
+// (codes + scale/zero of 4 groups) and one value stage.  Bounds the number
+// of resident waves per CU.
 constexpr int mfma_wave_lds_bytes(int k_bits, int v_bits) {
-  return 2 * (4 * (kGroup * kHeadDim * k_bits / 8 + 64) + 4 * kHeadDim * 2 * 4 +
-              4 * kGroup * v_bits / 32 * kHeadDim * 4) +
-         4 * 4 * kGroup * 4;
+  return 2 * (4 * (kGroup * kHeadDim * k_bits / 8 + 64) + 2 * 4 * kHeadDim * 2) +
+         (4 * kGroup * v_bits / 32 * kHeadDim * 4 + 2 * 4 * kHeadDim * 2);
 }
 constexpr int kLdsPerCu = 160 * 1024;  // MI355X (gfx950)
 
