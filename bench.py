@@ -40,6 +40,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cold-iters", type=int, default=20,
                    help="decode-only iterations with the last-level cache scrubbed")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run one plain 1 GiB device copy first (counter calibration "
+                        "for profiler runs)")
     return p.parse_args()
 
 
@@ -62,10 +65,24 @@ def algorithmic_bytes(w):
     return {"pack": U * pack, "flush_append": U * flush, "decode": U * decode}
 
 
-def traffic_from_profile(kernel_src):
-    """HBM bytes per pack launch measured by rocprofv3 counters, if the summary
-    under profiles/ was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "pack_c1_counters.txt")
+# the kernel each phase's roofline describes, and the source it is built from
+PHASE_KERNEL = {
+    "pack": ("pack_kernel", "kivi_pack.hip", "one launch: quantize + bit-pack the prefix, "
+             "copy the last window"),
+    "flush_append": ("pack_kernel", "kivi_pack.hip", "two launches: window flush, token copy"),
+    "decode": ("decode split + merge", None, "two launches: split-K attention, merge"),
+}
+
+
+def decode_source(w):
+    return "kivi_decode_mfma.hip" if w.gq == 4 else "kivi_decode.hip"
+
+
+def traffic_from_profile(kernel, workload, kernel_src):
+    """HBM bytes per launch of `kernel` on `workload` measured with rocprofv3
+    counters (profiles/<kernel>_<workload>_counters.txt), if they were taken on
+    the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -112,9 +129,10 @@ def run(args):
     torch.cuda.synchronize()
 
     def step(ev=None):
-        # ev: four HIP events bracketing the phases of layer 0
+        # ev: per layer, four HIP events bracketing the three phases; recorded
+        # on the stream every kernel is launched on
         for i, L in enumerate(layers):
-            rec = (lambda n: ev[n].record(stream)) if (ev is not None and i == 0) else (lambda n: None)
+            rec = (lambda n: ev[i][n].record(stream)) if ev is not None else (lambda n: None)
             c = L["cache"]
             c.reset()
             rec(0)
@@ -125,27 +143,33 @@ def run(args):
             c.decode_attn(L["q"], scale, out=L["out"])
             rec(3)
 
+    if args.copy_calibration:
+        # a plain copy of known size: 1 GiB read + 1 GiB written
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in layers]
+              for _ in range(args.steps)]
     # timed region: exactly `steps` steps between two synchronizations
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for k in range(args.steps):
+        step(events[k])
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps
 
-    # per-phase durations from HIP events on the launch stream (same steps,
-    # separate pass so the timed loop above carries no event overhead)
     phase = {"pack": [], "flush_append": [], "decode": []}
-    for _ in range(args.steps):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        step(ev)
-        torch.cuda.synchronize()
-        phase["pack"].append(ev[0].elapsed_time(ev[1]) * 1e-3)
-        phase["flush_append"].append(ev[1].elapsed_time(ev[2]) * 1e-3)
-        phase["decode"].append(ev[2].elapsed_time(ev[3]) * 1e-3)
+    for per_step in events:
+        for ev in per_step:
+            phase["pack"].append(ev[0].elapsed_time(ev[1]) * 1e-3)
+            phase["flush_append"].append(ev[1].elapsed_time(ev[2]) * 1e-3)
+            phase["decode"].append(ev[2].elapsed_time(ev[3]) * 1e-3)
 
     # decode alone with the 256 MB last-level cache scrubbed before each call
     scrub = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -212,18 +236,28 @@ def main():
     ab = algorithmic_bytes(w)
     layers_n = w.layers
     step_bytes = sum(ab.values()) * layers_n
+    # average launch-sequence duration per phase (HIP events in the timed steps)
+    avg = {k: float(np.mean(v)) for k, v in phase.items()}
     med = {k: float(np.median(v)) for k, v in phase.items()}
-    pack_gbps = ab["pack"] / med["pack"] / 1e9
-    src = os.path.join(ROOT, "kv_cache_bit_kivi_amd", "csrc", "kivi_pack.hip")
-    traffic = traffic_from_profile(src) if w.name == "c1" else None
     phases = {}
     for k in ("pack", "flush_append", "decode"):
-        g = ab[k] / med[k] / 1e9
-        phases[k] = {"bytes": ab[k], "us": med[k] * 1e6, "gbps": g, "frac": g / PEAK_GBPS}
+        g = ab[k] / avg[k] / 1e9
+        phases[k] = {"bytes": ab[k], "us_mean": avg[k] * 1e6, "us_median": med[k] * 1e6,
+                     "gbps": g, "frac": g / PEAK_GBPS, "launches": PHASE_KERNEL[k][2]}
     cold_med = float(np.median(cold))
-    phases["decode_cold_llc"] = {"bytes": ab["decode"], "us": cold_med * 1e6,
+    phases["decode_cold_llc"] = {"bytes": ab["decode"], "us_median": cold_med * 1e6,
                                  "gbps": ab["decode"] / cold_med / 1e9,
                                  "frac": ab["decode"] / cold_med / 1e9 / PEAK_GBPS}
+    # roofline of the phase that takes the most time (pack and decode are one
+    # dominant kernel each)
+    dom = max(("pack", "decode"), key=lambda k: avg[k])
+    kname, ksrc, _ = PHASE_KERNEL[dom]
+    if dom == "decode":
+        kname = "decode_mfma_gq4" if w.gq == 4 else "decode_split_valu"
+        ksrc = decode_source(w)
+    traffic = traffic_from_profile(kname, w.name,
+                                   os.path.join(ROOT, "kv_cache_bit_kivi_amd", "csrc", ksrc))
+    achieved = ab[dom] / avg[dom] / 1e9
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, layers)
     res = {
         "metric": METRIC,
@@ -243,9 +277,10 @@ def main():
                    "tokens": w.tokens, "k_bits": w.k_bits, "v_bits": w.v_bits,
                    "group_size": w.group_size, "residual_length": w.residual_length,
                    "kv_dtype": str(w.dtype).replace("torch.", ""), "layers": w.layers},
-        "roofline": {"bound": "hbm", "kernel": "pack (prefix bulk append)",
-                     "achieved": pack_gbps, "peak": PEAK_GBPS, "unit": "GB/s",
-                     "frac": pack_gbps / PEAK_GBPS, "traffic": traffic},
+        "roofline": {"bound": "hbm", "kernel": f"{kname} ({dom})",
+                     "achieved": achieved, "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_GBPS, "traffic": traffic,
+                     "bytes_per_launch": ab[dom], "us_per_launch": avg[dom] * 1e6},
         "cpu_baseline": cpu,
         "phases": phases,
     }

@@ -1,0 +1,58 @@
+"""Parity at the full workload sizes, in the launch configuration the benchmark
+times: bulk append of the prefix (one pack launch), append of the decode token
+(window flush + copy), then decode attention with the default split planner.
+
+The oracle runs on sampled (batch, kv head) units alone; their packed arrays
+must match bit for bit and the attention outputs of their query heads must be
+within 2e-3 of the oracle's."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_cache_bit_kivi_amd import kivi
+from kv_cache_bit_kivi_amd.inputs import WORKLOADS, bits16, make_layer
+from tests.gpu_helpers import assert_cache_equal, gpu_arrays, oracle_arrays, unit_oracle
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+TOL = 2e-3
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
+def test_fullsize_sampled_units(name):
+    w = WORKLOADS[name]
+    T = w.tokens
+    U = w.batch * w.kv_heads
+    print(f"workload {name}: B={w.batch} H={w.kv_heads} Hq={w.q_heads} T={T} "
+          f"bits={w.k_bits}/{w.v_bits} {w.dtype} (layer 0)", flush=True)
+    x = make_layer(w, seed=0, device=DEV, n_new=1)
+    cache = kivi.KiviCache(w.batch, w.kv_heads, T + 1, k_bits=w.k_bits, v_bits=w.v_bits,
+                           group_size=w.group_size, residual_length=w.residual_length,
+                           dtype=w.dtype, device=DEV)
+    cache.append(x.k[:, :, :T].contiguous(), x.v[:, :, :T].contiguous())
+    cache.append(x.k[:, :, T:].contiguous(), x.v[:, :, T:].contiguous())
+    scale = 1.0 / np.sqrt(w.head_dim)
+    out = cache.decode_attn(x.q.contiguous(), scale)
+    torch.cuda.synchronize()
+    v = cache.view()
+    assert (v.n_quant, v.n_resid) == (T, 1)  # every workload has T a multiple of R
+
+    rng = np.random.default_rng(U)
+    units = sorted({0, U - 1, int(rng.integers(1, U - 1))})
+    got = gpu_arrays(cache, units)
+    dt = oracle.BF16 if w.dtype == torch.bfloat16 else oracle.F16
+    for i, u in enumerate(units):
+        b, h = divmod(u, w.kv_heads)
+        print(f"workload {name}: unit {u} (batch {b}, kv head {h})", flush=True)
+        ref = unit_oracle(bits16(x.k[b, h]), bits16(x.v[b, h]), w, T + 1, dt)
+        assert (ref.n_quant, ref.n_resid) == (v.n_quant, v.n_resid)
+        mine = {k: a[i:i + 1] for k, a in got.items()}
+        assert_cache_equal(mine, oracle_arrays(ref), ref.n_quant, ref.n_resid, ref.capacity,
+                           ref.num_blocks)
+        heads = slice(h * w.gq, (h + 1) * w.gq)
+        o_ref = ref.decode_attn(bits16(x.q[b:b + 1, heads]), scale)
+        o_got = out[b:b + 1, heads].cpu().numpy().astype(np.float64)
+        err = np.abs(o_got - o_ref).max()
+        print(f"workload {name}: unit {u} attention max abs error {err:.2e}", flush=True)
+        assert err <= TOL
