@@ -354,7 +354,8 @@ kivi_status kivi_decode_attn(const kivi_cache* cc, const void* q, int32_t num_q_
   int n_split, per = 0, n_split_packed = 0, gps = 0;
   if (use_mfma) {
     // one wave per split; one round of as many waves as fit in LDS on every
-    // CU, each split a multiple of 4 groups; the window gets one extra split
+    // CU, each split a multiple of 4 groups; the window is one more partial,
+    // computed by the wave of the last packed split
     if (nqg > 0) {
       const int waves_per_cu =
           std::max(1, kivi::kLdsPerCu / kivi::mfma_wave_lds_bytes(c->cfg.k_bits, c->cfg.v_bits));

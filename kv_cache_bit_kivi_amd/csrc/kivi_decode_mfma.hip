@@ -24,8 +24,12 @@
 // columns = 4 heads x 4 channel groups m (p*S differs per m); each output
 // lane keeps the column of its own channel group.
 //
-// The residual window (at most R tokens, stored in kv dtype) is handled by an
-// extra wave per unit on the vector ALUs in fp32.
+// Softmax: the scores of a step pass through LDS so that each of the 64
+// lanes exponentiates 8 of them (the matrix layout leaves them on 16 lanes).
+//
+// The residual window (at most R tokens, stored in kv dtype) is handled on the
+// vector ALUs in fp32 by the wave of the unit's last packed split, after its
+// packed groups, as a partial of its own.
 #include <hip/hip_bf16.h>
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
@@ -38,6 +42,7 @@ namespace {
 constexpr int G = kGroup;
 constexpr int D = kHeadDim;
 constexpr int GQ = 4;
+constexpr int kRowP = 36;  // LDS row of one (stream, head): 32 scores + 4 floats padding
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -282,7 +287,7 @@ struct Stage {
   static constexpr int bytes = 2 * kBytes + vBytes;    // LDS per wave
   static constexpr int kLoads = (4 * kGroup + 2 * 4 * D * 2) / 1024;  // DMA instructions
   static constexpr int vLoads = (4 * vGroup + 2 * 4 * D * 2) / 1024;
-  static_assert(4 * kGroup >= GQ * GQ * G * 4, "probabilities fit in the key-code area");
+  static_assert(4 * kGroupPad >= GQ * GQ * 36 * 4, "scores fit in the key-code area");
 };
 static_assert(Stage<2, 2>::bytes == mfma_wave_lds_bytes(2, 2), "lds");
 static_assert(Stage<4, 4>::bytes == mfma_wave_lds_bytes(4, 4), "lds");
@@ -370,8 +375,8 @@ __global__ __launch_bounds__(64) void decode_mfma_gq4(DecodeArgs a) {
   const long long u = blockIdx.y;
   const int b = static_cast<int>(u / a.H), kvh = static_cast<int>(u % a.H);
 
-  if (split >= a.n_split_packed) {
-    window_wave<BF16>(a, u, b, kvh, split, reinterpret_cast<float (*)[D]>(smem),
+  if (a.n_split_packed == 0) {  // nothing packed yet: the window is the only split
+    window_wave<BF16>(a, u, b, kvh, 0, reinterpret_cast<float (*)[D]>(smem),
                       reinterpret_cast<float (*)[G]>(smem + GQ * D * 4));
     return;
   }
@@ -491,17 +496,37 @@ __global__ __launch_bounds__(64) void decode_mfma_gq4(DecodeArgs a) {
       for (int s = 0; s < 8; ++s) sc[s] = mfma(ak[s], bl[c], sc[s]);
     }
     // ------------------------------------------------------------- softmax
-    const bool live = diag && lk < ns;  // this lane's stream is lk
-    float mx = -INFINITY;
-    if (live) {
+    // The 16 diagonal lanes hold the step's 512 scores (head hq, stream lk,
+    // 32 tokens each).  They pass through LDS so that every lane takes 8 of
+    // them: lane (hq, j = lc & 3, lk) owns tokens 8j .. 8j+7 of stream lk.
+    // Rows of 32 scores are padded to 36 floats: the 16 rows start on
+    // distinct banks.
+    float* const sl = reinterpret_cast<float*>(cur);  // [stream][head][36]
+    wave_lds_sync();  // key codes of this stage fully read before they are overwritten
+    if (diag) {
 #pragma unroll
-      for (int s = 0; s < 8; ++s) mx = fmaxf(mx, fmaxf(fmaxf(sc[s][0], sc[s][1]), fmaxf(sc[s][2], sc[s][3])));
-      mx *= k_unscale;
+      for (int s = 0; s < 8; ++s)
+        *reinterpret_cast<f32x4*>(sl + (lk * GQ + hq) * kRowP + 4 * s) = sc[s] * k_unscale;
     }
+    // one wave's LDS operations complete in order: the reads see the writes
+    const int jt = lc & 3;
+    float* const myrow = sl + (lk * GQ + hq) * kRowP + 8 * jt;
+    float x[8];
+    {
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(myrow);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(myrow + 4);
+      const bool valid = lk < ns;  // streams past the last group hold no tokens
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = valid ? x0[i] : -INFINITY;
+        x[4 + i] = valid ? x1[i] : -INFINITY;
+      }
+    }
+    float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
     mx = fmaxf(mx, partner<1>(mx));
     mx = fmaxf(mx, partner<2>(mx));
     mx = swap_max<16>(mx);
-    mx = swap_max<32>(mx);  // max over the 4 streams and 32 rows of head hq
+    mx = swap_max<32>(mx);  // max over the 4 streams and 32 tokens of head hq
     const float m_new = fmaxf(m_run, mx);
     if (__any(m_new > m_run)) {
       const float alpha = (m_run == -INFINITY) ? 0.0f : fast_exp2(m_run - m_new);
@@ -514,25 +539,21 @@ __global__ __launch_bounds__(64) void decode_mfma_gq4(DecodeArgs a) {
       }
       m_run = m_new;
     }
-    float(*pl)[GQ][G] = reinterpret_cast<float (*)[GQ][G]>(cur);  // [stream][head][row]
-    wave_lds_sync();  // key codes of this stage fully read before pl overwrites them
-    if (live) {
-      // p scaled by the value-code factor of its row position: row t sits in
-      // pair class e'(t) = (t mod 8) / 2 of its run of 8
-      float nmc[4];
+    {
+      // p scaled by the value-code factor of its token position: token t
+      // sits in pair class e'(t) = (t mod 8) / 2 of its run of 8
+      f32x4 p0, p1;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) nmc[e] = static_cast<float>(VS::lf(e)) - m_run;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        f32x4 p;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int ep = 2 * (s & 1) + (r >> 1);
-          p[r] = fast_exp2(fmaf(sc[s][r], k_unscale, nmc[ep]));
-          lcls[ep] += p[r];
-        }
-        *reinterpret_cast<f32x4*>(&pl[lk][hq][4 * s]) = p;
+      for (int i = 0; i < 4; ++i) {
+        p0[i] = fast_exp2(x[i] + (static_cast<float>(VS::lf(i >> 1)) - m_run));
+        p1[i] = fast_exp2(x[4 + i] + (static_cast<float>(VS::lf(2 + (i >> 1))) - m_run));
       }
+      lcls[0] += p0[0] + p0[1];
+      lcls[1] += p0[2] + p0[3];
+      lcls[2] += p1[0] + p1[1];
+      lcls[3] += p1[2] + p1[3];
+      *reinterpret_cast<f32x4*>(myrow) = p0;
+      *reinterpret_cast<f32x4*>(myrow + 4) = p1;
     }
     // the value stage of this step was issued before K(step+1)
     if (more) {
@@ -550,8 +571,9 @@ __global__ __launch_bounds__(64) void decode_mfma_gq4(DecodeArgs a) {
       const int vmo = ((gs * 4 + mcol) * G + 8 * lk) * 2;
       const u32x4 vs = *reinterpret_cast<const u32x4*>(vstage + S::offVS + vmo);
       const u32x4 vz = *reinterpret_cast<const u32x4*>(vstage + S::offVZ + vmo);
-      const f32x4 p0 = *reinterpret_cast<const f32x4*>(&pl[gs][hq][8 * lk]);
-      const f32x4 p1 = *reinterpret_cast<const f32x4*>(&pl[gs][hq][8 * lk + 4]);
+      const float* prow = sl + (gs * GQ + hq) * kRowP + 8 * lk;
+      const f32x4 p0 = *reinterpret_cast<const f32x4*>(prow);
+      const f32x4 p1 = *reinterpret_cast<const f32x4*>(prow + 4);
       const float p[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
       u32x4 h4, l4;
 #pragma unroll
@@ -574,7 +596,7 @@ __global__ __launch_bounds__(64) void decode_mfma_gq4(DecodeArgs a) {
 #pragma unroll
       for (int be = 0; be < 8; ++be) o[be] = mfma(av[be], bpl, o[be]);
     }
-    wave_lds_sync();  // value stage and pl fully read
+    wave_lds_sync();  // value stage and probabilities fully read
     if (more) issue_vstage<KB, VB>(a, u, g0 + 4, min(4, ge - g0 - 4), vstage);
   }
 
@@ -611,11 +633,18 @@ __global__ __launch_bounds__(64) void decode_mfma_gq4(DecodeArgs a) {
       *reinterpret_cast<f32x4*>(P + 2 + 32 * lk + 8 * r + 4) = x1;
     }
   }
+  // the last packed split also takes the window (its own partial); every
+  // stage load has completed and the LDS is free again
+  if (split == a.n_split_packed - 1 && a.n_resid > 0) {
+    window_wave<BF16>(a, u, b, kvh, a.n_split_packed, reinterpret_cast<float (*)[D]>(smem),
+                      reinterpret_cast<float (*)[G]>(smem + GQ * D * 4));
+  }
 }
 
 template <int KB, int VB, bool BF16>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  dim3 grid(a.n_split, a.B * a.H);
+  // one workgroup per packed split; the last one also runs the window
+  dim3 grid(a.n_split_packed > 0 ? a.n_split_packed : 1, a.B * a.H);
   hipLaunchKernelGGL((decode_mfma_gq4<KB, VB, BF16>), grid, dim3(64), 0, stream, a);
   return hipGetLastError();
 }
