@@ -41,18 +41,27 @@
  * (4-bit) after a shift therefore yields two codes, one per 16-bit lane.
  *
  * Codes are packed along the axis that the attention contraction runs over
- * (channels for q.K, tokens for p.V), not along the quantization group:
- *   k_codes  uint32 [B*H][cap][D / Pk]     word w of token t holds channels
- *                                          w*Pk .. w*Pk + Pk - 1
- *   k_scale  fp16   [B*H][NB][D]           one {S} per (block, channel)
- *   k_zero   fp16   [B*H][NB][D]           one {Z} per (block, channel)
- *   v_codes  uint32 [B*H][NB][G / Pv][D]   word w of (block g, channel d)
- *                                          holds rows w*Pv .. w*Pv + Pv - 1;
- *                                          the D words of one w are adjacent
- *   v_scale  fp16   [B*H][NB][D / G][G]    one {S} per (token, channel group)
- *   v_zero   fp16   [B*H][NB][D / G][G]
- *   k_resid, v_resid  kv_dtype [B*H][R][D] residual window, slot i holds the
- *                                          token n_quant + i
+ * (channels for q.K, tokens for p.V), not along the quantization group.
+ *
+ * Every (unit u, block g) of packed tokens is one contiguous record of
+ *   block_bytes = G*D*bk/8 + G*D*bv/8 + 8*D
+ * bytes at  blocks + (u * NB + g) * block_bytes  (3 KiB for D = 128, G = 32,
+ * 2-bit keys and values), so that a decode step streams one region:
+ *   offset                        field    type / shape
+ *   0                             k_codes  uint32 [G][D / Pk]   word w of row
+ *                                          j holds channels w*Pk .. w*Pk+Pk-1
+ *   G*D*bk/8                      v_codes  uint32 [G / Pv][D]   word (w, d)
+ *                                          holds rows w*Pv .. w*Pv + Pv - 1 of
+ *                                          channel d; the D words of one w are
+ *                                          adjacent
+ *   + G*D*bv/8                    k_scale  fp16 [D]     {S} per channel
+ *   + 2*D                         k_zero   fp16 [D]     {Z} per channel
+ *   + 4*D                         v_scale  fp16 [D / G][G]  {S} per (channel
+ *                                          group, row)
+ *   + 6*D                         v_zero   fp16 [D / G][G]
+ * The residual window is stored apart:
+ *   k_resid, v_resid  kv_dtype [B*H][R][D]  slot i holds the token
+ *                                          n_quant + i
  * Tokens [0, n_quant) are packed, tokens [n_quant, n_quant + n_resid) are in
  * the residual window.  Entries beyond those are unspecified.
  *
@@ -117,17 +126,19 @@ typedef struct {
 
 /* Device pointers into the cache buffer plus the host counters. */
 typedef struct {
-  int32_t n_quant;   /* tokens packed; a multiple of R */
-  int32_t n_resid;   /* tokens in the residual window, 0..R */
-  int32_t capacity;  /* cap: max_tokens rounded up to a multiple of R */
-  int32_t num_blocks;/* NB = cap / G */
-  uint32_t *k_codes, *v_codes;
-  uint16_t *k_scale, *k_zero, *v_scale, *v_zero; /* fp16 bit patterns */
-  void *k_resid, *v_resid;                        /* kv_dtype */
+  int32_t n_quant;     /* tokens packed; a multiple of R */
+  int32_t n_resid;     /* tokens in the residual window, 0..R */
+  int32_t capacity;    /* cap: max_tokens rounded up to a multiple of R */
+  int32_t num_blocks;  /* NB = cap / G */
+  int32_t block_bytes; /* bytes of one block record */
+  /* byte offsets of the fields inside a block record */
+  int32_t off_k_codes, off_v_codes, off_k_scale, off_k_zero, off_v_scale, off_v_zero;
+  void* blocks;        /* [B*H][NB] block records */
+  void *k_resid, *v_resid; /* kv_dtype */
 } kivi_cache_view;
 
-/* Bytes of device memory the cache for `cfg` needs (all arrays above, each
- * 256-byte aligned).  Pure arithmetic; no device is touched. */
+/* Bytes of device memory the cache for `cfg` needs (the block records and
+ * the two window arrays, each 256-byte aligned).  Pure arithmetic; no device is touched. */
 kivi_status kivi_cache_bytes(const kivi_config* cfg, size_t* bytes);
 
 /* Creates an empty cache (n_quant = n_resid = 0) over the caller's device

@@ -34,12 +34,7 @@ struct kivi_cache {
   int forced_splits;
   int cu_count;  // queried on first decode
   bool poisoned;
-  uint32_t* k_codes;
-  uint16_t* k_scale;
-  uint16_t* k_zero;
-  uint32_t* v_codes;
-  uint16_t* v_scale;
-  uint16_t* v_zero;
+  uint8_t* blocks;  // [B*H][nb] block records
   uint16_t* k_resid;
   uint16_t* v_resid;
 };
@@ -63,7 +58,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t off[8];  // k_codes, k_scale, k_zero, v_codes, v_scale, v_zero, k_resid, v_resid
+  size_t off[3];  // blocks, k_resid, v_resid
   size_t total;
   int cap, nb;
 };
@@ -101,18 +96,14 @@ Layout layout_of(const kivi_config* c) {
   const size_t D = c->head_dim, G = c->group_size, R = c->residual_length;
   L.cap = (int)(((size_t)c->max_tokens + R - 1) / R * R);
   L.nb = (int)(L.cap / G);
-  const size_t sizes[8] = {
-      U * L.cap * (D * c->k_bits / 32) * 4,  // k_codes
-      U * L.nb * D * 2,                      // k_scale
-      U * L.nb * D * 2,                      // k_zero
-      U * L.nb * D * (G * c->v_bits / 32) * 4,  // v_codes
-      U * L.nb * D * 2,                      // v_scale ([block][D/G][G] = D per block)
-      U * L.nb * D * 2,                      // v_zero
-      U * R * D * 2,                         // k_resid
-      U * R * D * 2,                         // v_resid
+  const size_t block_bytes = G * D * (c->k_bits + c->v_bits) / 8 + 8 * D;
+  const size_t sizes[3] = {
+      U * L.nb * block_bytes,  // block records
+      U * R * D * 2,           // k_resid
+      U * R * D * 2,           // v_resid
   };
   size_t o = 0;
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 3; ++i) {
     L.off[i] = o;
     o = align_up(o + sizes[i]);
   }
@@ -124,12 +115,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 kivi::PackArgs base_pack_args(const kivi_cache* c) {
   kivi::PackArgs a{};
-  a.k_codes = c->k_codes;
-  a.k_scale = c->k_scale;
-  a.k_zero = c->k_zero;
-  a.v_codes = c->v_codes;
-  a.v_scale = c->v_scale;
-  a.v_zero = c->v_zero;
+  a.blocks = c->blocks;
   a.k_resid = c->k_resid;
   a.v_resid = c->v_resid;
   a.cap = c->cap;
@@ -215,14 +201,9 @@ kivi_status kivi_cache_create(const kivi_config* cfg, void* dev_buf, size_t dev_
   c->cap = L.cap;
   c->nb = L.nb;
   char* base = static_cast<char*>(dev_buf);
-  c->k_codes = reinterpret_cast<uint32_t*>(base + L.off[0]);
-  c->k_scale = reinterpret_cast<uint16_t*>(base + L.off[1]);
-  c->k_zero = reinterpret_cast<uint16_t*>(base + L.off[2]);
-  c->v_codes = reinterpret_cast<uint32_t*>(base + L.off[3]);
-  c->v_scale = reinterpret_cast<uint16_t*>(base + L.off[4]);
-  c->v_zero = reinterpret_cast<uint16_t*>(base + L.off[5]);
-  c->k_resid = reinterpret_cast<uint16_t*>(base + L.off[6]);
-  c->v_resid = reinterpret_cast<uint16_t*>(base + L.off[7]);
+  c->blocks = reinterpret_cast<uint8_t*>(base + L.off[0]);
+  c->k_resid = reinterpret_cast<uint16_t*>(base + L.off[1]);
+  c->v_resid = reinterpret_cast<uint16_t*>(base + L.off[2]);
   *out = c;
   return KIVI_OK;
 }
@@ -357,13 +338,35 @@ kivi_status kivi_decode_attn(const kivi_cache* cc, const void* q, int32_t num_q_
     // CU, each split a multiple of 4 groups; the window is one more partial,
     // computed by the wave of the last packed split
     if (nqg > 0) {
-      const int waves_per_cu =
-          std::max(1, kivi::kLdsPerCu / kivi::mfma_wave_lds_bytes(c->cfg.k_bits, c->cfg.v_bits));
-      int want = c->forced_splits > 0 ? c->forced_splits
-                                      : (waves_per_cu * c->cu_count + units - 1) / units;
-      want = std::max(1, std::min({want, (nqg + 3) / 4, kivi::kMaxSplits - 1}));
-      gps = ((nqg + want - 1) / want + 3) / 4 * 4;
-      n_split_packed = (nqg + gps - 1) / gps;
+      // resident waves per CU: LDS stages, and at most 2 waves per SIMD
+      // (register budget of the kernel)
+      const int waves_per_cu = std::max(
+          1, std::min(8, kivi::kLdsPerCu / kivi::mfma_wave_lds_bytes(c->cfg.k_bits, c->cfg.v_bits)));
+      const long long slots = (long long)waves_per_cu * c->cu_count;
+      const int max_split = std::max(1, std::min((nqg + 3) / 4, kivi::kMaxSplits - 1));
+      auto plan = [&](int want, int& g, int& np) {
+        g = ((nqg + want - 1) / want + 3) / 4 * 4;  // groups per split, whole steps of 4
+        np = (nqg + g - 1) / g;
+      };
+      if (c->forced_splits > 0) {
+        plan(std::min(c->forced_splits, max_split), gps, n_split_packed);
+      } else {
+        // minimise (rounds of resident waves) x (steps per wave): every
+        // split of one launch takes the same time, so a partly filled last
+        // round costs a whole wave duration
+        long long best = -1;
+        for (int want = 1; want <= max_split; ++want) {
+          int g, np;
+          plan(want, g, np);
+          const long long rounds = ((long long)units * np + slots - 1) / slots;
+          const long long cost = rounds * (g / 4 + 1);  // +1: per-wave set-up and partial
+          if (best < 0 || cost < best) {
+            best = cost;
+            gps = g;
+            n_split_packed = np;
+          }
+        }
+      }
     }
     n_split = n_split_packed + (c->n_resid > 0 ? 1 : 0);
   } else {
@@ -380,12 +383,7 @@ kivi_status kivi_decode_attn(const kivi_cache* cc, const void* q, int32_t num_q_
   }
 
   kivi::DecodeArgs a{};
-  a.k_codes = c->k_codes;
-  a.k_scale = c->k_scale;
-  a.k_zero = c->k_zero;
-  a.v_codes = c->v_codes;
-  a.v_scale = c->v_scale;
-  a.v_zero = c->v_zero;
+  a.blocks = c->blocks;
   a.k_resid = c->k_resid;
   a.v_resid = c->v_resid;
   a.q = static_cast<const uint16_t*>(q);
@@ -424,12 +422,15 @@ kivi_status kivi_cache_get_view(const kivi_cache* c, kivi_cache_view* v) {
   v->n_resid = c->n_resid;
   v->capacity = c->cap;
   v->num_blocks = c->nb;
-  v->k_codes = c->k_codes;
-  v->v_codes = c->v_codes;
-  v->k_scale = c->k_scale;
-  v->k_zero = c->k_zero;
-  v->v_scale = c->v_scale;
-  v->v_zero = c->v_zero;
+  const kivi::BlockLayout bl = kivi::block_layout(c->cfg.k_bits, c->cfg.v_bits);
+  v->block_bytes = bl.bytes;
+  v->off_k_codes = bl.k_codes;
+  v->off_v_codes = bl.v_codes;
+  v->off_k_scale = bl.k_scale;
+  v->off_k_zero = bl.k_zero;
+  v->off_v_scale = bl.v_scale;
+  v->off_v_zero = bl.v_zero;
+  v->blocks = c->blocks;
   v->k_resid = c->k_resid;
   v->v_resid = c->v_resid;
   return KIVI_OK;

@@ -50,7 +50,8 @@ __device__ __forceinline__ uint32_t code_at(uint32_t word, int i) {
 template <int KB, int VB, bool BF16, int GQ>
 __global__ __launch_bounds__(256) void decode_split_valu(DecodeArgs a) {
   constexpr int PK = 32 / KB, KW = D / PK;
-  constexpr int PV = 32 / VB, VW = G / PV;
+  constexpr int PV = 32 / VB;
+  constexpr BlockLayout BL = block_layout(KB, VB);
 
   __shared__ float qs[GQ][D];
   __shared__ float kS[D], kZ[D];
@@ -86,15 +87,15 @@ __global__ __launch_bounds__(256) void decode_split_valu(DecodeArgs a) {
     const bool packed = it < nqb;
     const int rc = it - nqb;  // window chunk index when !packed
     const int ntok = packed ? G : min(G, a.n_resid - rc * G);
+    const uint8_t* const rec = a.blocks + (u * a.nb + (packed ? it : 0)) * BL.bytes;
     if (packed) {
-      const long long mk = (u * a.nb + it) * D;  // key meta [block][d]
-      const long long mv = (u * a.nb + it) * D;  // value meta [block][m][row], 4*32 = D entries
+      // key meta [d]; value meta [m][row], 4 * 32 = D entries
       if (tid < D) {
-        kS[tid] = h2f(a.k_scale[mk + tid]);
-        vS[tid] = h2f(a.v_scale[mv + tid]);
+        kS[tid] = h2f(reinterpret_cast<const uint16_t*>(rec + BL.k_scale)[tid]);
+        vS[tid] = h2f(reinterpret_cast<const uint16_t*>(rec + BL.v_scale)[tid]);
       } else {
-        kZ[tid - D] = h2f(a.k_zero[mk + tid - D]);
-        vZ[tid - D] = h2f(a.v_zero[mv + tid - D]);
+        kZ[tid - D] = h2f(reinterpret_cast<const uint16_t*>(rec + BL.k_zero)[tid - D]);
+        vZ[tid - D] = h2f(reinterpret_cast<const uint16_t*>(rec + BL.v_zero)[tid - D]);
       }
     }
     __syncthreads();
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(256) void decode_split_valu(DecodeArgs a) {
       for (int j = 0; j < GQ; ++j) acc[j] = 0.0f;
       if (t < ntok) {
         if (packed) {
-          const uint32_t* kw = a.k_codes + (u * a.cap + (long long)it * G + t) * KW;
+          const uint32_t* kw = reinterpret_cast<const uint32_t*>(rec + BL.k_codes) + t * KW;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int d = sl * 16 + i;
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(256) void decode_split_valu(DecodeArgs a) {
 #pragma unroll
       for (int j = 0; j < GQ; ++j) o[j] *= st_a[j];
       if (packed) {
-        const uint32_t* vw = a.v_codes + (u * a.nb + it) * VW * D + d;  // word w at vw[w * D]
+        const uint32_t* vw = reinterpret_cast<const uint32_t*>(rec + BL.v_codes) + d;  // word w at vw[w * D]
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int row = half * 16 + i;

@@ -309,18 +309,20 @@ __device__ __forceinline__ void issue_kstage(const DecodeArgs& a, long long u, i
   using S = Stage<KB, VB>;
   const int lane = threadIdx.x;
   const int glast = g0 + ns - 1;
-  const uint8_t* kc = reinterpret_cast<const uint8_t*>(a.k_codes) + (u * a.cap) * (long long)S::kRow;
+  constexpr BlockLayout BL = block_layout(KB, VB);
+  const uint8_t* const unit = a.blocks + (u * a.nb) * (long long)BL.bytes;
 #pragma unroll
   for (int gi = 0; gi < 4; ++gi) {
     const long long g = min(g0 + gi, glast);
 #pragma unroll
     for (int j = 0; j < S::kGroup / 1024; ++j)
-      dma16(kc + g * S::kGroup + j * 1024 + lane * 16, dst + gi * S::kGroupPad + j * 1024);
+      dma16(unit + g * BL.bytes + BL.k_codes + j * 1024 + lane * 16, dst + gi * S::kGroupPad + j * 1024);
   }
-  const int g = min(g0 + (lane >> 4), glast);  // 256 bytes per group and array
-  const long long km = (u * a.nb + g) * D * 2 + (lane & 15) * 16;
-  dma16(reinterpret_cast<const uint8_t*>(a.k_scale) + km, dst + S::offKS);
-  dma16(reinterpret_cast<const uint8_t*>(a.k_zero) + km, dst + S::offKZ);
+  // scale and zero: 256 bytes per group and field, 16 lanes per group
+  const int g = min(g0 + (lane >> 4), glast);
+  const uint8_t* const meta = unit + g * (long long)BL.bytes + (lane & 15) * 16;
+  dma16(meta + BL.k_scale, dst + S::offKS);
+  dma16(meta + BL.k_zero, dst + S::offKZ);
 }
 
 // Value stage of groups [g0, g0 + ns): Stage::vLoads instructions.
@@ -330,18 +332,19 @@ __device__ __forceinline__ void issue_vstage(const DecodeArgs& a, long long u, i
   using S = Stage<KB, VB>;
   const int lane = threadIdx.x;
   const int glast = g0 + ns - 1;
-  const uint8_t* vc = reinterpret_cast<const uint8_t*>(a.v_codes) + (u * a.nb) * (long long)S::vGroup;
+  constexpr BlockLayout BL = block_layout(KB, VB);
+  const uint8_t* const unit = a.blocks + (u * a.nb) * (long long)BL.bytes;
 #pragma unroll
   for (int gi = 0; gi < 4; ++gi) {
     const long long g = min(g0 + gi, glast);
 #pragma unroll
     for (int j = 0; j < S::vGroup / 1024; ++j)
-      dma16(vc + g * S::vGroup + j * 1024 + lane * 16, dst + gi * S::vGroup + j * 1024);
+      dma16(unit + g * BL.bytes + BL.v_codes + j * 1024 + lane * 16, dst + gi * S::vGroup + j * 1024);
   }
   const int g = min(g0 + (lane >> 4), glast);
-  const long long vm = (u * a.nb + g) * D * 2 + (lane & 15) * 16;
-  dma16(reinterpret_cast<const uint8_t*>(a.v_scale) + vm, dst + S::offVS);
-  dma16(reinterpret_cast<const uint8_t*>(a.v_zero) + vm, dst + S::offVZ);
+  const uint8_t* const meta = unit + g * (long long)BL.bytes + (lane & 15) * 16;
+  dma16(meta + BL.v_scale, dst + S::offVS);
+  dma16(meta + BL.v_zero, dst + S::offVZ);
 }
 
 // Waits until at most N vector-memory operations of this wave are in flight

@@ -11,6 +11,21 @@ constexpr int kGroup = 32;       // G: tokens per key group, channels per value 
 constexpr int kHeadDim = 128;    // D handled by the kernels
 constexpr int kMaxSplits = 256;  // upper bound on decode token splits
 
+// Byte offsets of the fields of one packed block record (one unit, G
+// tokens) and its size; the layout is documented in include/kivi.h.
+struct BlockLayout {
+  int k_codes, v_codes, k_scale, k_zero, v_scale, v_zero, bytes;
+};
+__host__ __device__ constexpr BlockLayout block_layout(int k_bits, int v_bits) {
+  return BlockLayout{0,
+                     kGroup * kHeadDim * k_bits / 8,
+                     kGroup * kHeadDim * (k_bits + v_bits) / 8,
+                     kGroup * kHeadDim * (k_bits + v_bits) / 8 + 2 * kHeadDim,
+                     kGroup * kHeadDim * (k_bits + v_bits) / 8 + 4 * kHeadDim,
+                     kGroup * kHeadDim * (k_bits + v_bits) / 8 + 6 * kHeadDim,
+                     kGroup * kHeadDim * (k_bits + v_bits) / 8 + 8 * kHeadDim};
+}
+
 // One launch of the pack kernel: quantize + bit-pack `nblk` blocks of G
 // tokens per unit, and copy `r_count` tokens per unit into the window.
 struct PackArgs {
@@ -29,12 +44,7 @@ struct PackArgs {
   int r_count;
   int r_dst_slot0;
   // cache arrays
-  uint32_t* k_codes;
-  uint16_t* k_scale;
-  uint16_t* k_zero;
-  uint32_t* v_codes;
-  uint16_t* v_scale;
-  uint16_t* v_zero;
+  uint8_t* blocks;  // [units][nb] block records
   uint16_t* k_resid;
   uint16_t* v_resid;
   int cap;    // token capacity per unit
@@ -45,12 +55,7 @@ struct PackArgs {
 
 // One decode-attention launch (split kernel + merge kernel).
 struct DecodeArgs {
-  const uint32_t* k_codes;
-  const uint16_t* k_scale;
-  const uint16_t* k_zero;
-  const uint32_t* v_codes;
-  const uint16_t* v_scale;
-  const uint16_t* v_zero;
+  const uint8_t* blocks;  // [B*H][nb] block records
   const uint16_t* k_resid;
   const uint16_t* v_resid;
   const uint16_t* q;   // [B][Hq][D] kv dtype

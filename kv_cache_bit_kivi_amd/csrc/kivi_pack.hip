@@ -112,8 +112,10 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
   }
 
   // ---- stage the key and value tiles of this block
+  constexpr BlockLayout BL = block_layout(KB, VB);
   const int blk = item;
   const int gblk = a.dst_blk0 + blk;
+  uint8_t* const rec = a.blocks + (u * a.nb + gblk) * BL.bytes;  // this block's record
   {
     const long long base = u * a.src_unit_stride + (long long)(a.src_tok0 + blk * G) * D;
     for (int c = tid; c < G * D / 8; c += 256) {
@@ -141,9 +143,8 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
     kmn[d] = mn;
     ksc[d] = s;
     krc[d] = rcp;
-    const long long mi = (u * a.nb + gblk) * D + d;
-    a.k_scale[mi] = f16_bits_canon(s);
-    a.k_zero[mi] = f16_bits_canon(mn);
+    reinterpret_cast<uint16_t*>(rec + BL.k_scale)[d] = f16_bits_canon(s);
+    reinterpret_cast<uint16_t*>(rec + BL.k_zero)[d] = f16_bits_canon(mn);
   } else {
     // value group: row t, channels m*G .. m*G+G-1; thread index m*G + t
     const int i = tid - D;
@@ -160,9 +161,8 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
     vmn[i] = mn;
     vsc[i] = s;
     vrc[i] = rcp;
-    const long long mi = (u * a.nb + gblk) * (D / G) * G + i;  // [block][m][row]
-    a.v_scale[mi] = f16_bits_canon(s);
-    a.v_zero[mi] = f16_bits_canon(mn);
+    reinterpret_cast<uint16_t*>(rec + BL.v_scale)[i] = f16_bits_canon(s);  // [m][row]
+    reinterpret_cast<uint16_t*>(rec + BL.v_zero)[i] = f16_bits_canon(mn);
   }
   __syncthreads();
 
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
       const uint32_t c = quant_code<QK>(to_f32<BF16>(kt[t * RS + d]), kmn[d], ksc[d], krc[d]);
       word |= c << code_shift<KB>(i);
     }
-    a.k_codes[(u * a.cap + (long long)gblk * G + t) * KW + w] = word;
+    reinterpret_cast<uint32_t*>(rec + BL.k_codes)[t * KW + w] = word;
   }
 
   // ---- value code words: channel d, word w holds rows w*PV .. w*PV+PV-1;
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
       const uint32_t c = quant_code<QV>(to_f32<BF16>(vt[t * RS + d]), vmn[si], vsc[si], vrc[si]);
       word |= c << code_shift<VB>(i);
     }
-    a.v_codes[((u * a.nb + gblk) * VW + w) * D + d] = word;
+    reinterpret_cast<uint32_t*>(rec + BL.v_codes)[w * D + d] = word;
   }
 }
 

@@ -44,9 +44,11 @@ class kivi_cache_view(ctypes.Structure):
     _fields_ = [
         ("n_quant", ctypes.c_int32), ("n_resid", ctypes.c_int32),
         ("capacity", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
-        ("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
-        ("k_scale", ctypes.c_void_p), ("k_zero", ctypes.c_void_p),
-        ("v_scale", ctypes.c_void_p), ("v_zero", ctypes.c_void_p),
+        ("block_bytes", ctypes.c_int32),
+        ("off_k_codes", ctypes.c_int32), ("off_v_codes", ctypes.c_int32),
+        ("off_k_scale", ctypes.c_int32), ("off_k_zero", ctypes.c_int32),
+        ("off_v_scale", ctypes.c_int32), ("off_v_zero", ctypes.c_int32),
+        ("blocks", ctypes.c_void_p),
         ("k_resid", ctypes.c_void_p), ("v_resid", ctypes.c_void_p),
     ]
 
@@ -242,25 +244,32 @@ class KiviCache:
         return self.view().n_resid
 
     def arrays(self):
-        """Device tensors aliasing the packed-layout arrays (flat)."""
+        """Device tensors aliasing the cache fields, shaped [B*H][...] per unit.
+        The packed fields are strided views into the block records: unit u,
+        block g, field f lies at blocks + (u * NB + g) * block_bytes + off_f."""
         torch = self.torch
         v = self.view()
         c = self.cfg
         U = c.batch * c.num_kv_heads
-        cap, nb, D, G, R = v.capacity, v.num_blocks, c.head_dim, c.group_size, c.residual_length
+        nb, D, G, R = v.num_blocks, c.head_dim, c.group_size, c.residual_length
         base = self.buffer.data_ptr()
+        ob = v.blocks - base
+        recs = self.buffer[ob:ob + U * nb * v.block_bytes].view(U, nb, v.block_bytes)
+
+        def field(off, nbytes, dt):
+            return recs[:, :, off:off + nbytes].view(dt)  # [U][nb][n]
 
         def sub(ptr, n, dt, esize):
             off = ptr - base
-            return self.buffer[off:off + n * esize].view(dt)
+            return self.buffer[off:off + n * esize].view(dt).view(U, -1)
 
         return {
-            "k_codes": sub(v.k_codes, U * cap * D * c.k_bits // 32, torch.int32, 4),
-            "k_scale": sub(v.k_scale, U * nb * D, torch.int16, 2),
-            "k_zero": sub(v.k_zero, U * nb * D, torch.int16, 2),
-            "v_codes": sub(v.v_codes, U * nb * D * G * c.v_bits // 32, torch.int32, 4),
-            "v_scale": sub(v.v_scale, U * nb * D, torch.int16, 2),
-            "v_zero": sub(v.v_zero, U * nb * D, torch.int16, 2),
+            "k_codes": field(v.off_k_codes, G * D * c.k_bits // 8, torch.int32),
+            "k_scale": field(v.off_k_scale, 2 * D, torch.int16),
+            "k_zero": field(v.off_k_zero, 2 * D, torch.int16),
+            "v_codes": field(v.off_v_codes, G * D * c.v_bits // 8, torch.int32),
+            "v_scale": field(v.off_v_scale, 2 * D, torch.int16),
+            "v_zero": field(v.off_v_zero, 2 * D, torch.int16),
             "k_resid": sub(v.k_resid, U * R * D, torch.int16, 2),
             "v_resid": sub(v.v_resid, U * R * D, torch.int16, 2),
         }

@@ -16,10 +16,9 @@ def gpu_arrays(cache, units=None):
     U = c.batch * c.num_kv_heads
     out = {}
     for name, t in cache.arrays().items():
-        t = t.view(U, -1)
         if units is not None:
             t = t[torch.as_tensor(units, device=t.device)]
-        a = t.cpu().numpy()
+        a = t.contiguous().view(t.shape[0], -1).cpu().numpy()
         out[name] = a.view(np.uint32) if "codes" in name else a.view(np.uint16)
     return out
 

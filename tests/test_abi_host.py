@@ -89,7 +89,8 @@ def test_create_errors():
     h = _make(c)
     v = kivi.kivi_cache_get_view(h)
     assert (v.n_quant, v.n_resid, v.capacity, v.num_blocks) == (0, 0, 384, 12)
-    assert v.k_codes == FAKE_DEV
+    assert v.blocks == FAKE_DEV
+    assert (v.block_bytes, v.off_v_codes, v.off_k_scale, v.off_v_zero) == (3072, 1024, 2048, 2816)
     kivi.kivi_cache_destroy(h)
 
 
