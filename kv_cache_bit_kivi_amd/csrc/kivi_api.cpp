@@ -338,11 +338,11 @@ kivi_status kivi_decode_attn(const kivi_cache* cc, const void* q, int32_t num_q_
     // CU, each split a multiple of 4 groups; the window is one more partial,
     // computed by the wave of the last packed split
     if (nqg > 0) {
-      // resident waves per CU: LDS stages, and at most 2 waves per SIMD
-      // (register budget of the kernel)
-      const int waves_per_cu = std::max(
-          1, std::min(8, kivi::kLdsPerCu / kivi::mfma_wave_lds_bytes(c->cfg.k_bits, c->cfg.v_bits)));
-      const long long slots = (long long)waves_per_cu * c->cu_count;
+      // resident workgroups (key + value wave) per CU: LDS, and at most 6
+      // (3 waves per SIMD at the kernel's register budget)
+      const int wgs_per_cu = std::max(
+          1, std::min(6, kivi::kLdsPerCu / kivi::mfma_wg_lds_bytes(c->cfg.k_bits, c->cfg.v_bits)));
+      const long long slots = (long long)wgs_per_cu * c->cu_count;
       const int max_split = std::max(1, std::min((nqg + 3) / 4, kivi::kMaxSplits - 1));
       auto plan = [&](int want, int& g, int& np) {
         g = ((nqg + want - 1) / want + 3) / 4 * 4;  // groups per split, whole steps of 4

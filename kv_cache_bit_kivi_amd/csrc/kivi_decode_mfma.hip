@@ -7,7 +7,10 @@
 // the memory saving to turn into speed (page "KV-Cache Quantization: I Ran the
 // Experiments", "Where it still breaks", item 3).
 //
-// One wave per (unit, split).  The scales are folded into the dense operand
+// One workgroup of two waves per (unit, split): a key wave computes scores
+// and the online softmax, a value wave accumulates p.V one step behind it;
+// they meet once per step at a workgroup barrier and hand over the
+// probabilities through LDS.  The scales are folded into the dense operand
 // of each product so that the codes themselves feed the matrix cores:
 //   q . k^_t   = sum_d (q_d S_gd) c_td + sum_d q_d Z_gd         (key group g)
 //   sum_t p_t v^_t,d = sum_t (p_t S_tm) c_td + sum_t p_t Z_tm   (value group m)
@@ -28,8 +31,8 @@
 // lanes exponentiates 8 of them (the matrix layout leaves them on 16 lanes).
 //
 // The residual window (at most R tokens, stored in kv dtype) is handled on the
-// vector ALUs in fp32 by the wave of the unit's last packed split, after its
-// packed groups, as a partial of its own.
+// vector ALUs in fp32 by the value wave of the unit's last packed split, after
+// its packed groups, as a partial of its own.
 #include <hip/hip_bf16.h>
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
@@ -182,17 +185,39 @@ __device__ __forceinline__ float xor_max(float v, int m) { return fmaxf(v, __shf
 __device__ __forceinline__ float xor_sum(float v, int m) { return v + __shfl_xor(v, m); }
 
 // ---------------------------------------------------------------------------
-// Residual window on the vector ALUs (one wave, fp32), written as the last
-// split of the unit.
+// Synchronisation.  global->LDS loads are counted by vmcnt and complete in
+// issue order; one wave's LDS operations execute in order, so waiting for
+// this wave's own LDS operations (lgkmcnt) orders its LDS traffic without
+// draining the loads still in flight.  (__syncthreads would wait for them.)
+
+// Waits until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Both waves of the workgroup: this wave's LDS writes are complete, then
+// meet.  Outstanding global->LDS loads stay in flight.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// Residual window on the vector ALUs (one wave, fp32), written as its own
+// partial.  qsh / psh: LDS scratch of this wave.
 template <bool BF16>
 __device__ void window_wave(const DecodeArgs& a, long long u, int b, int kvh, int split,
                             float (*qsh)[D], float (*psh)[G]) {
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   for (int i = lane; i < GQ * D; i += 64) {
     qsh[i / D][i % D] =
         to_f32<BF16>(a.q[((long long)b * a.Hq + kvh * GQ + i / D) * D + i % D]) * a.qscale;
   }
-  __syncthreads();
+  wave_lds_sync();
   float m[GQ], l[GQ], o[GQ][2];
 #pragma unroll
   for (int h = 0; h < GQ; ++h) {
@@ -235,7 +260,7 @@ __device__ void window_wave(const DecodeArgs& a, long long u, int b, int kvh, in
       o[h][1] *= alpha;
       if (lane < G) psh[h][lane] = p;
     }
-    __syncthreads();
+    wave_lds_sync();
     const int n = min(G, a.n_resid - c0);
     for (int tt = 0; tt < n; ++tt) {
       const uint32_t vv = *reinterpret_cast<const uint32_t*>(a.v_resid + (u * a.R + c0 + tt) * D + 2 * lane);
@@ -247,7 +272,7 @@ __device__ void window_wave(const DecodeArgs& a, long long u, int b, int kvh, in
         o[h][1] = fmaf(psh[h][tt], v1, o[h][1]);
       }
     }
-    __syncthreads();
+    wave_lds_sync();
   }
 #pragma unroll
   for (int h = 0; h < GQ; ++h) {
@@ -262,18 +287,17 @@ __device__ void window_wave(const DecodeArgs& a, long long u, int b, int kvh, in
 }
 
 // ---------------------------------------------------------------------------
-// LDS stages of one step (4 consecutive packed groups of one unit), filled
-// by direct global->LDS loads (64 lanes x 16 bytes = 1 KiB per instruction).
-// Key stage (double-buffered):
-//   K codes  4 groups x 32 rows x D*KB/8 bytes (token-major rows); each group
-//            padded by 64 bytes so the 4 groups fall on different banks
-//   K scale  4 x D fp16, K zero 4 x D fp16
-// Value stage (single-buffered, refilled right after the value side of the
-// previous step):
-//   V codes  4 groups x (G/PV words) x D words
-//   V scale  4 x 4 x G fp16, V zero likewise
-// The probabilities of a step (4 x 4 x 32 fp32) reuse the key-code area of
-// the current key stage, whose codes are consumed before the softmax.
+// LDS of one workgroup.  A step covers 4 consecutive packed groups of one
+// unit; stages are filled by direct global->LDS loads (64 lanes x 16 bytes =
+// 1 KiB per instruction).
+//   key stage   x2 (key wave): codes 4 groups x 32 rows x D*KB/8 bytes, each
+//               group padded by 64 bytes (the 4 groups fall on different
+//               banks); scale 4 x D fp16; zero 4 x D fp16.  The step's scores
+//               reuse the code area once the codes are in registers.
+//   value stage x2 (value wave): codes 4 groups x (G/PV words) x D words;
+//               scale 4 x 4 x G fp16; zero likewise.
+//   hand-over   x2: probabilities [stream][head][kRowP] fp32 and the
+//               rescale factor of each head, written by the key wave.
 template <int KB, int VB>
 struct Stage {
   static constexpr int kRow = D * KB / 8;              // bytes per key row
@@ -284,14 +308,19 @@ struct Stage {
   static constexpr int vGroup = (G * VB / 32) * D * 4; // 1 or 2 KiB
   static constexpr int offVS = 4 * vGroup, offVZ = offVS + 4 * D * 2;
   static constexpr int vBytes = offVZ + 4 * D * 2;
-  static constexpr int bytes = 2 * kBytes + vBytes;    // LDS per wave
+  static constexpr int offAlpha = 4 * GQ * kRowP * 4;   // in a hand-over buffer
+  static constexpr int pBytes = offAlpha + 16 * 4;
+  static constexpr int offV0 = 2 * kBytes, offP0 = offV0 + 2 * vBytes;
+  static constexpr int bytes = offP0 + 2 * pBytes;     // LDS per workgroup
   static constexpr int kLoads = (4 * kGroup + 2 * 4 * D * 2) / 1024;  // DMA instructions
   static constexpr int vLoads = (4 * vGroup + 2 * 4 * D * 2) / 1024;
-  static_assert(4 * kGroupPad >= GQ * GQ * 36 * 4, "scores fit in the key-code area");
+  static_assert(4 * kGroupPad >= 4 * GQ * kRowP * 4, "scores fit in the key-code area");
+  static_assert(vBytes >= (GQ * D + GQ * G) * 4, "window scratch fits in a value stage");
 };
-static_assert(Stage<2, 2>::bytes == mfma_wave_lds_bytes(2, 2), "lds");
-static_assert(Stage<4, 4>::bytes == mfma_wave_lds_bytes(4, 4), "lds");
-static_assert(Stage<2, 4>::bytes == mfma_wave_lds_bytes(2, 4), "lds");
+static_assert(Stage<2, 2>::bytes == mfma_wg_lds_bytes(2, 2), "lds");
+static_assert(Stage<4, 4>::bytes == mfma_wg_lds_bytes(4, 4), "lds");
+static_assert(Stage<2, 4>::bytes == mfma_wg_lds_bytes(2, 4), "lds");
+static_assert(Stage<4, 2>::bytes == mfma_wg_lds_bytes(4, 2), "lds");
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef const __attribute__((address_space(1))) void glb_void_t;
@@ -307,9 +336,9 @@ template <int KB, int VB>
 __device__ __forceinline__ void issue_kstage(const DecodeArgs& a, long long u, int g0, int ns,
                                              uint8_t* dst) {
   using S = Stage<KB, VB>;
-  const int lane = threadIdx.x;
-  const int glast = g0 + ns - 1;
   constexpr BlockLayout BL = block_layout(KB, VB);
+  const int lane = threadIdx.x & 63;
+  const int glast = g0 + ns - 1;
   const uint8_t* const unit = a.blocks + (u * a.nb) * (long long)BL.bytes;
 #pragma unroll
   for (int gi = 0; gi < 4; ++gi) {
@@ -330,9 +359,9 @@ template <int KB, int VB>
 __device__ __forceinline__ void issue_vstage(const DecodeArgs& a, long long u, int g0, int ns,
                                              uint8_t* dst) {
   using S = Stage<KB, VB>;
-  const int lane = threadIdx.x;
-  const int glast = g0 + ns - 1;
   constexpr BlockLayout BL = block_layout(KB, VB);
+  const int lane = threadIdx.x & 63;
+  const int glast = g0 + ns - 1;
   const uint8_t* const unit = a.blocks + (u * a.nb) * (long long)BL.bytes;
 #pragma unroll
   for (int gi = 0; gi < 4; ++gi) {
@@ -347,53 +376,21 @@ __device__ __forceinline__ void issue_vstage(const DecodeArgs& a, long long u, i
   dma16(meta + BL.v_zero, dst + S::offVZ);
 }
 
-// Waits until at most N vector-memory operations of this wave are in flight
-// (loads complete in issue order).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Orders LDS traffic inside the (single-wave) workgroup without waiting for
-// the stage loads still in flight: LDS operations of one wave execute in
-// order, so completing this wave's own LDS operations is enough.
-// (__syncthreads would also wait for every outstanding global load.)
-__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
+// ---------------------------------------------------------------------------
+// Key wave: scores of each step on the matrix cores, online softmax, and the
+// probabilities handed to the value wave.  Writes m and l of the partial.
 template <int KB, int VB, bool BF16>
-__global__ __launch_bounds__(64) void decode_mfma_gq4(DecodeArgs a) {
-  // one wave per workgroup: the in-loop synchronisation relies on it
+__device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b, int kvh, int split,
+                                         int gb, int ge, int n_steps, uint8_t* smem) {
   using S = Stage<KB, VB>;
   using KS = CodeScale<KB>;
   using VS = CodeScale<VB>;
-  constexpr int KL = KB;                    // key words per lane (32 channels)
-  __shared__ __align__(16) uint8_t smem[S::bytes];
-  uint8_t* const vstage = smem + 2 * S::kBytes;
-
-  const int lane = threadIdx.x;
+  constexpr int KL = KB;  // key words per lane (32 channels)
+  const int lane = threadIdx.x & 63;
   const int lc = lane & 15, lk = lane >> 4;
-  const int split = blockIdx.x;
-  const long long u = blockIdx.y;
-  const int b = static_cast<int>(u / a.H), kvh = static_cast<int>(u % a.H);
-
-  if (a.n_split_packed == 0) {  // nothing packed yet: the window is the only split
-    window_wave<BF16>(a, u, b, kvh, 0, reinterpret_cast<float (*)[D]>(smem),
-                      reinterpret_cast<float (*)[G]>(smem + GQ * D * 4));
-    return;
-  }
-
-  const int nqg = a.n_quant / G;
-  const int gb = split * a.groups_per_split;
-  const int ge = min(nqg, gb + a.groups_per_split);
-  const int n_steps = (ge - gb + 3) / 4;
-  if (n_steps > 0) {
-    issue_kstage<KB, VB>(a, u, gb, min(4, ge - gb), smem);
-    issue_vstage<KB, VB>(a, u, gb, min(4, ge - gb), vstage);
-  }
-
   const int hq = lc >> 2;  // head of this lane's B / C columns
+  const int jt = lc & 3;
+
   // q' = q * softmax_scale * log2(e) for head hq, channels 32*lk .. 32*lk+31,
   // times the code-position factor 2^lf of the key codes it multiplies
   float qf[32];
@@ -411,32 +408,25 @@ __global__ __launch_bounds__(64) void decode_mfma_gq4(DecodeArgs a) {
       }
     }
   }
+  issue_kstage<KB, VB>(a, u, gb, min(4, ge - gb), smem);
   constexpr float k_unscale = static_cast<float>(1 << (24 - KS::F));  // product -> score
-  constexpr float v_unscale = static_cast<float>(1 << (24 - VS::F));  // product -> output
 
-  const bool diag = (lc & 3) == lk;  // lane holds scores / outputs (stream or m = lk)
+  const bool diag = (lc & 3) == lk;  // lane holds scores (stream lk)
   float m_run = -INFINITY;           // running max of head hq (base 2)
   float lcls[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // sum of scaled p, per pair class e'
-  float zcls[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // sum of scaled p * Z, per pair class e'
-  f32x4 o[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   for (int step = 0; step < n_steps; ++step) {
     const int g0 = gb + 4 * step;
     const int ns = min(4, ge - g0);
     uint8_t* cur = smem + (step & 1) * S::kBytes;
-    const bool more = step + 1 < n_steps;
-    // in flight, oldest first: K(step), V(step) [, K(step+1)]
-    if (more) {
+    if (step + 1 < n_steps) {
       issue_kstage<KB, VB>(a, u, g0 + 4, min(4, ge - g0 - 4), smem + ((step + 1) & 1) * S::kBytes);
-      wait_vm<S::vLoads + S::kLoads>();
+      wait_vm<S::kLoads>();
     } else {
-      wait_vm<S::vLoads>();
+      wait_vm<0>();
     }
     wave_lds_sync();
 
-    // ------------------------------------------------------------- key side
     const int ga = lc >> 2;  // stream of this lane's A row
     const int gc = lc & 3;   // stream of this lane's B column
     const u32x4* sBp = reinterpret_cast<const u32x4*>(cur + S::offKS + gc * D * 2 + 64 * lk);
@@ -498,26 +488,25 @@ __global__ __launch_bounds__(64) void decode_mfma_gq4(DecodeArgs a) {
 #pragma unroll
       for (int s = 0; s < 8; ++s) sc[s] = mfma(ak[s], bl[c], sc[s]);
     }
+
     // ------------------------------------------------------------- softmax
     // The 16 diagonal lanes hold the step's 512 scores (head hq, stream lk,
     // 32 tokens each).  They pass through LDS so that every lane takes 8 of
     // them: lane (hq, j = lc & 3, lk) owns tokens 8j .. 8j+7 of stream lk.
-    // Rows of 32 scores are padded to 36 floats: the 16 rows start on
+    // Rows of 32 scores are padded to kRowP floats: the 16 rows start on
     // distinct banks.
-    float* const sl = reinterpret_cast<float*>(cur);  // [stream][head][36]
+    float* const sl = reinterpret_cast<float*>(cur);  // [stream][head][kRowP]
     wave_lds_sync();  // key codes of this stage fully read before they are overwritten
     if (diag) {
 #pragma unroll
       for (int s = 0; s < 8; ++s)
         *reinterpret_cast<f32x4*>(sl + (lk * GQ + hq) * kRowP + 4 * s) = sc[s] * k_unscale;
     }
-    // one wave's LDS operations complete in order: the reads see the writes
-    const int jt = lc & 3;
-    float* const myrow = sl + (lk * GQ + hq) * kRowP + 8 * jt;
+    const int row = (lk * GQ + hq) * kRowP + 8 * jt;
     float x[8];
     {
-      const f32x4 x0 = *reinterpret_cast<const f32x4*>(myrow);
-      const f32x4 x1 = *reinterpret_cast<const f32x4*>(myrow + 4);
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(sl + row);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(sl + row + 4);
       const bool valid = lk < ns;  // streams past the last group hold no tokens
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -531,42 +520,87 @@ __global__ __launch_bounds__(64) void decode_mfma_gq4(DecodeArgs a) {
     mx = swap_max<16>(mx);
     mx = swap_max<32>(mx);  // max over the 4 streams and 32 tokens of head hq
     const float m_new = fmaxf(m_run, mx);
-    if (__any(m_new > m_run)) {
-      const float alpha = (m_run == -INFINITY) ? 0.0f : fast_exp2(m_run - m_new);
+    // rescale factor of the running sums; exactly 1 when the max holds
+    const float alpha = !(m_new > m_run) ? 1.0f : (m_run == -INFINITY ? 0.0f : fast_exp2(m_run - m_new));
+    m_run = m_new;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) o[i] *= alpha;
+    for (int e = 0; e < 4; ++e) lcls[e] *= alpha;
+    // p scaled by the value-code factor of its token position: token t sits
+    // in pair class e'(t) = (t mod 8) / 2 of its run of 8
+    f32x4 p0, p1;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        zcls[e] *= alpha;
-        lcls[e] *= alpha;
-      }
-      m_run = m_new;
+    for (int i = 0; i < 4; ++i) {
+      p0[i] = fast_exp2(x[i] + (static_cast<float>(VS::lf(i >> 1)) - m_run));
+      p1[i] = fast_exp2(x[4 + i] + (static_cast<float>(VS::lf(2 + (i >> 1))) - m_run));
     }
-    {
-      // p scaled by the value-code factor of its token position: token t
-      // sits in pair class e'(t) = (t mod 8) / 2 of its run of 8
-      f32x4 p0, p1;
+    lcls[0] += p0[0] + p0[1];
+    lcls[1] += p0[2] + p0[3];
+    lcls[2] += p1[0] + p1[1];
+    lcls[3] += p1[2] + p1[3];
+    // hand-over buffer of this step: the value wave consumed it two steps ago
+    float* const hp = reinterpret_cast<float*>(smem + S::offP0 + (step & 1) * S::pBytes);
+    *reinterpret_cast<f32x4*>(hp + row) = p0;
+    *reinterpret_cast<f32x4*>(hp + row + 4) = p1;
+    if (lk == 0 && jt == 0) hp[S::offAlpha / 4 + hq] = alpha;
+    wg_barrier();  // step's probabilities ready
+  }
+
+  float l = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p0[i] = fast_exp2(x[i] + (static_cast<float>(VS::lf(i >> 1)) - m_run));
-        p1[i] = fast_exp2(x[4 + i] + (static_cast<float>(VS::lf(2 + (i >> 1))) - m_run));
-      }
-      lcls[0] += p0[0] + p0[1];
-      lcls[1] += p0[2] + p0[3];
-      lcls[2] += p1[0] + p1[1];
-      lcls[3] += p1[2] + p1[3];
-      *reinterpret_cast<f32x4*>(myrow) = p0;
-      *reinterpret_cast<f32x4*>(myrow + 4) = p1;
-    }
-    // the value stage of this step was issued before K(step+1)
+  for (int e = 0; e < 4; ++e) l = fmaf(lcls[e], 1.0f / static_cast<float>(1 << VS::lf(e)), l);
+  l = l + partner<1>(l);
+  l = l + partner<2>(l);
+  l = swap_sum<16>(l);
+  l = swap_sum<32>(l);  // the 16 lanes of head hq
+  if (lk == 0 && jt == 0) {
+    float* P = a.partial + (((long long)b * a.Hq + kvh * GQ + hq) * a.n_split + split) * (D + 2);
+    P[0] = m_run;
+    P[1] = l;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Value wave: p.V of each step on the matrix cores, one step behind the key
+// wave.  Writes o of the partial; the last split also runs the window.
+template <int KB, int VB, bool BF16>
+__device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int b, int kvh, int split,
+                                           int gb, int ge, int n_steps, uint8_t* smem) {
+  using S = Stage<KB, VB>;
+  using VS = CodeScale<VB>;
+  const int lane = threadIdx.x & 63;
+  const int lc = lane & 15, lk = lane >> 4;
+  const int hq = lc >> 2;
+  const int mcol = lc & 3;  // channel group of this lane's B column
+  uint8_t* const vbase = smem + S::offV0;
+  issue_vstage<KB, VB>(a, u, gb, min(4, ge - gb), vbase);
+  constexpr float v_unscale = static_cast<float>(1 << (24 - VS::F));  // product -> output
+
+  float zcls[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // sum of scaled p * Z, per pair class e'
+  f32x4 o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (int step = 0; step < n_steps; ++step) {
+    const int g0 = gb + 4 * step;
+    const int ns = min(4, ge - g0);
+    const uint8_t* vstage = vbase + (step & 1) * S::vBytes;
+    const bool more = step + 1 < n_steps;
+    if (more) issue_vstage<KB, VB>(a, u, g0 + 4, min(4, ge - g0 - 4), vbase + ((step + 1) & 1) * S::vBytes);
+    wg_barrier();  // the key wave has written this step's probabilities
     if (more) {
-      wait_vm<S::kLoads>();
+      wait_vm<S::vLoads>();
     } else {
       wait_vm<0>();
     }
     wave_lds_sync();
-    // ------------------------------------------------------------- value side
-    const int mcol = lc & 3;  // channel group of this lane's B column
+    const float* hp = reinterpret_cast<const float*>(smem + S::offP0 + (step & 1) * S::pBytes);
+    const float alpha = hp[S::offAlpha / 4 + hq];
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] *= alpha;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) zcls[e] *= alpha;
+    }
     for (int gs = 0; gs < ns; ++gs) {
       const int w = (VB == 2) ? (lk >> 1) : lk;
       const u32x4* vp = reinterpret_cast<const u32x4*>(vstage + gs * S::vGroup + (w * D + 8 * lc) * 4);
@@ -574,7 +608,7 @@ __global__ __launch_bounds__(64) void decode_mfma_gq4(DecodeArgs a) {
       const int vmo = ((gs * 4 + mcol) * G + 8 * lk) * 2;
       const u32x4 vs = *reinterpret_cast<const u32x4*>(vstage + S::offVS + vmo);
       const u32x4 vz = *reinterpret_cast<const u32x4*>(vstage + S::offVZ + vmo);
-      const float* prow = sl + (gs * GQ + hq) * kRowP + 8 * lk;
+      const float* prow = hp + (gs * GQ + hq) * kRowP + 8 * lk;
       const f32x4 p0 = *reinterpret_cast<const f32x4*>(prow);
       const f32x4 p1 = *reinterpret_cast<const f32x4*>(prow + 4);
       const float p[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
@@ -599,31 +633,16 @@ __global__ __launch_bounds__(64) void decode_mfma_gq4(DecodeArgs a) {
 #pragma unroll
       for (int be = 0; be < 8; ++be) o[be] = mfma(av[be], bpl, o[be]);
     }
-    wave_lds_sync();  // value stage and probabilities fully read
-    if (more) issue_vstage<KB, VB>(a, u, g0 + 4, min(4, ge - g0 - 4), vstage);
   }
 
-  // ------------------------------------------------------------- partials
-  float l = 0.0f, z = 0.0f;
+  float z = 0.0f;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float f = 1.0f / static_cast<float>(1 << VS::lf(e));
-    l = fmaf(lcls[e], f, l);
-    z = fmaf(zcls[e], f, z);
-  }
-  l = l + partner<1>(l);
-  l = l + partner<2>(l);
-  l = swap_sum<16>(l);
-  l = swap_sum<32>(l);
+  for (int e = 0; e < 4; ++e) z = fmaf(zcls[e], 1.0f / static_cast<float>(1 << VS::lf(e)), z);
   z = swap_sum<16>(z);
   z = swap_sum<32>(z);  // sum over the 4 row chunks: head hq, channel group lc & 3
-  float* P = a.partial + (((long long)b * a.Hq + kvh * GQ + hq) * a.n_split + split) * (D + 2);
-  if (lk == 0 && (lc & 3) == 0) {
-    P[0] = m_run;
-    P[1] = l;
-  }
-  if (diag) {
+  if ((lc & 3) == lk) {
     // rows 4*lk + r of channel block be = channel 32*lk + 8*r + be
+    float* P = a.partial + (((long long)b * a.Hq + kvh * GQ + hq) * a.n_split + split) * (D + 2);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       f32x4 x0, x1;
@@ -636,11 +655,39 @@ __global__ __launch_bounds__(64) void decode_mfma_gq4(DecodeArgs a) {
       *reinterpret_cast<f32x4*>(P + 2 + 32 * lk + 8 * r + 4) = x1;
     }
   }
-  // the last packed split also takes the window (its own partial); every
-  // stage load has completed and the LDS is free again
+  // the last packed split also takes the window (its own partial); this
+  // wave's stage loads have completed and its value stages are free
   if (split == a.n_split_packed - 1 && a.n_resid > 0) {
-    window_wave<BF16>(a, u, b, kvh, a.n_split_packed, reinterpret_cast<float (*)[D]>(smem),
-                      reinterpret_cast<float (*)[G]>(smem + GQ * D * 4));
+    wave_lds_sync();
+    window_wave<BF16>(a, u, b, kvh, a.n_split_packed, reinterpret_cast<float (*)[D]>(vbase),
+                      reinterpret_cast<float (*)[G]>(vbase + GQ * D * 4));
+  }
+}
+
+template <int KB, int VB, bool BF16>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma_gq4(DecodeArgs a) {
+  using S = Stage<KB, VB>;
+  __shared__ __align__(16) uint8_t smem[S::bytes];
+  const int wave = threadIdx.x >> 6;  // 0: key wave, 1: value wave
+  const int split = blockIdx.x;
+  const long long u = blockIdx.y;
+  const int b = static_cast<int>(u / a.H), kvh = static_cast<int>(u % a.H);
+
+  if (a.n_split_packed == 0) {  // nothing packed yet: the window is the only split
+    if (wave == 1)
+      window_wave<BF16>(a, u, b, kvh, 0, reinterpret_cast<float (*)[D]>(smem + S::offV0),
+                        reinterpret_cast<float (*)[G]>(smem + S::offV0 + GQ * D * 4));
+    return;
+  }
+  const int nqg = a.n_quant / G;
+  const int gb = split * a.groups_per_split;
+  const int ge = min(nqg, gb + a.groups_per_split);
+  const int n_steps = (ge - gb + 3) / 4;  // >= 1: every split holds a group
+  // Both waves run the same number of steps and meet at one barrier per step.
+  if (wave == 0) {
+    key_wave<KB, VB, BF16>(a, u, b, kvh, split, gb, ge, n_steps, smem);
+  } else {
+    value_wave<KB, VB, BF16>(a, u, b, kvh, split, gb, ge, n_steps, smem);
   }
 }
 
@@ -648,7 +695,7 @@ template <int KB, int VB, bool BF16>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   // one workgroup per packed split; the last one also runs the window
   dim3 grid(a.n_split_packed > 0 ? a.n_split_packed : 1, a.B * a.H);
-  hipLaunchKernelGGL((decode_mfma_gq4<KB, VB, BF16>), grid, dim3(64), 0, stream, a);
+  hipLaunchKernelGGL((decode_mfma_gq4<KB, VB, BF16>), grid, dim3(128), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -71,12 +71,13 @@ struct DecodeArgs {
   float qscale;         // softmax_scale * log2(e): scores in base-2 units
 };
 
-// LDS bytes of one wave of the matrix-core decode kernel: two key stages
-// (codes + scale/zero of 4 groups) and one value stage.  Bounds the number
-// of resident waves per CU.
-constexpr int mfma_wave_lds_bytes(int k_bits, int v_bits) {
+// LDS bytes of one workgroup (key wave + value wave) of the matrix-core
+// decode kernel: two key stages, two value stages and two hand-over buffers.
+// Bounds the number of resident workgroups per CU.
+constexpr int mfma_wg_lds_bytes(int k_bits, int v_bits) {
   return 2 * (4 * (kGroup * kHeadDim * k_bits / 8 + 64) + 2 * 4 * kHeadDim * 2) +
-         (4 * kGroup * v_bits / 32 * kHeadDim * 4 + 2 * 4 * kHeadDim * 2);
+         2 * (4 * kGroup * v_bits / 32 * kHeadDim * 4 + 2 * 4 * kHeadDim * 2) +
+         2 * (4 * 4 * 36 * 4 + 16 * 4);
 }
 constexpr int kLdsPerCu = 160 * 1024;  // MI355X (gfx950)
 
