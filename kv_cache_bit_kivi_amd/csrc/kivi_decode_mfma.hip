@@ -445,10 +445,15 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
         for (int i = 0; i < KL; ++i) kw[s][i] = v[i];
       }
     }
-    // B = q' * S (hi, lo) for head hq and group g0 + gc; zero-point term
-    // sum_d q'_d Z_d of the same (head, group) on the vector ALUs
-    half8_t bh[4], bl[4];
+    // B = q' * S (hi, lo) for head hq and group g0 + gc, built per block of
+    // 32 channels right before its products (the vector work of block c+1
+    // overlaps the matrix products of block c); zero-point term
+    // sum_d q'_d Z_d of the same (head, group) on the vector ALUs, added to
+    // the scores afterwards
     float bcls[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // per pair class: q' carries 2^lf(e)
+    f32x4 sc[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) sc[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const u32x4 sB = sBp[c], zB = zBp[c];
@@ -463,31 +468,21 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
         bcls[e] = fmaf(q0, lo_half(zB[e]), bcls[e]);
         bcls[e] = fmaf(q1, hi_half(zB[e]), bcls[e]);
       }
-      bh[c] = as_h8(h4);
-      bl[c] = as_h8(l4);
+      const half8_t bh = as_h8(h4), bl = as_h8(l4);
+      half8_t ak[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        ak[s] = (KB == 2) ? codes8<2>(kw[s][c >> 1], c & 1) : codes8<4>(kw[s][c & (KL - 1)], false);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) sc[s] = mfma(ak[s], bh, sc[s]);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) sc[s] = mfma(ak[s], bl, sc[s]);
     }
     float bias = 0.0f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) bias = fmaf(bcls[e], 1.0f / static_cast<float>(1 << KS::lf(e)), bias);
     bias = swap_sum<16>(bias);
     bias = swap_sum<32>(bias);  // all 128 channels: head hq, group g0 + (lc & 3)
-    // accumulators start at the zero-point term, in product units
-    const float b0 = bias * (1.0f / k_unscale);
-    const f32x4 binit = f32x4{b0, b0, b0, b0};
-    // scores of 8 steps x 4 rows; row 4*ga + r = token 4*s + r of stream ga;
-    // 8 independent accumulators so consecutive MFMAs never depend
-    f32x4 sc[8];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      half8_t ak[8];
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-        ak[s] = (KB == 2) ? codes8<2>(kw[s][c >> 1], c & 1) : codes8<4>(kw[s][c & (KL - 1)], false);
-#pragma unroll
-      for (int s = 0; s < 8; ++s) sc[s] = mfma(ak[s], bh[c], c == 0 ? binit : sc[s]);
-#pragma unroll
-      for (int s = 0; s < 8; ++s) sc[s] = mfma(ak[s], bl[c], sc[s]);
-    }
 
     // ------------------------------------------------------------- softmax
     // The 16 diagonal lanes hold the step's 512 scores (head hq, stream lk,
@@ -500,7 +495,7 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
     if (diag) {
 #pragma unroll
       for (int s = 0; s < 8; ++s)
-        *reinterpret_cast<f32x4*>(sl + (lk * GQ + hq) * kRowP + 4 * s) = sc[s] * k_unscale;
+        *reinterpret_cast<f32x4*>(sl + (lk * GQ + hq) * kRowP + 4 * s) = sc[s] * k_unscale + bias;
     }
     const int row = (lk * GQ + hq) * kRowP + 8 * jt;
     float x[8];
