@@ -56,22 +56,65 @@ __device__ __forceinline__ void group_consts(float mn, float mx, float& s, float
   }
 }
 
-// Code of x: clamp(rne(RN(RN(x - mn) / s)), 0, qmax).
+// Code of x: rne(RN(RN(x - mn) / s)).  The clamp to [0, qmax] of the
+// definition never changes a code here: 0 <= RN(x - mn) <= RN(mx - mn) and
+// s = RN(RN(mx - mn) / qmax), so RN(RN(x - mn) / s) <= qmax * (1 + 2^-23),
+// which rounds to at most qmax.
+//
 // Fast path y = RN(d * rcp).  With rcp = RN(1/s), |y - RN(d / s)| is below
 // 3 * 2^-24 * |d / s| <= 3 * 2^-24 * 16 < 2^-18, so rounding y to an integer
-// gives the same result unless y lies within 2^-18 of a half-integer; those
-// rare elements (and NaN from the tiny-scale case) redo the exact division.
-template <int QMAX>
-__device__ __forceinline__ uint32_t quant_code(float x, float mn, float s, float rcp) {
-  const float d = x - mn;
+// gives the same result unless y lies within 2^-18 of a half-integer; `redo`
+// records those (and NaN from the tiny-scale case), and the caller then
+// recomputes its codes with exact_code.
+__device__ __forceinline__ float fast_code_d(float d, float rcp, bool& redo) {
   const float y = d * rcp;
-  float r = rintf(y);
-  const float f = y - r;  // exact: y and r are within 1/2 of each other
-  if (!(fabsf(f) <= 0.49999237060546875f)) {  // 0.5 - 2^-17
-    r = rintf(d / s);
+  const float r = rintf(y);
+  redo |= !(fabsf(y - r) <= 0.49999237060546875f);  // 0.5 - 2^-17
+  return r;
+}
+
+// d = RN(x - mn) for element SEL (0: low, 1: high half) of a packed pair.
+// fp16: one v_fma_mix_f32 computes x * 1 - mn with a single rounding (the
+// fp16 operand is widened exactly), i.e. the same RN(x - mn).
+template <bool BF16, int SEL>
+__device__ __forceinline__ float diff(uint32_t pair, float mn) {
+  if constexpr (BF16) {
+    const float x = SEL ? __uint_as_float(pair & 0xffff0000u) : __uint_as_float(pair << 16);
+    return x - mn;
+  } else {
+    float d;
+    if constexpr (SEL == 0) {
+      asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(pair), "v"(mn));
+    } else {
+      asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(pair), "v"(mn));
+    }
+    return d;
   }
-  r = fminf(fmaxf(r, 0.0f), static_cast<float>(QMAX));
-  return static_cast<uint32_t>(r);
+}
+
+// Codes are accumulated as exact binary32 integers: the even codes of a word
+// (its low half) as sum c * 2^(b*k) and the odd codes likewise; each half
+// stays below 2^16, so every fma is exact.
+__device__ __forceinline__ uint32_t halves_to_word(float lo, float hi) {
+  return static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
+}
+
+// Code by the definition (one IEEE division); every code is 0 when s == 0.
+__device__ __forceinline__ float exact_code(float x, float mn, float s) {
+  return s == 0.0f ? 0.0f : rintf((x - mn) / s);
+}
+
+__device__ __forceinline__ float lo_f16(uint32_t w) { return __half2float(__ushort_as_half(static_cast<uint16_t>(w))); }
+__device__ __forceinline__ float hi_f16(uint32_t w) { return __half2float(__ushort_as_half(static_cast<uint16_t>(w >> 16))); }
+template <bool BF16>
+__device__ __forceinline__ float lo_x(uint32_t w) {
+  if constexpr (BF16) return __uint_as_float(w << 16);
+  else return lo_f16(w);
+}
+template <bool BF16>
+__device__ __forceinline__ float hi_x(uint32_t w) {
+  if constexpr (BF16) return __uint_as_float(w & 0xffff0000u);
+  else return hi_f16(w);
 }
 
 // Bit offset of code i in a word: even codes low half-word, odd codes high.
@@ -80,18 +123,23 @@ __device__ __forceinline__ int code_shift(int i) {
   return BITS * (i >> 1) + 16 * (i & 1);
 }
 
+// Orders this workgroup's LDS traffic; unlike __syncthreads it does not wait
+// for the scale/zero stores just issued to complete.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <int KB, int VB, bool BF16>
 __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
   constexpr int QK = (1 << KB) - 1, QV = (1 << VB) - 1;
   constexpr int PK = 32 / KB;  // key codes (channels) per word
   constexpr int KW = D / PK;   // key words per token
   constexpr int PV = 32 / VB;  // value codes (rows) per word
-  constexpr int VW = G / PV;   // value words per (block, channel)
 
   __shared__ __align__(16) uint16_t kt[G * RS];
   __shared__ __align__(16) uint16_t vt[G * RS];
-  __shared__ float kmn[D], ksc[D], krc[D];
-  __shared__ float vmn[4 * G], vsc[4 * G], vrc[4 * G];  // index m * G + row
+  __shared__ __align__(16) float kmn[D], ksc[D], krc[D];
+  __shared__ __align__(16) float vmn[4 * G], vsc[4 * G], vrc[4 * G];  // index m * G + row
 
   const int tid = threadIdx.x;
   const int item = blockIdx.x;
@@ -117,14 +165,17 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
   const int gblk = a.dst_blk0 + blk;
   uint8_t* const rec = a.blocks + (u * a.nb + gblk) * BL.bytes;  // this block's record
   {
-    const long long base = u * a.src_unit_stride + (long long)(a.src_tok0 + blk * G) * D;
-    for (int c = tid; c < G * D / 8; c += 256) {
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      const uint4 kx = *reinterpret_cast<const uint4*>(a.k_src + base + row * D + col);
-      const uint4 vx = *reinterpret_cast<const uint4*>(a.v_src + base + row * D + col);
-      *reinterpret_cast<uint4*>(&kt[row * RS + col]) = kx;
-      *reinterpret_cast<uint4*>(&vt[row * RS + col]) = vx;
-    }
+    // 16-byte pieces c = tid and c = tid + 256 of the 32 x 128 tiles
+    const int row = tid / (D / 8), col = (tid % (D / 8)) * 8;
+    const long long base = u * a.src_unit_stride + (long long)(a.src_tok0 + blk * G) * D + row * D + col;
+    const uint4 k0 = *reinterpret_cast<const uint4*>(a.k_src + base);
+    const uint4 k1 = *reinterpret_cast<const uint4*>(a.k_src + base + 16 * D);
+    const uint4 v0 = *reinterpret_cast<const uint4*>(a.v_src + base);
+    const uint4 v1 = *reinterpret_cast<const uint4*>(a.v_src + base + 16 * D);
+    *reinterpret_cast<uint4*>(&kt[row * RS + col]) = k0;
+    *reinterpret_cast<uint4*>(&kt[(row + 16) * RS + col]) = k1;
+    *reinterpret_cast<uint4*>(&vt[row * RS + col]) = v0;
+    *reinterpret_cast<uint4*>(&vt[(row + 16) * RS + col]) = v1;
   }
   __syncthreads();
 
@@ -164,35 +215,123 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
     reinterpret_cast<uint16_t*>(rec + BL.v_scale)[i] = f16_bits_canon(s);  // [m][row]
     reinterpret_cast<uint16_t*>(rec + BL.v_zero)[i] = f16_bits_canon(mn);
   }
-  __syncthreads();
+  lds_barrier();
 
-  // ---- key code words: token row t, word w holds channels w*PK .. w*PK+PK-1
-  for (int wi = tid; wi < G * KW; wi += 256) {
-    const int t = wi / KW, w = wi % KW;
-    uint32_t word = 0;
+  if (tid < 128) {
+    // ---- key code words: word w of token t holds channels w*PK .. w*PK+PK-1.
+    // Thread: one word index w, tokens tg, tg + TS, ... (NT tokens); the
+    // channels of the word are taken 8 at a time (fewer live registers).
+    constexpr int TS = 128 / KW, NT = G / TS;
+    const int w = tid % KW, tg = tid / KW;
+    float wlo[NT], whi[NT];  // the word's even / odd codes as exact integers
+    bool redo = false;
 #pragma unroll
-    for (int i = 0; i < PK; ++i) {
-      const int d = w * PK + i;
-      const uint32_t c = quant_code<QK>(to_f32<BF16>(kt[t * RS + d]), kmn[d], ksc[d], krc[d]);
-      word |= c << code_shift<KB>(i);
-    }
-    reinterpret_cast<uint32_t*>(rec + BL.k_codes)[t * KW + w] = word;
-  }
-
-  // ---- value code words: channel d, word w holds rows w*PV .. w*PV+PV-1;
-  // word-major, so consecutive threads write consecutive channels
-  for (int wi = tid; wi < D * VW; wi += 256) {
-    const int w = wi / D, d = wi % D;
-    const int m = d / G;
-    uint32_t word = 0;
+    for (int j = 0; j < NT; ++j) wlo[j] = whi[j] = 0.0f;
+#pragma unroll 1
+    for (int c8 = 0; c8 < PK; c8 += 8) {
+      const int d0 = w * PK + c8;
+      float mn[8], rc[8];
 #pragma unroll
-    for (int i = 0; i < PV; ++i) {
-      const int t = w * PV + i;
-      const int si = m * G + t;
-      const uint32_t c = quant_code<QV>(to_f32<BF16>(vt[t * RS + d]), vmn[si], vsc[si], vrc[si]);
-      word |= c << code_shift<VB>(i);
+      for (int i = 0; i < 8; i += 4) {
+        const float4 a4 = *reinterpret_cast<const float4*>(&kmn[d0 + i]);
+        const float4 c4 = *reinterpret_cast<const float4*>(&krc[d0 + i]);
+        mn[i] = a4.x; mn[i + 1] = a4.y; mn[i + 2] = a4.z; mn[i + 3] = a4.w;
+        rc[i] = c4.x; rc[i + 1] = c4.y; rc[i + 2] = c4.z; rc[i + 3] = c4.w;
+      }
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const uint4 v = *reinterpret_cast<const uint4*>(&kt[(tg + j * TS) * RS + d0]);
+        const uint32_t xw[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+          // codes c8 + i (even: low half) and c8 + i + 1 (odd: high half),
+          // both at bit KB * (c8 + i) / 2 of their half
+          const float wt = static_cast<float>(1 << (KB * ((c8 + i) >> 1)));
+          wlo[j] = fmaf(fast_code_d(diff<BF16, 0>(xw[i >> 1], mn[i]), rc[i], redo), wt, wlo[j]);
+          whi[j] = fmaf(fast_code_d(diff<BF16, 1>(xw[i >> 1], mn[i + 1]), rc[i + 1], redo), wt, whi[j]);
+        }
+      }
     }
-    reinterpret_cast<uint32_t*>(rec + BL.v_codes)[w * D + d] = word;
+    uint32_t word[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) word[j] = halves_to_word(wlo[j], whi[j]);
+    if (redo) {  // rare: recompute this thread's words with the exact division
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int t = tg + j * TS;
+        uint32_t wd = 0;
+        for (int i = 0; i < PK; ++i) {
+          const float x = to_f32<BF16>(kt[t * RS + w * PK + i]);
+          wd |= static_cast<uint32_t>(exact_code(x, kmn[w * PK + i], ksc[w * PK + i])) << code_shift<KB>(i);
+        }
+        word[j] = wd;
+      }
+    }
+    uint32_t* const kc = reinterpret_cast<uint32_t*>(rec + BL.k_codes);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) kc[(tg + j * TS) * KW + w] = word[j];
+  } else {
+    // ---- value code words: word w of channel d holds rows w*PV .. w*PV+PV-1;
+    // word-major, the D words of one w adjacent.  Thread: channels d0, d0+1
+    // (same channel group m) and rows 16*h .. 16*h+15 (16 / PV words each),
+    // taken 8 rows at a time.
+    const int i0 = tid - 128;
+    const int d0 = 2 * (i0 % 64), h = i0 / 64;
+    const int m = d0 / G;
+    constexpr int NW = 16 / PV;  // words per channel for these 16 rows
+    float l0[NW], h0[NW], l1[NW], h1[NW];  // even / odd codes of channels d0, d0+1
+    bool redo = false;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) l0[k] = h0[k] = l1[k] = h1[k] = 0.0f;
+#pragma unroll
+    for (int r8 = 0; r8 < 16; r8 += 8) {
+      const int sbase = m * G + 16 * h + r8;
+      float mn[8], rc[8];
+#pragma unroll
+      for (int j = 0; j < 8; j += 4) {
+        const float4 a4 = *reinterpret_cast<const float4*>(&vmn[sbase + j]);
+        const float4 c4 = *reinterpret_cast<const float4*>(&vrc[sbase + j]);
+        mn[j] = a4.x; mn[j + 1] = a4.y; mn[j + 2] = a4.z; mn[j + 3] = a4.w;
+        rc[j] = c4.x; rc[j + 1] = c4.y; rc[j + 2] = c4.z; rc[j + 3] = c4.w;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = r8 + j;  // row 16*h + r: word r / PV, position r % PV
+        const uint32_t xw = *reinterpret_cast<const uint32_t*>(&vt[(16 * h + r) * RS + d0]);
+        const int k = r / PV, pos = r % PV;
+        const float wt = static_cast<float>(1 << (VB * (pos >> 1)));
+        const float c0 = fast_code_d(diff<BF16, 0>(xw, mn[j]), rc[j], redo);  // channel d0
+        const float c1 = fast_code_d(diff<BF16, 1>(xw, mn[j]), rc[j], redo);  // channel d0 + 1
+        if (pos & 1) {
+          h0[k] = fmaf(c0, wt, h0[k]);
+          h1[k] = fmaf(c1, wt, h1[k]);
+        } else {
+          l0[k] = fmaf(c0, wt, l0[k]);
+          l1[k] = fmaf(c1, wt, l1[k]);
+        }
+      }
+    }
+    uint32_t w0[NW], w1[NW];
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      w0[k] = halves_to_word(l0[k], h0[k]);
+      w1[k] = halves_to_word(l1[k], h1[k]);
+    }
+    if (redo) {  // rare: recompute with the exact division
+#pragma unroll
+      for (int k = 0; k < NW; ++k) w0[k] = w1[k] = 0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int si = m * G + 16 * h + r;
+        const uint32_t xw = *reinterpret_cast<const uint32_t*>(&vt[(16 * h + r) * RS + d0]);
+        w0[r / PV] |= static_cast<uint32_t>(exact_code(lo_x<BF16>(xw), vmn[si], vsc[si])) << code_shift<VB>(r % PV);
+        w1[r / PV] |= static_cast<uint32_t>(exact_code(hi_x<BF16>(xw), vmn[si], vsc[si])) << code_shift<VB>(r % PV);
+      }
+    }
+    uint32_t* const vc = reinterpret_cast<uint32_t*>(rec + BL.v_codes);
+#pragma unroll
+    for (int k = 0; k < NW; ++k)
+      *reinterpret_cast<uint2*>(&vc[(h * NW + k) * D + d0]) = make_uint2(w0[k], w1[k]);
   }
 }
 
