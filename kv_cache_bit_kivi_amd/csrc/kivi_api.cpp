@@ -331,7 +331,8 @@ kivi_status kivi_decode_attn(const kivi_cache* cc, const void* q, int32_t num_q_
   const int G = c->cfg.group_size;
   const int units = c->cfg.batch * c->cfg.num_kv_heads;
   const int nqg = c->n_quant / G;
-  const bool use_mfma = gq == 4;
+  // matrix-core kernel: up to 4 query heads per kv head share one wave
+  const bool use_mfma = gq == 1 || gq == 2 || gq == 4;
   int n_split, per = 0, n_split_packed = 0, gps = 0;
   if (use_mfma) {
     // one wave per split; one round of as many waves as fit in LDS on every

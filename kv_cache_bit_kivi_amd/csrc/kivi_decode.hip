@@ -261,7 +261,7 @@ hipError_t launch_decode(const DecodeArgs& a, int k_bits, int v_bits, int kv_dty
   const bool bf = kv_dtype == 1;
   hipError_t e = hipErrorInvalidValue;
   if (use_mfma) {
-    e = launch_decode_mfma_gq4(a, k_bits, v_bits, kv_dtype, stream);
+    e = launch_decode_mfma(a, k_bits, v_bits, kv_dtype, stream);
   } else {
 #define KIVI_SPLIT_CASE(KB, VB)                                                   \
   if (k_bits == KB && v_bits == VB)                                               \

@@ -1,5 +1,7 @@
-// kivi_decode_mfma.hip - decode attention for 4 query heads per kv head
-// (grouped-query attention), with both contractions on the matrix cores.
+// kivi_decode_mfma.hip - decode attention with both contractions on the
+// matrix cores, for 1, 2 or 4 query heads per kv head (multi-head and
+// grouped-query attention).  The matrix columns hold 4 head slots; with
+// fewer heads the spare slots carry zeros and are masked out.
 //
 // Method: split-K decode attention over the packed cache (dequantized value =
 // code * scale + zero, page "KIVI: Asymmetric 2-Bit KV Cache Quantization
@@ -44,7 +46,7 @@ namespace {
 
 constexpr int G = kGroup;
 constexpr int D = kHeadDim;
-constexpr int GQ = 4;
+constexpr int GQ = 4;  // head slots of a wave (matrix columns); NQ <= GQ are used
 constexpr int kRowP = 36;  // LDS row of one (stream, head): 32 scores + 4 floats padding
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
@@ -209,18 +211,18 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // ---------------------------------------------------------------------------
 // Residual window on the vector ALUs (one wave, fp32), written as its own
 // partial.  qsh / psh: LDS scratch of this wave.
-template <bool BF16>
+template <bool BF16, int NQ>
 __device__ void window_wave(const DecodeArgs& a, long long u, int b, int kvh, int split,
                             float (*qsh)[D], float (*psh)[G]) {
   const int lane = threadIdx.x & 63;
-  for (int i = lane; i < GQ * D; i += 64) {
+  for (int i = lane; i < NQ * D; i += 64) {
     qsh[i / D][i % D] =
-        to_f32<BF16>(a.q[((long long)b * a.Hq + kvh * GQ + i / D) * D + i % D]) * a.qscale;
+        to_f32<BF16>(a.q[((long long)b * a.Hq + kvh * NQ + i / D) * D + i % D]) * a.qscale;
   }
   wave_lds_sync();
-  float m[GQ], l[GQ], o[GQ][2];
+  float m[NQ], l[NQ], o[NQ][2];
 #pragma unroll
-  for (int h = 0; h < GQ; ++h) {
+  for (int h = 0; h < NQ; ++h) {
     m[h] = -INFINITY;
     l[h] = 0.0f;
     o[h][0] = o[h][1] = 0.0f;
@@ -229,7 +231,9 @@ __device__ void window_wave(const DecodeArgs& a, long long u, int b, int kvh, in
   for (int c0 = 0; c0 < a.n_resid; c0 += G) {
     const int t = c0 + (lane & 31);
     const bool live = t < a.n_resid;
-    float acc[GQ] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float acc[NQ];
+#pragma unroll
+    for (int h = 0; h < NQ; ++h) acc[h] = 0.0f;
     if (live) {
       const uint16_t* kr = a.k_resid + (u * a.R + t) * D + 64 * half;
       for (int d0 = 0; d0 < 64; d0 += 8) {
@@ -239,12 +243,12 @@ __device__ void window_wave(const DecodeArgs& a, long long u, int b, int kvh, in
         for (int i = 0; i < 8; ++i) {
           const float kx = to_f32<BF16>(static_cast<uint16_t>(ww[i >> 1] >> (16 * (i & 1))));
 #pragma unroll
-          for (int h = 0; h < GQ; ++h) acc[h] = fmaf(qsh[h][64 * half + d0 + i], kx, acc[h]);
+          for (int h = 0; h < NQ; ++h) acc[h] = fmaf(qsh[h][64 * half + d0 + i], kx, acc[h]);
         }
       }
     }
 #pragma unroll
-    for (int h = 0; h < GQ; ++h) {
+    for (int h = 0; h < NQ; ++h) {
       float s = acc[h] + __shfl_xor(acc[h], 32);
       s = live ? s : -INFINITY;
       float mx = s;
@@ -267,7 +271,7 @@ __device__ void window_wave(const DecodeArgs& a, long long u, int b, int kvh, in
       const float v0 = to_f32<BF16>(static_cast<uint16_t>(vv & 0xffffu));
       const float v1 = to_f32<BF16>(static_cast<uint16_t>(vv >> 16));
 #pragma unroll
-      for (int h = 0; h < GQ; ++h) {
+      for (int h = 0; h < NQ; ++h) {
         o[h][0] = fmaf(psh[h][tt], v0, o[h][0]);
         o[h][1] = fmaf(psh[h][tt], v1, o[h][1]);
       }
@@ -275,8 +279,8 @@ __device__ void window_wave(const DecodeArgs& a, long long u, int b, int kvh, in
     wave_lds_sync();
   }
 #pragma unroll
-  for (int h = 0; h < GQ; ++h) {
-    float* P = a.partial + (((long long)b * a.Hq + kvh * GQ + h) * a.n_split + split) * (D + 2);
+  for (int h = 0; h < NQ; ++h) {
+    float* P = a.partial + (((long long)b * a.Hq + kvh * NQ + h) * a.n_split + split) * (D + 2);
     P[2 + 2 * lane] = o[h][0];
     P[3 + 2 * lane] = o[h][1];
     if (lane == 0) {
@@ -379,7 +383,7 @@ __device__ __forceinline__ void issue_vstage(const DecodeArgs& a, long long u, i
 // ---------------------------------------------------------------------------
 // Key wave: scores of each step on the matrix cores, online softmax, and the
 // probabilities handed to the value wave.  Writes m and l of the partial.
-template <int KB, int VB, bool BF16>
+template <int KB, int VB, bool BF16, int NQ>
 __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b, int kvh, int split,
                                          int gb, int ge, int n_steps, uint8_t* smem) {
   using S = Stage<KB, VB>;
@@ -393,9 +397,10 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
 
   // q' = q * softmax_scale * log2(e) for head hq, channels 32*lk .. 32*lk+31,
   // times the code-position factor 2^lf of the key codes it multiplies
+  // (head slots hq >= NQ carry q' = 0 and are masked out of the softmax)
   float qf[32];
-  {
-    const uint16_t* qp = a.q + ((long long)b * a.Hq + kvh * GQ + hq) * D + 32 * lk;
+  if (hq < NQ) {
+    const uint16_t* qp = a.q + ((long long)b * a.Hq + kvh * NQ + hq) * D + 32 * lk;
 #pragma unroll
     for (int i = 0; i < 32; i += 8) {
       const uint4 v = *reinterpret_cast<const uint4*>(qp + i);
@@ -407,6 +412,9 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
                     static_cast<float>(1 << KS::lf(ep));
       }
     }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) qf[i] = 0.0f;
   }
   issue_kstage<KB, VB>(a, u, gb, min(4, ge - gb), smem);
   constexpr float k_unscale = static_cast<float>(1 << (24 - KS::F));  // product -> score
@@ -502,7 +510,8 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
     {
       const f32x4 x0 = *reinterpret_cast<const f32x4*>(sl + row);
       const f32x4 x1 = *reinterpret_cast<const f32x4*>(sl + row + 4);
-      const bool valid = lk < ns;  // streams past the last group hold no tokens
+      // streams past the last group hold no tokens; slots hq >= NQ no head
+      const bool valid = lk < ns && hq < NQ;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         x[i] = valid ? x0[i] : -INFINITY;
@@ -547,8 +556,8 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
   l = l + partner<2>(l);
   l = swap_sum<16>(l);
   l = swap_sum<32>(l);  // the 16 lanes of head hq
-  if (lk == 0 && jt == 0) {
-    float* P = a.partial + (((long long)b * a.Hq + kvh * GQ + hq) * a.n_split + split) * (D + 2);
+  if (lk == 0 && jt == 0 && hq < NQ) {
+    float* P = a.partial + (((long long)b * a.Hq + kvh * NQ + hq) * a.n_split + split) * (D + 2);
     P[0] = m_run;
     P[1] = l;
   }
@@ -557,7 +566,7 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
 // ---------------------------------------------------------------------------
 // Value wave: p.V of each step on the matrix cores, one step behind the key
 // wave.  Writes o of the partial; the last split also runs the window.
-template <int KB, int VB, bool BF16>
+template <int KB, int VB, bool BF16, int NQ>
 __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int b, int kvh, int split,
                                            int gb, int ge, int n_steps, uint8_t* smem) {
   using S = Stage<KB, VB>;
@@ -635,9 +644,9 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
   for (int e = 0; e < 4; ++e) z = fmaf(zcls[e], 1.0f / static_cast<float>(1 << VS::lf(e)), z);
   z = swap_sum<16>(z);
   z = swap_sum<32>(z);  // sum over the 4 row chunks: head hq, channel group lc & 3
-  if ((lc & 3) == lk) {
+  if ((lc & 3) == lk && hq < NQ) {
     // rows 4*lk + r of channel block be = channel 32*lk + 8*r + be
-    float* P = a.partial + (((long long)b * a.Hq + kvh * GQ + hq) * a.n_split + split) * (D + 2);
+    float* P = a.partial + (((long long)b * a.Hq + kvh * NQ + hq) * a.n_split + split) * (D + 2);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       f32x4 x0, x1;
@@ -654,13 +663,13 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
   // wave's stage loads have completed and its value stages are free
   if (split == a.n_split_packed - 1 && a.n_resid > 0) {
     wave_lds_sync();
-    window_wave<BF16>(a, u, b, kvh, a.n_split_packed, reinterpret_cast<float (*)[D]>(vbase),
+    window_wave<BF16, NQ>(a, u, b, kvh, a.n_split_packed, reinterpret_cast<float (*)[D]>(vbase),
                       reinterpret_cast<float (*)[G]>(vbase + GQ * D * 4));
   }
 }
 
-template <int KB, int VB, bool BF16>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma_gq4(DecodeArgs a) {
+template <int KB, int VB, bool BF16, int NQ>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma(DecodeArgs a) {
   using S = Stage<KB, VB>;
   __shared__ __align__(16) uint8_t smem[S::bytes];
   const int wave = threadIdx.x >> 6;  // 0: key wave, 1: value wave
@@ -670,7 +679,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
 
   if (a.n_split_packed == 0) {  // nothing packed yet: the window is the only split
     if (wave == 1)
-      window_wave<BF16>(a, u, b, kvh, 0, reinterpret_cast<float (*)[D]>(smem + S::offV0),
+      window_wave<BF16, NQ>(a, u, b, kvh, 0, reinterpret_cast<float (*)[D]>(smem + S::offV0),
                         reinterpret_cast<float (*)[G]>(smem + S::offV0 + GQ * D * 4));
     return;
   }
@@ -680,27 +689,37 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
   const int n_steps = (ge - gb + 3) / 4;  // >= 1: every split holds a group
   // Both waves run the same number of steps and meet at one barrier per step.
   if (wave == 0) {
-    key_wave<KB, VB, BF16>(a, u, b, kvh, split, gb, ge, n_steps, smem);
+    key_wave<KB, VB, BF16, NQ>(a, u, b, kvh, split, gb, ge, n_steps, smem);
   } else {
-    value_wave<KB, VB, BF16>(a, u, b, kvh, split, gb, ge, n_steps, smem);
+    value_wave<KB, VB, BF16, NQ>(a, u, b, kvh, split, gb, ge, n_steps, smem);
   }
 }
 
-template <int KB, int VB, bool BF16>
+template <int KB, int VB, bool BF16, int NQ>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   // one workgroup per packed split; the last one also runs the window
   dim3 grid(a.n_split_packed > 0 ? a.n_split_packed : 1, a.B * a.H);
-  hipLaunchKernelGGL((decode_mfma_gq4<KB, VB, BF16>), grid, dim3(128), 0, stream, a);
+  hipLaunchKernelGGL((decode_mfma<KB, VB, BF16, NQ>), grid, dim3(128), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int KB, int VB, bool BF16>
+hipError_t launch_nq(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.gq) {
+    case 1: return launch_t<KB, VB, BF16, 1>(a, stream);
+    case 2: return launch_t<KB, VB, BF16, 2>(a, stream);
+    case 4: return launch_t<KB, VB, BF16, 4>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
-hipError_t launch_decode_mfma_gq4(const DecodeArgs& a, int k_bits, int v_bits, int kv_dtype,
-                                  hipStream_t stream) {
+hipError_t launch_decode_mfma(const DecodeArgs& a, int k_bits, int v_bits, int kv_dtype,
+                              hipStream_t stream) {
   const bool bf = kv_dtype == 1;
 #define KIVI_MFMA_CASE(KB, VB) \
-  if (k_bits == KB && v_bits == VB) return bf ? launch_t<KB, VB, true>(a, stream) : launch_t<KB, VB, false>(a, stream);
+  if (k_bits == KB && v_bits == VB) return bf ? launch_nq<KB, VB, true>(a, stream) : launch_nq<KB, VB, false>(a, stream);
   KIVI_MFMA_CASE(2, 2)
   KIVI_MFMA_CASE(2, 4)
   KIVI_MFMA_CASE(4, 2)

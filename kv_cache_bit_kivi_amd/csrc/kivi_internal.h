@@ -85,10 +85,10 @@ constexpr int kLdsPerCu = 160 * 1024;  // MI355X (gfx950)
 hipError_t launch_pack(const PackArgs& a, int k_bits, int v_bits, int kv_dtype,
                        hipStream_t stream);
 hipError_t launch_resid_copy(const PackArgs& a, int kv_dtype, hipStream_t stream);
-// use_mfma selects the matrix-core kernel (4 query heads per kv head).
+// use_mfma selects the matrix-core kernel (1, 2 or 4 query heads per kv head).
 hipError_t launch_decode(const DecodeArgs& a, int k_bits, int v_bits, int kv_dtype,
                          int out_dtype, bool use_mfma, hipStream_t stream);
-hipError_t launch_decode_mfma_gq4(const DecodeArgs& a, int k_bits, int v_bits, int kv_dtype,
+hipError_t launch_decode_mfma(const DecodeArgs& a, int k_bits, int v_bits, int kv_dtype,
                                   hipStream_t stream);
 
 }  // namespace kivi
