@@ -25,6 +25,7 @@ namespace {
 constexpr int G = kGroup;
 constexpr int D = kHeadDim;
 constexpr int RS = D + 8;  // LDS row stride in 16-bit elements (272 bytes)
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 template <bool BF16>
 __device__ __forceinline__ float to_f32(uint16_t h) {
@@ -40,10 +41,11 @@ __device__ __forceinline__ uint16_t f16_bits_canon(float f) {
   return f == 0.0f ? uint16_t(0) : __half_as_ushort(__float2half_rn(f));
 }
 
-// Per-group constants: minimum, binary32 scale s = (max - min) / qmax and the
-// reciprocal used by the fast path.  rcp = 0 when s == 0 (every code is then
-// 0) and NaN when s is so small that RN(1/s) could leave the normal range
-// (every code then takes the exact division).
+// Per-group constants: minimum, binary32 scale s = (max - min) / qmax (IEEE
+// division) and the reciprocal used by the fast path, v_rcp_f32 (within 1 ulp
+// of 1/s; the fast-path bound below allows 4 ulp).  rcp = 0 when s == 0
+// (every code is then 0) and NaN when s is so small that 1/s could leave the
+// normal range (every code then takes the exact division).
 template <int QMAX>
 __device__ __forceinline__ void group_consts(float mn, float mx, float& s, float& rcp) {
   s = (mx - mn) / static_cast<float>(QMAX);
@@ -52,7 +54,7 @@ __device__ __forceinline__ void group_consts(float mn, float mx, float& s, float
   } else if (s < 0x1p-100f) {
     rcp = __builtin_nanf("");
   } else {
-    rcp = 1.0f / s;
+    rcp = __builtin_amdgcn_rcpf(s);
   }
 }
 
@@ -61,11 +63,13 @@ __device__ __forceinline__ void group_consts(float mn, float mx, float& s, float
 // s = RN(RN(mx - mn) / qmax), so RN(RN(x - mn) / s) <= qmax * (1 + 2^-23),
 // which rounds to at most qmax.
 //
-// Fast path y = RN(d * rcp).  With rcp = RN(1/s), |y - RN(d / s)| is below
-// 3 * 2^-24 * |d / s| <= 3 * 2^-24 * 16 < 2^-18, so rounding y to an integer
-// gives the same result unless y lies within 2^-18 of a half-integer; `redo`
-// records those (and NaN from the tiny-scale case), and the caller then
-// recomputes its codes with exact_code.
+// Fast path y = RN(d * rcp).  With rcp = (1/s)(1 + e), |e| <= 4 * 2^-24, and
+// d / s <= 16: |y - d / s| <= 16 * (2^-22 + 2^-24 + 2^-46) < 1.25 * 2^-18 and
+// |RN(d / s) - d / s| <= 16 * 2^-24 = 0.25 * 2^-18, so y is within 1.5 * 2^-18
+// of RN(d / s).  Rounding y to an integer therefore gives the same result
+// unless y lies within 2^-17 of a half-integer; `redo` records those (and
+// NaN from the tiny-scale case), and the caller then recomputes its codes
+// with exact_code.
 __device__ __forceinline__ float fast_code_d(float d, float rcp, bool& redo) {
   const float y = d * rcp;
   const float r = rintf(y);
@@ -179,33 +183,77 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
   }
   __syncthreads();
 
-  // ---- group statistics
-  if (tid < D) {
-    // key group: channel d over the G rows of the block
-    const int d = tid;
-    float mn = to_f32<BF16>(kt[d]), mx = mn;
-    for (int t = 1; t < G; ++t) {
-      const float x = to_f32<BF16>(kt[t * RS + d]);
-      mn = fminf(mn, x);
-      mx = fmaxf(mx, x);
+  // ---- group statistics (min/max are exact in the input format; fp16
+  // pairs use the packed min/max instructions)
+  if (tid < D / 2) {
+    // key groups: channels 2p, 2p+1 over the G rows of the block
+    const int p2 = 2 * tid;
+    float mn0, mx0, mn1, mx1;
+    if constexpr (BF16) {
+      uint32_t x = *reinterpret_cast<const uint32_t*>(&kt[p2]);
+      mn0 = mx0 = __uint_as_float(x << 16);
+      mn1 = mx1 = __uint_as_float(x & 0xffff0000u);
+      for (int t = 1; t < G; ++t) {
+        x = *reinterpret_cast<const uint32_t*>(&kt[t * RS + p2]);
+        const float lo = __uint_as_float(x << 16), hi = __uint_as_float(x & 0xffff0000u);
+        mn0 = fminf(mn0, lo); mx0 = fmaxf(mx0, lo);
+        mn1 = fminf(mn1, hi); mx1 = fmaxf(mx1, hi);
+      }
+    } else {
+      half2_t mn = *reinterpret_cast<const half2_t*>(&kt[p2]), mx = mn;
+#pragma unroll 8
+      for (int t = 1; t < G; ++t) {
+        const half2_t x = *reinterpret_cast<const half2_t*>(&kt[t * RS + p2]);
+        mn = __builtin_elementwise_min(mn, x);
+        mx = __builtin_elementwise_max(mx, x);
+      }
+      mn0 = static_cast<float>(mn[0]); mn1 = static_cast<float>(mn[1]);
+      mx0 = static_cast<float>(mx[0]); mx1 = static_cast<float>(mx[1]);
     }
-    float s, rcp;
-    group_consts<QK>(mn, mx, s, rcp);
-    kmn[d] = mn;
-    ksc[d] = s;
-    krc[d] = rcp;
-    reinterpret_cast<uint16_t*>(rec + BL.k_scale)[d] = f16_bits_canon(s);
-    reinterpret_cast<uint16_t*>(rec + BL.k_zero)[d] = f16_bits_canon(mn);
-  } else {
-    // value group: row t, channels m*G .. m*G+G-1; thread index m*G + t
-    const int i = tid - D;
+    float s0, r0, s1, r1;
+    group_consts<QK>(mn0, mx0, s0, r0);
+    group_consts<QK>(mn1, mx1, s1, r1);
+    kmn[p2] = mn0; ksc[p2] = s0; krc[p2] = r0;
+    kmn[p2 + 1] = mn1; ksc[p2 + 1] = s1; krc[p2 + 1] = r1;
+    reinterpret_cast<uint32_t*>(rec + BL.k_scale)[tid] =
+        f16_bits_canon(s0) | (static_cast<uint32_t>(f16_bits_canon(s1)) << 16);
+    reinterpret_cast<uint32_t*>(rec + BL.k_zero)[tid] =
+        f16_bits_canon(mn0) | (static_cast<uint32_t>(f16_bits_canon(mn1)) << 16);
+  } else if (tid < D / 2 + 4 * G) {
+    // value group: row t, channels m*G .. m*G+G-1; index i = m*G + t
+    const int i = tid - D / 2;
     const int m = i / G, t = i % G;
-    const uint16_t* row = &vt[t * RS + m * G];
-    float mn = to_f32<BF16>(row[0]), mx = mn;
-    for (int c = 1; c < G; ++c) {
-      const float x = to_f32<BF16>(row[c]);
-      mn = fminf(mn, x);
-      mx = fmaxf(mx, x);
+    const uint4* row = reinterpret_cast<const uint4*>(&vt[t * RS + m * G]);
+    float mn, mx;
+    if constexpr (BF16) {
+      mn = INFINITY;
+      mx = -INFINITY;
+#pragma unroll
+      for (int c = 0; c < G / 8; ++c) {
+        const uint4 v = row[c];
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float lo = __uint_as_float(w4[j] << 16), hi = __uint_as_float(w4[j] & 0xffff0000u);
+          mn = fminf(mn, fminf(lo, hi));
+          mx = fmaxf(mx, fmaxf(lo, hi));
+        }
+      }
+    } else {
+      half2_t pmn, pmx;
+#pragma unroll
+      for (int c = 0; c < G / 8; ++c) {
+        const uint4 v = row[c];
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const half2_t x = __builtin_bit_cast(half2_t, w4[j]);
+          pmn = (c == 0 && j == 0) ? x : __builtin_elementwise_min(pmn, x);
+          pmx = (c == 0 && j == 0) ? x : __builtin_elementwise_max(pmx, x);
+        }
+      }
+      mn = fminf(static_cast<float>(pmn[0]), static_cast<float>(pmn[1]));
+      mx = fmaxf(static_cast<float>(pmx[0]), static_cast<float>(pmx[1]));
     }
     float s, rcp;
     group_consts<QV>(mn, mx, s, rcp);
