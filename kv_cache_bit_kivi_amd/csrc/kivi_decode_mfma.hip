@@ -294,31 +294,33 @@ __device__ void window_wave(const DecodeArgs& a, long long u, int b, int kvh, in
 // LDS of one workgroup.  A step covers 4 consecutive packed groups of one
 // unit; stages are filled by direct global->LDS loads (64 lanes x 16 bytes =
 // 1 KiB per instruction).
-//   key stage   x2 (key wave): codes 4 groups x 32 rows x D*KB/8 bytes, each
-//               group padded by 64 bytes (the 4 groups fall on different
-//               banks); scale 4 x D fp16; zero 4 x D fp16.  The step's scores
-//               reuse the code area once the codes are in registers.
+//   key codes   x1 (key wave): 4 groups x 32 rows x D*KB/8 bytes, each group
+//               padded by 64 bytes (the 4 groups fall on different banks);
+//               refilled with the next step's codes as soon as this step's
+//               are in registers
+//   key meta    x2: scale 4 x D fp16, zero 4 x D fp16
 //   value stage x2 (value wave): codes 4 groups x (G/PV words) x D words;
 //               scale 4 x 4 x G fp16; zero likewise.
-//   hand-over   x2: probabilities [stream][head][kRowP] fp32 and the
-//               rescale factor of each head, written by the key wave.
+//   hand-over   x2: scores, then in place probabilities [stream][head][kRowP]
+//               fp32, and the rescale factor of each head, written by the key
+//               wave.
 template <int KB, int VB>
 struct Stage {
   static constexpr int kRow = D * KB / 8;              // bytes per key row
   static constexpr int kGroup = G * kRow;              // 1 or 2 KiB
   static constexpr int kGroupPad = kGroup + 64;
-  static constexpr int offKS = 4 * kGroupPad, offKZ = offKS + 4 * D * 2;
-  static constexpr int kBytes = offKZ + 4 * D * 2;
+  static constexpr int kCodeBytes = 4 * kGroupPad;
+  static constexpr int kMetaBytes = 2 * 4 * D * 2;       // scale, then zero
+  static constexpr int offKM0 = kCodeBytes;
   static constexpr int vGroup = (G * VB / 32) * D * 4; // 1 or 2 KiB
   static constexpr int offVS = 4 * vGroup, offVZ = offVS + 4 * D * 2;
   static constexpr int vBytes = offVZ + 4 * D * 2;
   static constexpr int offAlpha = 4 * GQ * kRowP * 4;   // in a hand-over buffer
   static constexpr int pBytes = offAlpha + 16 * 4;
-  static constexpr int offV0 = 2 * kBytes, offP0 = offV0 + 2 * vBytes;
+  static constexpr int offV0 = offKM0 + 2 * kMetaBytes, offP0 = offV0 + 2 * vBytes;
   static constexpr int bytes = offP0 + 2 * pBytes;     // LDS per workgroup
   static constexpr int kLoads = (4 * kGroup + 2 * 4 * D * 2) / 1024;  // DMA instructions
   static constexpr int vLoads = (4 * vGroup + 2 * 4 * D * 2) / 1024;
-  static_assert(4 * kGroupPad >= 4 * GQ * kRowP * 4, "scores fit in the key-code area");
   static_assert(vBytes >= (GQ * D + GQ * G) * 4, "window scratch fits in a value stage");
 };
 static_assert(Stage<2, 2>::bytes == mfma_wg_lds_bytes(2, 2), "lds");
@@ -334,11 +336,12 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
   __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)lds_dst, 16, 0, 0);
 }
 
-// Key stage of groups [g0, g0 + ns): Stage::kLoads instructions; slots of
-// missing groups re-read the last valid group (addresses stay inside).
+// Key stage of groups [g0, g0 + ns): codes to `dst`, scale and zero to
+// `meta`; Stage::kLoads instructions.  Slots of missing groups re-read the
+// last valid group (addresses stay inside).
 template <int KB, int VB>
 __device__ __forceinline__ void issue_kstage(const DecodeArgs& a, long long u, int g0, int ns,
-                                             uint8_t* dst) {
+                                             uint8_t* dst, uint8_t* meta_dst) {
   using S = Stage<KB, VB>;
   constexpr BlockLayout BL = block_layout(KB, VB);
   const int lane = threadIdx.x & 63;
@@ -354,8 +357,8 @@ __device__ __forceinline__ void issue_kstage(const DecodeArgs& a, long long u, i
   // scale and zero: 256 bytes per group and field, 16 lanes per group
   const int g = min(g0 + (lane >> 4), glast);
   const uint8_t* const meta = unit + g * (long long)BL.bytes + (lane & 15) * 16;
-  dma16(meta + BL.k_scale, dst + S::offKS);
-  dma16(meta + BL.k_zero, dst + S::offKZ);
+  dma16(meta + BL.k_scale, meta_dst);
+  dma16(meta + BL.k_zero, meta_dst + 4 * D * 2);
 }
 
 // Value stage of groups [g0, g0 + ns): Stage::vLoads instructions.
@@ -416,7 +419,7 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
 #pragma unroll
     for (int i = 0; i < 32; ++i) qf[i] = 0.0f;
   }
-  issue_kstage<KB, VB>(a, u, gb, min(4, ge - gb), smem);
+  issue_kstage<KB, VB>(a, u, gb, min(4, ge - gb), smem, smem + S::offKM0);
   constexpr float k_unscale = static_cast<float>(1 << (24 - KS::F));  // product -> score
 
   const bool diag = (lc & 3) == lk;  // lane holds scores (stream lk)
@@ -426,20 +429,16 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
   for (int step = 0; step < n_steps; ++step) {
     const int g0 = gb + 4 * step;
     const int ns = min(4, ge - g0);
-    uint8_t* cur = smem + (step & 1) * S::kBytes;
-    if (step + 1 < n_steps) {
-      issue_kstage<KB, VB>(a, u, g0 + 4, min(4, ge - g0 - 4), smem + ((step + 1) & 1) * S::kBytes);
-      wait_vm<S::kLoads>();
-    } else {
-      wait_vm<0>();
-    }
+    // this step's codes and metadata are the only loads of this wave in flight
+    wait_vm<0>();
     wave_lds_sync();
+    const uint8_t* const meta = smem + S::offKM0 + (step & 1) * S::kMetaBytes;
 
     const int ga = lc >> 2;  // stream of this lane's A row
     const int gc = lc & 3;   // stream of this lane's B column
-    const u32x4* sBp = reinterpret_cast<const u32x4*>(cur + S::offKS + gc * D * 2 + 64 * lk);
-    const u32x4* zBp = reinterpret_cast<const u32x4*>(cur + S::offKZ + gc * D * 2 + 64 * lk);
-    const uint8_t* krow = cur + ga * S::kGroupPad + (lc & 3) * S::kRow + 4 * KL * lk;
+    const u32x4* sBp = reinterpret_cast<const u32x4*>(meta + gc * D * 2 + 64 * lk);
+    const u32x4* zBp = reinterpret_cast<const u32x4*>(meta + 4 * D * 2 + gc * D * 2 + 64 * lk);
+    const uint8_t* krow = smem + ga * S::kGroupPad + (lc & 3) * S::kRow + 4 * KL * lk;
     uint32_t kw[8][KL];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -453,6 +452,12 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
         for (int i = 0; i < KL; ++i) kw[s][i] = v[i];
       }
     }
+    // the codes are in registers: refill the code buffer (and the other
+    // metadata buffer, last read by the previous step) with the next step
+    wave_lds_sync();
+    if (step + 1 < n_steps)
+      issue_kstage<KB, VB>(a, u, g0 + 4, min(4, ge - g0 - 4), smem,
+                           smem + S::offKM0 + ((step + 1) & 1) * S::kMetaBytes);
     // B = q' * S (hi, lo) for head hq and group g0 + gc, built per block of
     // 32 channels right before its products (the vector work of block c+1
     // overlaps the matrix products of block c); zero-point term
@@ -494,12 +499,13 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
 
     // ------------------------------------------------------------- softmax
     // The 16 diagonal lanes hold the step's 512 scores (head hq, stream lk,
-    // 32 tokens each).  They pass through LDS so that every lane takes 8 of
-    // them: lane (hq, j = lc & 3, lk) owns tokens 8j .. 8j+7 of stream lk.
+    // 32 tokens each).  They pass through this step's hand-over buffer (its
+    // previous contents were consumed by the value wave two steps ago) so
+    // that every lane takes 8 of them: lane (hq, j = lc & 3, lk) owns tokens
+    // 8j .. 8j+7 of stream lk, and overwrites them with their probabilities.
     // Rows of 32 scores are padded to kRowP floats: the 16 rows start on
     // distinct banks.
-    float* const sl = reinterpret_cast<float*>(cur);  // [stream][head][kRowP]
-    wave_lds_sync();  // key codes of this stage fully read before they are overwritten
+    float* const sl = reinterpret_cast<float*>(smem + S::offP0 + (step & 1) * S::pBytes);
     if (diag) {
 #pragma unroll
       for (int s = 0; s < 8; ++s)
@@ -541,11 +547,9 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
     lcls[1] += p0[2] + p0[3];
     lcls[2] += p1[0] + p1[1];
     lcls[3] += p1[2] + p1[3];
-    // hand-over buffer of this step: the value wave consumed it two steps ago
-    float* const hp = reinterpret_cast<float*>(smem + S::offP0 + (step & 1) * S::pBytes);
-    *reinterpret_cast<f32x4*>(hp + row) = p0;
-    *reinterpret_cast<f32x4*>(hp + row + 4) = p1;
-    if (lk == 0 && jt == 0) hp[S::offAlpha / 4 + hq] = alpha;
+    *reinterpret_cast<f32x4*>(sl + row) = p0;
+    *reinterpret_cast<f32x4*>(sl + row + 4) = p1;
+    if (lk == 0 && jt == 0) sl[S::offAlpha / 4 + hq] = alpha;
     wg_barrier();  // step's probabilities ready
   }
 

@@ -72,10 +72,10 @@ struct DecodeArgs {
 };
 
 // LDS bytes of one workgroup (key wave + value wave) of the matrix-core
-// decode kernel: two key stages, two value stages and two hand-over buffers.
-// Bounds the number of resident workgroups per CU.
+// decode kernel: one key-code buffer, two key-metadata buffers, two value
+// stages and two hand-over buffers.  Bounds the resident workgroups per CU.
 constexpr int mfma_wg_lds_bytes(int k_bits, int v_bits) {
-  return 2 * (4 * (kGroup * kHeadDim * k_bits / 8 + 64) + 2 * 4 * kHeadDim * 2) +
+  return 4 * (kGroup * kHeadDim * k_bits / 8 + 64) + 2 * (2 * 4 * kHeadDim * 2) +
          2 * (4 * kGroup * v_bits / 32 * kHeadDim * 4 + 2 * 4 * kHeadDim * 2) +
          2 * (4 * 4 * 36 * 4 + 16 * 4);
 }
