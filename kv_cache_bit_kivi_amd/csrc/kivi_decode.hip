@@ -210,22 +210,58 @@ __global__ __launch_bounds__(256) void decode_split_valu(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge of the per-split partial softmax states; one workgroup per (b, j).
+// Merge of the per-split partial softmax states; one workgroup per (b, j):
+//   M = max_s m_s,  out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+// The split weights are computed once, in parallel, and the D outputs then
+// stream the o_s with several loads in flight per thread.
 template <int OUT>
 __global__ __launch_bounds__(D) void decode_merge(DecodeArgs a) {
+  __shared__ float wsh[kMaxSplits];
+  __shared__ float red[2][D / 64];
   const long long bj = blockIdx.x;
-  const int d = threadIdx.x;
-  const float* P = a.partial + bj * a.n_split * (D + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, P[s * (D + 2)]);
-  float L = 0.0f, O = 0.0f;
-  for (int s = 0; s < a.n_split; ++s) {
-    const float ms = P[s * (D + 2)];
-    if (ms == -INFINITY) continue;  // a split that saw no token
-    const float w = exp2f(ms - M);
-    L = fmaf(w, P[s * (D + 2) + 1], L);
-    O = fmaf(w, P[s * (D + 2) + 2 + d], O);
+  const int d = threadIdx.x, lane = d & 63, wv = d >> 6;
+  const int ns = a.n_split;
+  const float* P = a.partial + bj * ns * (D + 2);
+  float ms[kMaxSplits / D], mx = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kMaxSplits / D; ++k) {
+    const int s = d + k * D;
+    ms[k] = s < ns ? P[s * (D + 2)] : -INFINITY;
+    mx = fmaxf(mx, ms[k]);
   }
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if (lane == 0) red[0][wv] = mx;
+  __syncthreads();
+  float M = red[0][0];
+#pragma unroll
+  for (int w = 1; w < D / 64; ++w) M = fmaxf(M, red[0][w]);
+  float lsum = 0.0f;
+#pragma unroll
+  for (int k = 0; k < kMaxSplits / D; ++k) {
+    const int s = d + k * D;
+    if (s < ns) {
+      // a split that saw no token has m = -inf and weight 0
+      const float w = ms[k] == -INFINITY ? 0.0f : exp2f(ms[k] - M);
+      wsh[s] = w;
+      lsum = fmaf(w, P[s * (D + 2) + 1], lsum);
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off);
+  if (lane == 0) red[1][wv] = lsum;
+  __syncthreads();
+  float L = 0.0f;
+#pragma unroll
+  for (int w = 0; w < D / 64; ++w) L += red[1][w];
+  float O = 0.0f;
+  int s = 0;
+  for (; s + 8 <= ns; s += 8) {
+    float x[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = P[(s + k) * (D + 2) + 2 + d];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) O = fmaf(wsh[s + k], x[k], O);
+  }
+  for (; s < ns; ++s) O = fmaf(wsh[s], P[s * (D + 2) + 2 + d], O);
   const float r = O / L;
   if constexpr (OUT == 2) {
     static_cast<float*>(a.out)[bj * D + d] = r;
