@@ -200,6 +200,13 @@ __device__ __forceinline__ void wait_vm() {
 
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// Keeps the compiler from moving LDS accesses across this point.  LDS
+// operations of one wave execute in issue order, so LDS data written by some
+// lanes is visible to reads issued after it by other lanes of the wave; the
+// compiler, which reasons per lane, must not reorder such a read above the
+// write.
+__device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory"); }
+
 // Both waves of the workgroup: this wave's LDS writes are complete, then
 // meet.  Outstanding global->LDS loads stay in flight.
 __device__ __forceinline__ void wg_barrier() {
@@ -316,7 +323,8 @@ struct Stage {
   static constexpr int offVS = 4 * vGroup, offVZ = offVS + 4 * D * 2;
   static constexpr int vBytes = offVZ + 4 * D * 2;
   static constexpr int offAlpha = 4 * GQ * kRowP * 4;   // in a hand-over buffer
-  static constexpr int pBytes = offAlpha + 16 * 4;
+  static constexpr int offBias = offAlpha + 16;          // zero-point terms [stream][head]
+  static constexpr int pBytes = offBias + 16 * 4;
   static constexpr int offV0 = offKM0 + 2 * kMetaBytes, offP0 = offV0 + 2 * vBytes;
   static constexpr int bytes = offP0 + 2 * pBytes;     // LDS per workgroup
   static constexpr int kLoads = (4 * kGroup + 2 * 4 * D * 2) / 1024;  // DMA instructions
@@ -506,22 +514,27 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
     // Rows of 32 scores are padded to kRowP floats: the 16 rows start on
     // distinct banks.
     float* const sl = reinterpret_cast<float*>(smem + S::offP0 + (step & 1) * S::pBytes);
+    // (raw products; each reader applies the scale and its stream's
+    // zero-point term to its own 8 scores)
     if (diag) {
 #pragma unroll
       for (int s = 0; s < 8; ++s)
-        *reinterpret_cast<f32x4*>(sl + (lk * GQ + hq) * kRowP + 4 * s) = sc[s] * k_unscale + bias;
+        *reinterpret_cast<f32x4*>(sl + (lk * GQ + hq) * kRowP + 4 * s) = sc[s];
+      sl[S::offBias / 4 + lk * GQ + hq] = bias;
     }
+    wave_lds_order();  // the reads below take values written by the diagonal lanes
     const int row = (lk * GQ + hq) * kRowP + 8 * jt;
     float x[8];
     {
       const f32x4 x0 = *reinterpret_cast<const f32x4*>(sl + row);
       const f32x4 x1 = *reinterpret_cast<const f32x4*>(sl + row + 4);
+      const float bz = sl[S::offBias / 4 + lk * GQ + hq];
       // streams past the last group hold no tokens; slots hq >= NQ no head
       const bool valid = lk < ns && hq < NQ;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        x[i] = valid ? x0[i] : -INFINITY;
-        x[4 + i] = valid ? x1[i] : -INFINITY;
+        x[i] = valid ? fmaf(x0[i], k_unscale, bz) : -INFINITY;
+        x[4 + i] = valid ? fmaf(x1[i], k_unscale, bz) : -INFINITY;
       }
     }
     float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));

@@ -77,7 +77,7 @@ struct DecodeArgs {
 constexpr int mfma_wg_lds_bytes(int k_bits, int v_bits) {
   return 4 * (kGroup * kHeadDim * k_bits / 8 + 64) + 2 * (2 * 4 * kHeadDim * 2) +
          2 * (4 * kGroup * v_bits / 32 * kHeadDim * 4 + 2 * 4 * kHeadDim * 2) +
-         2 * (4 * 4 * 36 * 4 + 16 * 4);
+         2 * (4 * 4 * 36 * 4 + 16 + 16 * 4);
 }
 constexpr int kLdsPerCu = 160 * 1024;  // MI355X (gfx950)
 
