@@ -75,7 +75,7 @@ PHASE_KERNEL = {
 
 
 def decode_source(w):
-    return "kivi_decode_mfma.hip" if w.gq == 4 else "kivi_decode.hip"
+    return "kivi_decode_mfma.hip" if w.gq in (1, 2, 4) else "kivi_decode.hip"
 
 
 def traffic_from_profile(kernel, workload, kernel_src):
@@ -129,19 +129,22 @@ def run(args):
     torch.cuda.synchronize()
 
     def step(ev=None):
-        # ev: per layer, four HIP events bracketing the three phases; recorded
-        # on the stream every kernel is launched on
-        for i, L in enumerate(layers):
-            rec = (lambda n: ev[i][n].record(stream)) if ev is not None else (lambda n: None)
-            c = L["cache"]
-            c.reset()
-            rec(0)
-            c.append(L["kp"], L["vp"])
-            rec(1)
-            c.append(L["kn"], L["vn"])
-            rec(2)
-            c.decode_attn(L["q"], scale, out=L["out"])
-            rec(3)
+        # one pass of the hot path over every layer, phase by phase: the prefix
+        # of every layer packed, then every layer's decode token appended, then
+        # decode attention for every layer.  ev: four HIP events bracketing the
+        # three phase groups, recorded on the stream every kernel is launched on
+        rec = (lambda n: ev[n].record(stream)) if ev is not None else (lambda n: None)
+        rec(0)
+        for L in layers:
+            L["cache"].reset()
+            L["cache"].append(L["kp"], L["vp"])
+        rec(1)
+        for L in layers:
+            L["cache"].append(L["kn"], L["vn"])
+        rec(2)
+        for L in layers:
+            L["cache"].decode_attn(L["q"], scale, out=L["out"])
+        rec(3)
 
     if args.copy_calibration:
         # a plain copy of known size: 1 GiB read + 1 GiB written
@@ -155,8 +158,7 @@ def run(args):
         step()
     torch.cuda.synchronize()
 
-    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in layers]
-              for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     # timed region: exactly `steps` steps between two synchronizations
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -164,12 +166,13 @@ def run(args):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps
 
+    # per step, the average duration of one layer's launches of each phase
     phase = {"pack": [], "flush_append": [], "decode": []}
-    for per_step in events:
-        for ev in per_step:
-            phase["pack"].append(ev[0].elapsed_time(ev[1]) * 1e-3)
-            phase["flush_append"].append(ev[1].elapsed_time(ev[2]) * 1e-3)
-            phase["decode"].append(ev[2].elapsed_time(ev[3]) * 1e-3)
+    n = len(layers)
+    for ev in events:
+        phase["pack"].append(ev[0].elapsed_time(ev[1]) * 1e-3 / n)
+        phase["flush_append"].append(ev[1].elapsed_time(ev[2]) * 1e-3 / n)
+        phase["decode"].append(ev[2].elapsed_time(ev[3]) * 1e-3 / n)
 
     # decode alone with the 256 MB last-level cache scrubbed before each call
     scrub = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -188,39 +191,37 @@ def run(args):
 
 
 def cpu_baseline(w, layers):
-    """The oracle, as it stands, on a bounded sample of the same workload:
-    whole batch rows of the first layer (prefix + decode token appended, then
-    decode attention for every query head of the sampled units)."""
+    """The oracle, as it stands, on a bounded sample of the same workload: one
+    step (prefix pack, decode-token append, decode attention for every query
+    head) on one batch row of the first layer at a time, cycling through the
+    rows until about ten seconds of CPU work are done."""
     import numpy as np
 
     import oracle
     from kv_cache_bit_kivi_amd.inputs import bits16
 
     L = layers[0]
-    # rows of the batch so that the sample is about 10-30 s of CPU work
-    rows = {"c0": 1, "c1": 8, "c2": 1, "c3": 4, "c4": 1}[w.name]
-    units_per_row = w.kv_heads
-    if w.name in ("c2", "c4"):
-        units_per_row = {"c2": 4, "c4": 1}[w.name]  # first kv heads of row 0
-    k = bits16(L["kp"][:rows, :units_per_row])
-    v = bits16(L["vp"][:rows, :units_per_row])
-    kn = bits16(L["kn"][:rows, :units_per_row])
-    vn = bits16(L["vn"][:rows, :units_per_row])
-    q = bits16(L["q"][:rows, : units_per_row * w.gq])
     dt = oracle.BF16 if "bfloat" in str(w.dtype) else oracle.F16
-    t0 = time.perf_counter()
-    ref = oracle.OracleCache(rows, units_per_row, w.head_dim, w.tokens + 1, w.k_bits, w.v_bits,
-                             w.group_size, w.residual_length, dt)
-    ref.append(k, v)
-    ref.append(kn, vn)
-    ref.decode_attn(q, 1.0 / np.sqrt(w.head_dim))
-    t = time.perf_counter() - t0
-    frac = rows * units_per_row / (w.batch * w.kv_heads)
-    b = sum(algorithmic_bytes(w).values()) * frac
+    done, t = 0, 0.0
+    while t < 10.0:
+        r = done % w.batch
+        rows = slice(r, r + 1)
+        k, v = bits16(L["kp"][rows]), bits16(L["vp"][rows])
+        kn, vn = bits16(L["kn"][rows]), bits16(L["vn"][rows])
+        q = bits16(L["q"][rows])
+        t0 = time.perf_counter()
+        ref = oracle.OracleCache(1, w.kv_heads, w.head_dim, w.tokens + 1, w.k_bits,
+                                 w.v_bits, w.group_size, w.residual_length, dt)
+        ref.append(k, v)
+        ref.append(kn, vn)
+        ref.decode_attn(q, 1.0 / np.sqrt(w.head_dim))
+        t += time.perf_counter() - t0
+        done += 1
+    b = sum(algorithmic_bytes(w).values()) * done / w.batch
     return {"value": b / t / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{rows} of {w.batch} sequences x {units_per_row} of {w.kv_heads} kv heads, "
-                      f"one step of layer 0 (prefix pack, decode-token append, decode attention); "
-                      f"{t:.1f} s wall"}
+            "sample": f"{done} batch rows (all {w.kv_heads} kv heads each, cycling through the "
+                      f"{w.batch} rows of layer 0), one step each (prefix pack, decode-token "
+                      f"append, decode attention); {t:.1f} s of oracle time"}
 
 
 def main():
@@ -253,7 +254,7 @@ def main():
     dom = max(("pack", "decode"), key=lambda k: avg[k])
     kname, ksrc, _ = PHASE_KERNEL[dom]
     if dom == "decode":
-        kname = "decode_mfma_gq4" if w.gq == 4 else "decode_split_valu"
+        kname = "decode_mfma" if w.gq in (1, 2, 4) else "decode_split_valu"
         ksrc = decode_source(w)
     traffic = traffic_from_profile(kname, w.name,
                                    os.path.join(ROOT, "kv_cache_bit_kivi_amd", "csrc", ksrc))
