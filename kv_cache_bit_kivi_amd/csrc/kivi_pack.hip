@@ -44,18 +44,16 @@ __device__ __forceinline__ uint16_t f16_bits_canon(float f) {
 // Per-group constants: minimum, binary32 scale s = (max - min) / qmax (IEEE
 // division) and the reciprocal used by the fast path, v_rcp_f32 (within 1 ulp
 // of 1/s; the fast-path bound below allows 4 ulp).  rcp = 0 when s == 0
-// (every code is then 0) and NaN when s is so small that 1/s could leave the
-// normal range (every code then takes the exact division).
+// (every code is then 0).  Returns true when s is so small that 1/s could
+// leave the normal range; rcp is then 0 and the block's codes must take the
+// exact division.  Only bf16 inputs can get there: the smallest nonzero fp16
+// scale is 2^-24 / 15.
 template <int QMAX>
-__device__ __forceinline__ void group_consts(float mn, float mx, float& s, float& rcp) {
+__device__ __forceinline__ bool group_consts(float mn, float mx, float& s, float& rcp) {
   s = (mx - mn) / static_cast<float>(QMAX);
-  if (s == 0.0f) {
-    rcp = 0.0f;
-  } else if (s < 0x1p-100f) {
-    rcp = __builtin_nanf("");
-  } else {
-    rcp = __builtin_amdgcn_rcpf(s);
-  }
+  const bool tiny = s != 0.0f && s < 0x1p-100f;
+  rcp = (s == 0.0f || tiny) ? 0.0f : __builtin_amdgcn_rcpf(s);
+  return tiny;
 }
 
 // Code of x: rne(RN(RN(x - mn) / s)).  The clamp to [0, qmax] of the
@@ -67,15 +65,16 @@ __device__ __forceinline__ void group_consts(float mn, float mx, float& s, float
 // d / s <= 16: |y - d / s| <= 16 * (2^-22 + 2^-24 + 2^-46) < 1.25 * 2^-18 and
 // |RN(d / s) - d / s| <= 16 * 2^-24 = 0.25 * 2^-18, so y is within 1.5 * 2^-18
 // of RN(d / s).  Rounding y to an integer therefore gives the same result
-// unless y lies within 2^-17 of a half-integer; `redo` records those (and
-// NaN from the tiny-scale case), and the caller then recomputes its codes
-// with exact_code.
-__device__ __forceinline__ float fast_code_d(float d, float rcp, bool& redo) {
+// unless y lies within 2^-17 of a half-integer.  `dev` keeps the largest
+// |y - rint(y)| seen (one v_max per code, no per-code compare); a thread whose
+// dev exceeds 0.5 - 2^-17 recomputes its codes with exact_code.
+__device__ __forceinline__ float fast_code_d(float d, float rcp, float& dev) {
   const float y = d * rcp;
   const float r = rintf(y);
-  redo |= !(fabsf(y - r) <= 0.49999237060546875f);  // 0.5 - 2^-17
+  dev = fmaxf(dev, fabsf(y - r));
   return r;
 }
+constexpr float kTieMargin = 0.49999237060546875f;  // 0.5 - 2^-17
 
 // d = RN(x - mn) for element SEL (0: low, 1: high half) of a packed pair.
 // fp16: one v_fma_mix_f32 computes x * 1 - mn with a single rounding (the
@@ -144,6 +143,9 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
   __shared__ __align__(16) uint16_t vt[G * RS];
   __shared__ __align__(16) float kmn[D], ksc[D], krc[D];
   __shared__ __align__(16) float vmn[4 * G], vsc[4 * G], vrc[4 * G];  // index m * G + row
+  // set when some group of the block has a scale below 2^-100; kept in the
+  // padding of the first key row (the LDS total stays at 20 KiB)
+  int& tiny_scale = *reinterpret_cast<int*>(&kt[D]);
 
   const int tid = threadIdx.x;
   const int item = blockIdx.x;
@@ -180,6 +182,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
     *reinterpret_cast<uint4*>(&kt[(row + 16) * RS + col]) = k1;
     *reinterpret_cast<uint4*>(&vt[row * RS + col]) = v0;
     *reinterpret_cast<uint4*>(&vt[(row + 16) * RS + col]) = v1;
+    if (tid == 0) tiny_scale = 0;
   }
   __syncthreads();
 
@@ -211,8 +214,9 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
       mx0 = static_cast<float>(mx[0]); mx1 = static_cast<float>(mx[1]);
     }
     float s0, r0, s1, r1;
-    group_consts<QK>(mn0, mx0, s0, r0);
-    group_consts<QK>(mn1, mx1, s1, r1);
+    const bool t0 = group_consts<QK>(mn0, mx0, s0, r0);
+    const bool t1 = group_consts<QK>(mn1, mx1, s1, r1);
+    if (t0 || t1) tiny_scale = 1;
     kmn[p2] = mn0; ksc[p2] = s0; krc[p2] = r0;
     kmn[p2 + 1] = mn1; ksc[p2 + 1] = s1; krc[p2 + 1] = r1;
     reinterpret_cast<uint32_t*>(rec + BL.k_scale)[tid] =
@@ -256,7 +260,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
       mx = fmaxf(static_cast<float>(pmx[0]), static_cast<float>(pmx[1]));
     }
     float s, rcp;
-    group_consts<QV>(mn, mx, s, rcp);
+    if (group_consts<QV>(mn, mx, s, rcp)) tiny_scale = 1;
     vmn[i] = mn;
     vsc[i] = s;
     vrc[i] = rcp;
@@ -272,7 +276,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
     constexpr int TS = 128 / KW, NT = G / TS;
     const int w = tid % KW, tg = tid / KW;
     float wlo[NT], whi[NT];  // the word's even / odd codes as exact integers
-    bool redo = false;
+    float dev = 0.0f;
 #pragma unroll
     for (int j = 0; j < NT; ++j) wlo[j] = whi[j] = 0.0f;
 #pragma unroll 1
@@ -295,15 +299,15 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
           // codes c8 + i (even: low half) and c8 + i + 1 (odd: high half),
           // both at bit KB * (c8 + i) / 2 of their half
           const float wt = static_cast<float>(1 << (KB * ((c8 + i) >> 1)));
-          wlo[j] = fmaf(fast_code_d(diff<BF16, 0>(xw[i >> 1], mn[i]), rc[i], redo), wt, wlo[j]);
-          whi[j] = fmaf(fast_code_d(diff<BF16, 1>(xw[i >> 1], mn[i + 1]), rc[i + 1], redo), wt, whi[j]);
+          wlo[j] = fmaf(fast_code_d(diff<BF16, 0>(xw[i >> 1], mn[i]), rc[i], dev), wt, wlo[j]);
+          whi[j] = fmaf(fast_code_d(diff<BF16, 1>(xw[i >> 1], mn[i + 1]), rc[i + 1], dev), wt, whi[j]);
         }
       }
     }
     uint32_t word[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) word[j] = halves_to_word(wlo[j], whi[j]);
-    if (redo) {  // rare: recompute this thread's words with the exact division
+    if (dev > kTieMargin || tiny_scale) {  // rare: recompute this thread's words exactly
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
         const int t = tg + j * TS;
@@ -328,7 +332,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
     const int m = d0 / G;
     constexpr int NW = 16 / PV;  // words per channel for these 16 rows
     float l0[NW], h0[NW], l1[NW], h1[NW];  // even / odd codes of channels d0, d0+1
-    bool redo = false;
+    float dev = 0.0f;
 #pragma unroll
     for (int k = 0; k < NW; ++k) l0[k] = h0[k] = l1[k] = h1[k] = 0.0f;
 #pragma unroll
@@ -348,8 +352,8 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
         const uint32_t xw = *reinterpret_cast<const uint32_t*>(&vt[(16 * h + r) * RS + d0]);
         const int k = r / PV, pos = r % PV;
         const float wt = static_cast<float>(1 << (VB * (pos >> 1)));
-        const float c0 = fast_code_d(diff<BF16, 0>(xw, mn[j]), rc[j], redo);  // channel d0
-        const float c1 = fast_code_d(diff<BF16, 1>(xw, mn[j]), rc[j], redo);  // channel d0 + 1
+        const float c0 = fast_code_d(diff<BF16, 0>(xw, mn[j]), rc[j], dev);  // channel d0
+        const float c1 = fast_code_d(diff<BF16, 1>(xw, mn[j]), rc[j], dev);  // channel d0 + 1
         if (pos & 1) {
           h0[k] = fmaf(c0, wt, h0[k]);
           h1[k] = fmaf(c1, wt, h1[k]);
@@ -365,7 +369,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
       w0[k] = halves_to_word(l0[k], h0[k]);
       w1[k] = halves_to_word(l1[k], h1[k]);
     }
-    if (redo) {  // rare: recompute with the exact division
+    if (dev > kTieMargin || tiny_scale) {  // rare: recompute with the exact division
 #pragma unroll
       for (int k = 0; k < NW; ++k) w0[k] = w1[k] = 0;
 #pragma unroll

@@ -221,3 +221,31 @@ def test_quantizer_hard_cases_bitexact(bits):
     ref.append(bits16(kk), bits16(vv))
     assert ref.n_quant == 32
     _compare(cache, ref)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_tiny_scales_bf16_bitexact(bits):
+    # bf16 groups whose scale falls below 2^-100 (spreads near 2^-120 and
+    # subnormal inputs) next to ordinary groups: the kernel's reciprocal path
+    # cannot serve them and the block must take the exact division
+    rng = np.random.default_rng(5 + bits)
+    T = 64
+    K = rng.standard_normal((T, 128)).astype(np.float32)
+    V = rng.standard_normal((T, 128)).astype(np.float32)
+    base = np.float32(2.0 ** -118)
+    K[:, 5] = base * (1 + rng.integers(0, 8, T) / 128)           # spread of a few bf16 ulps
+    K[:, 9] = rng.integers(0, 6, T) * np.float32(2.0 ** -133)   # bf16 subnormals
+    K[32:, 70] = -base * (1 + rng.integers(0, 4, 32) / 64)     # second block only
+    V[3, 32:64] = base * (1 + rng.integers(0, 8, 32) / 128)
+    V[40, 96:128] = rng.integers(0, 3, 32) * np.float32(2.0 ** -131)
+    k = torch.from_numpy(K).to(torch.bfloat16)[None, None]
+    v = torch.from_numpy(V).to(torch.bfloat16)[None, None]
+    kk = torch.cat([k, k[:, :, :1]], 2)  # one more token flushes both blocks
+    vv = torch.cat([v, v[:, :, :1]], 2)
+    w = small("tiny", 1, 1, 1, T + 1, bits, bits, torch.bfloat16, residual_length=32)
+    cache = _gpu_cache(w, T + 1)
+    cache.append(kk.contiguous().to(DEV), vv.contiguous().to(DEV))
+    ref = oracle.OracleCache(1, 1, 128, T + 1, bits, bits, 32, 32, oracle.BF16)
+    ref.append(bits16(kk), bits16(vv))
+    assert ref.n_quant == T
+    _compare(cache, ref)
