@@ -25,7 +25,6 @@ namespace {
 constexpr int G = kGroup;
 constexpr int D = kHeadDim;
 constexpr int RS = D + 8;  // LDS row stride in 16-bit elements (272 bytes)
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 template <bool BF16>
 __device__ __forceinline__ float to_f32(uint16_t h) {
@@ -126,6 +125,30 @@ __device__ __forceinline__ int code_shift(int i) {
   return BITS * (i >> 1) + 16 * (i & 1);
 }
 
+// Minimum and maximum without the NaN quieting the compiler inserts before
+// each IEEE min/max (inputs are finite, so the plain instructions give the
+// same results): packed fp16 pairs, and three binary32 values.
+__device__ __forceinline__ uint32_t pk_min_f16(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_pk_min_f16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ uint32_t pk_max_f16(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_pk_max_f16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float min3_f32(float a, float b, float c) {
+  float r;
+  asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max3_f32(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // Orders this workgroup's LDS traffic; unlike __syncthreads it does not wait
 // for the scale/zero stores just issued to complete.
 __device__ __forceinline__ void lds_barrier() {
@@ -196,22 +219,25 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
       uint32_t x = *reinterpret_cast<const uint32_t*>(&kt[p2]);
       mn0 = mx0 = __uint_as_float(x << 16);
       mn1 = mx1 = __uint_as_float(x & 0xffff0000u);
-      for (int t = 1; t < G; ++t) {
-        x = *reinterpret_cast<const uint32_t*>(&kt[t * RS + p2]);
-        const float lo = __uint_as_float(x << 16), hi = __uint_as_float(x & 0xffff0000u);
-        mn0 = fminf(mn0, lo); mx0 = fmaxf(mx0, lo);
-        mn1 = fminf(mn1, hi); mx1 = fmaxf(mx1, hi);
+#pragma unroll 4
+      for (int t = 1; t < G; t += 2) {
+        const uint32_t x0 = *reinterpret_cast<const uint32_t*>(&kt[t * RS + p2]);
+        const uint32_t x1 = t + 1 < G ? *reinterpret_cast<const uint32_t*>(&kt[(t + 1) * RS + p2]) : x0;
+        const float l0 = __uint_as_float(x0 << 16), h0 = __uint_as_float(x0 & 0xffff0000u);
+        const float l1 = __uint_as_float(x1 << 16), h1 = __uint_as_float(x1 & 0xffff0000u);
+        mn0 = min3_f32(mn0, l0, l1); mx0 = max3_f32(mx0, l0, l1);
+        mn1 = min3_f32(mn1, h0, h1); mx1 = max3_f32(mx1, h0, h1);
       }
     } else {
-      half2_t mn = *reinterpret_cast<const half2_t*>(&kt[p2]), mx = mn;
+      uint32_t mn = *reinterpret_cast<const uint32_t*>(&kt[p2]), mx = mn;
 #pragma unroll 8
       for (int t = 1; t < G; ++t) {
-        const half2_t x = *reinterpret_cast<const half2_t*>(&kt[t * RS + p2]);
-        mn = __builtin_elementwise_min(mn, x);
-        mx = __builtin_elementwise_max(mx, x);
+        const uint32_t x = *reinterpret_cast<const uint32_t*>(&kt[t * RS + p2]);
+        mn = pk_min_f16(mn, x);
+        mx = pk_max_f16(mx, x);
       }
-      mn0 = static_cast<float>(mn[0]); mn1 = static_cast<float>(mn[1]);
-      mx0 = static_cast<float>(mx[0]); mx1 = static_cast<float>(mx[1]);
+      mn0 = lo_f16(mn); mn1 = hi_f16(mn);
+      mx0 = lo_f16(mx); mx1 = hi_f16(mx);
     }
     float s0, r0, s1, r1;
     const bool t0 = group_consts<QK>(mn0, mx0, s0, r0);
@@ -239,25 +265,25 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float lo = __uint_as_float(w4[j] << 16), hi = __uint_as_float(w4[j] & 0xffff0000u);
-          mn = fminf(mn, fminf(lo, hi));
-          mx = fmaxf(mx, fmaxf(lo, hi));
+          mn = min3_f32(mn, lo, hi);
+          mx = max3_f32(mx, lo, hi);
         }
       }
     } else {
-      half2_t pmn, pmx;
+      uint32_t pmn = 0, pmx = 0;
 #pragma unroll
       for (int c = 0; c < G / 8; ++c) {
         const uint4 v = row[c];
         const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const half2_t x = __builtin_bit_cast(half2_t, w4[j]);
-          pmn = (c == 0 && j == 0) ? x : __builtin_elementwise_min(pmn, x);
-          pmx = (c == 0 && j == 0) ? x : __builtin_elementwise_max(pmx, x);
+          pmn = (c == 0 && j == 0) ? w4[j] : pk_min_f16(pmn, w4[j]);
+          pmx = (c == 0 && j == 0) ? w4[j] : pk_max_f16(pmx, w4[j]);
         }
       }
-      mn = fminf(static_cast<float>(pmn[0]), static_cast<float>(pmn[1]));
-      mx = fmaxf(static_cast<float>(pmx[0]), static_cast<float>(pmx[1]));
+      // fp16 -> binary32 is exact and order preserving
+      mn = fminf(lo_f16(pmn), hi_f16(pmn));
+      mx = fmaxf(lo_f16(pmx), hi_f16(pmx));
     }
     float s, rcp;
     if (group_consts<QV>(mn, mx, s, rcp)) tiny_scale = 1;
