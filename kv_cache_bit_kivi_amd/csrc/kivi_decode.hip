@@ -216,19 +216,27 @@ __global__ __launch_bounds__(256) void decode_split_valu(DecodeArgs a) {
 // stream the o_s with several loads in flight per thread.
 template <int OUT>
 __global__ __launch_bounds__(D) void decode_merge(DecodeArgs a) {
+  constexpr int kPre = 16;  // splits whose o_s values are loaded up front
   __shared__ float wsh[kMaxSplits];
   __shared__ float red[2][D / 64];
   const long long bj = blockIdx.x;
   const int d = threadIdx.x, lane = d & 63, wv = d >> 6;
   const int ns = a.n_split;
   const float* P = a.partial + bj * ns * (D + 2);
-  float ms[kMaxSplits / D], mx = -INFINITY;
+  // every load of the first kPre splits is issued before any is used: one
+  // memory round trip for (m, l) and those o_s together
+  float ms[kMaxSplits / D], ls[kMaxSplits / D], xo[kPre];
 #pragma unroll
   for (int k = 0; k < kMaxSplits / D; ++k) {
     const int s = d + k * D;
     ms[k] = s < ns ? P[s * (D + 2)] : -INFINITY;
-    mx = fmaxf(mx, ms[k]);
+    ls[k] = s < ns ? P[s * (D + 2) + 1] : 0.0f;
   }
+#pragma unroll
+  for (int k = 0; k < kPre; ++k) xo[k] = k < ns ? P[k * (D + 2) + 2 + d] : 0.0f;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kMaxSplits / D; ++k) mx = fmaxf(mx, ms[k]);
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   if (lane == 0) red[0][wv] = mx;
   __syncthreads();
@@ -243,7 +251,7 @@ __global__ __launch_bounds__(D) void decode_merge(DecodeArgs a) {
       // a split that saw no token has m = -inf and weight 0
       const float w = ms[k] == -INFINITY ? 0.0f : exp2f(ms[k] - M);
       wsh[s] = w;
-      lsum = fmaf(w, P[s * (D + 2) + 1], lsum);
+      lsum = fmaf(w, ls[k], lsum);
     }
   }
   for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off);
@@ -253,7 +261,10 @@ __global__ __launch_bounds__(D) void decode_merge(DecodeArgs a) {
 #pragma unroll
   for (int w = 0; w < D / 64; ++w) L += red[1][w];
   float O = 0.0f;
-  int s = 0;
+#pragma unroll
+  for (int k = 0; k < kPre; ++k)
+    if (k < ns) O = fmaf(wsh[k], xo[k], O);
+  int s = kPre;
   for (; s + 8 <= ns; s += 8) {
     float x[8];
 #pragma unroll
