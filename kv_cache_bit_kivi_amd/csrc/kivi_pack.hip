@@ -26,15 +26,6 @@ constexpr int G = kGroup;
 constexpr int D = kHeadDim;
 constexpr int RS = D + 8;  // LDS row stride in 16-bit elements (272 bytes)
 
-template <bool BF16>
-__device__ __forceinline__ float to_f32(uint16_t h) {
-  if constexpr (BF16) {
-    return __uint_as_float(static_cast<uint32_t>(h) << 16);
-  } else {
-    return __half2float(__ushort_as_half(h));
-  }
-}
-
 // fp16 bit pattern of a binary32 value, nearest-even; zero is stored as +0.
 __device__ __forceinline__ uint16_t f16_bits_canon(float f) {
   return f == 0.0f ? uint16_t(0) : __half_as_ushort(__float2half_rn(f));
@@ -64,16 +55,27 @@ __device__ __forceinline__ bool group_consts(float mn, float mx, float& s, float
 // d / s <= 16: |y - d / s| <= 16 * (2^-22 + 2^-24 + 2^-46) < 1.25 * 2^-18 and
 // |RN(d / s) - d / s| <= 16 * 2^-24 = 0.25 * 2^-18, so y is within 1.5 * 2^-18
 // of RN(d / s).  Rounding y to an integer therefore gives the same result
-// unless y lies within 2^-17 of a half-integer.  `dev` keeps the largest
-// |y - rint(y)| seen (one v_max per code, no per-code compare); a thread whose
-// dev exceeds 0.5 - 2^-17 recomputes its codes with exact_code.
-__device__ __forceinline__ float fast_code_d(float d, float rcp, float& dev) {
+// unless y lies within 2^-17 of a half-integer.
+//
+// The fast pass (CAREFUL false) only keeps in `dev` the largest |y - rint(y)|
+// seen (one v_max per code, no per-code compare).  A thread whose dev exceeds
+// 0.5 - 2^-17, or any thread of a block with a tiny scale, runs the careful
+// pass: the same loop, in which only the codes near a tie (all codes, in a
+// tiny-scale block) take the IEEE division of the definition.  Exact ties
+// are common with 16-bit inputs (an element at the midpoint of its group),
+// so the careful pass must stay cheap.
+constexpr float kTieMargin = 0.49999237060546875f;  // 0.5 - 2^-17
+template <bool CAREFUL>
+__device__ __forceinline__ float code_of(float d, float rcp, float s, bool tiny, float& dev) {
   const float y = d * rcp;
-  const float r = rintf(y);
-  dev = fmaxf(dev, fabsf(y - r));
+  float r = rintf(y);
+  if constexpr (CAREFUL) {
+    if (tiny || !(fabsf(y - r) <= kTieMargin)) r = s == 0.0f ? 0.0f : rintf(d / s);
+  } else {
+    dev = fmaxf(dev, fabsf(y - r));
+  }
   return r;
 }
-constexpr float kTieMargin = 0.49999237060546875f;  // 0.5 - 2^-17
 
 // d = RN(x - mn) for element SEL (0: low, 1: high half) of a packed pair.
 // fp16: one v_fma_mix_f32 computes x * 1 - mn with a single rounding (the
@@ -101,29 +103,8 @@ __device__ __forceinline__ uint32_t halves_to_word(float lo, float hi) {
   return static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
 }
 
-// Code by the definition (one IEEE division); every code is 0 when s == 0.
-__device__ __forceinline__ float exact_code(float x, float mn, float s) {
-  return s == 0.0f ? 0.0f : rintf((x - mn) / s);
-}
-
 __device__ __forceinline__ float lo_f16(uint32_t w) { return __half2float(__ushort_as_half(static_cast<uint16_t>(w))); }
 __device__ __forceinline__ float hi_f16(uint32_t w) { return __half2float(__ushort_as_half(static_cast<uint16_t>(w >> 16))); }
-template <bool BF16>
-__device__ __forceinline__ float lo_x(uint32_t w) {
-  if constexpr (BF16) return __uint_as_float(w << 16);
-  else return lo_f16(w);
-}
-template <bool BF16>
-__device__ __forceinline__ float hi_x(uint32_t w) {
-  if constexpr (BF16) return __uint_as_float(w & 0xffff0000u);
-  else return hi_f16(w);
-}
-
-// Bit offset of code i in a word: even codes low half-word, odd codes high.
-template <int BITS>
-__device__ __forceinline__ int code_shift(int i) {
-  return BITS * (i >> 1) + 16 * (i & 1);
-}
 
 // Minimum and maximum without the NaN quieting the compiler inserts before
 // each IEEE min/max (inputs are finite, so the plain instructions give the
@@ -153,6 +134,107 @@ __device__ __forceinline__ float max3_f32(float a, float b, float c) {
 // for the scale/zero stores just issued to complete.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Key code words of one thread: word w (channels w*PK .. w*PK+PK-1) of
+// tokens tg, tg + TS, ...; the channels are taken 8 at a time (fewer live
+// registers).  kt: the staged key tile; kmn, krc, ksc: per channel minimum,
+// reciprocal and scale.
+template <int KB, bool BF16, bool CAREFUL>
+__device__ __forceinline__ void key_words(const uint16_t* kt, const float* kmn, const float* krc,
+                                          const float* ksc, int w, int tg, bool tiny,
+                                          uint32_t* word, float& dev) {
+  constexpr int PK = 32 / KB, KW = D / PK, TS = 128 / KW, NT = G / TS;
+  float wlo[NT], whi[NT];  // the word's even / odd codes as exact integers
+#pragma unroll
+  for (int j = 0; j < NT; ++j) wlo[j] = whi[j] = 0.0f;
+#pragma unroll 1
+  for (int c8 = 0; c8 < PK; c8 += 8) {
+    const int d0 = w * PK + c8;
+    float mn[8], rc[8], sc[8];
+#pragma unroll
+    for (int i = 0; i < 8; i += 4) {
+      const float4 a4 = *reinterpret_cast<const float4*>(&kmn[d0 + i]);
+      const float4 c4 = *reinterpret_cast<const float4*>(&krc[d0 + i]);
+      mn[i] = a4.x; mn[i + 1] = a4.y; mn[i + 2] = a4.z; mn[i + 3] = a4.w;
+      rc[i] = c4.x; rc[i + 1] = c4.y; rc[i + 2] = c4.z; rc[i + 3] = c4.w;
+      if constexpr (CAREFUL) {
+        const float4 s4 = *reinterpret_cast<const float4*>(&ksc[d0 + i]);
+        sc[i] = s4.x; sc[i + 1] = s4.y; sc[i + 2] = s4.z; sc[i + 3] = s4.w;
+      } else {
+        sc[i] = sc[i + 1] = sc[i + 2] = sc[i + 3] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const uint4 v = *reinterpret_cast<const uint4*>(&kt[(tg + j * TS) * RS + d0]);
+      const uint32_t xw[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        // codes c8 + i (even: low half) and c8 + i + 1 (odd: high half),
+        // both at bit KB * (c8 + i) / 2 of their half
+        const float wt = static_cast<float>(1 << (KB * ((c8 + i) >> 1)));
+        wlo[j] = fmaf(code_of<CAREFUL>(diff<BF16, 0>(xw[i >> 1], mn[i]), rc[i], sc[i], tiny, dev), wt, wlo[j]);
+        whi[j] = fmaf(code_of<CAREFUL>(diff<BF16, 1>(xw[i >> 1], mn[i + 1]), rc[i + 1], sc[i + 1], tiny, dev),
+                      wt, whi[j]);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NT; ++j) word[j] = halves_to_word(wlo[j], whi[j]);
+}
+
+// Value code words of one thread: channels d0, d0 + 1 (one channel group) and
+// rows 16*h .. 16*h+15, taken 8 rows at a time.  vt: the staged value tile;
+// vmn, vrc, vsc: per (group, row) minimum, reciprocal and scale.
+template <int VB, bool BF16, bool CAREFUL>
+__device__ __forceinline__ void value_words(const uint16_t* vt, const float* vmn, const float* vrc,
+                                            const float* vsc, int d0, int h, bool tiny,
+                                            uint32_t* w0, uint32_t* w1, float& dev) {
+  constexpr int PV = 32 / VB, NW = 16 / PV;
+  const int m = d0 / G;
+  float l0[NW], h0[NW], l1[NW], h1[NW];  // even / odd codes of channels d0, d0+1
+#pragma unroll
+  for (int k = 0; k < NW; ++k) l0[k] = h0[k] = l1[k] = h1[k] = 0.0f;
+#pragma unroll
+  for (int r8 = 0; r8 < 16; r8 += 8) {
+    const int sbase = m * G + 16 * h + r8;
+    float mn[8], rc[8], sc[8];
+#pragma unroll
+    for (int j = 0; j < 8; j += 4) {
+      const float4 a4 = *reinterpret_cast<const float4*>(&vmn[sbase + j]);
+      const float4 c4 = *reinterpret_cast<const float4*>(&vrc[sbase + j]);
+      mn[j] = a4.x; mn[j + 1] = a4.y; mn[j + 2] = a4.z; mn[j + 3] = a4.w;
+      rc[j] = c4.x; rc[j + 1] = c4.y; rc[j + 2] = c4.z; rc[j + 3] = c4.w;
+      if constexpr (CAREFUL) {
+        const float4 s4 = *reinterpret_cast<const float4*>(&vsc[sbase + j]);
+        sc[j] = s4.x; sc[j + 1] = s4.y; sc[j + 2] = s4.z; sc[j + 3] = s4.w;
+      } else {
+        sc[j] = sc[j + 1] = sc[j + 2] = sc[j + 3] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = r8 + j;  // row 16*h + r: word r / PV, position r % PV
+      const uint32_t xw = *reinterpret_cast<const uint32_t*>(&vt[(16 * h + r) * RS + d0]);
+      const int k = r / PV, pos = r % PV;
+      const float wt = static_cast<float>(1 << (VB * (pos >> 1)));
+      const float c0 = code_of<CAREFUL>(diff<BF16, 0>(xw, mn[j]), rc[j], sc[j], tiny, dev);  // channel d0
+      const float c1 = code_of<CAREFUL>(diff<BF16, 1>(xw, mn[j]), rc[j], sc[j], tiny, dev);  // channel d0 + 1
+      if (pos & 1) {
+        h0[k] = fmaf(c0, wt, h0[k]);
+        h1[k] = fmaf(c1, wt, h1[k]);
+      } else {
+        l0[k] = fmaf(c0, wt, l0[k]);
+        l1[k] = fmaf(c1, wt, l1[k]);
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < NW; ++k) {
+    w0[k] = halves_to_word(l0[k], h0[k]);
+    w1[k] = halves_to_word(l1[k], h1[k]);
+  }
 }
 
 template <int KB, int VB, bool BF16>
@@ -295,55 +377,18 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
   }
   lds_barrier();
 
+  const bool tiny = tiny_scale != 0;
   if (tid < 128) {
     // ---- key code words: word w of token t holds channels w*PK .. w*PK+PK-1.
-    // Thread: one word index w, tokens tg, tg + TS, ... (NT tokens); the
-    // channels of the word are taken 8 at a time (fewer live registers).
+    // Thread: one word index w, tokens tg, tg + TS, ... (NT tokens).
     constexpr int TS = 128 / KW, NT = G / TS;
     const int w = tid % KW, tg = tid / KW;
-    float wlo[NT], whi[NT];  // the word's even / odd codes as exact integers
-    float dev = 0.0f;
-#pragma unroll
-    for (int j = 0; j < NT; ++j) wlo[j] = whi[j] = 0.0f;
-#pragma unroll 1
-    for (int c8 = 0; c8 < PK; c8 += 8) {
-      const int d0 = w * PK + c8;
-      float mn[8], rc[8];
-#pragma unroll
-      for (int i = 0; i < 8; i += 4) {
-        const float4 a4 = *reinterpret_cast<const float4*>(&kmn[d0 + i]);
-        const float4 c4 = *reinterpret_cast<const float4*>(&krc[d0 + i]);
-        mn[i] = a4.x; mn[i + 1] = a4.y; mn[i + 2] = a4.z; mn[i + 3] = a4.w;
-        rc[i] = c4.x; rc[i + 1] = c4.y; rc[i + 2] = c4.z; rc[i + 3] = c4.w;
-      }
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const uint4 v = *reinterpret_cast<const uint4*>(&kt[(tg + j * TS) * RS + d0]);
-        const uint32_t xw[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-          // codes c8 + i (even: low half) and c8 + i + 1 (odd: high half),
-          // both at bit KB * (c8 + i) / 2 of their half
-          const float wt = static_cast<float>(1 << (KB * ((c8 + i) >> 1)));
-          wlo[j] = fmaf(fast_code_d(diff<BF16, 0>(xw[i >> 1], mn[i]), rc[i], dev), wt, wlo[j]);
-          whi[j] = fmaf(fast_code_d(diff<BF16, 1>(xw[i >> 1], mn[i + 1]), rc[i + 1], dev), wt, whi[j]);
-        }
-      }
-    }
     uint32_t word[NT];
-#pragma unroll
-    for (int j = 0; j < NT; ++j) word[j] = halves_to_word(wlo[j], whi[j]);
-    if (dev > kTieMargin || tiny_scale) {  // rare: recompute this thread's words exactly
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const int t = tg + j * TS;
-        uint32_t wd = 0;
-        for (int i = 0; i < PK; ++i) {
-          const float x = to_f32<BF16>(kt[t * RS + w * PK + i]);
-          wd |= static_cast<uint32_t>(exact_code(x, kmn[w * PK + i], ksc[w * PK + i])) << code_shift<KB>(i);
-        }
-        word[j] = wd;
-      }
+    float dev = 0.0f;
+    key_words<KB, BF16, false>(kt, kmn, krc, ksc, w, tg, false, word, dev);
+    if (dev > kTieMargin || tiny) {
+      asm volatile("" ::: "memory");  // reload the tile: nothing kept live across the passes
+      key_words<KB, BF16, true>(kt, kmn, krc, ksc, w, tg, tiny, word, dev);
     }
     uint32_t* const kc = reinterpret_cast<uint32_t*>(rec + BL.k_codes);
 #pragma unroll
@@ -351,60 +396,16 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
   } else {
     // ---- value code words: word w of channel d holds rows w*PV .. w*PV+PV-1;
     // word-major, the D words of one w adjacent.  Thread: channels d0, d0+1
-    // (same channel group m) and rows 16*h .. 16*h+15 (16 / PV words each),
-    // taken 8 rows at a time.
+    // (same channel group) and rows 16*h .. 16*h+15 (16 / PV words each).
     const int i0 = tid - 128;
     const int d0 = 2 * (i0 % 64), h = i0 / 64;
-    const int m = d0 / G;
-    constexpr int NW = 16 / PV;  // words per channel for these 16 rows
-    float l0[NW], h0[NW], l1[NW], h1[NW];  // even / odd codes of channels d0, d0+1
-    float dev = 0.0f;
-#pragma unroll
-    for (int k = 0; k < NW; ++k) l0[k] = h0[k] = l1[k] = h1[k] = 0.0f;
-#pragma unroll
-    for (int r8 = 0; r8 < 16; r8 += 8) {
-      const int sbase = m * G + 16 * h + r8;
-      float mn[8], rc[8];
-#pragma unroll
-      for (int j = 0; j < 8; j += 4) {
-        const float4 a4 = *reinterpret_cast<const float4*>(&vmn[sbase + j]);
-        const float4 c4 = *reinterpret_cast<const float4*>(&vrc[sbase + j]);
-        mn[j] = a4.x; mn[j + 1] = a4.y; mn[j + 2] = a4.z; mn[j + 3] = a4.w;
-        rc[j] = c4.x; rc[j + 1] = c4.y; rc[j + 2] = c4.z; rc[j + 3] = c4.w;
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int r = r8 + j;  // row 16*h + r: word r / PV, position r % PV
-        const uint32_t xw = *reinterpret_cast<const uint32_t*>(&vt[(16 * h + r) * RS + d0]);
-        const int k = r / PV, pos = r % PV;
-        const float wt = static_cast<float>(1 << (VB * (pos >> 1)));
-        const float c0 = fast_code_d(diff<BF16, 0>(xw, mn[j]), rc[j], dev);  // channel d0
-        const float c1 = fast_code_d(diff<BF16, 1>(xw, mn[j]), rc[j], dev);  // channel d0 + 1
-        if (pos & 1) {
-          h0[k] = fmaf(c0, wt, h0[k]);
-          h1[k] = fmaf(c1, wt, h1[k]);
-        } else {
-          l0[k] = fmaf(c0, wt, l0[k]);
-          l1[k] = fmaf(c1, wt, l1[k]);
-        }
-      }
-    }
+    constexpr int NW = 16 / PV;
     uint32_t w0[NW], w1[NW];
-#pragma unroll
-    for (int k = 0; k < NW; ++k) {
-      w0[k] = halves_to_word(l0[k], h0[k]);
-      w1[k] = halves_to_word(l1[k], h1[k]);
-    }
-    if (dev > kTieMargin || tiny_scale) {  // rare: recompute with the exact division
-#pragma unroll
-      for (int k = 0; k < NW; ++k) w0[k] = w1[k] = 0;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int si = m * G + 16 * h + r;
-        const uint32_t xw = *reinterpret_cast<const uint32_t*>(&vt[(16 * h + r) * RS + d0]);
-        w0[r / PV] |= static_cast<uint32_t>(exact_code(lo_x<BF16>(xw), vmn[si], vsc[si])) << code_shift<VB>(r % PV);
-        w1[r / PV] |= static_cast<uint32_t>(exact_code(hi_x<BF16>(xw), vmn[si], vsc[si])) << code_shift<VB>(r % PV);
-      }
+    float dev = 0.0f;
+    value_words<VB, BF16, false>(vt, vmn, vrc, vsc, d0, h, false, w0, w1, dev);
+    if (dev > kTieMargin || tiny) {
+      asm volatile("" ::: "memory");  // reload the tile: nothing kept live across the passes
+      value_words<VB, BF16, true>(vt, vmn, vrc, vsc, d0, h, tiny, w0, w1, dev);
     }
     uint32_t* const vc = reinterpret_cast<uint32_t*>(rec + BL.v_codes);
 #pragma unroll
