@@ -406,6 +406,8 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
   const int hq = lc >> 2;  // head of this lane's B / C columns
   const int jt = lc & 3;
 
+  // the first stage's loads go out before q is read: their latencies overlap
+  issue_kstage<KB, VB>(a, u, gb, min(4, ge - gb), smem, smem + S::offKM0);
   // q' = q * softmax_scale * log2(e) for head hq, channels 32*lk .. 32*lk+31,
   // times the code-position factor 2^lf of the key codes it multiplies
   // (head slots hq >= NQ carry q' = 0 and are masked out of the softmax)
@@ -427,7 +429,6 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
 #pragma unroll
     for (int i = 0; i < 32; ++i) qf[i] = 0.0f;
   }
-  issue_kstage<KB, VB>(a, u, gb, min(4, ge - gb), smem, smem + S::offKM0);
   constexpr float k_unscale = static_cast<float>(1 << (24 - KS::F));  // product -> score
 
   const bool diag = (lc & 3) == lk;  // lane holds scores (stream lk)
