@@ -116,6 +116,21 @@ __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uin
   lo = pk_rne(minus_half<0>(hi, x0), minus_half<1>(hi, x1));
 }
 
+// Exact product of two fp16 pairs as hi + lo fp16 pairs: hi = RN(a * b)
+// (v_pk_mul_f16) and lo = RN(a * b - hi) (v_pk_fma_f16, one rounding of the
+// exact value).  An fp16 product has at most 22 significant bits, so lo is
+// the exact remainder unless it falls below the fp16 subnormal step 2^-24
+// (an absolute error of at most 2^-25).  |a * b| must stay below 65504.
+__device__ __forceinline__ void mul_pair_exact(uint32_t a, uint32_t b, uint32_t& hi, uint32_t& lo) {
+  asm("v_pk_mul_f16 %0, %1, %2" : "=v"(hi) : "v"(a), "v"(b));
+  asm("v_pk_fma_f16 %0, %1, %2, %3 neg_lo:[0,0,1] neg_hi:[0,0,1]" : "=v"(lo) : "v"(a), "v"(b), "v"(hi));
+}
+
+// acc + a.x * b.x + a.y * b.y for fp16 pairs a, b (v_dot2_f32_f16).
+__device__ __forceinline__ float dot2_acc(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), acc, false);
+}
+
 // Code extraction.  Two codes of a split-half word sit at bits [s, s+b) and
 // [16+s, 16+s+b); masking the word (or the word shifted right by 8) in place
 // leaves them as fp16 subnormals c * 2^(t-24), t = 0, 2, 4, 6 (2-bit) or
@@ -408,10 +423,13 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
 
   // the first stage's loads go out before q is read: their latencies overlap
   issue_kstage<KB, VB>(a, u, gb, min(4, ge - gb), smem, smem + S::offKM0);
-  // q' = q * softmax_scale * log2(e) for head hq, channels 32*lk .. 32*lk+31,
-  // times the code-position factor 2^lf of the key codes it multiplies
-  // (head slots hq >= NQ carry q' = 0 and are masked out of the softmax)
-  float qf[32];
+  // q'' = q * 2^(lf(e) - 3) as fp16 pairs for head hq, channels 32*lk ..
+  // 32*lk+31 (pair p: channels 2p, 2p+1; e = p & 3 its pair class in the run
+  // of 8): the code-position factor of the key codes it multiplies, over 8.
+  // Power-of-two factors keep q'' exact (a bf16 q is rounded to fp16 once).
+  // softmax_scale * log2(e) multiplies the scores afterwards.  Head slots
+  // hq >= NQ carry q'' = 0 and are masked out of the softmax.
+  uint32_t q2[16];
   if (hq < NQ) {
     const uint16_t* qp = a.q + ((long long)b * a.Hq + kvh * NQ + hq) * D + 32 * lk;
 #pragma unroll
@@ -419,17 +437,19 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
       const uint4 v = *reinterpret_cast<const uint4*>(qp + i);
       const uint32_t ww[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int ep = (j >> 1);  // pair index inside the run of 8 channels
-        qf[i + j] = to_f32<BF16>(static_cast<uint16_t>(ww[j >> 1] >> (16 * (j & 1)))) * a.qscale *
-                    static_cast<float>(1 << KS::lf(ep));
+      for (int e = 0; e < 4; ++e) {
+        const float f = KS::lf(e) >= 3 ? static_cast<float>(1 << (KS::lf(e) - 3))
+                                       : 1.0f / static_cast<float>(1 << (3 - KS::lf(e)));
+        q2[i / 2 + e] = pk_rne(to_f32<BF16>(static_cast<uint16_t>(ww[e])) * f,
+                               to_f32<BF16>(static_cast<uint16_t>(ww[e] >> 16)) * f);
       }
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 32; ++i) qf[i] = 0.0f;
+    for (int i = 0; i < 16; ++i) q2[i] = 0u;
   }
-  constexpr float k_unscale = static_cast<float>(1 << (24 - KS::F));  // product -> score
+  // raw product -> score: products are c q S 2^(F-27)
+  const float k_unscale = a.qscale * static_cast<float>(1 << (27 - KS::F));
 
   const bool diag = (lc & 3) == lk;  // lane holds scores (stream lk)
   float m_run = -INFINITY;           // running max of head hq (base 2)
@@ -472,7 +492,7 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
     // overlaps the matrix products of block c); zero-point term
     // sum_d q'_d Z_d of the same (head, group) on the vector ALUs, added to
     // the scores afterwards
-    float bcls[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // per pair class: q' carries 2^lf(e)
+    float bcls[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // per pair class: q'' carries 2^(lf(e) - 3)
     f32x4 sc[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) sc[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -482,13 +502,12 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
       u32x4 h4, l4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float q0 = qf[8 * c + 2 * e], q1 = qf[8 * c + 2 * e + 1];
+        const uint32_t qq = q2[4 * c + e];
         uint32_t hi, lo;
-        split_pair(times_half<0>(q0, sB[e]), times_half<1>(q1, sB[e]), hi, lo);
+        mul_pair_exact(qq, sB[e], hi, lo);
         h4[e] = hi;
         l4[e] = lo;
-        bcls[e] = fmaf(q0, lo_half(zB[e]), bcls[e]);
-        bcls[e] = fmaf(q1, hi_half(zB[e]), bcls[e]);
+        bcls[e] = dot2_acc(qq, zB[e], bcls[e]);
       }
       const half8_t bh = as_h8(h4), bl = as_h8(l4);
       half8_t ak[8];
@@ -502,9 +521,11 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
     }
     float bias = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) bias = fmaf(bcls[e], 1.0f / static_cast<float>(1 << KS::lf(e)), bias);
+    for (int e = 0; e < 4; ++e)
+      bias = fmaf(bcls[e], KS::lf(e) >= 3 ? 1.0f / static_cast<float>(1 << (KS::lf(e) - 3))
+                                          : static_cast<float>(1 << (3 - KS::lf(e))), bias);
     bias = swap_sum<16>(bias);
-    bias = swap_sum<32>(bias);  // all 128 channels: head hq, group g0 + (lc & 3)
+    bias = swap_sum<32>(bias) * a.qscale;  // all 128 channels: head hq, group g0 + (lc & 3)
 
     // ------------------------------------------------------------- softmax
     // The 16 diagonal lanes hold the step's 512 scores (head hq, stream lk,
