@@ -126,6 +126,13 @@ __device__ __forceinline__ void mul_pair_exact(uint32_t a, uint32_t b, uint32_t&
   asm("v_pk_fma_f16 %0, %1, %2, %3 neg_lo:[0,0,1] neg_hi:[0,0,1]" : "=v"(lo) : "v"(a), "v"(b), "v"(hi));
 }
 
+// a * b + c for fp16 pairs (v_pk_fma_f16, one rounding).
+__device__ __forceinline__ uint32_t fma_pair(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm("v_pk_fma_f16 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // acc + a.x * b.x + a.y * b.y for fp16 pairs a, b (v_dot2_f32_f16).
 __device__ __forceinline__ float dot2_acc(uint32_t a, uint32_t b, float acc) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), acc, false);
@@ -582,8 +589,16 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
     lcls[1] += p0[2] + p0[3];
     lcls[2] += p1[0] + p1[1];
     lcls[3] += p1[2] + p1[3];
-    *reinterpret_cast<f32x4*>(sl + row) = p0;
-    *reinterpret_cast<f32x4*>(sl + row + 4) = p1;
+    // handed over as fp16 pairs hi (nearest) and lo (nearest of the exact
+    // remainder): p = hi + lo within 2^-22 relative; the value wave then
+    // multiplies them by its scales with packed fp16 operations
+    uint32_t ph[4], pl[4];
+    split_pair(p0[0], p0[1], ph[0], pl[0]);
+    split_pair(p0[2], p0[3], ph[1], pl[1]);
+    split_pair(p1[0], p1[1], ph[2], pl[2]);
+    split_pair(p1[2], p1[3], ph[3], pl[3]);
+    *reinterpret_cast<u32x4*>(sl + row) = u32x4{ph[0], ph[1], ph[2], ph[3]};
+    *reinterpret_cast<u32x4*>(sl + row + 4) = u32x4{pl[0], pl[1], pl[2], pl[3]};
     if (lk == 0 && jt == 0) sl[S::offAlpha / 4 + hq] = alpha;
     wg_barrier();  // step's probabilities ready
   }
@@ -651,19 +666,20 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
       const int vmo = ((gs * 4 + mcol) * G + 8 * lk) * 2;
       const u32x4 vs = *reinterpret_cast<const u32x4*>(vstage + S::offVS + vmo);
       const u32x4 vz = *reinterpret_cast<const u32x4*>(vstage + S::offVZ + vmo);
+      // p of tokens 8*lk .. 8*lk+7 as fp16 pairs hi and lo (pair e: tokens
+      // 2e, 2e+1); B = p * S as hi + lo: the exact product of the hi parts,
+      // plus the lo parts' product, rounded once with the remainder
       const float* prow = hp + (gs * GQ + hq) * kRowP + 8 * lk;
-      const f32x4 p0 = *reinterpret_cast<const f32x4*>(prow);
-      const f32x4 p1 = *reinterpret_cast<const f32x4*>(prow + 4);
-      const float p[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+      const u32x4 ph = *reinterpret_cast<const u32x4*>(prow);
+      const u32x4 pl = *reinterpret_cast<const u32x4*>(prow + 4);
       u32x4 h4, l4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         uint32_t hi, lo;
-        split_pair(times_half<0>(p[2 * e], vs[e]), times_half<1>(p[2 * e + 1], vs[e]), hi, lo);
+        mul_pair_exact(ph[e], vs[e], hi, lo);
         h4[e] = hi;
-        l4[e] = lo;
-        zcls[e] = fmaf(p[2 * e], lo_half(vz[e]), zcls[e]);
-        zcls[e] = fmaf(p[2 * e + 1], hi_half(vz[e]), zcls[e]);
+        l4[e] = fma_pair(pl[e], vs[e], lo);
+        zcls[e] = dot2_acc(pl[e], vz[e], dot2_acc(ph[e], vz[e], zcls[e]));
       }
       const half8_t bph = as_h8(h4), bpl = as_h8(l4);
       const uint32_t vc[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
