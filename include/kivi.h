@@ -190,6 +190,12 @@ kivi_status kivi_decode_attn_workspace_bytes(const kivi_cache* cache,
  * The token axis is split across workgroups and the per-split partial
  * softmax states are merged exactly (log-sum-exp) in a second kernel; the
  * workspace holds those partials.
+ * With 1, 2 or 4 query heads per kv head the products run on the matrix
+ * cores with fp16 operands (hi + lo pairs, about 22 significant bits).  Their
+ * range needs, besides finite inputs, |q| * S < 8188 for every key scale S
+ * (2-bit keys; 32752 for 4-bit keys) and S < 1023 for every value scale
+ * (2-bit values; 4094 for 4-bit), i.e. value groups spanning less than about
+ * 3000 (2-bit) or 61000 (4-bit); results beyond that are unspecified.
  * Errors: INVALID_ARG (nulls, Hq not a positive multiple of H, bad dtype),
  * EMPTY (T == 0), BUFFER_TOO_SMALL (ws_bytes below the workspace query),
  * HIP. */
