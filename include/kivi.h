@@ -126,8 +126,10 @@ typedef struct {
 
 /* Device pointers into the cache buffer plus the host counters. */
 typedef struct {
-  int32_t n_quant;     /* tokens packed; a multiple of R */
-  int32_t n_resid;     /* tokens in the residual window, 0..R */
+  int32_t n_quant;     /* tokens packed; a multiple of R (-1 while the
+                          sequences hold different lengths: see
+                          kivi_cache_get_lengths) */
+  int32_t n_resid;     /* tokens in the residual window, 0..R (-1 likewise) */
   int32_t capacity;    /* cap: max_tokens rounded up to a multiple of R */
   int32_t num_blocks;  /* NB = cap / G */
   int32_t block_bytes; /* bytes of one block record */
@@ -170,8 +172,35 @@ kivi_status kivi_cache_reset(kivi_cache* cache);
 kivi_status kivi_append(kivi_cache* cache, const void* k, const void* v,
                         int32_t n_tokens, void* stream);
 
-/* Packs the residual window if it holds exactly R tokens (n_quant += R,
- * n_resid = 0); otherwise does nothing and returns KIVI_OK. */
+/* Appends n_tokens[b] tokens to sequence b (0 <= n_tokens[b] <= n_max, a
+ * host array of `batch` entries).  k and v are device arrays of kv_dtype laid
+ * out [B][H][n_max][D]; sequence b takes its first n_tokens[b] tokens.  Each
+ * sequence follows the rules of kivi_append on its own lengths, so sequences
+ * may hold different lengths afterwards (many concurrent requests, each with
+ * its own cache: page "KV cache quantization with KIVI INT2 setup guide",
+ * section "VRAM Before/After and What It Buys You in Batch Size").  The work
+ * runs as at most four launches per 32 sequences.  kivi_append on such a
+ * cache appends n_tokens to every sequence.
+ * Errors: INVALID_ARG (null cache/n_tokens, n_tokens[b] outside [0, n_max],
+ * null or unaligned k/v when some n_tokens[b] > 0), CAPACITY (a sequence
+ * would exceed max_tokens; nothing is appended), HIP. */
+kivi_status kivi_append_varlen(kivi_cache* cache, const void* k, const void* v,
+                               const int32_t* n_tokens, int32_t n_max, void* stream);
+
+/* Forgets every token of the `count` sequences listed in seqs (host array),
+ * without touching device memory; their next append starts from an empty
+ * cache (a finished request's slot taken by a new one).
+ * Errors: INVALID_ARG (null cache, null seqs with count > 0, an index
+ * outside [0, batch)). */
+kivi_status kivi_cache_reset_sequences(kivi_cache* cache, const int32_t* seqs, int32_t count);
+
+/* Per-sequence counters: n_quant[b] and n_resid[b] for b < batch (host
+ * arrays).  Equal to the view's counters while every sequence has the same
+ * lengths. */
+kivi_status kivi_cache_get_lengths(const kivi_cache* cache, int32_t* n_quant, int32_t* n_resid);
+
+/* Packs the residual window of every sequence whose window holds exactly R
+ * tokens (n_quant += R, n_resid = 0); the others are left alone. */
 kivi_status kivi_flush_residual(kivi_cache* cache, void* stream);
 
 /* Workspace bytes kivi_decode_attn needs for num_q_heads query heads at any
@@ -196,9 +225,12 @@ kivi_status kivi_decode_attn_workspace_bytes(const kivi_cache* cache,
  * (2-bit keys; 32752 for 4-bit keys) and S < 1023 for every value scale
  * (2-bit values; 4094 for 4-bit), i.e. value groups spanning less than about
  * 3000 (2-bit) or 61000 (4-bit); results beyond that are unspecified.
+ * Sequences of different lengths each attend over their own tokens; a
+ * sequence without tokens gets zeros.  The splits are then planned for the
+ * longest sequence, and each launch pair covers 64 sequences.
  * Errors: INVALID_ARG (nulls, Hq not a positive multiple of H, bad dtype),
- * EMPTY (T == 0), BUFFER_TOO_SMALL (ws_bytes below the workspace query),
- * HIP. */
+ * EMPTY (no sequence holds a token), BUFFER_TOO_SMALL (ws_bytes below the
+ * workspace query), HIP. */
 kivi_status kivi_decode_attn(const kivi_cache* cache, const void* q,
                              int32_t num_q_heads, float softmax_scale,
                              void* out, int32_t out_dtype, void* workspace,

@@ -21,6 +21,7 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "../../include/kivi.h"
 #include "kivi_internal.h"
@@ -29,8 +30,12 @@ struct kivi_cache {
   kivi_config cfg;
   int cap;  // token capacity per unit (max_tokens rounded up to R)
   int nb;   // blocks per unit
-  int n_quant;
+  int n_quant;  // every sequence's, or the largest when ragged
   int n_resid;
+  // sequences of different lengths (per-sequence appends or resets): the
+  // per-sequence counters below are then the state
+  bool ragged;
+  std::vector<int> sq, sr;  // n_quant, n_resid of each sequence (ragged)
   int forced_splits;
   int cu_count;  // queried on first decode
   bool poisoned;
@@ -165,6 +170,150 @@ kivi_status copy_to_window(kivi_cache* c, const uint16_t* k, const uint16_t* v,
   return KIVI_OK;
 }
 
+// ---- sequences of different lengths
+//
+// Each sequence follows the single-sequence rules above.  A ragged append
+// runs in up to four phases, each one pack launch per chunk of kPackChunk
+// sequences with per-sequence work: (A) pack the full windows of sequences
+// receiving tokens, (B) top up windows that the new tokens overflow, (C) pack
+// those, (D) pack whole windows straight from the input and copy the rest
+// into the window.
+
+void make_ragged(kivi_cache* c) {
+  if (c->ragged) return;
+  c->sq.assign(c->cfg.batch, c->n_quant);
+  c->sr.assign(c->cfg.batch, c->n_resid);
+  c->ragged = true;
+}
+
+// Back to the uniform representation when every sequence has the same
+// lengths; otherwise n_quant / n_resid become the largest ones.
+void settle(kivi_cache* c) {
+  if (!c->ragged) return;
+  bool same = true;
+  int mq = 0, mr = 0;
+  for (int b = 0; b < c->cfg.batch; ++b) {
+    same = same && c->sq[b] == c->sq[0] && c->sr[b] == c->sr[0];
+    mq = std::max(mq, c->sq[b]);
+    mr = std::max(mr, c->sr[b]);
+  }
+  c->n_quant = mq;
+  c->n_resid = mr;
+  if (same) c->ragged = false;
+}
+
+// One ragged pack phase: ops[b] for every sequence (empty ops do nothing).
+kivi_status launch_ragged_phase(kivi_cache* c, const std::vector<kivi::SeqOp>& ops,
+                                const uint16_t* k_src, const uint16_t* v_src, long long src_stride,
+                                const uint16_t* rk_src, const uint16_t* rv_src, long long r_stride,
+                                hipStream_t s) {
+  const int B = c->cfg.batch, H = c->cfg.num_kv_heads;
+  for (int b0 = 0; b0 < B; b0 += kivi::kPackChunk) {
+    const int nseq = std::min(kivi::kPackChunk, B - b0);
+    bool any = false;
+    kivi::PackArgs a = base_pack_args(c);
+    a.ragged = 1;
+    a.unit0 = b0 * H;
+    a.H = H;
+    a.units = nseq * H;
+    a.k_src = k_src;
+    a.v_src = v_src;
+    a.src_unit_stride = src_stride;
+    a.rk_src = rk_src;
+    a.rv_src = rv_src;
+    a.r_src_unit_stride = r_stride;
+    for (int i = 0; i < nseq; ++i) {
+      a.op[i] = ops[b0 + i];
+      any = any || a.op[i].nblk > 0 || a.op[i].r_count > 0;
+    }
+    if (!any) continue;
+    hipError_t e = kivi::launch_pack(a, c->cfg.k_bits, c->cfg.v_bits, c->cfg.kv_dtype, s);
+    if (e != hipSuccess) return hip_fail(c, e, "pack launch (sequences of different lengths)");
+  }
+  return KIVI_OK;
+}
+
+// Packs the full window of every sequence with flush[b] set.
+kivi_status ragged_flush(kivi_cache* c, const std::vector<char>& flush, hipStream_t s) {
+  const int B = c->cfg.batch, R = c->cfg.residual_length, G = c->cfg.group_size;
+  std::vector<kivi::SeqOp> ops(B, kivi::SeqOp{0, 0, 0, 0, 0, 0});
+  bool any = false;
+  for (int b = 0; b < B; ++b) {
+    if (!flush[b]) continue;
+    ops[b].nblk = R / G;
+    ops[b].dst_blk0 = c->sq[b] / G;
+    any = true;
+  }
+  if (!any) return KIVI_OK;
+  const long long stride = (long long)R * c->cfg.head_dim;
+  kivi_status st = launch_ragged_phase(c, ops, c->k_resid, c->v_resid, stride, nullptr, nullptr, 0, s);
+  if (st != KIVI_OK) return st;
+  for (int b = 0; b < B; ++b) {
+    if (!flush[b]) continue;
+    c->sq[b] += R;
+    c->sr[b] = 0;
+  }
+  return KIVI_OK;
+}
+
+// Appends n[b] tokens to sequence b from k, v laid out [B][H][n_max][D].
+kivi_status ragged_append(kivi_cache* c, const uint16_t* k, const uint16_t* v, const int32_t* n,
+                          int n_max, hipStream_t s) {
+  const int B = c->cfg.batch, R = c->cfg.residual_length, G = c->cfg.group_size;
+  const long long stride = (long long)n_max * c->cfg.head_dim;
+  make_ragged(c);
+  kivi_status st;
+  // (A) a full window is packed before the next token enters it
+  std::vector<char> fl(B, 0);
+  for (int b = 0; b < B; ++b) fl[b] = n[b] > 0 && c->sr[b] == R;
+  if ((st = ragged_flush(c, fl, s)) != KIVI_OK) return st;
+  // (B) top up windows the new tokens overflow, (C) pack them
+  std::vector<int> pos(B, 0);
+  std::vector<kivi::SeqOp> ops(B, kivi::SeqOp{0, 0, 0, 0, 0, 0});
+  bool any = false;
+  for (int b = 0; b < B; ++b) {
+    fl[b] = c->sr[b] > 0 && c->sr[b] + n[b] > R;
+    if (!fl[b]) continue;
+    pos[b] = R - c->sr[b];
+    ops[b].r_count = pos[b];
+    ops[b].r_dst_slot0 = c->sr[b];
+    any = true;
+  }
+  if (any) {
+    if ((st = launch_ragged_phase(c, ops, nullptr, nullptr, 0, k, v, stride, s)) != KIVI_OK) return st;
+    for (int b = 0; b < B; ++b)
+      if (fl[b]) c->sr[b] = R;
+    if ((st = ragged_flush(c, fl, s)) != KIVI_OK) return st;
+  }
+  // (D) the rest: whole windows straight from the input, the last 1..R
+  // tokens into an empty window; or everything into a partly filled window
+  std::vector<int> nq2(c->sq), nr2(c->sr);
+  any = false;
+  for (int b = 0; b < B; ++b) {
+    ops[b] = kivi::SeqOp{0, 0, 0, 0, 0, 0};
+    const int rem = n[b] - pos[b];
+    if (rem <= 0) continue;
+    any = true;
+    if (c->sr[b] == 0) {
+      const int keep = (rem - 1) % R + 1;
+      const int npack = rem - keep;
+      ops[b] = kivi::SeqOp{pos[b], npack / G, c->sq[b] / G, pos[b] + npack, keep, 0};
+      nq2[b] += npack;
+      nr2[b] = keep;
+    } else {
+      ops[b] = kivi::SeqOp{0, 0, 0, pos[b], rem, c->sr[b]};
+      nr2[b] += rem;
+    }
+  }
+  if (any) {
+    if ((st = launch_ragged_phase(c, ops, k, v, stride, k, v, stride, s)) != KIVI_OK) return st;
+    c->sq = nq2;
+    c->sr = nr2;
+  }
+  settle(c);
+  return KIVI_OK;
+}
+
 size_t workspace_bytes_for(const kivi_cache* c, int hq, int n_split) {
   return (size_t)c->cfg.batch * hq * n_split * (c->cfg.head_dim + 2) * sizeof(float);
 }
@@ -218,6 +367,30 @@ kivi_status kivi_cache_reset(kivi_cache* cache) {
   if (cache->poisoned) return fail(KIVI_ERR_HIP, "cache handle is poisoned by an earlier HIP error");
   cache->n_quant = 0;
   cache->n_resid = 0;
+  cache->ragged = false;
+  return KIVI_OK;
+}
+
+kivi_status kivi_cache_reset_sequences(kivi_cache* c, const int32_t* seqs, int32_t count) {
+  if (!c) return fail(KIVI_ERR_INVALID_ARG, "cache is NULL");
+  if (c->poisoned) return fail(KIVI_ERR_HIP, "cache handle is poisoned by an earlier HIP error");
+  if (count < 0 || (count > 0 && !seqs)) return fail(KIVI_ERR_INVALID_ARG, "bad sequence list");
+  for (int i = 0; i < count; ++i)
+    if (seqs[i] < 0 || seqs[i] >= c->cfg.batch)
+      return fail(KIVI_ERR_INVALID_ARG, "sequence %d out of range [0, %d)", seqs[i], c->cfg.batch);
+  if (count == 0) return KIVI_OK;
+  make_ragged(c);
+  for (int i = 0; i < count; ++i) c->sq[seqs[i]] = c->sr[seqs[i]] = 0;
+  settle(c);
+  return KIVI_OK;
+}
+
+kivi_status kivi_cache_get_lengths(const kivi_cache* c, int32_t* n_quant, int32_t* n_resid) {
+  if (!c || !n_quant || !n_resid) return fail(KIVI_ERR_INVALID_ARG, "cache and outputs must not be NULL");
+  for (int b = 0; b < c->cfg.batch; ++b) {
+    n_quant[b] = c->ragged ? c->sq[b] : c->n_quant;
+    n_resid[b] = c->ragged ? c->sr[b] : c->n_resid;
+  }
   return KIVI_OK;
 }
 
@@ -229,13 +402,22 @@ kivi_status kivi_append(kivi_cache* c, const void* k, const void* v, int32_t n_t
   if (n_tokens == 0) return KIVI_OK;
   if (!k || !v) return fail(KIVI_ERR_INVALID_ARG, "k and v must not be NULL");
   if (!aligned16(k) || !aligned16(v)) return fail(KIVI_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
-  if ((long long)c->n_quant + c->n_resid + n_tokens > c->cfg.max_tokens)
+  int longest = c->n_quant + c->n_resid;
+  if (c->ragged) {
+    longest = 0;
+    for (int b = 0; b < c->cfg.batch; ++b) longest = std::max(longest, c->sq[b] + c->sr[b]);
+  }
+  if ((long long)longest + n_tokens > c->cfg.max_tokens)
     return fail(KIVI_ERR_CAPACITY, "appending %d tokens to %d exceeds max_tokens %d", n_tokens,
-                c->n_quant + c->n_resid, c->cfg.max_tokens);
+                longest, c->cfg.max_tokens);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint16_t* kk = static_cast<const uint16_t*>(k);
   const uint16_t* vv = static_cast<const uint16_t*>(v);
+  if (c->ragged) {  // every sequence takes n_tokens, each from its own state
+    const std::vector<int32_t> n(c->cfg.batch, n_tokens);
+    return ragged_append(c, kk, vv, n.data(), n_tokens, s);
+  }
   const int R = c->cfg.residual_length, G = c->cfg.group_size, D = c->cfg.head_dim;
   const long long stride = (long long)n_tokens * D;
   kivi_status st;
@@ -281,9 +463,44 @@ kivi_status kivi_append(kivi_cache* c, const void* k, const void* v, int32_t n_t
   return KIVI_OK;
 }
 
+kivi_status kivi_append_varlen(kivi_cache* c, const void* k, const void* v, const int32_t* n_tokens,
+                               int32_t n_max, void* stream) {
+  if (!c) return fail(KIVI_ERR_INVALID_ARG, "cache is NULL");
+  if (c->poisoned) return fail(KIVI_ERR_HIP, "cache handle is poisoned by an earlier HIP error");
+  if (!n_tokens) return fail(KIVI_ERR_INVALID_ARG, "n_tokens is NULL");
+  if (n_max < 0) return fail(KIVI_ERR_INVALID_ARG, "n_max must be >= 0");
+  const int B = c->cfg.batch;
+  bool any = false, all_max = true;
+  for (int b = 0; b < B; ++b) {
+    if (n_tokens[b] < 0 || n_tokens[b] > n_max)
+      return fail(KIVI_ERR_INVALID_ARG, "n_tokens[%d] = %d is outside [0, n_max = %d]", b, n_tokens[b], n_max);
+    any = any || n_tokens[b] > 0;
+    all_max = all_max && n_tokens[b] == n_max;
+  }
+  if (!any) return KIVI_OK;
+  if (!k || !v) return fail(KIVI_ERR_INVALID_ARG, "k and v must not be NULL");
+  if (!aligned16(k) || !aligned16(v)) return fail(KIVI_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
+  for (int b = 0; b < B; ++b) {
+    const int t = c->ragged ? c->sq[b] + c->sr[b] : c->n_quant + c->n_resid;
+    if ((long long)t + n_tokens[b] > c->cfg.max_tokens)
+      return fail(KIVI_ERR_CAPACITY, "sequence %d: appending %d tokens to %d exceeds max_tokens %d", b,
+                  n_tokens[b], t, c->cfg.max_tokens);
+  }
+  if (all_max && !c->ragged) return kivi_append(c, k, v, n_max, stream);
+  return ragged_append(c, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), n_tokens,
+                       n_max, static_cast<hipStream_t>(stream));
+}
+
 kivi_status kivi_flush_residual(kivi_cache* c, void* stream) {
   if (!c) return fail(KIVI_ERR_INVALID_ARG, "cache is NULL");
   if (c->poisoned) return fail(KIVI_ERR_HIP, "cache handle is poisoned by an earlier HIP error");
+  if (c->ragged) {
+    std::vector<char> fl(c->cfg.batch, 0);
+    for (int b = 0; b < c->cfg.batch; ++b) fl[b] = c->sr[b] == c->cfg.residual_length;
+    kivi_status st = ragged_flush(c, fl, static_cast<hipStream_t>(stream));
+    if (st == KIVI_OK) settle(c);
+    return st;
+  }
   if (c->n_resid != c->cfg.residual_length) return KIVI_OK;
   return flush_window(c, static_cast<hipStream_t>(stream));
 }
@@ -404,9 +621,29 @@ kivi_status kivi_decode_attn(const kivi_cache* cc, const void* q, int32_t num_q_
   a.n_split_packed = n_split_packed;
   a.groups_per_split = gps;
   a.qscale = softmax_scale * 1.4426950408889634f;  // log2(e): base-2 softmax
-  hipError_t e = kivi::launch_decode(a, c->cfg.k_bits, c->cfg.v_bits, c->cfg.kv_dtype, out_dtype,
-                                     use_mfma, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(c, e, "decode launch");
+  if (!c->ragged) {
+    hipError_t e = kivi::launch_decode(a, c->cfg.k_bits, c->cfg.v_bits, c->cfg.kv_dtype, out_dtype,
+                                       use_mfma, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(c, e, "decode launch");
+    return KIVI_OK;
+  }
+  // sequences of different lengths: the splits are planned for the longest
+  // (n_quant, n_resid hold the largest); each launch covers kDecodeChunk
+  // sequences with their own lengths, and splits past a sequence's end
+  // leave empty partials
+  a.ragged = 1;
+  for (int b0 = 0; b0 < c->cfg.batch; b0 += kivi::kDecodeChunk) {
+    const int nseq = std::min(kivi::kDecodeChunk, c->cfg.batch - b0);
+    a.seq0 = b0;
+    a.B = nseq;
+    for (int i = 0; i < nseq; ++i) {
+      a.seq_len[i][0] = c->sq[b0 + i];
+      a.seq_len[i][1] = c->sr[b0 + i];
+    }
+    hipError_t e = kivi::launch_decode(a, c->cfg.k_bits, c->cfg.v_bits, c->cfg.kv_dtype, out_dtype,
+                                       use_mfma, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(c, e, "decode launch (sequences of different lengths)");
+  }
   return KIVI_OK;
 }
 
@@ -419,8 +656,8 @@ kivi_status kivi_set_decode_splits(kivi_cache* c, int32_t n_split) {
 
 kivi_status kivi_cache_get_view(const kivi_cache* c, kivi_cache_view* v) {
   if (!c || !v) return fail(KIVI_ERR_INVALID_ARG, "cache and view must not be NULL");
-  v->n_quant = c->n_quant;
-  v->n_resid = c->n_resid;
+  v->n_quant = c->ragged ? -1 : c->n_quant;  // per sequence: kivi_cache_get_lengths
+  v->n_resid = c->ragged ? -1 : c->n_resid;
   v->capacity = c->cap;
   v->num_blocks = c->nb;
   const kivi::BlockLayout bl = kivi::block_layout(c->cfg.k_bits, c->cfg.v_bits);

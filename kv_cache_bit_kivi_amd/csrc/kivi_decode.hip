@@ -62,8 +62,16 @@ __global__ __launch_bounds__(256) void decode_split_valu(DecodeArgs a) {
 
   const int tid = threadIdx.x;
   const int split = blockIdx.x;
-  const long long u = blockIdx.y;
-  const int b = static_cast<int>(u / a.H), h = static_cast<int>(u % a.H);
+  const int h = static_cast<int>(blockIdx.y % a.H);
+  // this unit's sequence and lengths: the launch's, or its own in a ragged
+  // launch (a split past the sequence's end leaves an empty partial)
+  int b = static_cast<int>(blockIdx.y / a.H), nq = a.n_quant, nr = a.n_resid;
+  if (a.ragged) {
+    nq = a.seq_len[b][0];
+    nr = a.seq_len[b][1];
+    b += a.seq0;
+  }
+  const long long u = (long long)b * a.H + h;
 
   for (int i = tid; i < GQ * D; i += 256) {
     const int j = i / D, d = i % D;
@@ -77,8 +85,8 @@ __global__ __launch_bounds__(256) void decode_split_valu(DecodeArgs a) {
 #pragma unroll
   for (int j = 0; j < GQ; ++j) o[j] = 0.0f;
 
-  const int nqb = a.n_quant / G;
-  const int n_items = nqb + (a.n_resid + G - 1) / G;
+  const int nqb = nq / G;
+  const int n_items = nqb + (nr + G - 1) / G;
   const int i0 = split * a.items_per_split;
   const int i1 = min(n_items, i0 + a.items_per_split);
   __syncthreads();
@@ -86,7 +94,7 @@ __global__ __launch_bounds__(256) void decode_split_valu(DecodeArgs a) {
   for (int it = i0; it < i1; ++it) {
     const bool packed = it < nqb;
     const int rc = it - nqb;  // window chunk index when !packed
-    const int ntok = packed ? G : min(G, a.n_resid - rc * G);
+    const int ntok = packed ? G : min(G, nr - rc * G);
     const uint8_t* const rec = a.blocks + (u * a.nb + (packed ? it : 0)) * BL.bytes;
     if (packed) {
       // key meta [d]; value meta [m][row], 4 * 32 = D entries
@@ -219,7 +227,7 @@ __global__ __launch_bounds__(D) void decode_merge(DecodeArgs a) {
   constexpr int kPre = 16;  // splits whose o_s values are loaded up front
   __shared__ float wsh[kMaxSplits];
   __shared__ float red[2][D / 64];
-  const long long bj = blockIdx.x;
+  const long long bj = (long long)a.seq0 * a.Hq + blockIdx.x;  // seq0 = 0 unless ragged
   const int d = threadIdx.x, lane = d & 63, wv = d >> 6;
   const int ns = a.n_split;
   const float* P = a.partial + bj * ns * (D + 2);
@@ -273,7 +281,8 @@ __global__ __launch_bounds__(D) void decode_merge(DecodeArgs a) {
     for (int k = 0; k < 8; ++k) O = fmaf(wsh[s + k], x[k], O);
   }
   for (; s < ns; ++s) O = fmaf(wsh[s], P[s * (D + 2) + 2 + d], O);
-  const float r = O / L;
+  // a sequence without tokens (ragged caches only) gets zeros
+  const float r = L > 0.0f ? O / L : 0.0f;
   if constexpr (OUT == 2) {
     static_cast<float*>(a.out)[bj * D + d] = r;
   } else if constexpr (OUT == 1) {

@@ -241,7 +241,7 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // Residual window on the vector ALUs (one wave, fp32), written as its own
 // partial.  qsh / psh: LDS scratch of this wave.
 template <bool BF16, int NQ>
-__device__ void window_wave(const DecodeArgs& a, long long u, int b, int kvh, int split,
+__device__ void window_wave(const DecodeArgs& a, long long u, int b, int kvh, int split, int nr,
                             float (*qsh)[D], float (*psh)[G]) {
   const int lane = threadIdx.x & 63;
   for (int i = lane; i < NQ * D; i += 64) {
@@ -257,9 +257,9 @@ __device__ void window_wave(const DecodeArgs& a, long long u, int b, int kvh, in
     o[h][0] = o[h][1] = 0.0f;
   }
   const int half = lane >> 5;
-  for (int c0 = 0; c0 < a.n_resid; c0 += G) {
+  for (int c0 = 0; c0 < nr; c0 += G) {
     const int t = c0 + (lane & 31);
-    const bool live = t < a.n_resid;
+    const bool live = t < nr;
     float acc[NQ];
 #pragma unroll
     for (int h = 0; h < NQ; ++h) acc[h] = 0.0f;
@@ -294,7 +294,7 @@ __device__ void window_wave(const DecodeArgs& a, long long u, int b, int kvh, in
       if (lane < G) psh[h][lane] = p;
     }
     wave_lds_sync();
-    const int n = min(G, a.n_resid - c0);
+    const int n = min(G, nr - c0);
     for (int tt = 0; tt < n; ++tt) {
       const uint32_t vv = *reinterpret_cast<const uint32_t*>(a.v_resid + (u * a.R + c0 + tt) * D + 2 * lane);
       const float v0 = to_f32<BF16>(static_cast<uint16_t>(vv & 0xffffu));
@@ -622,7 +622,7 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
 // wave.  Writes o of the partial; the last split also runs the window.
 template <int KB, int VB, bool BF16, int NQ>
 __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int b, int kvh, int split,
-                                           int gb, int ge, int n_steps, uint8_t* smem) {
+                                           int gb, int ge, int n_steps, int nr, uint8_t* smem) {
   using S = Stage<KB, VB>;
   using VS = CodeScale<VB>;
   const int lane = threadIdx.x & 63;
@@ -714,11 +714,12 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
       *reinterpret_cast<f32x4*>(P + 2 + 32 * lk + 8 * r + 4) = x1;
     }
   }
-  // the last packed split also takes the window (its own partial); this
-  // wave's stage loads have completed and its value stages are free
-  if (split == a.n_split_packed - 1 && a.n_resid > 0) {
+  // the last packed split also takes the window (its own partial, empty
+  // for a sequence without window tokens in a ragged launch); this wave's
+  // stage loads have completed and its value stages are free
+  if (split == a.n_split_packed - 1 && a.n_split > a.n_split_packed) {
     wave_lds_sync();
-    window_wave<BF16, NQ>(a, u, b, kvh, a.n_split_packed, reinterpret_cast<float (*)[D]>(vbase),
+    window_wave<BF16, NQ>(a, u, b, kvh, a.n_split_packed, nr, reinterpret_cast<float (*)[D]>(vbase),
                       reinterpret_cast<float (*)[G]>(vbase + GQ * D * 4));
   }
 }
@@ -729,30 +730,50 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
   __shared__ __align__(16) uint8_t smem[S::bytes];
   const int wave = threadIdx.x >> 6;  // 0: key wave, 1: value wave
   const int split = blockIdx.x;
-  const long long u = blockIdx.y;
-  const int b = static_cast<int>(u / a.H), kvh = static_cast<int>(u % a.H);
+  const int kvh = static_cast<int>(blockIdx.y % a.H);
+  // this unit's sequence and lengths: the launch's, or its own in a ragged launch
+  int b = static_cast<int>(blockIdx.y / a.H), nq = a.n_quant, nr = a.n_resid;
+  if (a.ragged) {
+    nq = a.seq_len[b][0];
+    nr = a.seq_len[b][1];
+    b += a.seq0;
+  }
+  const long long u = (long long)b * a.H + kvh;
 
   if (a.n_split_packed == 0) {  // nothing packed yet: the window is the only split
     if (wave == 1)
-      window_wave<BF16, NQ>(a, u, b, kvh, 0, reinterpret_cast<float (*)[D]>(smem + S::offV0),
+      window_wave<BF16, NQ>(a, u, b, kvh, 0, nr, reinterpret_cast<float (*)[D]>(smem + S::offV0),
                         reinterpret_cast<float (*)[G]>(smem + S::offV0 + GQ * D * 4));
     return;
   }
-  const int nqg = a.n_quant / G;
+  const int nqg = nq / G;
   const int gb = split * a.groups_per_split;
   const int ge = min(nqg, gb + a.groups_per_split);
+  if (gb >= nqg) {
+    // (ragged) this sequence ends before this split: an empty partial
+    // (m = -inf, l = 0, o = 0); the last packed split still takes the window
+    for (int i = threadIdx.x; i < NQ * (D + 2); i += 128) {
+      float* P = a.partial + (((long long)b * a.Hq + kvh * NQ + i / (D + 2)) * a.n_split + split) * (D + 2);
+      P[i % (D + 2)] = i % (D + 2) == 0 ? -INFINITY : 0.0f;
+    }
+    if (wave == 1 && split == a.n_split_packed - 1 && a.n_split > a.n_split_packed)
+      window_wave<BF16, NQ>(a, u, b, kvh, a.n_split_packed, nr, reinterpret_cast<float (*)[D]>(smem + S::offV0),
+                        reinterpret_cast<float (*)[G]>(smem + S::offV0 + GQ * D * 4));
+    return;
+  }
   const int n_steps = (ge - gb + 3) / 4;  // >= 1: every split holds a group
   // Both waves run the same number of steps and meet at one barrier per step.
   if (wave == 0) {
     key_wave<KB, VB, BF16, NQ>(a, u, b, kvh, split, gb, ge, n_steps, smem);
   } else {
-    value_wave<KB, VB, BF16, NQ>(a, u, b, kvh, split, gb, ge, n_steps, smem);
+    value_wave<KB, VB, BF16, NQ>(a, u, b, kvh, split, gb, ge, n_steps, nr, smem);
   }
 }
 
 template <int KB, int VB, bool BF16, int NQ>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  // one workgroup per packed split; the last one also runs the window
+  // one workgroup per packed split; the last one also runs the window.
+  // A ragged launch covers a.B sequences from a.seq0.
   dim3 grid(a.n_split_packed > 0 ? a.n_split_packed : 1, a.B * a.H);
   hipLaunchKernelGGL((decode_mfma<KB, VB, BF16, NQ>), grid, dim3(128), 0, stream, a);
   return hipGetLastError();

@@ -26,8 +26,18 @@ __host__ __device__ constexpr BlockLayout block_layout(int k_bits, int v_bits) {
                      kGroup * kHeadDim * (k_bits + v_bits) / 8 + 8 * kHeadDim};
 }
 
+// Per-sequence work of a pack launch over sequences of different lengths
+// (same fields as the uniform ones of PackArgs).
+struct SeqOp {
+  int src_tok0, nblk, dst_blk0, r_src_tok0, r_count, r_dst_slot0;
+};
+constexpr int kPackChunk = 32;    // sequences per ragged pack launch
+constexpr int kDecodeChunk = 64;  // sequences per ragged decode launch
+
 // One launch of the pack kernel: quantize + bit-pack `nblk` blocks of G
 // tokens per unit, and copy `r_count` tokens per unit into the window.
+// Ragged launches (ragged != 0) cover units unit0 .. unit0 + gridDim.y - 1,
+// H per sequence, and take each sequence's work from op[] instead.
 struct PackArgs {
   // tokens to pack: unit u, token i is at src + u * src_unit_stride + i * D
   const uint16_t* k_src;
@@ -51,6 +61,10 @@ struct PackArgs {
   int nb;     // blocks per unit (cap / G)
   int R;      // window length
   int units;  // B * H
+  int ragged;
+  int unit0;  // ragged: first unit of the launch (a sequence boundary)
+  int H;      // ragged: units per sequence
+  SeqOp op[kPackChunk];
 };
 
 // One decode-attention launch (split kernel + merge kernel).
@@ -69,6 +83,12 @@ struct DecodeArgs {
   int n_split_packed;   // matrix kernel: splits over packed groups (window split follows)
   int groups_per_split; // matrix kernel: packed groups per split, a multiple of 4
   float qscale;         // softmax_scale * log2(e): scores in base-2 units
+  // ragged launches (ragged != 0) cover sequences seq0 .. seq0 + gridDim.y / H
+  // - 1 and take each one's lengths from seq_len[][2] = (n_quant, n_resid);
+  // n_quant and n_resid above are then the largest of the whole cache
+  int ragged;
+  int seq0;
+  int seq_len[kDecodeChunk][2];
 };
 
 // LDS bytes of one workgroup (key wave + value wave) of the matrix-core

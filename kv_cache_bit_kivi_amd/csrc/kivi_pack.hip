@@ -254,16 +254,30 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
 
   const int tid = threadIdx.x;
   const int item = blockIdx.x;
-  const long long u = blockIdx.y;
+  // this unit's work: the launch's, or its sequence's in a ragged launch
+  long long u = blockIdx.y;
+  int nblk = a.nblk, src_tok0 = a.src_tok0, dst_blk0 = a.dst_blk0;
+  int r_src_tok0 = a.r_src_tok0, r_count = a.r_count, r_dst_slot0 = a.r_dst_slot0;
+  if (a.ragged) {
+    const SeqOp& o = a.op[blockIdx.y / a.H];
+    u = a.unit0 + (long long)blockIdx.y;
+    nblk = o.nblk;
+    src_tok0 = o.src_tok0;
+    dst_blk0 = o.dst_blk0;
+    r_src_tok0 = o.r_src_tok0;
+    r_count = o.r_count;
+    r_dst_slot0 = o.r_dst_slot0;
+    if (item >= nblk + (r_count + G - 1) / G) return;  // the grid covers the longest sequence
+  }
 
-  if (item >= a.nblk) {
+  if (item >= nblk) {
     // ---- residual-window copy: 32 tokens per workgroup
-    const int t0 = (item - a.nblk) * G;
-    const int n = min(G, a.r_count - t0);
+    const int t0 = (item - nblk) * G;
+    const int n = min(G, r_count - t0);
     for (int c = tid; c < n * (D / 8); c += 256) {
       const int t = t0 + c / (D / 8), col = (c % (D / 8)) * 8;
-      const long long src = u * a.r_src_unit_stride + (long long)(a.r_src_tok0 + t) * D + col;
-      const long long dst = (u * a.R + a.r_dst_slot0 + t) * D + col;
+      const long long src = u * a.r_src_unit_stride + (long long)(r_src_tok0 + t) * D + col;
+      const long long dst = (u * a.R + r_dst_slot0 + t) * D + col;
       *reinterpret_cast<uint4*>(a.k_resid + dst) = *reinterpret_cast<const uint4*>(a.rk_src + src);
       *reinterpret_cast<uint4*>(a.v_resid + dst) = *reinterpret_cast<const uint4*>(a.rv_src + src);
     }
@@ -273,12 +287,12 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
   // ---- stage the key and value tiles of this block
   constexpr BlockLayout BL = block_layout(KB, VB);
   const int blk = item;
-  const int gblk = a.dst_blk0 + blk;
+  const int gblk = dst_blk0 + blk;
   uint8_t* const rec = a.blocks + (u * a.nb + gblk) * BL.bytes;  // this block's record
   {
     // 16-byte pieces c = tid and c = tid + 256 of the 32 x 128 tiles
     const int row = tid / (D / 8), col = (tid % (D / 8)) * 8;
-    const long long base = u * a.src_unit_stride + (long long)(a.src_tok0 + blk * G) * D + row * D + col;
+    const long long base = u * a.src_unit_stride + (long long)(src_tok0 + blk * G) * D + row * D + col;
     const uint4 k0 = *reinterpret_cast<const uint4*>(a.k_src + base);
     const uint4 k1 = *reinterpret_cast<const uint4*>(a.k_src + base + 16 * D);
     const uint4 v0 = *reinterpret_cast<const uint4*>(a.v_src + base);
@@ -416,8 +430,13 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
 
 template <int KB, int VB, bool BF16>
 hipError_t launch_pack_t(const PackArgs& a, hipStream_t stream) {
-  const int items = a.nblk + (a.r_count + G - 1) / G;
-  if (items == 0) return hipSuccess;
+  int items = a.nblk + (a.r_count + G - 1) / G;
+  if (a.ragged) {  // a.units units of a.units / a.H sequences: the longest sets the grid
+    items = 0;
+    for (int i = 0; i < a.units / a.H; ++i)
+      items = max(items, a.op[i].nblk + (a.op[i].r_count + G - 1) / G);
+  }
+  if (items == 0 || a.units == 0) return hipSuccess;
   dim3 grid(items, a.units);
   hipLaunchKernelGGL((pack_kernel<KB, VB, BF16>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();

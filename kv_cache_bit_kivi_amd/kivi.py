@@ -31,6 +31,7 @@ EXPORTED = (
     "kivi_append", "kivi_flush_residual", "kivi_decode_attn_workspace_bytes",
     "kivi_decode_attn", "kivi_set_decode_splits", "kivi_cache_get_view",
     "kivi_status_string", "kivi_last_error_message",
+    "kivi_append_varlen", "kivi_cache_reset_sequences", "kivi_cache_get_lengths",
 )
 
 
@@ -73,6 +74,9 @@ def _load():
         "kivi_cache_reset": ([vp], i32),
         "kivi_append": ([vp, vp, vp, i32, vp], i32),
         "kivi_flush_residual": ([vp, vp], i32),
+        "kivi_append_varlen": ([vp, vp, vp, ctypes.POINTER(i32), i32, vp], i32),
+        "kivi_cache_reset_sequences": ([vp, ctypes.POINTER(i32), i32], i32),
+        "kivi_cache_get_lengths": ([vp, ctypes.POINTER(i32), ctypes.POINTER(i32)], i32),
         "kivi_decode_attn_workspace_bytes": ([vp, i32, ctypes.POINTER(sz)], i32),
         "kivi_decode_attn": ([vp, vp, i32, ctypes.c_float, vp, i32, vp, sz, vp], i32),
         "kivi_set_decode_splits": ([vp, i32], i32),
@@ -133,6 +137,29 @@ def kivi_append(h, k_ptr, v_ptr, n_tokens, stream):
 
 def kivi_flush_residual(h, stream):
     _check(lib.kivi_flush_residual(h, ctypes.c_void_p(stream)))
+
+
+def _i32_array(values):
+    values = [int(x) for x in values]
+    return (ctypes.c_int32 * max(1, len(values)))(*values), len(values)
+
+
+def kivi_append_varlen(h, k_ptr, v_ptr, n_tokens, n_max, stream):
+    arr, _ = _i32_array(n_tokens)
+    _check(lib.kivi_append_varlen(h, ctypes.c_void_p(k_ptr), ctypes.c_void_p(v_ptr), arr, n_max,
+                                  ctypes.c_void_p(stream)))
+
+
+def kivi_cache_reset_sequences(h, seqs):
+    arr, n = _i32_array(seqs)
+    _check(lib.kivi_cache_reset_sequences(h, arr, n))
+
+
+def kivi_cache_get_lengths(h, batch):
+    nq = (ctypes.c_int32 * batch)()
+    nr = (ctypes.c_int32 * batch)()
+    _check(lib.kivi_cache_get_lengths(h, nq, nr))
+    return list(nq), list(nr)
 
 
 def kivi_decode_attn_workspace_bytes(h, num_q_heads):
@@ -201,6 +228,22 @@ class KiviCache:
         self._check_kv(k, n)
         self._check_kv(v, n)
         kivi_append(self.handle, k.data_ptr(), v.data_ptr(), n, self._stream(stream))
+
+    def append_varlen(self, k, v, n_tokens, stream=None):
+        """Sequence b appends its first n_tokens[b] tokens of k, v [B][H][n_max][D]."""
+        n_max = k.shape[2]
+        self._check_kv(k, n_max)
+        self._check_kv(v, n_max)
+        assert len(n_tokens) == self.cfg.batch
+        kivi_append_varlen(self.handle, k.data_ptr(), v.data_ptr(), n_tokens, n_max,
+                           self._stream(stream))
+
+    def reset_sequences(self, seqs):
+        kivi_cache_reset_sequences(self.handle, seqs)
+
+    def lengths(self):
+        """(n_quant, n_resid) lists, one entry per sequence."""
+        return kivi_cache_get_lengths(self.handle, self.cfg.batch)
 
     def flush(self, stream=None):
         kivi_flush_residual(self.handle, self._stream(stream))

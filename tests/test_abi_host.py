@@ -119,6 +119,27 @@ def test_append_and_decode_errors_leave_state():
     kivi.kivi_cache_destroy(h)
 
 
+def test_varlen_entry_points_validate_before_launch():
+    # per-sequence appends, resets and lengths; nothing here reaches a kernel
+    h = _make()  # batch 2, max_tokens 300
+    V, S = kivi.kivi_append_varlen, kivi.KIVI_OK
+    assert status_of(V, h, FAKE_DEV, FAKE_DEV, [0, 0], 4, 0) == S  # nothing to append
+    assert status_of(V, h, FAKE_DEV, FAKE_DEV, [5, 1], 4, 0) == kivi.KIVI_ERR_INVALID_ARG  # > n_max
+    assert status_of(V, h, FAKE_DEV, FAKE_DEV, [-1, 1], 4, 0) == kivi.KIVI_ERR_INVALID_ARG
+    assert status_of(V, h, FAKE_DEV, FAKE_DEV, [1, 1], -1, 0) == kivi.KIVI_ERR_INVALID_ARG
+    assert status_of(V, h, 0, FAKE_DEV, [1, 0], 4, 0) == kivi.KIVI_ERR_INVALID_ARG
+    assert status_of(V, h, FAKE_DEV + 8, FAKE_DEV, [1, 0], 4, 0) == kivi.KIVI_ERR_INVALID_ARG
+    assert status_of(V, h, FAKE_DEV, FAKE_DEV, [0, 301], 301, 0) == kivi.KIVI_ERR_CAPACITY
+    assert status_of(kivi.kivi_cache_reset_sequences, h, [2]) == kivi.KIVI_ERR_INVALID_ARG
+    assert status_of(kivi.kivi_cache_reset_sequences, h, [-1]) == kivi.KIVI_ERR_INVALID_ARG
+    assert status_of(kivi.kivi_cache_reset_sequences, h, [1]) == S
+    assert status_of(kivi.kivi_cache_reset_sequences, h, []) == S
+    assert kivi.kivi_cache_get_lengths(h, 2) == ([0, 0], [0, 0])
+    v = kivi.kivi_cache_get_view(h)
+    assert (v.n_quant, v.n_resid) == (0, 0)  # equal lengths: the uniform counters
+    kivi.kivi_cache_destroy(h)
+
+
 def test_status_strings():
     for s in range(7):
         assert kivi.status_name(s).startswith("KIVI_")
