@@ -40,6 +40,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cold-iters", type=int, default=20,
                    help="decode-only iterations with the last-level cache scrubbed")
+    p.add_argument("--ragged", action="store_true",
+                   help="sequences of different lengths: sequence b's prefix has T_b tokens, "
+                        "drawn uniformly from [T/2, T] (seed 0)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run one plain 1 GiB device copy first (counter calibration "
                         "for profiler runs)")
@@ -48,21 +51,34 @@ def parse():
 
 # ------------------------------------------------------------ byte accounting
 
-def algorithmic_bytes(w):
-    """Bytes the method must move per step, per phase (whole batch).
+def algorithmic_bytes(w, lens=None):
+    """Bytes the method must move per step, per phase (whole batch), with
+    every sequence's prefix T tokens long or sequence b's lens[b] long.
     Codes: bits/8 per element; scale + zero: 4 bytes per group of G."""
-    U = w.batch * w.kv_heads
-    D, G, R, T = w.head_dim, w.group_size, w.residual_length, w.tokens
+    D, G, R = w.head_dim, w.group_size, w.residual_length
     e = 2  # fp16 / bf16
-    r = (T - 1) % R + 1
-    nq = T - r
     codes = lambda n: n * D * (w.k_bits + w.v_bits) // 8
     meta = lambda n: (n // G) * D * 4 + n * (D // G) * 4
-    pack = 2 * T * D * e + codes(nq) + meta(nq) + 2 * r * D * e
-    flush = 2 * R * D * e + codes(R) + meta(R) + 2 * (2 * D * e)  # + the appended token
-    nq2, r2 = nq + R, 1
-    decode = codes(nq2) + meta(nq2) + 2 * r2 * D * e + w.gq * D * e + w.gq * D * 4
-    return {"pack": U * pack, "flush_append": U * flush, "decode": U * decode}
+    tot = {"pack": 0, "flush_append": 0, "decode": 0}
+    for T in (lens if lens is not None else [w.tokens] * w.batch):
+        r = (T - 1) % R + 1
+        nq = T - r
+        tot["pack"] += 2 * T * D * e + codes(nq) + meta(nq) + 2 * r * D * e
+        token = 2 * (2 * D * e)  # the appended token, read and written
+        if r == R:  # the full window is packed before the token enters
+            tot["flush_append"] += 2 * R * D * e + codes(R) + meta(R) + token
+            nq2, r2 = nq + R, 1
+        else:
+            tot["flush_append"] += token
+            nq2, r2 = nq, r + 1
+        tot["decode"] += codes(nq2) + meta(nq2) + 2 * r2 * D * e + w.gq * D * e + w.gq * D * 4
+    return {k: w.kv_heads * v for k, v in tot.items()}
+
+
+def ragged_lengths(w):
+    """Prefix length of each sequence for --ragged: uniform in [T/2, T], seed 0."""
+    import numpy as np
+    return [int(x) for x in np.random.default_rng(0).integers(w.tokens // 2, w.tokens + 1, w.batch)]
 
 
 # the kernel each phase's roofline describes, and the source it is built from
@@ -112,6 +128,7 @@ def run(args):
     dev = torch.device("cuda:0")
     T = w.tokens
     scale = 1.0 / np.sqrt(w.head_dim)
+    lens = ragged_lengths(w) if args.ragged else None
     layers = []
     for layer in range(w.layers):
         x = make_layer(w, seed=layer, device=dev, n_new=1)
@@ -137,7 +154,10 @@ def run(args):
         rec(0)
         for L in layers:
             L["cache"].reset()
-            L["cache"].append(L["kp"], L["vp"])
+            if lens is None:
+                L["cache"].append(L["kp"], L["vp"])
+            else:  # sequence b takes the first lens[b] tokens of the prefix
+                L["cache"].append_varlen(L["kp"], L["vp"], lens)
         rec(1)
         for L in layers:
             L["cache"].append(L["kn"], L["vn"])
@@ -187,14 +207,15 @@ def run(args):
         torch.cuda.synchronize()
         cold.append(e0.elapsed_time(e1) * 1e-3)
     del scrub
-    return w, wall, phase, cold, layers
+    return w, wall, phase, cold, layers, lens
 
 
-def cpu_baseline(w, layers):
+def cpu_baseline(w, layers, lens=None):
     """The oracle, as it stands, on a bounded sample of the same workload: one
     step (prefix pack, decode-token append, decode attention for every query
-    head) on one batch row of the first layer at a time, cycling through the
-    rows until about ten seconds of CPU work are done."""
+    head) on one batch row of the first layer at a time (row b's prefix cut to
+    lens[b] tokens when given), cycling through the rows until about ten
+    seconds of CPU work are done."""
     import numpy as np
 
     import oracle
@@ -202,11 +223,12 @@ def cpu_baseline(w, layers):
 
     L = layers[0]
     dt = oracle.BF16 if "bfloat" in str(w.dtype) else oracle.F16
-    done, t = 0, 0.0
+    done, t, nbytes = 0, 0.0, 0
     while t < 10.0:
         r = done % w.batch
         rows = slice(r, r + 1)
-        k, v = bits16(L["kp"][rows]), bits16(L["vp"][rows])
+        T = w.tokens if lens is None else lens[r]
+        k, v = bits16(L["kp"][rows, :, :T]), bits16(L["vp"][rows, :, :T])
         kn, vn = bits16(L["kn"][rows]), bits16(L["vn"][rows])
         q = bits16(L["q"][rows])
         t0 = time.perf_counter()
@@ -217,7 +239,8 @@ def cpu_baseline(w, layers):
         ref.decode_attn(q, 1.0 / np.sqrt(w.head_dim))
         t += time.perf_counter() - t0
         done += 1
-    b = sum(algorithmic_bytes(w).values()) * done / w.batch
+        nbytes += sum(algorithmic_bytes(w, [T]).values())
+    b = nbytes
     return {"value": b / t / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{done} batch rows (all {w.kv_heads} kv heads each, cycling through the "
                       f"{w.batch} rows of layer 0), one step each (prefix pack, decode-token "
@@ -233,8 +256,8 @@ def main():
         sys.exit(2)
     import numpy as np
 
-    w, wall, phase, cold, layers = run(args)
-    ab = algorithmic_bytes(w)
+    w, wall, phase, cold, layers, lens = run(args)
+    ab = algorithmic_bytes(w, lens)
     layers_n = w.layers
     step_bytes = sum(ab.values()) * layers_n
     # average launch-sequence duration per phase (HIP events in the timed steps)
@@ -256,10 +279,11 @@ def main():
     if dom == "decode":
         kname = "decode_mfma" if w.gq in (1, 2, 4) else "decode_split_valu"
         ksrc = decode_source(w)
-    traffic = traffic_from_profile(kname, w.name,
-                                   os.path.join(ROOT, "kv_cache_bit_kivi_amd", "csrc", ksrc))
+    # (the committed counters describe the workload with every sequence T long)
+    traffic = None if lens is not None else traffic_from_profile(
+        kname, w.name, os.path.join(ROOT, "kv_cache_bit_kivi_amd", "csrc", ksrc))
     achieved = ab[dom] / avg[dom] / 1e9
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w, layers)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, layers, lens)
     res = {
         "metric": METRIC,
         "value": step_bytes / wall / 1e9,
@@ -277,7 +301,9 @@ def main():
                    "kv_heads": w.kv_heads, "q_heads": w.q_heads, "head_dim": w.head_dim,
                    "tokens": w.tokens, "k_bits": w.k_bits, "v_bits": w.v_bits,
                    "group_size": w.group_size, "residual_length": w.residual_length,
-                   "kv_dtype": str(w.dtype).replace("torch.", ""), "layers": w.layers},
+                   "kv_dtype": str(w.dtype).replace("torch.", ""), "layers": w.layers,
+                   "lengths": ("every sequence T" if lens is None else
+                               f"per sequence uniform in [T/2, T], seed 0 (mean {np.mean(lens):.0f})")},
         "roofline": {"bound": "hbm", "kernel": f"{kname} ({dom})",
                      "achieved": achieved, "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_GBPS, "traffic": traffic,

@@ -572,11 +572,19 @@ kivi_status kivi_decode_attn(const kivi_cache* cc, const void* q, int32_t num_q_
         // minimise (rounds of resident waves) x (steps per wave): every
         // split of one launch takes the same time, so a partly filled last
         // round costs a whole wave duration
+        // (sequences of different lengths: only the splits that hold groups
+        // of their sequence count; the others end at once)
         long long best = -1;
         for (int want = 1; want <= max_split; ++want) {
           int g, np;
           plan(want, g, np);
-          const long long rounds = ((long long)units * np + slots - 1) / slots;
+          long long work = (long long)units * np;
+          if (c->ragged) {
+            work = 0;
+            for (int b = 0; b < c->cfg.batch; ++b) work += (c->sq[b] / G + g - 1) / g;
+            work *= c->cfg.num_kv_heads;
+          }
+          const long long rounds = (work + slots - 1) / slots;
           const long long cost = rounds * (g / 4 + 1);  // +1: per-wave set-up and partial
           if (best < 0 || cost < best) {
             best = cost;
