@@ -236,6 +236,22 @@ kivi_status kivi_decode_attn(const kivi_cache* cache, const void* q,
                              void* out, int32_t out_dtype, void* workspace,
                              size_t ws_bytes, void* stream);
 
+/* One decode step: appends one token per sequence (k_new, v_new: device
+ * arrays of kv_dtype [B][H][D]) exactly as kivi_append with n_tokens = 1,
+ * then runs kivi_decode_attn over the cache including that token (the
+ * residual-window append and decode attention of one generated token, page
+ * "KIVI: Asymmetric 2-Bit KV Cache Quantization Guide", "Step 3").  With 1, 2
+ * or 4 query heads per kv head the token is read from k_new / v_new and
+ * stored into the window by the attention launch itself: one launch fewer
+ * than the two calls.  A full window is still packed first, in a launch of
+ * its own.  With 8 query heads per kv head it runs the two calls.
+ * Errors: those of kivi_decode_attn and kivi_append (INVALID_ARG for null or
+ * unaligned k_new / v_new, CAPACITY), all before anything is enqueued. */
+kivi_status kivi_append_decode_attn(kivi_cache* cache, const void* k_new, const void* v_new,
+                                    const void* q, int32_t num_q_heads, float softmax_scale,
+                                    void* out, int32_t out_dtype, void* workspace,
+                                    size_t ws_bytes, void* stream);
+
 /* Fixes the number of token splits used by kivi_decode_attn (0 restores the
  * automatic choice).  The value is clamped to [1, blocks + 1]. For tests of
  * split invariance and for tuning. */

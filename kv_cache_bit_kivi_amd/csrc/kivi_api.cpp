@@ -515,10 +515,14 @@ kivi_status kivi_decode_attn_workspace_bytes(const kivi_cache* c, int32_t num_q_
   return KIVI_OK;
 }
 
-kivi_status kivi_decode_attn(const kivi_cache* cc, const void* q, int32_t num_q_heads,
-                             float softmax_scale, void* out, int32_t out_dtype, void* workspace,
-                             size_t ws_bytes, void* stream) {
-  kivi_cache* c = const_cast<kivi_cache*>(cc);
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the decode entry points (the cache may still be empty:
+// the fused append adds a token first).
+kivi_status check_decode_args(const kivi_cache* c, const void* q, int32_t num_q_heads, void* out,
+                              int32_t out_dtype, void* workspace, size_t ws_bytes) {
   if (!c) return fail(KIVI_ERR_INVALID_ARG, "cache is NULL");
   if (c->poisoned) return fail(KIVI_ERR_HIP, "cache handle is poisoned by an earlier HIP error");
   if (!q || !out || !workspace) return fail(KIVI_ERR_INVALID_ARG, "q, out and workspace must not be NULL");
@@ -530,13 +534,20 @@ kivi_status kivi_decode_attn(const kivi_cache* cc, const void* q, int32_t num_q_
   const int gq = num_q_heads / c->cfg.num_kv_heads;
   if (gq != 1 && gq != 2 && gq != 4 && gq != 8)
     return fail(KIVI_ERR_UNSUPPORTED, "query heads per kv head must be 1, 2, 4 or 8 (got %d)", gq);
-  const int T = c->n_quant + c->n_resid;
-  if (T < 1) return fail(KIVI_ERR_EMPTY, "decode on an empty cache");
   size_t need = 0;
   kivi_decode_attn_workspace_bytes(c, num_q_heads, &need);
   if (ws_bytes < need)
     return fail(KIVI_ERR_BUFFER_TOO_SMALL, "workspace needs %zu bytes, got %zu", need, ws_bytes);
+  return KIVI_OK;
+}
 
+// Plans and launches decode attention over the current state.  With k_new
+// (matrix-core kernel only) each unit's newest window token is read from
+// k_new / v_new and stored into the window by the same launch.
+kivi_status decode_launch(kivi_cache* c, const void* q, int32_t num_q_heads, float softmax_scale,
+                          void* out, int32_t out_dtype, void* workspace, void* stream,
+                          const void* k_new, const void* v_new) {
+  const int gq = num_q_heads / c->cfg.num_kv_heads;
   if (c->cu_count == 0) {
     int dev = 0, cus = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -629,6 +640,10 @@ kivi_status kivi_decode_attn(const kivi_cache* cc, const void* q, int32_t num_q_
   a.n_split_packed = n_split_packed;
   a.groups_per_split = gps;
   a.qscale = softmax_scale * 1.4426950408889634f;  // log2(e): base-2 softmax
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.k_resid_w = c->k_resid;
+  a.v_resid_w = c->v_resid;
   if (!c->ragged) {
     hipError_t e = kivi::launch_decode(a, c->cfg.k_bits, c->cfg.v_bits, c->cfg.kv_dtype, out_dtype,
                                        use_mfma, static_cast<hipStream_t>(stream));
@@ -653,6 +668,62 @@ kivi_status kivi_decode_attn(const kivi_cache* cc, const void* q, int32_t num_q_
     if (e != hipSuccess) return hip_fail(c, e, "decode launch (sequences of different lengths)");
   }
   return KIVI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kivi_status kivi_decode_attn(const kivi_cache* cc, const void* q, int32_t num_q_heads,
+                             float softmax_scale, void* out, int32_t out_dtype, void* workspace,
+                             size_t ws_bytes, void* stream) {
+  kivi_cache* c = const_cast<kivi_cache*>(cc);
+  kivi_status st = check_decode_args(c, q, num_q_heads, out, out_dtype, workspace, ws_bytes);
+  if (st != KIVI_OK) return st;
+  if (c->n_quant + c->n_resid < 1) return fail(KIVI_ERR_EMPTY, "decode on an empty cache");
+  return decode_launch(c, q, num_q_heads, softmax_scale, out, out_dtype, workspace, stream, nullptr,
+                       nullptr);
+}
+
+kivi_status kivi_append_decode_attn(kivi_cache* c, const void* k_new, const void* v_new,
+                                    const void* q, int32_t num_q_heads, float softmax_scale,
+                                    void* out, int32_t out_dtype, void* workspace, size_t ws_bytes,
+                                    void* stream) {
+  kivi_status st = check_decode_args(c, q, num_q_heads, out, out_dtype, workspace, ws_bytes);
+  if (st != KIVI_OK) return st;
+  if (!k_new || !v_new) return fail(KIVI_ERR_INVALID_ARG, "k_new and v_new must not be NULL");
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(KIVI_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
+  int longest = c->n_quant + c->n_resid;
+  if (c->ragged) {
+    longest = 0;
+    for (int b = 0; b < c->cfg.batch; ++b) longest = std::max(longest, c->sq[b] + c->sr[b]);
+  }
+  if ((long long)longest + 1 > c->cfg.max_tokens)
+    return fail(KIVI_ERR_CAPACITY, "appending a token to %d exceeds max_tokens %d", longest,
+                c->cfg.max_tokens);
+  const int gq = num_q_heads / c->cfg.num_kv_heads;
+  if (gq == 8) {  // vector-ALU decode: the append stays a launch of its own
+    if ((st = kivi_append(c, k_new, v_new, 1, stream)) != KIVI_OK) return st;
+    return decode_launch(c, q, num_q_heads, softmax_scale, out, out_dtype, workspace, stream, nullptr,
+                         nullptr);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int R = c->cfg.residual_length;
+  // a full window is packed before the token enters it (a launch of its
+  // own, once every R steps); then the token takes the next window slot
+  if (c->ragged) {
+    std::vector<char> fl(c->cfg.batch, 0);
+    for (int b = 0; b < c->cfg.batch; ++b) fl[b] = c->sr[b] == R;
+    if ((st = ragged_flush(c, fl, s)) != KIVI_OK) return st;
+    for (int b = 0; b < c->cfg.batch; ++b) c->sr[b] += 1;
+    settle(c);
+  } else {
+    if (c->n_resid == R && (st = flush_window(c, s)) != KIVI_OK) return st;
+    c->n_resid += 1;
+  }
+  return decode_launch(c, q, num_q_heads, softmax_scale, out, out_dtype, workspace, stream, k_new,
+                       v_new);
 }
 
 kivi_status kivi_set_decode_splits(kivi_cache* c, int32_t n_split) {

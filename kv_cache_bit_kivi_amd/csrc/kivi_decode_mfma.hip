@@ -248,6 +248,15 @@ __device__ void window_wave(const DecodeArgs& a, long long u, int b, int kvh, in
     qsh[i / D][i % D] =
         to_f32<BF16>(a.q[((long long)b * a.Hq + kvh * NQ + i / D) * D + i % D]) * a.qscale;
   }
+  // fused append: the newest token (slot nr - 1) comes from k_new / v_new;
+  // this wave is the only one of the launch that touches the unit's window,
+  // so it also stores the token there
+  const int t_new = a.k_new ? nr - 1 : -1;
+  if (t_new >= 0) {
+    const long long src = u * D + 2 * lane, dst = (u * a.R + t_new) * D + 2 * lane;
+    *reinterpret_cast<uint32_t*>(a.k_resid_w + dst) = *reinterpret_cast<const uint32_t*>(a.k_new + src);
+    *reinterpret_cast<uint32_t*>(a.v_resid_w + dst) = *reinterpret_cast<const uint32_t*>(a.v_new + src);
+  }
   wave_lds_sync();
   float m[NQ], l[NQ], o[NQ][2];
 #pragma unroll
@@ -264,7 +273,7 @@ __device__ void window_wave(const DecodeArgs& a, long long u, int b, int kvh, in
 #pragma unroll
     for (int h = 0; h < NQ; ++h) acc[h] = 0.0f;
     if (live) {
-      const uint16_t* kr = a.k_resid + (u * a.R + t) * D + 64 * half;
+      const uint16_t* kr = (t == t_new ? a.k_new + u * D : a.k_resid + (u * a.R + t) * D) + 64 * half;
       for (int d0 = 0; d0 < 64; d0 += 8) {
         const uint4 kv = *reinterpret_cast<const uint4*>(kr + d0);
         const uint32_t ww[4] = {kv.x, kv.y, kv.z, kv.w};
@@ -296,7 +305,8 @@ __device__ void window_wave(const DecodeArgs& a, long long u, int b, int kvh, in
     wave_lds_sync();
     const int n = min(G, nr - c0);
     for (int tt = 0; tt < n; ++tt) {
-      const uint32_t vv = *reinterpret_cast<const uint32_t*>(a.v_resid + (u * a.R + c0 + tt) * D + 2 * lane);
+      const uint16_t* vr = c0 + tt == t_new ? a.v_new + u * D : a.v_resid + (u * a.R + c0 + tt) * D;
+      const uint32_t vv = *reinterpret_cast<const uint32_t*>(vr + 2 * lane);
       const float v0 = to_f32<BF16>(static_cast<uint16_t>(vv & 0xffffu));
       const float v1 = to_f32<BF16>(static_cast<uint16_t>(vv >> 16));
 #pragma unroll

@@ -89,6 +89,13 @@ struct DecodeArgs {
   int ragged;
   int seq0;
   int seq_len[kDecodeChunk][2];
+  // fused append (k_new != nullptr, matrix-core kernel only): each unit's
+  // newest window token, slot n_resid - 1, is read from k_new / v_new
+  // ([B][H][D]) and stored into the window by the wave that runs the window
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint16_t* k_resid_w;  // the window arrays, writable (fused append)
+  uint16_t* v_resid_w;
 };
 
 // LDS bytes of one workgroup (key wave + value wave) of the matrix-core

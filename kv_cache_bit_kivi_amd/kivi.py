@@ -32,6 +32,7 @@ EXPORTED = (
     "kivi_decode_attn", "kivi_set_decode_splits", "kivi_cache_get_view",
     "kivi_status_string", "kivi_last_error_message",
     "kivi_append_varlen", "kivi_cache_reset_sequences", "kivi_cache_get_lengths",
+    "kivi_append_decode_attn",
 )
 
 
@@ -79,6 +80,7 @@ def _load():
         "kivi_cache_get_lengths": ([vp, ctypes.POINTER(i32), ctypes.POINTER(i32)], i32),
         "kivi_decode_attn_workspace_bytes": ([vp, i32, ctypes.POINTER(sz)], i32),
         "kivi_decode_attn": ([vp, vp, i32, ctypes.c_float, vp, i32, vp, sz, vp], i32),
+        "kivi_append_decode_attn": ([vp, vp, vp, vp, i32, ctypes.c_float, vp, i32, vp, sz, vp], i32),
         "kivi_set_decode_splits": ([vp, i32], i32),
         "kivi_cache_get_view": ([vp, ctypes.POINTER(kivi_cache_view)], i32),
         "kivi_status_string": ([i32], ctypes.c_char_p),
@@ -173,6 +175,14 @@ def kivi_decode_attn(h, q_ptr, num_q_heads, softmax_scale, out_ptr, out_dtype, w
     _check(lib.kivi_decode_attn(h, ctypes.c_void_p(q_ptr), num_q_heads,
                                 float(softmax_scale), ctypes.c_void_p(out_ptr), out_dtype,
                                 ctypes.c_void_p(ws_ptr), ws_bytes, ctypes.c_void_p(stream)))
+
+
+def kivi_append_decode_attn(h, k_ptr, v_ptr, q_ptr, num_q_heads, softmax_scale, out_ptr,
+                            out_dtype, ws_ptr, ws_bytes, stream):
+    _check(lib.kivi_append_decode_attn(h, ctypes.c_void_p(k_ptr), ctypes.c_void_p(v_ptr),
+                                       ctypes.c_void_p(q_ptr), num_q_heads, float(softmax_scale),
+                                       ctypes.c_void_p(out_ptr), out_dtype, ctypes.c_void_p(ws_ptr),
+                                       ws_bytes, ctypes.c_void_p(stream)))
 
 
 def kivi_set_decode_splits(h, n_split):
@@ -273,6 +283,27 @@ class KiviCache:
         ws = self.workspace(Hq)
         kivi_decode_attn(self.handle, q.data_ptr(), Hq, softmax_scale, out.data_ptr(), od,
                          ws.data_ptr(), ws.numel(), self._stream(stream))
+        return out
+
+    def append_decode_attn(self, k_new, v_new, q, softmax_scale, out=None, out_dtype=None,
+                           stream=None):
+        """One decode step: append k_new, v_new [B][H][1][D] (one token per
+        sequence), then decode attention including it."""
+        torch = self.torch
+        c = self.cfg
+        self._check_kv(k_new, 1)
+        self._check_kv(v_new, 1)
+        assert q.is_contiguous() and q.dtype == self.dtype and q.device == self.device
+        B, Hq, D = q.shape
+        assert B == c.batch and D == c.head_dim
+        out_dtype = torch.float32 if out_dtype is None else out_dtype
+        if out is None:
+            out = torch.empty(B, Hq, D, dtype=out_dtype, device=self.device)
+        od = {torch.float16: KIVI_F16, torch.bfloat16: KIVI_BF16, torch.float32: KIVI_F32}[out.dtype]
+        ws = self.workspace(Hq)
+        kivi_append_decode_attn(self.handle, k_new.data_ptr(), v_new.data_ptr(), q.data_ptr(), Hq,
+                                softmax_scale, out.data_ptr(), od, ws.data_ptr(), ws.numel(),
+                                self._stream(stream))
         return out
 
     def view(self):

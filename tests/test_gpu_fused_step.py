@@ -1,0 +1,99 @@
+"""The fused decode step (kivi_append_decode_attn: one token appended per
+sequence and decode attention in the same launch) against the two calls it
+replaces, kivi_append + kivi_decode_attn, on identical inputs: outputs and
+cache contents bit-identical at every step, across window flushes, with
+equal and with different sequence lengths; and the final state against the
+oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_cache_bit_kivi_amd import kivi
+from kv_cache_bit_kivi_amd.inputs import bits16, make_layer, small
+from tests.gpu_helpers import assert_cache_equal, gpu_arrays, oracle_arrays
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+TOL = 2e-3
+
+#        name            B  H  Hq  kb vb dtype           R    prefill (None: 200 for all)  steps
+CASES = [("mha",          2, 2, 2,  2, 2, torch.float16,  128, None,                       140),
+         ("gq4_r32",      2, 2, 8,  2, 2, torch.float16,  32,  None,                       70),
+         ("gq2_bf16_4b",  1, 2, 4,  4, 4, torch.bfloat16, 64,  None,                       70),
+         ("gq8_fallback", 1, 1, 8,  2, 2, torch.float16,  32,  None,                       40),
+         ("ragged_gq4",   4, 1, 4,  2, 4, torch.float16,  32,  [0, 31, 32, 100],           70),
+         ("empty_start",  2, 1, 1,  2, 2, torch.float16,  32,  [0, 0],                     40)]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_fused_step_matches_append_then_decode(case):
+    name, B, H, Hq, kb, vb, dt, R, lens, steps = case
+    print(f"fused step {name}: B={B} H={H} Hq={Hq} bits={kb}/{vb} R={R} prefill {lens}", flush=True)
+    T0 = 200
+    max_tokens = T0 + steps + 1
+    w = small(name, B, H, Hq, max_tokens, kb, vb, dt, residual_length=R)
+    x = make_layer(w, seed=9, n_new=0)
+    qs = torch.randn(steps, B, Hq, 128, generator=torch.Generator().manual_seed(1)).to(dt)
+    mk = lambda: kivi.KiviCache(B, H, max_tokens, k_bits=kb, v_bits=vb, residual_length=R, dtype=dt,
+                                device=DEV)
+    fused, split = mk(), mk()
+    kd, vd = x.k.to(DEV), x.v.to(DEV)
+    if lens is None:
+        lens = [T0] * B
+    for c in (fused, split):
+        c.append_varlen(kd[:, :, :T0].contiguous(), vd[:, :, :T0].contiguous(), lens)
+    scale = 1.0 / np.sqrt(128)
+    for t in range(steps):
+        # token t of each sequence's continuation: input position lens[b] + t
+        kn = torch.stack([kd[b, :, lens[b] + t] for b in range(B)])[:, :, None].contiguous()
+        vn = torch.stack([vd[b, :, lens[b] + t] for b in range(B)])[:, :, None].contiguous()
+        q = qs[t].contiguous().to(DEV)
+        o1 = fused.append_decode_attn(kn, vn, q, scale)
+        split.append(kn, vn)
+        o2 = split.decode_attn(q, scale)
+        assert torch.equal(o1, o2), f"{name}: step {t}: fused and separate outputs differ"
+        assert fused.lengths() == split.lengths(), f"{name}: step {t}"
+    torch.cuda.synchronize()
+    a1, a2 = gpu_arrays(fused), gpu_arrays(split)
+    dtc = oracle.BF16 if dt == torch.bfloat16 else oracle.F16
+    kb16, vb16 = bits16(x.k), bits16(x.v)
+    nq, nr = fused.lengths()
+    worst = 0.0
+    for b in range(B):
+        ref = oracle.OracleCache(1, H, 128, max_tokens, kb, vb, 32, R, dtc)
+        n = lens[b] + steps
+        ref.append(kb16[b:b + 1, :, :n], vb16[b:b + 1, :, :n])
+        assert (ref.n_quant, ref.n_resid) == (nq[b], nr[b])
+        for got in (a1, a2):
+            mine = {k: v[b * H:(b + 1) * H] for k, v in got.items()}
+            assert_cache_equal(mine, oracle_arrays(ref), ref.n_quant, ref.n_resid, ref.capacity,
+                               ref.num_blocks)
+        o_ref = ref.decode_attn(bits16(qs[steps - 1][b:b + 1]), scale)
+        err = float(np.abs(o1[b:b + 1].cpu().numpy().astype(np.float64) - o_ref).max())
+        worst = max(worst, err)
+        assert err <= TOL, f"{name}: sequence {b}: {err:.3e}"
+    print(f"fused step {name}: last-step attention error {worst:.2e}", flush=True)
+
+
+def test_fused_step_errors_leave_state():
+    c = kivi.KiviCache(1, 1, 40, residual_length=32, device=DEV)
+    k = torch.zeros(1, 1, 1, 128, dtype=torch.float16, device=DEV)
+    q = torch.zeros(1, 1, 128, dtype=torch.float16, device=DEV)
+    out = torch.empty(1, 1, 128, dtype=torch.float32, device=DEV)
+    ws = c.workspace(1)
+    h = c.handle
+    with pytest.raises(kivi.KiviError) as e:
+        kivi.kivi_append_decode_attn(h, 0, k.data_ptr(), q.data_ptr(), 1, 0.1, out.data_ptr(),
+                                     kivi.KIVI_F32, ws.data_ptr(), ws.numel(), 0)
+    assert e.value.status == kivi.KIVI_ERR_INVALID_ARG
+    with pytest.raises(kivi.KiviError) as e:
+        kivi.kivi_append_decode_attn(h, k.data_ptr(), k.data_ptr(), q.data_ptr(), 1, 0.1,
+                                     out.data_ptr(), kivi.KIVI_F32, ws.data_ptr(), 8, 0)
+    assert e.value.status == kivi.KIVI_ERR_BUFFER_TOO_SMALL
+    c.append(torch.zeros(1, 1, 40, 128, dtype=torch.float16, device=DEV),
+             torch.zeros(1, 1, 40, 128, dtype=torch.float16, device=DEV))
+    with pytest.raises(kivi.KiviError) as e:
+        c.append_decode_attn(k, k, q, 0.1)
+    assert e.value.status == kivi.KIVI_ERR_CAPACITY
+    assert c.lengths() == ([32], [8])
