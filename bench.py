@@ -4,10 +4,11 @@ One step = one pass of the whole hot path over one layer's synthetic batch:
   1. bulk append of the T-token prefix: quantize + bit-pack every full
      window straight from the input, copy the last R tokens to the window
      (one pack launch);
-  2. append of the decode token: the full window is packed (flush) and the
-     token enters the window (two launches);
-  3. split-K decode attention over the packed cache plus the window, and the
-     cross-split merge (two launches).
+  2. the full window is packed before the decode token enters it (flush,
+     one launch);
+  3. the decode step: the token is appended and split-K decode attention
+     runs over the packed cache plus the window in the same launch, then the
+     cross-split merge (kivi_append_decode_attn, two launches).
 The cache is reset (host counters only) at the start of each step.
 
 Default workload: Llama-2-7B-shaped MHA layer, batch 8, 32 heads, T = 4096,
@@ -59,19 +60,19 @@ def algorithmic_bytes(w, lens=None):
     e = 2  # fp16 / bf16
     codes = lambda n: n * D * (w.k_bits + w.v_bits) // 8
     meta = lambda n: (n // G) * D * 4 + n * (D // G) * 4
-    tot = {"pack": 0, "flush_append": 0, "decode": 0}
+    tot = {"pack": 0, "flush": 0, "decode": 0}
     for T in (lens if lens is not None else [w.tokens] * w.batch):
         r = (T - 1) % R + 1
         nq = T - r
         tot["pack"] += 2 * T * D * e + codes(nq) + meta(nq) + 2 * r * D * e
-        token = 2 * (2 * D * e)  # the appended token, read and written
         if r == R:  # the full window is packed before the token enters
-            tot["flush_append"] += 2 * R * D * e + codes(R) + meta(R) + token
+            tot["flush"] += 2 * R * D * e + codes(R) + meta(R)
             nq2, r2 = nq + R, 1
         else:
-            tot["flush_append"] += token
             nq2, r2 = nq, r + 1
-        tot["decode"] += codes(nq2) + meta(nq2) + 2 * r2 * D * e + w.gq * D * e + w.gq * D * 4
+        token = 2 * (2 * D * e)  # the appended token, read and written into the window
+        tot["decode"] += (token + codes(nq2) + meta(nq2) + 2 * r2 * D * e + w.gq * D * e
+                          + w.gq * D * 4)
     return {k: w.kv_heads * v for k, v in tot.items()}
 
 
@@ -85,8 +86,9 @@ def ragged_lengths(w):
 PHASE_KERNEL = {
     "pack": ("pack_kernel", "kivi_pack.hip", "one launch: quantize + bit-pack the prefix, "
              "copy the last window"),
-    "flush_append": ("pack_kernel", "kivi_pack.hip", "two launches: window flush, token copy"),
-    "decode": ("decode split + merge", None, "two launches: split-K attention, merge"),
+    "flush": ("pack_kernel", "kivi_pack.hip", "one launch: window flush"),
+    "decode": ("decode split + merge", None, "two launches: token append + split-K attention, "
+               "merge"),
 }
 
 
@@ -160,10 +162,10 @@ def run(args):
                 L["cache"].append_varlen(L["kp"], L["vp"], lens)
         rec(1)
         for L in layers:
-            L["cache"].append(L["kn"], L["vn"])
+            L["cache"].flush()
         rec(2)
         for L in layers:
-            L["cache"].decode_attn(L["q"], scale, out=L["out"])
+            L["cache"].append_decode_attn(L["kn"], L["vn"], L["q"], scale, out=L["out"])
         rec(3)
 
     if args.copy_calibration:
@@ -187,11 +189,11 @@ def run(args):
     wall = (time.perf_counter() - t0) / args.steps
 
     # per step, the average duration of one layer's launches of each phase
-    phase = {"pack": [], "flush_append": [], "decode": []}
+    phase = {"pack": [], "flush": [], "decode": []}
     n = len(layers)
     for ev in events:
         phase["pack"].append(ev[0].elapsed_time(ev[1]) * 1e-3 / n)
-        phase["flush_append"].append(ev[1].elapsed_time(ev[2]) * 1e-3 / n)
+        phase["flush"].append(ev[1].elapsed_time(ev[2]) * 1e-3 / n)
         phase["decode"].append(ev[2].elapsed_time(ev[3]) * 1e-3 / n)
 
     # decode alone with the 256 MB last-level cache scrubbed before each call
@@ -264,7 +266,7 @@ def main():
     avg = {k: float(np.mean(v)) for k, v in phase.items()}
     med = {k: float(np.median(v)) for k, v in phase.items()}
     phases = {}
-    for k in ("pack", "flush_append", "decode"):
+    for k in ("pack", "flush", "decode"):
         g = ab[k] / avg[k] / 1e9
         phases[k] = {"bytes": ab[k], "us_mean": avg[k] * 1e6, "us_median": med[k] * 1e6,
                      "gbps": g, "frac": g / PEAK_GBPS, "launches": PHASE_KERNEL[k][2]}

@@ -632,7 +632,7 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
 // wave.  Writes o of the partial; the last split also runs the window.
 template <int KB, int VB, bool BF16, int NQ>
 __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int b, int kvh, int split,
-                                           int gb, int ge, int n_steps, int nr, uint8_t* smem) {
+                                           int gb, int ge, int n_steps, uint8_t* smem) {
   using S = Stage<KB, VB>;
   using VS = CodeScale<VB>;
   const int lane = threadIdx.x & 63;
@@ -724,14 +724,6 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
       *reinterpret_cast<f32x4*>(P + 2 + 32 * lk + 8 * r + 4) = x1;
     }
   }
-  // the last packed split also takes the window (its own partial, empty
-  // for a sequence without window tokens in a ragged launch); this wave's
-  // stage loads have completed and its value stages are free
-  if (split == a.n_split_packed - 1 && a.n_split > a.n_split_packed) {
-    wave_lds_sync();
-    window_wave<BF16, NQ>(a, u, b, kvh, a.n_split_packed, nr, reinterpret_cast<float (*)[D]>(vbase),
-                      reinterpret_cast<float (*)[G]>(vbase + GQ * D * 4));
-  }
 }
 
 template <int KB, int VB, bool BF16, int NQ>
@@ -750,33 +742,36 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
   }
   const long long u = (long long)b * a.H + kvh;
 
-  if (a.n_split_packed == 0) {  // nothing packed yet: the window is the only split
-    if (wave == 1)
-      window_wave<BF16, NQ>(a, u, b, kvh, 0, nr, reinterpret_cast<float (*)[D]>(smem + S::offV0),
-                        reinterpret_cast<float (*)[G]>(smem + S::offV0 + GQ * D * 4));
-    return;
-  }
-  const int nqg = nq / G;
-  const int gb = split * a.groups_per_split;
-  const int ge = min(nqg, gb + a.groups_per_split);
-  if (gb >= nqg) {
-    // (ragged) this sequence ends before this split: an empty partial
-    // (m = -inf, l = 0, o = 0); the last packed split still takes the window
-    for (int i = threadIdx.x; i < NQ * (D + 2); i += 128) {
-      float* P = a.partial + (((long long)b * a.Hq + kvh * NQ + i / (D + 2)) * a.n_split + split) * (D + 2);
-      P[i % (D + 2)] = i % (D + 2) == 0 ? -INFINITY : 0.0f;
+  if (a.n_split_packed > 0) {
+    const int nqg = nq / G;
+    const int gb = split * a.groups_per_split;
+    const int ge = min(nqg, gb + a.groups_per_split);
+    if (gb >= nqg) {
+      // (ragged) this sequence ends before this split: an empty partial
+      // (m = -inf, l = 0, o = 0)
+      for (int i = threadIdx.x; i < NQ * (D + 2); i += 128) {
+        float* P = a.partial + (((long long)b * a.Hq + kvh * NQ + i / (D + 2)) * a.n_split + split) * (D + 2);
+        P[i % (D + 2)] = i % (D + 2) == 0 ? -INFINITY : 0.0f;
+      }
+    } else {
+      const int n_steps = (ge - gb + 3) / 4;  // >= 1: every split holds a group
+      // Both waves run the same number of steps and meet at one barrier per step.
+      if (wave == 0) {
+        key_wave<KB, VB, BF16, NQ>(a, u, b, kvh, split, gb, ge, n_steps, smem);
+      } else {
+        value_wave<KB, VB, BF16, NQ>(a, u, b, kvh, split, gb, ge, n_steps, smem);
+      }
     }
-    if (wave == 1 && split == a.n_split_packed - 1 && a.n_split > a.n_split_packed)
-      window_wave<BF16, NQ>(a, u, b, kvh, a.n_split_packed, nr, reinterpret_cast<float (*)[D]>(smem + S::offV0),
-                        reinterpret_cast<float (*)[G]>(smem + S::offV0 + GQ * D * 4));
-    return;
   }
-  const int n_steps = (ge - gb + 3) / 4;  // >= 1: every split holds a group
-  // Both waves run the same number of steps and meet at one barrier per step.
-  if (wave == 0) {
-    key_wave<KB, VB, BF16, NQ>(a, u, b, kvh, split, gb, ge, n_steps, smem);
-  } else {
-    value_wave<KB, VB, BF16, NQ>(a, u, b, kvh, split, gb, ge, n_steps, nr, smem);
+  // The window is one more partial (slot n_split_packed), run by the value
+  // wave of the last packed split (of the only workgroup when nothing is
+  // packed yet); empty for a sequence without window tokens in a ragged
+  // launch.  That wave's stage loads have completed, so its value stages
+  // serve as scratch.
+  if (wave == 1 && a.n_split > a.n_split_packed && split == max(a.n_split_packed - 1, 0)) {
+    wave_lds_sync();
+    window_wave<BF16, NQ>(a, u, b, kvh, a.n_split_packed, nr, reinterpret_cast<float (*)[D]>(smem + S::offV0),
+                      reinterpret_cast<float (*)[G]>(smem + S::offV0 + GQ * D * 4));
   }
 }
 
