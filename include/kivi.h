@@ -194,6 +194,26 @@ kivi_status kivi_append_varlen(kivi_cache* cache, const void* k, const void* v,
  * outside [0, batch)). */
 kivi_status kivi_cache_reset_sequences(kivi_cache* cache, const int32_t* seqs, int32_t count);
 
+/* Paged block records.  With a table set, block g (tokens 32 g .. 32 g + 31)
+ * of sequence b lives in page P = table[b * page_stride + g] of the block
+ * region, and kv head h of it at record P * H + h (the region then holds
+ * num_pages pages of H records; the default is the unit-major layout,
+ * record (b * H + h) * NB + g).  A caller that manages its own page
+ * allocation (quantized blocks in paged KV memory: page "KV-Cache
+ * Quantization: I Ran the Experiments So You Don't Have To", "Component 4 -
+ * Serving architecture & manifests", Figure 8) maps each sequence's blocks
+ * to free pages and may hand a freed page to another sequence.
+ * `table` is a device array of int32 [B][page_stride] that must stay valid
+ * and unchanged while work using it is in flight; the kernels read it and
+ * clamp every entry into [0, num_pages), so a wrong table gives wrong results
+ * but never touches memory outside the region.  Entries are needed for the
+ * blocks a sequence holds.  NULL restores the unit-major layout.  Changing
+ * the layout of a cache that holds packed tokens reinterprets them.
+ * Errors: INVALID_ARG (null cache, page_stride < NB, num_pages outside
+ * [1, batch * NB], unaligned table). */
+kivi_status kivi_cache_set_page_table(kivi_cache* cache, const int32_t* table,
+                                      int32_t page_stride, int32_t num_pages);
+
 /* Per-sequence counters: n_quant[b] and n_resid[b] for b < batch (host
  * arrays).  Equal to the view's counters while every sequence has the same
  * lengths. */

@@ -36,6 +36,9 @@ struct kivi_cache {
   // per-sequence counters below are then the state
   bool ragged;
   std::vector<int> sq, sr;  // n_quant, n_resid of each sequence (ragged)
+  // paged block records (kivi_cache_set_page_table); nullptr: unit-major
+  const int32_t* page_table;
+  int page_stride, num_pages;
   int forced_splits;
   int cu_count;  // queried on first decode
   bool poisoned;
@@ -127,6 +130,10 @@ kivi::PackArgs base_pack_args(const kivi_cache* c) {
   a.nb = c->nb;
   a.R = c->cfg.residual_length;
   a.units = c->cfg.batch * c->cfg.num_kv_heads;
+  a.H = c->cfg.num_kv_heads;
+  a.page_table = c->page_table;
+  a.page_stride = c->page_stride;
+  a.num_pages = c->num_pages;
   return a;
 }
 
@@ -385,6 +392,26 @@ kivi_status kivi_cache_reset_sequences(kivi_cache* c, const int32_t* seqs, int32
   return KIVI_OK;
 }
 
+kivi_status kivi_cache_set_page_table(kivi_cache* c, const int32_t* table, int32_t page_stride,
+                                      int32_t num_pages) {
+  if (!c) return fail(KIVI_ERR_INVALID_ARG, "cache is NULL");
+  if (!table) {
+    c->page_table = nullptr;
+    c->page_stride = c->num_pages = 0;
+    return KIVI_OK;
+  }
+  if (reinterpret_cast<uintptr_t>(table) % 4) return fail(KIVI_ERR_INVALID_ARG, "table must be 4-byte aligned");
+  if (page_stride < c->nb)
+    return fail(KIVI_ERR_INVALID_ARG, "page_stride (%d) must cover the %d blocks of a sequence", page_stride, c->nb);
+  if (num_pages < 1 || (long long)num_pages > (long long)c->cfg.batch * c->nb)
+    return fail(KIVI_ERR_INVALID_ARG, "num_pages (%d) must be in [1, batch * blocks = %lld]", num_pages,
+                (long long)c->cfg.batch * c->nb);
+  c->page_table = table;
+  c->page_stride = page_stride;
+  c->num_pages = num_pages;
+  return KIVI_OK;
+}
+
 kivi_status kivi_cache_get_lengths(const kivi_cache* c, int32_t* n_quant, int32_t* n_resid) {
   if (!c || !n_quant || !n_resid) return fail(KIVI_ERR_INVALID_ARG, "cache and outputs must not be NULL");
   for (int b = 0; b < c->cfg.batch; ++b) {
@@ -640,6 +667,9 @@ kivi_status decode_launch(kivi_cache* c, const void* q, int32_t num_q_heads, flo
   a.n_split_packed = n_split_packed;
   a.groups_per_split = gps;
   a.qscale = softmax_scale * 1.4426950408889634f;  // log2(e): base-2 softmax
+  a.page_table = c->page_table;
+  a.page_stride = c->page_stride;
+  a.num_pages = c->num_pages;
   a.k_new = static_cast<const uint16_t*>(k_new);
   a.v_new = static_cast<const uint16_t*>(v_new);
   a.k_resid_w = c->k_resid;

@@ -95,7 +95,8 @@ __global__ __launch_bounds__(256) void decode_split_valu(DecodeArgs a) {
     const bool packed = it < nqb;
     const int rc = it - nqb;  // window chunk index when !packed
     const int ntok = packed ? G : min(G, nr - rc * G);
-    const uint8_t* const rec = a.blocks + (u * a.nb + (packed ? it : 0)) * BL.bytes;
+    const uint8_t* const rec =
+        a.blocks + record_index(a.page_table, a.page_stride, a.num_pages, a.nb, a.H, u, packed ? it : 0) * BL.bytes;
     if (packed) {
       // key meta [d]; value meta [m][row], 4 * 32 = D entries
       if (tid < D) {

@@ -126,13 +126,6 @@ __device__ __forceinline__ void mul_pair_exact(uint32_t a, uint32_t b, uint32_t&
   asm("v_pk_fma_f16 %0, %1, %2, %3 neg_lo:[0,0,1] neg_hi:[0,0,1]" : "=v"(lo) : "v"(a), "v"(b), "v"(hi));
 }
 
-// a * b + c for fp16 pairs (v_pk_fma_f16, one rounding).
-__device__ __forceinline__ uint32_t fma_pair(uint32_t a, uint32_t b, uint32_t c) {
-  uint32_t r;
-  asm("v_pk_fma_f16 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-
 // acc + a.x * b.x + a.y * b.y for fp16 pairs a, b (v_dot2_f32_f16).
 __device__ __forceinline__ float dot2_acc(uint32_t a, uint32_t b, float acc) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), acc, false);
@@ -376,49 +369,69 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
   __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)lds_dst, 16, 0, 0);
 }
 
+// Records of groups g0 .. g0 + 3 of unit u (unit-major, or through the page
+// table when PAGED); slots past the last valid group g0 + ns - 1 repeat it
+// (addresses stay inside).
+template <int KB, int VB, bool PAGED>
+__device__ __forceinline__ void step_records(const DecodeArgs& a, long long u, int g0, int ns,
+                                             const uint8_t* (&rp)[4]) {
+  constexpr BlockLayout BL = block_layout(KB, VB);
+  if constexpr (PAGED) {
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi)
+      rp[gi] = a.blocks + record_index(a.page_table, a.page_stride, a.num_pages, a.nb, a.H, u,
+                                       min(g0 + gi, g0 + ns - 1)) * BL.bytes;
+  } else {
+    const uint8_t* const unit = a.blocks + (u * a.nb) * (long long)BL.bytes;
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) rp[gi] = unit + (long long)min(g0 + gi, g0 + ns - 1) * BL.bytes;
+  }
+}
+
+// The record of this lane's metadata slot (lanes 16 i .. 16 i + 15: group i).
+__device__ __forceinline__ const uint8_t* lane_record(const uint8_t* const (&rp)[4], int lane) {
+  const int i = lane >> 4;
+  return i == 0 ? rp[0] : i == 1 ? rp[1] : i == 2 ? rp[2] : rp[3];
+}
+
 // Key stage of groups [g0, g0 + ns): codes to `dst`, scale and zero to
-// `meta`; Stage::kLoads instructions.  Slots of missing groups re-read the
-// last valid group (addresses stay inside).
-template <int KB, int VB>
+// `meta`; Stage::kLoads instructions.
+template <int KB, int VB, bool PAGED>
 __device__ __forceinline__ void issue_kstage(const DecodeArgs& a, long long u, int g0, int ns,
                                              uint8_t* dst, uint8_t* meta_dst) {
   using S = Stage<KB, VB>;
   constexpr BlockLayout BL = block_layout(KB, VB);
   const int lane = threadIdx.x & 63;
-  const int glast = g0 + ns - 1;
-  const uint8_t* const unit = a.blocks + (u * a.nb) * (long long)BL.bytes;
+  const uint8_t* rp[4];
+  step_records<KB, VB, PAGED>(a, u, g0, ns, rp);
 #pragma unroll
   for (int gi = 0; gi < 4; ++gi) {
-    const long long g = min(g0 + gi, glast);
 #pragma unroll
     for (int j = 0; j < S::kGroup / 1024; ++j)
-      dma16(unit + g * BL.bytes + BL.k_codes + j * 1024 + lane * 16, dst + gi * S::kGroupPad + j * 1024);
+      dma16(rp[gi] + BL.k_codes + j * 1024 + lane * 16, dst + gi * S::kGroupPad + j * 1024);
   }
   // scale and zero: 256 bytes per group and field, 16 lanes per group
-  const int g = min(g0 + (lane >> 4), glast);
-  const uint8_t* const meta = unit + g * (long long)BL.bytes + (lane & 15) * 16;
+  const uint8_t* const meta = lane_record(rp, lane) + (lane & 15) * 16;
   dma16(meta + BL.k_scale, meta_dst);
   dma16(meta + BL.k_zero, meta_dst + 4 * D * 2);
 }
 
 // Value stage of groups [g0, g0 + ns): Stage::vLoads instructions.
-template <int KB, int VB>
+template <int KB, int VB, bool PAGED>
 __device__ __forceinline__ void issue_vstage(const DecodeArgs& a, long long u, int g0, int ns,
                                              uint8_t* dst) {
   using S = Stage<KB, VB>;
   constexpr BlockLayout BL = block_layout(KB, VB);
   const int lane = threadIdx.x & 63;
-  const int glast = g0 + ns - 1;
-  const uint8_t* const unit = a.blocks + (u * a.nb) * (long long)BL.bytes;
+  const uint8_t* rp[4];
+  step_records<KB, VB, PAGED>(a, u, g0, ns, rp);
 #pragma unroll
   for (int gi = 0; gi < 4; ++gi) {
-    const long long g = min(g0 + gi, glast);
 #pragma unroll
     for (int j = 0; j < S::vGroup / 1024; ++j)
-      dma16(unit + g * BL.bytes + BL.v_codes + j * 1024 + lane * 16, dst + gi * S::vGroup + j * 1024);
+      dma16(rp[gi] + BL.v_codes + j * 1024 + lane * 16, dst + gi * S::vGroup + j * 1024);
   }
-  const int g = min(g0 + (lane >> 4), glast);
-  const uint8_t* const meta = unit + g * (long long)BL.bytes + (lane & 15) * 16;
+  const uint8_t* const meta = lane_record(rp, lane) + (lane & 15) * 16;
   dma16(meta + BL.v_scale, dst + S::offVS);
   dma16(meta + BL.v_zero, dst + S::offVZ);
 }
@@ -426,7 +439,7 @@ __device__ __forceinline__ void issue_vstage(const DecodeArgs& a, long long u, i
 // ---------------------------------------------------------------------------
 // Key wave: scores of each step on the matrix cores, online softmax, and the
 // probabilities handed to the value wave.  Writes m and l of the partial.
-template <int KB, int VB, bool BF16, int NQ>
+template <int KB, int VB, bool BF16, int NQ, bool PAGED>
 __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b, int kvh, int split,
                                          int gb, int ge, int n_steps, uint8_t* smem) {
   using S = Stage<KB, VB>;
@@ -439,7 +452,7 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
   const int jt = lc & 3;
 
   // the first stage's loads go out before q is read: their latencies overlap
-  issue_kstage<KB, VB>(a, u, gb, min(4, ge - gb), smem, smem + S::offKM0);
+  issue_kstage<KB, VB, PAGED>(a, u, gb, min(4, ge - gb), smem, smem + S::offKM0);
   // q'' = q * 2^(lf(e) - 3) as fp16 pairs for head hq, channels 32*lk ..
   // 32*lk+31 (pair p: channels 2p, 2p+1; e = p & 3 its pair class in the run
   // of 8): the code-position factor of the key codes it multiplies, over 8.
@@ -502,7 +515,7 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
     // metadata buffer, last read by the previous step) with the next step
     wave_lds_sync();
     if (step + 1 < n_steps)
-      issue_kstage<KB, VB>(a, u, g0 + 4, min(4, ge - g0 - 4), smem,
+      issue_kstage<KB, VB, PAGED>(a, u, g0 + 4, min(4, ge - g0 - 4), smem,
                            smem + S::offKM0 + ((step + 1) & 1) * S::kMetaBytes);
     // B = q' * S (hi, lo) for head hq and group g0 + gc, built per block of
     // 32 channels right before its products (the vector work of block c+1
@@ -599,16 +612,8 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
     lcls[1] += p0[2] + p0[3];
     lcls[2] += p1[0] + p1[1];
     lcls[3] += p1[2] + p1[3];
-    // handed over as fp16 pairs hi (nearest) and lo (nearest of the exact
-    // remainder): p = hi + lo within 2^-22 relative; the value wave then
-    // multiplies them by its scales with packed fp16 operations
-    uint32_t ph[4], pl[4];
-    split_pair(p0[0], p0[1], ph[0], pl[0]);
-    split_pair(p0[2], p0[3], ph[1], pl[1]);
-    split_pair(p1[0], p1[1], ph[2], pl[2]);
-    split_pair(p1[2], p1[3], ph[3], pl[3]);
-    *reinterpret_cast<u32x4*>(sl + row) = u32x4{ph[0], ph[1], ph[2], ph[3]};
-    *reinterpret_cast<u32x4*>(sl + row + 4) = u32x4{pl[0], pl[1], pl[2], pl[3]};
+    *reinterpret_cast<f32x4*>(sl + row) = p0;
+    *reinterpret_cast<f32x4*>(sl + row + 4) = p1;
     if (lk == 0 && jt == 0) sl[S::offAlpha / 4 + hq] = alpha;
     wg_barrier();  // step's probabilities ready
   }
@@ -630,7 +635,7 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
 // ---------------------------------------------------------------------------
 // Value wave: p.V of each step on the matrix cores, one step behind the key
 // wave.  Writes o of the partial; the last split also runs the window.
-template <int KB, int VB, bool BF16, int NQ>
+template <int KB, int VB, bool BF16, int NQ, bool PAGED>
 __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int b, int kvh, int split,
                                            int gb, int ge, int n_steps, uint8_t* smem) {
   using S = Stage<KB, VB>;
@@ -640,7 +645,7 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
   const int hq = lc >> 2;
   const int mcol = lc & 3;  // channel group of this lane's B column
   uint8_t* const vbase = smem + S::offV0;
-  issue_vstage<KB, VB>(a, u, gb, min(4, ge - gb), vbase);
+  issue_vstage<KB, VB, PAGED>(a, u, gb, min(4, ge - gb), vbase);
   constexpr float v_unscale = static_cast<float>(1 << (24 - VS::F));  // product -> output
 
   float zcls[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // sum of scaled p * Z, per pair class e'
@@ -653,7 +658,7 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
     const int ns = min(4, ge - g0);
     const uint8_t* vstage = vbase + (step & 1) * S::vBytes;
     const bool more = step + 1 < n_steps;
-    if (more) issue_vstage<KB, VB>(a, u, g0 + 4, min(4, ge - g0 - 4), vbase + ((step + 1) & 1) * S::vBytes);
+    if (more) issue_vstage<KB, VB, PAGED>(a, u, g0 + 4, min(4, ge - g0 - 4), vbase + ((step + 1) & 1) * S::vBytes);
     wg_barrier();  // the key wave has written this step's probabilities
     if (more) {
       wait_vm<S::vLoads>();
@@ -676,20 +681,22 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
       const int vmo = ((gs * 4 + mcol) * G + 8 * lk) * 2;
       const u32x4 vs = *reinterpret_cast<const u32x4*>(vstage + S::offVS + vmo);
       const u32x4 vz = *reinterpret_cast<const u32x4*>(vstage + S::offVZ + vmo);
-      // p of tokens 8*lk .. 8*lk+7 as fp16 pairs hi and lo (pair e: tokens
-      // 2e, 2e+1); B = p * S as hi + lo: the exact product of the hi parts,
-      // plus the lo parts' product, rounded once with the remainder
+      // p of tokens 8*lk .. 8*lk+7 (pair e: tokens 2e, 2e+1); B = p * S as
+      // fp16 hi + lo of the binary32 product (the probabilities are not exact
+      // in fp16, so the product is formed in binary32 and split)
       const float* prow = hp + (gs * GQ + hq) * kRowP + 8 * lk;
-      const u32x4 ph = *reinterpret_cast<const u32x4*>(prow);
-      const u32x4 pl = *reinterpret_cast<const u32x4*>(prow + 4);
+      const f32x4 p0 = *reinterpret_cast<const f32x4*>(prow);
+      const f32x4 p1 = *reinterpret_cast<const f32x4*>(prow + 4);
+      const float p[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
       u32x4 h4, l4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         uint32_t hi, lo;
-        mul_pair_exact(ph[e], vs[e], hi, lo);
+        split_pair(times_half<0>(p[2 * e], vs[e]), times_half<1>(p[2 * e + 1], vs[e]), hi, lo);
         h4[e] = hi;
-        l4[e] = fma_pair(pl[e], vs[e], lo);
-        zcls[e] = dot2_acc(pl[e], vz[e], dot2_acc(ph[e], vz[e], zcls[e]));
+        l4[e] = lo;
+        zcls[e] = fmaf(p[2 * e], lo_half(vz[e]), zcls[e]);
+        zcls[e] = fmaf(p[2 * e + 1], hi_half(vz[e]), zcls[e]);
       }
       const half8_t bph = as_h8(h4), bpl = as_h8(l4);
       const uint32_t vc[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
@@ -726,7 +733,7 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
   }
 }
 
-template <int KB, int VB, bool BF16, int NQ>
+template <int KB, int VB, bool BF16, int NQ, bool PAGED>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma(DecodeArgs a) {
   using S = Stage<KB, VB>;
   __shared__ __align__(16) uint8_t smem[S::bytes];
@@ -757,9 +764,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
       const int n_steps = (ge - gb + 3) / 4;  // >= 1: every split holds a group
       // Both waves run the same number of steps and meet at one barrier per step.
       if (wave == 0) {
-        key_wave<KB, VB, BF16, NQ>(a, u, b, kvh, split, gb, ge, n_steps, smem);
+        key_wave<KB, VB, BF16, NQ, PAGED>(a, u, b, kvh, split, gb, ge, n_steps, smem);
       } else {
-        value_wave<KB, VB, BF16, NQ>(a, u, b, kvh, split, gb, ge, n_steps, smem);
+        value_wave<KB, VB, BF16, NQ, PAGED>(a, u, b, kvh, split, gb, ge, n_steps, smem);
       }
     }
   }
@@ -775,21 +782,21 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
   }
 }
 
-template <int KB, int VB, bool BF16, int NQ>
+template <int KB, int VB, bool BF16, int NQ, bool PAGED>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   // one workgroup per packed split; the last one also runs the window.
   // A ragged launch covers a.B sequences from a.seq0.
   dim3 grid(a.n_split_packed > 0 ? a.n_split_packed : 1, a.B * a.H);
-  hipLaunchKernelGGL((decode_mfma<KB, VB, BF16, NQ>), grid, dim3(128), 0, stream, a);
+  hipLaunchKernelGGL((decode_mfma<KB, VB, BF16, NQ, PAGED>), grid, dim3(128), 0, stream, a);
   return hipGetLastError();
 }
 
 template <int KB, int VB, bool BF16>
 hipError_t launch_nq(const DecodeArgs& a, hipStream_t stream) {
   switch (a.gq) {
-    case 1: return launch_t<KB, VB, BF16, 1>(a, stream);
-    case 2: return launch_t<KB, VB, BF16, 2>(a, stream);
-    case 4: return launch_t<KB, VB, BF16, 4>(a, stream);
+    case 1: return a.page_table ? launch_t<KB, VB, BF16, 1, true>(a, stream) : launch_t<KB, VB, BF16, 1, false>(a, stream);
+    case 2: return a.page_table ? launch_t<KB, VB, BF16, 2, true>(a, stream) : launch_t<KB, VB, BF16, 2, false>(a, stream);
+    case 4: return a.page_table ? launch_t<KB, VB, BF16, 4, true>(a, stream) : launch_t<KB, VB, BF16, 4, false>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -26,6 +26,19 @@ __host__ __device__ constexpr BlockLayout block_layout(int k_bits, int v_bits) {
                      kGroup * kHeadDim * (k_bits + v_bits) / 8 + 8 * kHeadDim};
 }
 
+// Paged block records (page_table != nullptr): block g of sequence b, kv
+// head h lives at blocks + (P * H + h) * block_bytes with page
+// P = page_table[b * page_stride + g], clamped into [0, num_pages) so that a
+// wrong table can never address memory outside the pool.
+__host__ __device__ inline long long record_index(const int32_t* page_table, int page_stride, int num_pages,
+                                                 int nb, int H, long long u, int g) {
+  if (!page_table) return u * nb + g;
+  const long long b = u / H;
+  int p = page_table[b * page_stride + g];
+  p = p < 0 ? 0 : (p >= num_pages ? num_pages - 1 : p);
+  return (long long)p * H + (u - b * H);
+}
+
 // Per-sequence work of a pack launch over sequences of different lengths
 // (same fields as the uniform ones of PackArgs).
 struct SeqOp {
@@ -61,6 +74,8 @@ struct PackArgs {
   int nb;     // blocks per unit (cap / G)
   int R;      // window length
   int units;  // B * H
+  const int32_t* page_table;  // paged block records (nullptr: unit-major)
+  int page_stride, num_pages;
   int ragged;
   int unit0;  // ragged: first unit of the launch (a sequence boundary)
   int H;      // ragged: units per sequence
@@ -77,6 +92,8 @@ struct DecodeArgs {
   float* partial;      // [B][Hq][n_split][D + 2] fp32 (m, l, o[D])
   int B, H, Hq, gq;
   int cap, nb, R;
+  const int32_t* page_table;  // paged block records (nullptr: unit-major)
+  int page_stride, num_pages;
   int n_quant, n_resid;
   int n_split;
   int items_per_split;  // vector kernel: work items (blocks, then window chunks) per split

@@ -288,7 +288,8 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
   constexpr BlockLayout BL = block_layout(KB, VB);
   const int blk = item;
   const int gblk = dst_blk0 + blk;
-  uint8_t* const rec = a.blocks + (u * a.nb + gblk) * BL.bytes;  // this block's record
+  uint8_t* const rec =  // this block's record
+      a.blocks + record_index(a.page_table, a.page_stride, a.num_pages, a.nb, a.H, u, gblk) * BL.bytes;
   {
     // 16-byte pieces c = tid and c = tid + 256 of the 32 x 128 tiles
     const int row = tid / (D / 8), col = (tid % (D / 8)) * 8;

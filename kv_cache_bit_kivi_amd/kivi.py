@@ -32,7 +32,7 @@ EXPORTED = (
     "kivi_decode_attn", "kivi_set_decode_splits", "kivi_cache_get_view",
     "kivi_status_string", "kivi_last_error_message",
     "kivi_append_varlen", "kivi_cache_reset_sequences", "kivi_cache_get_lengths",
-    "kivi_append_decode_attn",
+    "kivi_append_decode_attn", "kivi_cache_set_page_table",
 )
 
 
@@ -78,6 +78,7 @@ def _load():
         "kivi_append_varlen": ([vp, vp, vp, ctypes.POINTER(i32), i32, vp], i32),
         "kivi_cache_reset_sequences": ([vp, ctypes.POINTER(i32), i32], i32),
         "kivi_cache_get_lengths": ([vp, ctypes.POINTER(i32), ctypes.POINTER(i32)], i32),
+        "kivi_cache_set_page_table": ([vp, vp, i32, i32], i32),
         "kivi_decode_attn_workspace_bytes": ([vp, i32, ctypes.POINTER(sz)], i32),
         "kivi_decode_attn": ([vp, vp, i32, ctypes.c_float, vp, i32, vp, sz, vp], i32),
         "kivi_append_decode_attn": ([vp, vp, vp, vp, i32, ctypes.c_float, vp, i32, vp, sz, vp], i32),
@@ -155,6 +156,10 @@ def kivi_append_varlen(h, k_ptr, v_ptr, n_tokens, n_max, stream):
 def kivi_cache_reset_sequences(h, seqs):
     arr, n = _i32_array(seqs)
     _check(lib.kivi_cache_reset_sequences(h, arr, n))
+
+
+def kivi_cache_set_page_table(h, table_ptr, page_stride, num_pages):
+    _check(lib.kivi_cache_set_page_table(h, ctypes.c_void_p(table_ptr), page_stride, num_pages))
 
 
 def kivi_cache_get_lengths(h, batch):
@@ -247,6 +252,28 @@ class KiviCache:
         assert len(n_tokens) == self.cfg.batch
         kivi_append_varlen(self.handle, k.data_ptr(), v.data_ptr(), n_tokens, n_max,
                            self._stream(stream))
+
+    def set_page_table(self, table, num_pages):
+        """Paged block records: table is a device int32 tensor [B][page_stride]
+        (kept alive here); None restores the unit-major layout."""
+        if table is None:
+            self._page_table = None
+            kivi_cache_set_page_table(self.handle, 0, 0, 0)
+            return
+        t = self.torch
+        assert table.dtype == t.int32 and table.is_contiguous() and table.device == self.device
+        assert table.dim() == 2 and table.shape[0] == self.cfg.batch
+        kivi_cache_set_page_table(self.handle, table.data_ptr(), table.shape[1], num_pages)
+        self._page_table = table
+
+    def record_index(self, u, g):
+        """Index of the block record of unit u, block g in the block region."""
+        H = self.cfg.num_kv_heads
+        pt = getattr(self, "_page_table", None)
+        if pt is None:
+            return u * self.view().num_blocks + g
+        b, h = divmod(u, H)
+        return int(pt[b, g].item()) * H + h
 
     def reset_sequences(self, seqs):
         kivi_cache_reset_sequences(self.handle, seqs)
