@@ -140,6 +140,18 @@ def test_varlen_entry_points_validate_before_launch():
     kivi.kivi_cache_destroy(h)
 
 
+def test_page_table_validation_host():
+    h = _make()  # batch 2, 12 blocks per sequence
+    P = kivi.kivi_cache_set_page_table
+    assert status_of(P, h, FAKE_DEV, 11, 4) == kivi.KIVI_ERR_INVALID_ARG  # stride < blocks
+    assert status_of(P, h, FAKE_DEV, 12, 0) == kivi.KIVI_ERR_INVALID_ARG
+    assert status_of(P, h, FAKE_DEV, 12, 25) == kivi.KIVI_ERR_INVALID_ARG  # > batch * blocks
+    assert status_of(P, h, FAKE_DEV + 2, 12, 4) == kivi.KIVI_ERR_INVALID_ARG
+    assert status_of(P, h, FAKE_DEV, 12, 24) == kivi.KIVI_OK
+    assert status_of(P, h, 0, 0, 0) == kivi.KIVI_OK  # back to the unit-major layout
+    kivi.kivi_cache_destroy(h)
+
+
 def test_status_strings():
     for s in range(7):
         assert kivi.status_name(s).startswith("KIVI_")
