@@ -612,10 +612,20 @@ kivi_status decode_launch(kivi_cache* c, const void* q, int32_t num_q_heads, flo
         // round costs a whole wave duration
         // (sequences of different lengths: only the splits that hold groups
         // of their sequence count; the others end at once)
+        // For ragged caches every multiple of 4 is a candidate split size
+        // (the divisions of the longest sequence alone are too coarse to
+        // fill a round with the shorter ones).
         long long best = -1;
-        for (int want = 1; want <= max_split; ++want) {
+        const int n_cand = c->ragged ? (nqg + 3) / 4 : max_split;
+        for (int i = 1; i <= n_cand; ++i) {
           int g, np;
-          plan(want, g, np);
+          if (c->ragged) {
+            g = 4 * i;
+            np = (nqg + g - 1) / g;
+            if (np > kivi::kMaxSplits - 1) continue;
+          } else {
+            plan(i, g, np);
+          }
           long long work = (long long)units * np;
           if (c->ragged) {
             work = 0;
