@@ -88,9 +88,9 @@ kivi_status check_config(const kivi_config* c) {
                 c->residual_length);
   if (c->kv_dtype != KIVI_F16 && c->kv_dtype != KIVI_BF16)
     return fail(KIVI_ERR_INVALID_ARG, "kv_dtype must be KIVI_F16 or KIVI_BF16");
-  if (c->head_dim != kivi::kHeadDim || c->group_size != kivi::kGroup)
-    return fail(KIVI_ERR_UNSUPPORTED, "kernels are built for head_dim %d and group_size %d",
-                kivi::kHeadDim, kivi::kGroup);
+  if (c->head_dim != kivi::kHeadDim || (c->group_size != 32 && c->group_size != 64))
+    return fail(KIVI_ERR_UNSUPPORTED, "kernels are built for head_dim %d and group_size 32 or 64",
+                kivi::kHeadDim);
   if ((long long)c->batch * c->num_kv_heads > 65535)
     return fail(KIVI_ERR_UNSUPPORTED, "batch * num_kv_heads must be at most 65535");
   if ((long long)c->max_tokens + c->residual_length > (1LL << 30))
@@ -130,6 +130,7 @@ kivi::PackArgs base_pack_args(const kivi_cache* c) {
   a.nb = c->nb;
   a.R = c->cfg.residual_length;
   a.units = c->cfg.batch * c->cfg.num_kv_heads;
+  a.G = c->cfg.group_size;
   a.H = c->cfg.num_kv_heads;
   a.page_table = c->page_table;
   a.page_stride = c->page_stride;
@@ -561,6 +562,8 @@ kivi_status check_decode_args(const kivi_cache* c, const void* q, int32_t num_q_
   const int gq = num_q_heads / c->cfg.num_kv_heads;
   if (gq != 1 && gq != 2 && gq != 4 && gq != 8)
     return fail(KIVI_ERR_UNSUPPORTED, "query heads per kv head must be 1, 2, 4 or 8 (got %d)", gq);
+  if (gq == 8 && c->cfg.group_size != kivi::kGroup)
+    return fail(KIVI_ERR_UNSUPPORTED, "8 query heads per kv head need group_size %d", kivi::kGroup);
   size_t need = 0;
   kivi_decode_attn_workspace_bytes(c, num_q_heads, &need);
   if (ws_bytes < need)
@@ -583,7 +586,9 @@ kivi_status decode_launch(kivi_cache* c, const void* q, int32_t num_q_heads, flo
     c->cu_count = cus;
   }
 
-  const int G = c->cfg.group_size;
+  // the kernels walk the packed tokens in streams of 32 (a block of G = 32,
+  // or half a block of G = 64; the vector kernel only takes G = 32)
+  const int G = kivi::kStream;
   const int units = c->cfg.batch * c->cfg.num_kv_heads;
   const int nqg = c->n_quant / G;
   // matrix-core kernel: up to 4 query heads per kv head share one wave
@@ -669,6 +674,7 @@ kivi_status decode_launch(kivi_cache* c, const void* q, int32_t num_q_heads, flo
   a.gq = gq;
   a.cap = c->cap;
   a.nb = c->nb;
+  a.G = c->cfg.group_size;
   a.R = c->cfg.residual_length;
   a.n_quant = c->n_quant;
   a.n_resid = c->n_resid;
@@ -779,7 +785,7 @@ kivi_status kivi_cache_get_view(const kivi_cache* c, kivi_cache_view* v) {
   v->n_resid = c->ragged ? -1 : c->n_resid;
   v->capacity = c->cap;
   v->num_blocks = c->nb;
-  const kivi::BlockLayout bl = kivi::block_layout(c->cfg.k_bits, c->cfg.v_bits);
+  const kivi::BlockLayout bl = kivi::block_layout(c->cfg.k_bits, c->cfg.v_bits, c->cfg.group_size);
   v->block_bytes = bl.bytes;
   v->off_k_codes = bl.k_codes;
   v->off_v_codes = bl.v_codes;

@@ -369,69 +369,86 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
   __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)lds_dst, 16, 0, 0);
 }
 
-// Records of groups g0 .. g0 + 3 of unit u (unit-major, or through the page
-// table when PAGED); slots past the last valid group g0 + ns - 1 repeat it
-// (addresses stay inside).
-template <int KB, int VB, bool PAGED>
+// Records of streams g0 .. g0 + 3 of unit u (unit-major, or through the
+// page table when PAGED).  A stream is 32 tokens: a whole block of G = 32, or
+// half `hf` of a block of G = 64.  Slots past the last valid stream
+// g0 + ns - 1 repeat it (addresses stay inside).
+template <int KB, int VB, int GT, bool PAGED>
 __device__ __forceinline__ void step_records(const DecodeArgs& a, long long u, int g0, int ns,
-                                             const uint8_t* (&rp)[4]) {
-  constexpr BlockLayout BL = block_layout(KB, VB);
-  if constexpr (PAGED) {
+                                             const uint8_t* (&rp)[4], int (&hf)[4]) {
+  constexpr BlockLayout BL = block_layout(KB, VB, GT);
+  constexpr int SPB = GT / kStream;  // streams per block
 #pragma unroll
-    for (int gi = 0; gi < 4; ++gi)
-      rp[gi] = a.blocks + record_index(a.page_table, a.page_stride, a.num_pages, a.nb, a.H, u,
-                                       min(g0 + gi, g0 + ns - 1)) * BL.bytes;
-  } else {
-    const uint8_t* const unit = a.blocks + (u * a.nb) * (long long)BL.bytes;
-#pragma unroll
-    for (int gi = 0; gi < 4; ++gi) rp[gi] = unit + (long long)min(g0 + gi, g0 + ns - 1) * BL.bytes;
+  for (int gi = 0; gi < 4; ++gi) {
+    const int g = min(g0 + gi, g0 + ns - 1);
+    hf[gi] = g % SPB;
+    if constexpr (PAGED) {
+      rp[gi] = a.blocks + record_index(a.page_table, a.page_stride, a.num_pages, a.nb, a.H, u, g / SPB) * BL.bytes;
+    } else {
+      rp[gi] = a.blocks + (u * a.nb + g / SPB) * (long long)BL.bytes;
+    }
   }
 }
 
-// The record of this lane's metadata slot (lanes 16 i .. 16 i + 15: group i).
+// The record (and half) of this lane's metadata slot (lanes 16 i .. 16 i +
+// 15: stream i).
 __device__ __forceinline__ const uint8_t* lane_record(const uint8_t* const (&rp)[4], int lane) {
   const int i = lane >> 4;
   return i == 0 ? rp[0] : i == 1 ? rp[1] : i == 2 ? rp[2] : rp[3];
 }
+__device__ __forceinline__ int lane_half(const int (&hf)[4], int lane) {
+  const int i = lane >> 4;
+  return i == 0 ? hf[0] : i == 1 ? hf[1] : i == 2 ? hf[2] : hf[3];
+}
 
-// Key stage of groups [g0, g0 + ns): codes to `dst`, scale and zero to
+// Key stage of streams [g0, g0 + ns): codes to `dst`, scale and zero to
 // `meta`; Stage::kLoads instructions.
-template <int KB, int VB, bool PAGED>
+template <int KB, int VB, int GT, bool PAGED>
 __device__ __forceinline__ void issue_kstage(const DecodeArgs& a, long long u, int g0, int ns,
                                              uint8_t* dst, uint8_t* meta_dst) {
   using S = Stage<KB, VB>;
-  constexpr BlockLayout BL = block_layout(KB, VB);
+  constexpr BlockLayout BL = block_layout(KB, VB, GT);
   const int lane = threadIdx.x & 63;
   const uint8_t* rp[4];
-  step_records<KB, VB, PAGED>(a, u, g0, ns, rp);
+  int hf[4];
+  step_records<KB, VB, GT, PAGED>(a, u, g0, ns, rp, hf);
 #pragma unroll
   for (int gi = 0; gi < 4; ++gi) {
 #pragma unroll
-    for (int j = 0; j < S::kGroup / 1024; ++j)
-      dma16(rp[gi] + BL.k_codes + j * 1024 + lane * 16, dst + gi * S::kGroupPad + j * 1024);
+    for (int j = 0; j < S::kGroup / 1024; ++j)  // a stream's rows: kGroup bytes from row 32 * hf
+      dma16(rp[gi] + BL.k_codes + hf[gi] * S::kGroup + j * 1024 + lane * 16,
+            dst + gi * S::kGroupPad + j * 1024);
   }
-  // scale and zero: 256 bytes per group and field, 16 lanes per group
+  // scale and zero of the stream's block: 256 bytes per stream and field, 16
+  // lanes per stream
   const uint8_t* const meta = lane_record(rp, lane) + (lane & 15) * 16;
   dma16(meta + BL.k_scale, meta_dst);
   dma16(meta + BL.k_zero, meta_dst + 4 * D * 2);
 }
 
 // Value stage of groups [g0, g0 + ns): Stage::vLoads instructions.
-template <int KB, int VB, bool PAGED>
+template <int KB, int VB, int GT, bool PAGED>
 __device__ __forceinline__ void issue_vstage(const DecodeArgs& a, long long u, int g0, int ns,
                                              uint8_t* dst) {
   using S = Stage<KB, VB>;
-  constexpr BlockLayout BL = block_layout(KB, VB);
+  constexpr BlockLayout BL = block_layout(KB, VB, GT);
   const int lane = threadIdx.x & 63;
   const uint8_t* rp[4];
-  step_records<KB, VB, PAGED>(a, u, g0, ns, rp);
+  int hf[4];
+  step_records<KB, VB, GT, PAGED>(a, u, g0, ns, rp, hf);
 #pragma unroll
   for (int gi = 0; gi < 4; ++gi) {
 #pragma unroll
-    for (int j = 0; j < S::vGroup / 1024; ++j)
-      dma16(rp[gi] + BL.v_codes + j * 1024 + lane * 16, dst + gi * S::vGroup + j * 1024);
+    for (int j = 0; j < S::vGroup / 1024; ++j)  // the stream's words: vGroup bytes from word row hf * VB
+      dma16(rp[gi] + BL.v_codes + hf[gi] * S::vGroup + j * 1024 + lane * 16, dst + gi * S::vGroup + j * 1024);
   }
-  const uint8_t* const meta = lane_record(rp, lane) + (lane & 15) * 16;
+  // scale and zero of the stream's 32 tokens, stage layout [stream][4 channel
+  // groups of 32][32 tokens]; a block stores [D / G][G], so with G = 64 two
+  // channel groups of 32 share one stored group.  Lane: stream lane / 16,
+  // channel group c / 4 and 8 tokens (c % 4) of c = lane % 16.
+  const int c = lane & 15;
+  const int off = ((32 * (c >> 2)) / GT * GT + kStream * lane_half(hf, lane) + 8 * (c & 3)) * 2;
+  const uint8_t* const meta = lane_record(rp, lane) + off;
   dma16(meta + BL.v_scale, dst + S::offVS);
   dma16(meta + BL.v_zero, dst + S::offVZ);
 }
@@ -439,7 +456,7 @@ __device__ __forceinline__ void issue_vstage(const DecodeArgs& a, long long u, i
 // ---------------------------------------------------------------------------
 // Key wave: scores of each step on the matrix cores, online softmax, and the
 // probabilities handed to the value wave.  Writes m and l of the partial.
-template <int KB, int VB, bool BF16, int NQ, bool PAGED>
+template <int KB, int VB, bool BF16, int NQ, int GT, bool PAGED>
 __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b, int kvh, int split,
                                          int gb, int ge, int n_steps, uint8_t* smem) {
   using S = Stage<KB, VB>;
@@ -452,7 +469,7 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
   const int jt = lc & 3;
 
   // the first stage's loads go out before q is read: their latencies overlap
-  issue_kstage<KB, VB, PAGED>(a, u, gb, min(4, ge - gb), smem, smem + S::offKM0);
+  issue_kstage<KB, VB, GT, PAGED>(a, u, gb, min(4, ge - gb), smem, smem + S::offKM0);
   // q'' = q * 2^(lf(e) - 3) as fp16 pairs for head hq, channels 32*lk ..
   // 32*lk+31 (pair p: channels 2p, 2p+1; e = p & 3 its pair class in the run
   // of 8): the code-position factor of the key codes it multiplies, over 8.
@@ -515,7 +532,7 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
     // metadata buffer, last read by the previous step) with the next step
     wave_lds_sync();
     if (step + 1 < n_steps)
-      issue_kstage<KB, VB, PAGED>(a, u, g0 + 4, min(4, ge - g0 - 4), smem,
+      issue_kstage<KB, VB, GT, PAGED>(a, u, g0 + 4, min(4, ge - g0 - 4), smem,
                            smem + S::offKM0 + ((step + 1) & 1) * S::kMetaBytes);
     // B = q' * S (hi, lo) for head hq and group g0 + gc, built per block of
     // 32 channels right before its products (the vector work of block c+1
@@ -635,7 +652,7 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
 // ---------------------------------------------------------------------------
 // Value wave: p.V of each step on the matrix cores, one step behind the key
 // wave.  Writes o of the partial; the last split also runs the window.
-template <int KB, int VB, bool BF16, int NQ, bool PAGED>
+template <int KB, int VB, bool BF16, int NQ, int GT, bool PAGED>
 __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int b, int kvh, int split,
                                            int gb, int ge, int n_steps, uint8_t* smem) {
   using S = Stage<KB, VB>;
@@ -645,7 +662,7 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
   const int hq = lc >> 2;
   const int mcol = lc & 3;  // channel group of this lane's B column
   uint8_t* const vbase = smem + S::offV0;
-  issue_vstage<KB, VB, PAGED>(a, u, gb, min(4, ge - gb), vbase);
+  issue_vstage<KB, VB, GT, PAGED>(a, u, gb, min(4, ge - gb), vbase);
   constexpr float v_unscale = static_cast<float>(1 << (24 - VS::F));  // product -> output
 
   float zcls[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // sum of scaled p * Z, per pair class e'
@@ -658,7 +675,7 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
     const int ns = min(4, ge - g0);
     const uint8_t* vstage = vbase + (step & 1) * S::vBytes;
     const bool more = step + 1 < n_steps;
-    if (more) issue_vstage<KB, VB, PAGED>(a, u, g0 + 4, min(4, ge - g0 - 4), vbase + ((step + 1) & 1) * S::vBytes);
+    if (more) issue_vstage<KB, VB, GT, PAGED>(a, u, g0 + 4, min(4, ge - g0 - 4), vbase + ((step + 1) & 1) * S::vBytes);
     wg_barrier();  // the key wave has written this step's probabilities
     if (more) {
       wait_vm<S::vLoads>();
@@ -733,7 +750,7 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
   }
 }
 
-template <int KB, int VB, bool BF16, int NQ, bool PAGED>
+template <int KB, int VB, bool BF16, int NQ, int GT, bool PAGED>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma(DecodeArgs a) {
   using S = Stage<KB, VB>;
   __shared__ __align__(16) uint8_t smem[S::bytes];
@@ -750,7 +767,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
   const long long u = (long long)b * a.H + kvh;
 
   if (a.n_split_packed > 0) {
-    const int nqg = nq / G;
+    const int nqg = nq / kStream;  // packed streams of 32 tokens
     const int gb = split * a.groups_per_split;
     const int ge = min(nqg, gb + a.groups_per_split);
     if (gb >= nqg) {
@@ -764,9 +781,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
       const int n_steps = (ge - gb + 3) / 4;  // >= 1: every split holds a group
       // Both waves run the same number of steps and meet at one barrier per step.
       if (wave == 0) {
-        key_wave<KB, VB, BF16, NQ, PAGED>(a, u, b, kvh, split, gb, ge, n_steps, smem);
+        key_wave<KB, VB, BF16, NQ, GT, PAGED>(a, u, b, kvh, split, gb, ge, n_steps, smem);
       } else {
-        value_wave<KB, VB, BF16, NQ, PAGED>(a, u, b, kvh, split, gb, ge, n_steps, smem);
+        value_wave<KB, VB, BF16, NQ, GT, PAGED>(a, u, b, kvh, split, gb, ge, n_steps, smem);
       }
     }
   }
@@ -782,21 +799,28 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
   }
 }
 
-template <int KB, int VB, bool BF16, int NQ, bool PAGED>
+template <int KB, int VB, bool BF16, int NQ, int GT, bool PAGED>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   // one workgroup per packed split; the last one also runs the window.
   // A ragged launch covers a.B sequences from a.seq0.
   dim3 grid(a.n_split_packed > 0 ? a.n_split_packed : 1, a.B * a.H);
-  hipLaunchKernelGGL((decode_mfma<KB, VB, BF16, NQ, PAGED>), grid, dim3(128), 0, stream, a);
+  hipLaunchKernelGGL((decode_mfma<KB, VB, BF16, NQ, GT, PAGED>), grid, dim3(128), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int KB, int VB, bool BF16, int NQ>
+hipError_t launch_gp(const DecodeArgs& a, hipStream_t stream) {
+  if (a.G == 64)
+    return a.page_table ? launch_t<KB, VB, BF16, NQ, 64, true>(a, stream) : launch_t<KB, VB, BF16, NQ, 64, false>(a, stream);
+  return a.page_table ? launch_t<KB, VB, BF16, NQ, 32, true>(a, stream) : launch_t<KB, VB, BF16, NQ, 32, false>(a, stream);
 }
 
 template <int KB, int VB, bool BF16>
 hipError_t launch_nq(const DecodeArgs& a, hipStream_t stream) {
   switch (a.gq) {
-    case 1: return a.page_table ? launch_t<KB, VB, BF16, 1, true>(a, stream) : launch_t<KB, VB, BF16, 1, false>(a, stream);
-    case 2: return a.page_table ? launch_t<KB, VB, BF16, 2, true>(a, stream) : launch_t<KB, VB, BF16, 2, false>(a, stream);
-    case 4: return a.page_table ? launch_t<KB, VB, BF16, 4, true>(a, stream) : launch_t<KB, VB, BF16, 4, false>(a, stream);
+    case 1: return launch_gp<KB, VB, BF16, 1>(a, stream);
+    case 2: return launch_gp<KB, VB, BF16, 2>(a, stream);
+    case 4: return launch_gp<KB, VB, BF16, 4>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

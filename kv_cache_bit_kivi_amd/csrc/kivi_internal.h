@@ -7,7 +7,8 @@
 
 namespace kivi {
 
-constexpr int kGroup = 32;       // G: tokens per key group, channels per value group
+constexpr int kGroup = 32;       // default G: tokens per key group, channels per value group
+constexpr int kStream = 32;      // decode: tokens per stream (a group, or half of a 64-token group)
 constexpr int kHeadDim = 128;    // D handled by the kernels
 constexpr int kMaxSplits = 256;  // upper bound on decode token splits
 
@@ -16,14 +17,14 @@ constexpr int kMaxSplits = 256;  // upper bound on decode token splits
 struct BlockLayout {
   int k_codes, v_codes, k_scale, k_zero, v_scale, v_zero, bytes;
 };
-__host__ __device__ constexpr BlockLayout block_layout(int k_bits, int v_bits) {
+__host__ __device__ constexpr BlockLayout block_layout(int k_bits, int v_bits, int g = kGroup) {
   return BlockLayout{0,
-                     kGroup * kHeadDim * k_bits / 8,
-                     kGroup * kHeadDim * (k_bits + v_bits) / 8,
-                     kGroup * kHeadDim * (k_bits + v_bits) / 8 + 2 * kHeadDim,
-                     kGroup * kHeadDim * (k_bits + v_bits) / 8 + 4 * kHeadDim,
-                     kGroup * kHeadDim * (k_bits + v_bits) / 8 + 6 * kHeadDim,
-                     kGroup * kHeadDim * (k_bits + v_bits) / 8 + 8 * kHeadDim};
+                     g * kHeadDim * k_bits / 8,
+                     g * kHeadDim * (k_bits + v_bits) / 8,
+                     g * kHeadDim * (k_bits + v_bits) / 8 + 2 * kHeadDim,
+                     g * kHeadDim * (k_bits + v_bits) / 8 + 4 * kHeadDim,
+                     g * kHeadDim * (k_bits + v_bits) / 8 + 6 * kHeadDim,
+                     g * kHeadDim * (k_bits + v_bits) / 8 + 8 * kHeadDim};
 }
 
 // Paged block records (page_table != nullptr): block g of sequence b, kv
@@ -74,6 +75,7 @@ struct PackArgs {
   int nb;     // blocks per unit (cap / G)
   int R;      // window length
   int units;  // B * H
+  int G;      // tokens per block (32 or 64)
   const int32_t* page_table;  // paged block records (nullptr: unit-major)
   int page_stride, num_pages;
   int ragged;
@@ -92,6 +94,7 @@ struct DecodeArgs {
   float* partial;      // [B][Hq][n_split][D + 2] fp32 (m, l, o[D])
   int B, H, Hq, gq;
   int cap, nb, R;
+  int G;  // tokens per block (32 or 64); the kernels work in 32-token streams
   const int32_t* page_table;  // paged block records (nullptr: unit-major)
   int page_stride, num_pages;
   int n_quant, n_resid;

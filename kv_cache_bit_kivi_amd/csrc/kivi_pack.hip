@@ -1,4 +1,4 @@
-// kivi_pack.hip - quantize and bit-pack blocks of G = 32 tokens (keys per
+// kivi_pack.hip - quantize and bit-pack blocks of G = 32 or 64 tokens (keys per
 // channel, values per token) and copy tokens into the residual window.
 //
 // Method: page "KIVI: Asymmetric 2-Bit KV Cache Quantization Guide", "The
@@ -22,8 +22,8 @@
 namespace kivi {
 namespace {
 
-constexpr int G = kGroup;
 constexpr int D = kHeadDim;
+constexpr int kCopy = 32;  // window tokens copied per workgroup
 constexpr int RS = D + 8;  // LDS row stride in 16-bit elements (272 bytes)
 
 // fp16 bit pattern of a binary32 value, nearest-even; zero is stored as +0.
@@ -140,7 +140,7 @@ __device__ __forceinline__ void lds_barrier() {
 // tokens tg, tg + TS, ...; the channels are taken 8 at a time (fewer live
 // registers).  kt: the staged key tile; kmn, krc, ksc: per channel minimum,
 // reciprocal and scale.
-template <int KB, bool BF16, bool CAREFUL>
+template <int KB, int G, bool BF16, bool CAREFUL>
 __device__ __forceinline__ void key_words(const uint16_t* kt, const float* kmn, const float* krc,
                                           const float* ksc, int w, int tg, bool tiny,
                                           uint32_t* word, float& dev) {
@@ -185,20 +185,20 @@ __device__ __forceinline__ void key_words(const uint16_t* kt, const float* kmn, 
 }
 
 // Value code words of one thread: channels d0, d0 + 1 (one channel group) and
-// rows 16*h .. 16*h+15, taken 8 rows at a time.  vt: the staged value tile;
-// vmn, vrc, vsc: per (group, row) minimum, reciprocal and scale.
-template <int VB, bool BF16, bool CAREFUL>
+// rows (G/2)*h .. (G/2)*h + G/2 - 1, taken 8 rows at a time.  vt: the staged
+// value tile; vmn, vrc, vsc: per (group, row) minimum, reciprocal and scale.
+template <int VB, int G, bool BF16, bool CAREFUL>
 __device__ __forceinline__ void value_words(const uint16_t* vt, const float* vmn, const float* vrc,
                                             const float* vsc, int d0, int h, bool tiny,
                                             uint32_t* w0, uint32_t* w1, float& dev) {
-  constexpr int PV = 32 / VB, NW = 16 / PV;
+  constexpr int PV = 32 / VB, HR = G / 2, NW = HR / PV;
   const int m = d0 / G;
   float l0[NW], h0[NW], l1[NW], h1[NW];  // even / odd codes of channels d0, d0+1
 #pragma unroll
   for (int k = 0; k < NW; ++k) l0[k] = h0[k] = l1[k] = h1[k] = 0.0f;
 #pragma unroll
-  for (int r8 = 0; r8 < 16; r8 += 8) {
-    const int sbase = m * G + 16 * h + r8;
+  for (int r8 = 0; r8 < HR; r8 += 8) {
+    const int sbase = m * G + HR * h + r8;
     float mn[8], rc[8], sc[8];
 #pragma unroll
     for (int j = 0; j < 8; j += 4) {
@@ -215,8 +215,8 @@ __device__ __forceinline__ void value_words(const uint16_t* vt, const float* vmn
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int r = r8 + j;  // row 16*h + r: word r / PV, position r % PV
-      const uint32_t xw = *reinterpret_cast<const uint32_t*>(&vt[(16 * h + r) * RS + d0]);
+      const int r = r8 + j;  // row HR*h + r: word r / PV, position r % PV
+      const uint32_t xw = *reinterpret_cast<const uint32_t*>(&vt[(HR * h + r) * RS + d0]);
       const int k = r / PV, pos = r % PV;
       const float wt = static_cast<float>(1 << (VB * (pos >> 1)));
       const float c0 = code_of<CAREFUL>(diff<BF16, 0>(xw, mn[j]), rc[j], sc[j], tiny, dev);  // channel d0
@@ -237,7 +237,7 @@ __device__ __forceinline__ void value_words(const uint16_t* vt, const float* vmn
   }
 }
 
-template <int KB, int VB, bool BF16>
+template <int KB, int VB, bool BF16, int G>
 __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
   constexpr int QK = (1 << KB) - 1, QV = (1 << VB) - 1;
   constexpr int PK = 32 / KB;  // key codes (channels) per word
@@ -247,7 +247,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
   __shared__ __align__(16) uint16_t kt[G * RS];
   __shared__ __align__(16) uint16_t vt[G * RS];
   __shared__ __align__(16) float kmn[D], ksc[D], krc[D];
-  __shared__ __align__(16) float vmn[4 * G], vsc[4 * G], vrc[4 * G];  // index m * G + row
+  __shared__ __align__(16) float vmn[D], vsc[D], vrc[D];  // index m * G + row (D / G groups per row)
   // set when some group of the block has a scale below 2^-100; kept in the
   // padding of the first key row (the LDS total stays at 20 KiB)
   int& tiny_scale = *reinterpret_cast<int*>(&kt[D]);
@@ -267,13 +267,13 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
     r_src_tok0 = o.r_src_tok0;
     r_count = o.r_count;
     r_dst_slot0 = o.r_dst_slot0;
-    if (item >= nblk + (r_count + G - 1) / G) return;  // the grid covers the longest sequence
+    if (item >= nblk + (r_count + kCopy - 1) / kCopy) return;  // the grid covers the longest sequence
   }
 
   if (item >= nblk) {
     // ---- residual-window copy: 32 tokens per workgroup
-    const int t0 = (item - nblk) * G;
-    const int n = min(G, r_count - t0);
+    const int t0 = (item - nblk) * kCopy;
+    const int n = min(kCopy, r_count - t0);
     for (int c = tid; c < n * (D / 8); c += 256) {
       const int t = t0 + c / (D / 8), col = (c % (D / 8)) * 8;
       const long long src = u * a.r_src_unit_stride + (long long)(r_src_tok0 + t) * D + col;
@@ -285,23 +285,28 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
   }
 
   // ---- stage the key and value tiles of this block
-  constexpr BlockLayout BL = block_layout(KB, VB);
+  constexpr BlockLayout BL = block_layout(KB, VB, G);
   const int blk = item;
   const int gblk = dst_blk0 + blk;
   uint8_t* const rec =  // this block's record
       a.blocks + record_index(a.page_table, a.page_stride, a.num_pages, a.nb, a.H, u, gblk) * BL.bytes;
   {
-    // 16-byte pieces c = tid and c = tid + 256 of the 32 x 128 tiles
+    // 16-byte pieces tid, tid + 256, ... of the G x 128 tiles (rows 16
+    // apart), all loads issued before the first LDS store
+    constexpr int NP = G / 16;
     const int row = tid / (D / 8), col = (tid % (D / 8)) * 8;
     const long long base = u * a.src_unit_stride + (long long)(src_tok0 + blk * G) * D + row * D + col;
-    const uint4 k0 = *reinterpret_cast<const uint4*>(a.k_src + base);
-    const uint4 k1 = *reinterpret_cast<const uint4*>(a.k_src + base + 16 * D);
-    const uint4 v0 = *reinterpret_cast<const uint4*>(a.v_src + base);
-    const uint4 v1 = *reinterpret_cast<const uint4*>(a.v_src + base + 16 * D);
-    *reinterpret_cast<uint4*>(&kt[row * RS + col]) = k0;
-    *reinterpret_cast<uint4*>(&kt[(row + 16) * RS + col]) = k1;
-    *reinterpret_cast<uint4*>(&vt[row * RS + col]) = v0;
-    *reinterpret_cast<uint4*>(&vt[(row + 16) * RS + col]) = v1;
+    uint4 kx[NP], vx[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      kx[i] = *reinterpret_cast<const uint4*>(a.k_src + base + 16 * i * D);
+      vx[i] = *reinterpret_cast<const uint4*>(a.v_src + base + 16 * i * D);
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      *reinterpret_cast<uint4*>(&kt[(row + 16 * i) * RS + col]) = kx[i];
+      *reinterpret_cast<uint4*>(&vt[(row + 16 * i) * RS + col]) = vx[i];
+    }
     if (tid == 0) tiny_scale = 0;
   }
   __syncthreads();
@@ -346,7 +351,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
         f16_bits_canon(s0) | (static_cast<uint32_t>(f16_bits_canon(s1)) << 16);
     reinterpret_cast<uint32_t*>(rec + BL.k_zero)[tid] =
         f16_bits_canon(mn0) | (static_cast<uint32_t>(f16_bits_canon(mn1)) << 16);
-  } else if (tid < D / 2 + 4 * G) {
+  } else if (tid < D / 2 + D) {
     // value group: row t, channels m*G .. m*G+G-1; index i = m*G + t
     const int i = tid - D / 2;
     const int m = i / G, t = i % G;
@@ -400,10 +405,10 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
     const int w = tid % KW, tg = tid / KW;
     uint32_t word[NT];
     float dev = 0.0f;
-    key_words<KB, BF16, false>(kt, kmn, krc, ksc, w, tg, false, word, dev);
+    key_words<KB, G, BF16, false>(kt, kmn, krc, ksc, w, tg, false, word, dev);
     if (dev > kTieMargin || tiny) {
       asm volatile("" ::: "memory");  // reload the tile: nothing kept live across the passes
-      key_words<KB, BF16, true>(kt, kmn, krc, ksc, w, tg, tiny, word, dev);
+      key_words<KB, G, BF16, true>(kt, kmn, krc, ksc, w, tg, tiny, word, dev);
     }
     uint32_t* const kc = reinterpret_cast<uint32_t*>(rec + BL.k_codes);
 #pragma unroll
@@ -411,16 +416,16 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
   } else {
     // ---- value code words: word w of channel d holds rows w*PV .. w*PV+PV-1;
     // word-major, the D words of one w adjacent.  Thread: channels d0, d0+1
-    // (same channel group) and rows 16*h .. 16*h+15 (16 / PV words each).
+    // (same channel group) and rows (G/2)*h .. (G/2)*h + G/2 - 1.
     const int i0 = tid - 128;
     const int d0 = 2 * (i0 % 64), h = i0 / 64;
-    constexpr int NW = 16 / PV;
+    constexpr int NW = (G / 2) / PV;
     uint32_t w0[NW], w1[NW];
     float dev = 0.0f;
-    value_words<VB, BF16, false>(vt, vmn, vrc, vsc, d0, h, false, w0, w1, dev);
+    value_words<VB, G, BF16, false>(vt, vmn, vrc, vsc, d0, h, false, w0, w1, dev);
     if (dev > kTieMargin || tiny) {
       asm volatile("" ::: "memory");  // reload the tile: nothing kept live across the passes
-      value_words<VB, BF16, true>(vt, vmn, vrc, vsc, d0, h, tiny, w0, w1, dev);
+      value_words<VB, G, BF16, true>(vt, vmn, vrc, vsc, d0, h, tiny, w0, w1, dev);
     }
     uint32_t* const vc = reinterpret_cast<uint32_t*>(rec + BL.v_codes);
 #pragma unroll
@@ -431,15 +436,19 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
 
 template <int KB, int VB, bool BF16>
 hipError_t launch_pack_t(const PackArgs& a, hipStream_t stream) {
-  int items = a.nblk + (a.r_count + G - 1) / G;
+  int items = a.nblk + (a.r_count + kCopy - 1) / kCopy;
   if (a.ragged) {  // a.units units of a.units / a.H sequences: the longest sets the grid
     items = 0;
     for (int i = 0; i < a.units / a.H; ++i)
-      items = max(items, a.op[i].nblk + (a.op[i].r_count + G - 1) / G);
+      items = max(items, a.op[i].nblk + (a.op[i].r_count + kCopy - 1) / kCopy);
   }
   if (items == 0 || a.units == 0) return hipSuccess;
   dim3 grid(items, a.units);
-  hipLaunchKernelGGL((pack_kernel<KB, VB, BF16>), grid, dim3(256), 0, stream, a);
+  if (a.G == 64) {
+    hipLaunchKernelGGL((pack_kernel<KB, VB, BF16, 64>), grid, dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((pack_kernel<KB, VB, BF16, 32>), grid, dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -44,8 +44,8 @@ def valid_slices(n_quant, n_resid, cap, nb, D=128, G=32):
     }
 
 
-def assert_cache_equal(got, want, n_quant, n_resid, cap, nb):
-    sl = valid_slices(n_quant, n_resid, cap, nb)
+def assert_cache_equal(got, want, n_quant, n_resid, cap, nb, G=32):
+    sl = valid_slices(n_quant, n_resid, cap, nb, G=G)
     for name in ARRAYS:
         a, b = sl[name](got[name]), sl[name](want[name])
         assert a.shape == b.shape, (name, a.shape, b.shape)

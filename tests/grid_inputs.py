@@ -13,31 +13,41 @@ Guide", "The Three Structural Innovations of KIVI").
 import numpy as np
 
 
-def _groups(rng, n_groups, G, bits):
+def _groups(rng, n_groups, G, bits, extremes_in_first_half=False):
     qmax = (1 << bits) - 1
     codes = rng.integers(0, qmax + 1, size=(n_groups, G))
-    pos = rng.permutation(G)[:2]
-    lo = rng.integers(0, G, size=n_groups)
-    hi = (lo + 1 + rng.integers(0, G - 1, size=n_groups)) % G
+    span = G
+    if extremes_in_first_half:
+        # codes 0 and qmax only in the first G/2 slots; the second half draws
+        # from 1..qmax-1 with both ends present, so a quantizer that grouped
+        # G/2 elements would get a step of (qmax-2)/qmax of the true one there
+        span = G // 2
+        h = G // 2
+        codes[:, h:] = rng.integers(1, qmax, size=(n_groups, G - h))
+        codes[:, h] = 1
+        codes[:, h + 1] = qmax - 1
+    lo = rng.integers(0, span, size=n_groups)
+    hi = (lo + 1 + rng.integers(0, span - 1, size=n_groups)) % span
     codes[np.arange(n_groups), lo] = 0
     codes[np.arange(n_groups), hi] = qmax
-    del pos
     step = np.exp2(rng.integers(-3, 1, size=(n_groups, 1))).astype(np.float64)
     base = rng.integers(-32, 32, size=(n_groups, 1)) / 8.0
     return base + codes * step
 
 
-def grid_kv(B, H, T, D, G=32, k_bits=2, v_bits=2, seed=0, dtype=np.float16):
+def grid_kv(B, H, T, D, G=32, k_bits=2, v_bits=2, seed=0, dtype=np.float16,
+            extremes_in_first_half=False):
     """Returns K, V as float arrays [B][H][T][D] (values exact in fp16 and
     bf16) with T a multiple of G for the key grid; tokens past the last full
-    block are still grid values, which is harmless."""
+    block are still grid values, which is harmless.  With
+    extremes_in_first_half the grid is exact only for groups of exactly G."""
     rng = np.random.default_rng(seed)
     Tb = (T + G - 1) // G
     # keys: group = (b, h, block, channel) over G tokens
-    kg = _groups(rng, B * H * Tb * D, G, k_bits).reshape(B, H, Tb, D, G)
+    kg = _groups(rng, B * H * Tb * D, G, k_bits, extremes_in_first_half).reshape(B, H, Tb, D, G)
     K = kg.transpose(0, 1, 2, 4, 3).reshape(B, H, Tb * G, D)[:, :, :T]
     # values: group = (b, h, token, channel group) over G channels
-    vg = _groups(rng, B * H * T * (D // G), G, v_bits).reshape(B, H, T, D)
+    vg = _groups(rng, B * H * T * (D // G), G, v_bits, extremes_in_first_half).reshape(B, H, T, D)
     return K.astype(dtype), vg.astype(dtype)
 
 

@@ -52,7 +52,9 @@ def status_of(fn, *a):
     (dict(head_dim=100), kivi.KIVI_ERR_INVALID_ARG),
     (dict(kv_dtype=kivi.KIVI_F32), kivi.KIVI_ERR_INVALID_ARG),
     (dict(head_dim=64), kivi.KIVI_ERR_UNSUPPORTED),
-    (dict(group_size=64, residual_length=128), kivi.KIVI_ERR_UNSUPPORTED),
+    (dict(group_size=16, residual_length=128), kivi.KIVI_ERR_UNSUPPORTED),
+    (dict(group_size=64, residual_length=96), kivi.KIVI_ERR_INVALID_ARG),  # R % G != 0
+    (dict(group_size=64, residual_length=128), kivi.KIVI_OK),
     (dict(batch=300, num_kv_heads=300), kivi.KIVI_ERR_UNSUPPORTED),
     (dict(), kivi.KIVI_OK),
     (dict(k_bits=4, v_bits=2, kv_dtype=kivi.KIVI_BF16, residual_length=32), kivi.KIVI_OK),

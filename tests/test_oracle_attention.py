@@ -38,18 +38,23 @@ def test_window_only_is_plain_attention(oracle_mod, dtype):
     assert np.max(np.abs(out - ref)) < 1e-12
 
 
-@pytest.mark.parametrize("kb,vb,dtype,gq", [(2, 2, "f16", 1), (2, 2, "f16", 4),
-                                            (4, 4, "bf16", 4), (2, 4, "f16", 2)])
-def test_grid_exact_cache_is_plain_attention(oracle_mod, kb, vb, dtype, gq):
+@pytest.mark.parametrize("kb,vb,dtype,gq,G", [(2, 2, "f16", 1, 32), (2, 2, "f16", 4, 32),
+                                              (4, 4, "bf16", 4, 32), (2, 4, "f16", 2, 32),
+                                              (2, 2, "f16", 1, 64), (4, 2, "bf16", 4, 64),
+                                              (2, 4, "f16", 8, 64)])
+def test_grid_exact_cache_is_plain_attention(oracle_mod, kb, vb, dtype, gq, G):
     # Grid-exact groups dequantize to their inputs, so attention over the
     # packed cache equals plain attention on the raw tensors.  A wrong code
     # index, a transposed operand, a wrong kv-head mapping or a dropped
-    # zero-point term would each break the equality.
+    # zero-point term would each break the equality.  The grid is drawn per
+    # group of G, so at G = 64 a cache that grouped 32 tokens or channels (or
+    # read a scale of the wrong half) would not reproduce it either.
     B, H, D, T, R = 2, 2, 128, 3 * 64 + 45, 64
-    K, V = grid_kv(B, H, T, D, k_bits=kb, v_bits=vb, seed=kb * 7 + gq)
+    K, V = grid_kv(B, H, T, D, G=G, k_bits=kb, v_bits=vb, seed=kb * 7 + gq + G,
+                   extremes_in_first_half=G > 32)
     rng = np.random.default_rng(gq)
     q = _rand(rng, (B, H * gq, D), dtype)
-    c = oracle_mod.OracleCache(B, H, D, T, kb, vb, 32, R, 0 if dtype == "f16" else 1)
+    c = oracle_mod.OracleCache(B, H, D, T, kb, vb, G, R, 0 if dtype == "f16" else 1)
     c.append(to_bits(K, dtype), to_bits(V, dtype))
     assert (c.n_quant, c.n_resid) == (192, 45)
     out = c.decode_attn(to_bits(q, dtype), SCALE)
