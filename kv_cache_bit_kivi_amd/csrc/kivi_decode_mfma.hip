@@ -366,7 +366,7 @@ typedef const __attribute__((address_space(1))) void glb_void_t;
 
 __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
   // address-space conversions need C-style casts
-  __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)lds_dst, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)lds_dst, 16, 0, 2);
 }
 
 // Records of streams g0 .. g0 + 3 of unit u (unit-major, or through the

@@ -26,6 +26,23 @@ constexpr int D = kHeadDim;
 constexpr int kCopy = 32;  // window tokens copied per workgroup
 constexpr int RS = D + 8;  // LDS row stride in 16-bit elements (272 bytes)
 
+// Streaming accesses: the pack reads each input byte once and writes each
+// record byte once, so both go out with the non-temporal hint.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+template <typename T>
+__device__ __forceinline__ void store_stream(T* p, T v) {
+  __builtin_nontemporal_store(v, p);
+}
+__device__ __forceinline__ void store_stream2(uint32_t* p, uint32_t x, uint32_t y) {
+  const u32x2_t v = {x, y};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t*>(p));
+}
+
 // fp16 bit pattern of a binary32 value, nearest-even; zero is stored as +0.
 __device__ __forceinline__ uint16_t f16_bits_canon(float f) {
   return f == 0.0f ? uint16_t(0) : __half_as_ushort(__float2half_rn(f));
@@ -299,8 +316,8 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
     uint4 kx[NP], vx[NP];
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      kx[i] = *reinterpret_cast<const uint4*>(a.k_src + base + 16 * i * D);
-      vx[i] = *reinterpret_cast<const uint4*>(a.v_src + base + 16 * i * D);
+      kx[i] = load_stream16(a.k_src + base + 16 * i * D);
+      vx[i] = load_stream16(a.v_src + base + 16 * i * D);
     }
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
@@ -347,10 +364,10 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
     if (t0 || t1) tiny_scale = 1;
     kmn[p2] = mn0; ksc[p2] = s0; krc[p2] = r0;
     kmn[p2 + 1] = mn1; ksc[p2 + 1] = s1; krc[p2 + 1] = r1;
-    reinterpret_cast<uint32_t*>(rec + BL.k_scale)[tid] =
-        f16_bits_canon(s0) | (static_cast<uint32_t>(f16_bits_canon(s1)) << 16);
-    reinterpret_cast<uint32_t*>(rec + BL.k_zero)[tid] =
-        f16_bits_canon(mn0) | (static_cast<uint32_t>(f16_bits_canon(mn1)) << 16);
+    store_stream(reinterpret_cast<uint32_t*>(rec + BL.k_scale) + tid,
+                 f16_bits_canon(s0) | (static_cast<uint32_t>(f16_bits_canon(s1)) << 16));
+    store_stream(reinterpret_cast<uint32_t*>(rec + BL.k_zero) + tid,
+                 f16_bits_canon(mn0) | (static_cast<uint32_t>(f16_bits_canon(mn1)) << 16));
   } else if (tid < D / 2 + D) {
     // value group: row t, channels m*G .. m*G+G-1; index i = m*G + t
     const int i = tid - D / 2;
@@ -392,8 +409,8 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
     vmn[i] = mn;
     vsc[i] = s;
     vrc[i] = rcp;
-    reinterpret_cast<uint16_t*>(rec + BL.v_scale)[i] = f16_bits_canon(s);  // [m][row]
-    reinterpret_cast<uint16_t*>(rec + BL.v_zero)[i] = f16_bits_canon(mn);
+    store_stream(reinterpret_cast<uint16_t*>(rec + BL.v_scale) + i, f16_bits_canon(s));  // [m][row]
+    store_stream(reinterpret_cast<uint16_t*>(rec + BL.v_zero) + i, f16_bits_canon(mn));
   }
   lds_barrier();
 
@@ -412,7 +429,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
     }
     uint32_t* const kc = reinterpret_cast<uint32_t*>(rec + BL.k_codes);
 #pragma unroll
-    for (int j = 0; j < NT; ++j) kc[(tg + j * TS) * KW + w] = word[j];
+    for (int j = 0; j < NT; ++j) store_stream(kc + (tg + j * TS) * KW + w, word[j]);
   } else {
     // ---- value code words: word w of channel d holds rows w*PV .. w*PV+PV-1;
     // word-major, the D words of one w adjacent.  Thread: channels d0, d0+1
@@ -430,7 +447,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
     uint32_t* const vc = reinterpret_cast<uint32_t*>(rec + BL.v_codes);
 #pragma unroll
     for (int k = 0; k < NW; ++k)
-      *reinterpret_cast<uint2*>(&vc[(h * NW + k) * D + d0]) = make_uint2(w0[k], w1[k]);
+      store_stream2(&vc[(h * NW + k) * D + d0], w0[k], w1[k]);
   }
 }
 
