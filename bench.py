@@ -151,9 +151,14 @@ def run(args):
         # one pass of the hot path over every layer, phase by phase: the prefix
         # of every layer packed, then every layer's decode token appended, then
         # decode attention for every layer.  ev: four HIP events bracketing the
-        # three phase groups, recorded on the stream every kernel is launched on
+        # three phase groups, recorded on the stream every kernel is launched on.
+        # Consecutive steps share a boundary (the end of one step's decode is
+        # the start of the next step's pack): each record is a marker the next
+        # launch waits for, so one event per boundary keeps the steps' gaps
+        # to one marker each.
         rec = (lambda n: ev[n].record(stream)) if ev is not None else (lambda n: None)
-        rec(0)
+        if ev is not None and not getattr(ev, "shared_start", False):
+            rec(0)
         for L in layers:
             L["cache"].reset()
             if lens is None:
@@ -180,7 +185,16 @@ def run(args):
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    class Bounds(list):
+        shared_start = False
+
+    # step k's phase bounds are boundary events 3k .. 3k+3
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(3 * args.steps + 1)]
+    events = []
+    for k in range(args.steps):
+        e = Bounds(bounds[3 * k:3 * k + 4])
+        e.shared_start = k > 0  # recorded as the previous step's end
+        events.append(e)
     # timed region: exactly `steps` steps between two synchronizations
     t0 = time.perf_counter()
     for k in range(args.steps):
