@@ -118,7 +118,9 @@ typedef struct {
   int32_t max_tokens;      /* per-sequence capacity T_max >= 1 */
   int32_t k_bits;          /* 2 or 4 */
   int32_t v_bits;          /* 2 or 4 */
-  int32_t group_size;      /* G. Kernels: 32 */
+  int32_t group_size;      /* G. Kernels: 32 or 64 (64: not with 8 query
+                              heads per kv head, which decode_attn rejects
+                              with KIVI_ERR_UNSUPPORTED) */
   int32_t residual_length; /* R; positive multiple of G, at most 1024 */
   int32_t kv_dtype;        /* kivi_dtype: KIVI_F16 or KIVI_BF16 (inputs,
                               residual window and q) */
