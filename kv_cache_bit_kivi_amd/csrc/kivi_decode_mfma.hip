@@ -468,6 +468,9 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
   const int hq = lc >> 2;  // head of this lane's B / C columns
   const int jt = lc & 3;
 
+  // The value wave waits at every step's barrier for this wave's softmax, so
+  // this wave issues ahead of other workgroups' waves on its SIMD.
+  __builtin_amdgcn_s_setprio(1);
   // the first stage's loads go out before q is read: their latencies overlap
   issue_kstage<KB, VB, GT, PAGED>(a, u, gb, min(4, ge - gb), smem, smem + S::offKM0);
   // q'' = q * 2^(lf(e) - 3) as fp16 pairs for head hq, channels 32*lk ..

@@ -1,6 +1,8 @@
 """Parity at the full workload sizes, in the launch configuration the benchmark
-times: bulk append of the prefix (one pack launch), append of the decode token
-(window flush + copy), then decode attention with the default split planner.
+times: bulk append of the prefix (one pack launch), flush of the full window
+(one pack launch), then the decode step kivi_append_decode_attn (token append
+and split-K attention in one launch, then the merge) with the default split
+planner.
 
 The oracle runs on sampled (batch, kv head) units alone; their packed arrays
 must match bit for bit and the attention outputs of their query heads must be
@@ -31,9 +33,10 @@ def test_fullsize_sampled_units(name):
                            group_size=w.group_size, residual_length=w.residual_length,
                            dtype=w.dtype, device=DEV)
     cache.append(x.k[:, :, :T].contiguous(), x.v[:, :, :T].contiguous())
-    cache.append(x.k[:, :, T:].contiguous(), x.v[:, :, T:].contiguous())
+    cache.flush()
     scale = 1.0 / np.sqrt(w.head_dim)
-    out = cache.decode_attn(x.q.contiguous(), scale)
+    out = cache.append_decode_attn(x.k[:, :, T:].contiguous(), x.v[:, :, T:].contiguous(),
+                                   x.q.contiguous(), scale)
     torch.cuda.synchronize()
     v = cache.view()
     assert (v.n_quant, v.n_resid) == (T, 1)  # every workload has T a multiple of R
