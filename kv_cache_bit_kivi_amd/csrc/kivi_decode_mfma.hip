@@ -420,8 +420,10 @@ __device__ __forceinline__ void issue_kstage(const DecodeArgs& a, long long u, i
             dst + gi * S::kGroupPad + j * 1024);
   }
   // scale and zero of the stream's block: 256 bytes per stream and field, 16
-  // lanes per stream
-  const uint8_t* const meta = lane_record(rp, lane) + (lane & 15) * 16;
+  // lanes per stream.  Stream i's 16-byte chunk j lands in LDS slot
+  // (j + 4 i) mod 16 of the stream's 256 bytes: the key wave reads chunk
+  // 4 lk + c of four streams at once, which then fall on distinct banks.
+  const uint8_t* const meta = lane_record(rp, lane) + ((lane - 4 * (lane >> 4)) & 15) * 16;
   dma16(meta + BL.k_scale, meta_dst);
   dma16(meta + BL.k_zero, meta_dst + 4 * D * 2);
 }
@@ -515,8 +517,9 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
 
     const int ga = lc >> 2;  // stream of this lane's A row
     const int gc = lc & 3;   // stream of this lane's B column
-    const u32x4* sBp = reinterpret_cast<const u32x4*>(meta + gc * D * 2 + 64 * lk);
-    const u32x4* zBp = reinterpret_cast<const u32x4*>(meta + 4 * D * 2 + gc * D * 2 + 64 * lk);
+    // chunk 4 lk + c of stream gc sits in slot 4 ((lk + gc) mod 4) + c
+    const u32x4* sBp = reinterpret_cast<const u32x4*>(meta + gc * D * 2 + 64 * ((lk + gc) & 3));
+    const u32x4* zBp = reinterpret_cast<const u32x4*>(meta + 4 * D * 2 + gc * D * 2 + 64 * ((lk + gc) & 3));
     const uint8_t* krow = smem + ga * S::kGroupPad + (lc & 3) * S::kRow + 4 * KL * lk;
     uint32_t kw[8][KL];
 #pragma unroll
@@ -696,8 +699,11 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
     }
     for (int gs = 0; gs < ns; ++gs) {
       const int w = (VB == 2) ? (lk >> 1) : lk;
-      const u32x4* vp = reinterpret_cast<const u32x4*>(vstage + gs * S::vGroup + (w * D + 8 * lc) * 4);
-      const u32x4 v0 = vp[0], v1 = vp[1];
+      // words of channels 4 lc .. 4 lc + 3 and 64 + 4 lc .. 64 + 4 lc + 3: the
+      // 16 lanes of a read cover 256 contiguous bytes
+      const uint8_t* vrow = vstage + gs * S::vGroup + (w * D + 4 * lc) * 4;
+      const u32x4 v0 = *reinterpret_cast<const u32x4*>(vrow);
+      const u32x4 v1 = *reinterpret_cast<const u32x4*>(vrow + 64 * 4);
       const int vmo = ((gs * 4 + mcol) * G + 8 * lk) * 2;
       const u32x4 vs = *reinterpret_cast<const u32x4*>(vstage + S::offVS + vmo);
       const u32x4 vz = *reinterpret_cast<const u32x4*>(vstage + S::offVZ + vmo);
@@ -736,19 +742,18 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
   for (int e = 0; e < 4; ++e) z = fmaf(zcls[e], 1.0f / static_cast<float>(1 << VS::lf(e)), z);
   z = swap_sum<16>(z);
   z = swap_sum<32>(z);  // sum over the 4 row chunks: head hq, channel group lc & 3
-  if ((lc & 3) == lk && hq < NQ) {
-    // rows 4*lk + r of channel block be = channel 32*lk + 8*r + be
+  // Row 4 lk + r of product be is channel 16 lk + 4 r + be (be < 4) or
+  // 64 + 16 lk + 4 r + be - 4 (be >= 4), of channel group lk / 2 or
+  // 2 + lk / 2; the lane whose column holds that group writes it.
+  const int mh = (lc & 3) == (lk >> 1) ? 0 : (lc & 3) == 2 + (lk >> 1) ? 1 : -1;
+  if (mh >= 0 && hq < NQ) {
     float* P = a.partial + (((long long)b * a.Hq + kvh * NQ + hq) * a.n_split + split) * (D + 2);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      f32x4 x0, x1;
+      f32x4 x;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x0[i] = fmaf(o[i][r], v_unscale, z);
-        x1[i] = fmaf(o[4 + i][r], v_unscale, z);
-      }
-      *reinterpret_cast<f32x4*>(P + 2 + 32 * lk + 8 * r) = x0;
-      *reinterpret_cast<f32x4*>(P + 2 + 32 * lk + 8 * r + 4) = x1;
+      for (int i = 0; i < 4; ++i) x[i] = fmaf(mh == 0 ? o[i][r] : o[4 + i][r], v_unscale, z);
+      *reinterpret_cast<f32x4*>(P + 2 + 64 * mh + 16 * lk + 4 * r) = x;
     }
   }
 }
