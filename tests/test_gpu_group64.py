@@ -27,7 +27,9 @@ CASES = [("mha",         2, 2, 2,  300,  2, 2, torch.float16,  128),
          ("gq2_k2v4",    2, 1, 2,  1000, 2, 4, torch.float16,  64),
          ("gq4_k4v2",    1, 2, 8,  129,  4, 2, torch.float16,  64),
          ("T64",         1, 1, 4,  64,   2, 2, torch.float16,  64),
-         ("T1",          1, 1, 1,  1,    2, 2, torch.float16,  64)]
+         ("T1",          1, 1, 1,  1,    2, 2, torch.float16,  64),
+         ("r1024_flush", 1, 1, 4,  2048, 2, 2, torch.float16,  1024),
+         ("r256_gq4",    2, 1, 4,  900,  2, 2, torch.bfloat16, 256)]
 
 
 def _setup(case, extra=1):

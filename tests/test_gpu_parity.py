@@ -31,7 +31,13 @@ CASES = [("c0",            1, 1, 1, 1024, 2, 2, torch.float16, 128),
          ("gq4_k4v2_r32",  1, 1, 4, 333, 4, 2, torch.float16, 32),
          ("gq4_window",    1, 2, 8, 100, 2, 2, torch.bfloat16, 128),
          ("gq4_T129",      2, 1, 4, 129, 2, 2, torch.float16, 128),
-         ("gq4_long",      1, 1, 4, 4096, 2, 2, torch.float16, 128)]
+         ("gq4_long",      1, 1, 4, 4096, 2, 2, torch.float16, 128),
+         # windows up to the largest accepted (R = 1024): window-only, a full
+         # window that the decode token flushes, multi-head, 8 heads per kv head
+         ("r1024_window",  1, 2, 8, 1000, 2, 2, torch.float16, 1024),
+         ("r1024_flush",   1, 1, 2, 2048, 2, 2, torch.bfloat16, 1024),
+         ("r256_mha_4b",   2, 2, 2, 700, 4, 4, torch.float16, 256),
+         ("r1024_gq8",     1, 1, 8, 1500, 2, 2, torch.float16, 1024)]
 IDS = [c[0] for c in CASES]
 
 
