@@ -196,7 +196,7 @@ kivi_status kivi_append_varlen(kivi_cache* cache, const void* k, const void* v,
  * outside [0, batch)). */
 kivi_status kivi_cache_reset_sequences(kivi_cache* cache, const int32_t* seqs, int32_t count);
 
-/* Paged block records.  With a table set, block g (tokens 32 g .. 32 g + 31)
+/* Paged block records.  With a table set, block g (tokens G g .. G g + G - 1)
  * of sequence b lives in page P = table[b * page_stride + g] of the block
  * region, and kv head h of it at record P * H + h (the region then holds
  * num_pages pages of H records; the default is the unit-major layout,
@@ -251,6 +251,7 @@ kivi_status kivi_decode_attn_workspace_bytes(const kivi_cache* cache,
  * sequence without tokens gets zeros.  The splits are then planned for the
  * longest sequence, and each launch pair covers 64 sequences.
  * Errors: INVALID_ARG (nulls, Hq not a positive multiple of H, bad dtype),
+ * UNSUPPORTED (a ratio Hq / H other than 1, 2, 4 or 8; 8 with G = 64),
  * EMPTY (no sequence holds a token), BUFFER_TOO_SMALL (ws_bytes below the
  * workspace query), HIP. */
 kivi_status kivi_decode_attn(const kivi_cache* cache, const void* q,
