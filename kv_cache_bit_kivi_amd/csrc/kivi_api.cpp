@@ -622,6 +622,23 @@ kivi_status decode_launch(kivi_cache* c, const void* q, int32_t num_q_heads, flo
         // fill a round with the shorter ones).
         long long best = -1;
         const int n_cand = c->ragged ? (nqg + 3) / 4 : max_split;
+        // Ragged caches: the plans whose whole grid (the splits past a short
+        // sequence's end included) fits in one round of resident slots are
+        // preferred (a second round, even of short or empty splits, was
+        // measured slower), and among them the one with the
+        // smallest estimated time (steps per split + set-up) x (time of one
+        // step).  A step takes the time of a lone workgroup or, with k
+        // workgroups sharing a CU, k times the per-workgroup share of a fully
+        // occupied CU, whichever is longer: the split kernel is bound by the
+        // vector and matrix issue of its SIMDs.  In units of that share, a
+        // lone workgroup's step is kLone x (workgroups per CU at full
+        // occupancy): about 2.35 us against 3.7-4.1 us for a step of a full
+        // CU on c2-shaped data.  Measured on ragged c2 / c3 batches: 178 / 135
+        // us for the rounds model above, 148 / 108 us for the plans this
+        // picks.
+        constexpr double kSetup = 1.5, kLone = 0.57;
+        const double lone = kLone * wgs_per_cu;
+        double best1 = -1.0;
         for (int i = 1; i <= n_cand; ++i) {
           int g, np;
           if (c->ragged) {
@@ -636,10 +653,22 @@ kivi_status decode_launch(kivi_cache* c, const void* q, int32_t num_q_heads, flo
             work = 0;
             for (int b = 0; b < c->cfg.batch; ++b) work += (c->sq[b] / G + g - 1) / g;
             work *= c->cfg.num_kv_heads;
+            // (a ragged launch covers at most kDecodeChunk sequences)
+            const long long grid = (long long)np * std::min(c->cfg.batch, kivi::kDecodeChunk) * c->cfg.num_kv_heads;
+            if (grid <= slots) {
+              const double cost1 = (g / 4 + kSetup) * std::max(lone, work / (double)c->cu_count);
+              if (best1 < 0.0 || cost1 < best1) {
+                best1 = cost1;
+                gps = g;
+                n_split_packed = np;
+              }
+              continue;
+            }
+            if (best1 >= 0.0) continue;  // a one-round plan exists
           }
           const long long rounds = (work + slots - 1) / slots;
           const long long cost = rounds * (g / 4 + 1);  // +1: per-wave set-up and partial
-          if (best < 0 || cost < best) {
+          if (best1 < 0.0 && (best < 0 || cost < best)) {
             best = cost;
             gps = g;
             n_split_packed = np;
