@@ -633,9 +633,9 @@ kivi_status decode_launch(kivi_cache* c, const void* q, int32_t num_q_heads, flo
         // vector and matrix issue of its SIMDs.  In units of that share, a
         // lone workgroup's step is kLone x (workgroups per CU at full
         // occupancy): about 2.35 us against 3.7-4.1 us for a step of a full
-        // CU on c2-shaped data.  Measured on ragged c2 / c3 batches: 178 / 135
-        // us for the rounds model above, 148 / 108 us for the plans this
-        // picks.
+        // CU on c2-shaped data.  Interleaved runs on ragged batches: c3 135-139
+        // -> 115-125 us and c1 36.3-36.8 -> 33.0-33.9 us against the rounds
+        // model above; c2 unchanged within noise.
         constexpr double kSetup = 1.5, kLone = 0.57;
         const double lone = kLone * wgs_per_cu;
         double best1 = -1.0;
