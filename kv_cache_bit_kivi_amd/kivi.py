@@ -233,10 +233,23 @@ class KiviCache:
     def _stream(self, stream):
         return (self.torch.cuda.current_stream(self.device) if stream is None else stream).cuda_stream
 
+    def _check_tensor(self, t, dtype, what):
+        if not (t.is_contiguous() and t.dtype == dtype and t.device == self.device):
+            raise ValueError(f"{what} must be a contiguous {dtype} tensor on {self.device} "
+                             f"(got {t.dtype} on {t.device}, contiguous={t.is_contiguous()})")
+
     def _check_kv(self, t, n):
         c = self.cfg
-        assert t.is_contiguous() and t.dtype == self.dtype and t.device == self.device
-        assert tuple(t.shape) == (c.batch, c.num_kv_heads, n, c.head_dim), t.shape
+        self._check_tensor(t, self.dtype, "k/v")
+        if tuple(t.shape) != (c.batch, c.num_kv_heads, n, c.head_dim):
+            raise ValueError(f"k/v shape {tuple(t.shape)} is not "
+                             f"{(c.batch, c.num_kv_heads, n, c.head_dim)}")
+
+    def _check_q(self, q):
+        c = self.cfg
+        self._check_tensor(q, self.dtype, "q")
+        if q.dim() != 3 or q.shape[0] != c.batch or q.shape[2] != c.head_dim:
+            raise ValueError(f"q shape {tuple(q.shape)} is not ({c.batch}, Hq, {c.head_dim})")
 
     def append(self, k, v, stream=None):
         n = k.shape[2]
@@ -249,7 +262,8 @@ class KiviCache:
         n_max = k.shape[2]
         self._check_kv(k, n_max)
         self._check_kv(v, n_max)
-        assert len(n_tokens) == self.cfg.batch
+        if len(n_tokens) != self.cfg.batch:
+            raise ValueError(f"n_tokens has {len(n_tokens)} entries, batch is {self.cfg.batch}")
         kivi_append_varlen(self.handle, k.data_ptr(), v.data_ptr(), n_tokens, n_max,
                            self._stream(stream))
 
@@ -261,8 +275,9 @@ class KiviCache:
             kivi_cache_set_page_table(self.handle, 0, 0, 0)
             return
         t = self.torch
-        assert table.dtype == t.int32 and table.is_contiguous() and table.device == self.device
-        assert table.dim() == 2 and table.shape[0] == self.cfg.batch
+        self._check_tensor(table, t.int32, "table")
+        if table.dim() != 2 or table.shape[0] != self.cfg.batch:
+            raise ValueError(f"table shape {tuple(table.shape)} is not ({self.cfg.batch}, page_stride)")
         kivi_cache_set_page_table(self.handle, table.data_ptr(), table.shape[1], num_pages)
         self._page_table = table
 
@@ -300,9 +315,8 @@ class KiviCache:
     def decode_attn(self, q, softmax_scale, out=None, out_dtype=None, stream=None):
         torch = self.torch
         c = self.cfg
-        assert q.is_contiguous() and q.dtype == self.dtype and q.device == self.device
+        self._check_q(q)
         B, Hq, D = q.shape
-        assert B == c.batch and D == c.head_dim
         out_dtype = torch.float32 if out_dtype is None else out_dtype
         if out is None:
             out = torch.empty(B, Hq, D, dtype=out_dtype, device=self.device)
@@ -320,9 +334,8 @@ class KiviCache:
         c = self.cfg
         self._check_kv(k_new, 1)
         self._check_kv(v_new, 1)
-        assert q.is_contiguous() and q.dtype == self.dtype and q.device == self.device
+        self._check_q(q)
         B, Hq, D = q.shape
-        assert B == c.batch and D == c.head_dim
         out_dtype = torch.float32 if out_dtype is None else out_dtype
         if out is None:
             out = torch.empty(B, Hq, D, dtype=out_dtype, device=self.device)

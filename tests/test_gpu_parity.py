@@ -255,3 +255,22 @@ def test_tiny_scales_bf16_bitexact(bits):
     ref.append(bits16(kk), bits16(vv))
     assert ref.n_quant == T
     _compare(cache, ref)
+
+
+def test_binding_rejects_malformed_tensors():
+    # the KiviCache convenience layer checks dtype, layout and shape before
+    # calling the C ABI (which validates the arguments it can see)
+    cache = kivi.KiviCache(2, 2, 64, device=DEV)
+    good = torch.zeros(2, 2, 8, 128, dtype=torch.float16, device=DEV)
+    with pytest.raises(ValueError):
+        cache.append(good.to(torch.bfloat16), good)
+    with pytest.raises(ValueError):
+        cache.append(good.transpose(2, 3), good)
+    with pytest.raises(ValueError):
+        cache.append(good[:1].contiguous(), good[:1].contiguous())
+    with pytest.raises(ValueError):
+        cache.append_varlen(good, good, [8])
+    cache.append(good, good)
+    with pytest.raises(ValueError):
+        cache.decode_attn(torch.zeros(2, 4, 64, dtype=torch.float16, device=DEV), 0.1)
+    assert (cache.n_quant, cache.n_resid) == (0, 8)
