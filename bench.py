@@ -264,7 +264,19 @@ def cpu_baseline(w, layers, lens=None):
     return {"value": b / t / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{done} batch rows (all {w.kv_heads} kv heads each, cycling through the "
                       f"{w.batch} rows of layer 0), one step each (prefix pack, decode-token "
-                      f"append, decode attention); {t:.1f} s of oracle time"}
+                      f"append, decode attention); {t:.1f} s of oracle time; host CPU: "
+                      f"{cpu_model()}, {os.cpu_count()} logical CPUs visible"}
+
+
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), or "unknown"."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
