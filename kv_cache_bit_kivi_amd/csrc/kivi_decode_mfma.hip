@@ -667,6 +667,13 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
   const int lc = lane & 15, lk = lane >> 4;
   const int hq = lc >> 2;
   const int mcol = lc & 3;  // channel group of this lane's B column
+  // With fewer than 3 heads per kv head, head slots hq >= NQ are free: slot
+  // NQ + h carries the lo half of head h's p * S, so one product per channel
+  // block takes both halves (half the products); the two columns' sums are
+  // added once at the end.  With 4 heads each column holds hi, then lo.
+  constexpr bool kHiLoCols = NQ <= 2;
+  const int hsrc = kHiLoCols ? hq % NQ : hq;  // head whose probabilities this column takes
+  const int part = kHiLoCols ? hq / NQ : 0;   // 0: hi, 1: lo, 2 and 3 (NQ = 1): unused
   uint8_t* const vbase = smem + S::offV0;
   issue_vstage<KB, VB, GT, PAGED>(a, u, gb, min(4, ge - gb), vbase);
   constexpr float v_unscale = static_cast<float>(1 << (24 - VS::F));  // product -> output
@@ -690,7 +697,7 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
     }
     wave_lds_sync();
     const float* hp = reinterpret_cast<const float*>(smem + S::offP0 + (step & 1) * S::pBytes);
-    const float alpha = hp[S::offAlpha / 4 + hq];
+    const float alpha = hp[S::offAlpha / 4 + hsrc];
     if (__any(alpha != 1.0f)) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) o[i] *= alpha;
@@ -710,7 +717,7 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
       // p of tokens 8*lk .. 8*lk+7 (pair e: tokens 2e, 2e+1); B = p * S as
       // fp16 hi + lo of the binary32 product (the probabilities are not exact
       // in fp16, so the product is formed in binary32 and split)
-      const float* prow = hp + (gs * GQ + hq) * kRowP + 8 * lk;
+      const float* prow = hp + (gs * GQ + hsrc) * kRowP + 8 * lk;
       const f32x4 p0 = *reinterpret_cast<const f32x4*>(prow);
       const f32x4 p1 = *reinterpret_cast<const f32x4*>(prow + 4);
       const float p[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
@@ -730,10 +737,19 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
 #pragma unroll
       for (int be = 0; be < 8; ++be)
         av[be] = (VB == 2) ? codes8<2>(vc[be], lk & 1) : codes8<4>(vc[be], false);
+      if constexpr (kHiLoCols) {
+        u32x4 b4;
 #pragma unroll
-      for (int be = 0; be < 8; ++be) o[be] = mfma(av[be], bph, o[be]);
+        for (int e = 0; e < 4; ++e) b4[e] = part == 0 ? h4[e] : part == 1 ? l4[e] : 0u;
+        const half8_t bp = as_h8(b4);
 #pragma unroll
-      for (int be = 0; be < 8; ++be) o[be] = mfma(av[be], bpl, o[be]);
+        for (int be = 0; be < 8; ++be) o[be] = mfma(av[be], bp, o[be]);
+      } else {
+#pragma unroll
+        for (int be = 0; be < 8; ++be) o[be] = mfma(av[be], bph, o[be]);
+#pragma unroll
+        for (int be = 0; be < 8; ++be) o[be] = mfma(av[be], bpl, o[be]);
+      }
     }
   }
 
@@ -742,6 +758,13 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
   for (int e = 0; e < 4; ++e) z = fmaf(zcls[e], 1.0f / static_cast<float>(1 << VS::lf(e)), z);
   z = swap_sum<16>(z);
   z = swap_sum<32>(z);  // sum over the 4 row chunks: head hq, channel group lc & 3
+  if constexpr (kHiLoCols) {
+    // the lo column of head hq (< NQ) is 4 NQ lanes further in the row of 16
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[i][r] += __shfl_down(o[i][r], 4 * NQ, 16);
+  }
   // Row 4 lk + r of product be is channel 16 lk + 4 r + be (be < 4) or
   // 64 + 16 lk + 4 r + be - 4 (be >= 4), of channel group lk / 2 or
   // 2 + lk / 2; the lane whose column holds that group writes it.
