@@ -118,9 +118,7 @@ typedef struct {
   int32_t max_tokens;      /* per-sequence capacity T_max >= 1 */
   int32_t k_bits;          /* 2 or 4 */
   int32_t v_bits;          /* 2 or 4 */
-  int32_t group_size;      /* G. Kernels: 32 or 64 (64: not with 8 query
-                              heads per kv head, which decode_attn rejects
-                              with KIVI_ERR_UNSUPPORTED) */
+  int32_t group_size;      /* G. Kernels: 32 or 64 */
   int32_t residual_length; /* R; positive multiple of G, at most 1024 */
   int32_t kv_dtype;        /* kivi_dtype: KIVI_F16 or KIVI_BF16 (inputs,
                               residual window and q) */
@@ -251,7 +249,7 @@ kivi_status kivi_decode_attn_workspace_bytes(const kivi_cache* cache,
  * sequence without tokens gets zeros.  The splits are then planned for the
  * longest sequence, and each launch pair covers 64 sequences.
  * Errors: INVALID_ARG (nulls, Hq not a positive multiple of H, bad dtype),
- * UNSUPPORTED (a ratio Hq / H other than 1, 2, 4 or 8; 8 with G = 64),
+ * UNSUPPORTED (a ratio Hq / H other than 1, 2, 4 or 8),
  * EMPTY (no sequence holds a token), BUFFER_TOO_SMALL (ws_bytes below the
  * workspace query), HIP. */
 kivi_status kivi_decode_attn(const kivi_cache* cache, const void* q,

@@ -326,8 +326,11 @@ size_t workspace_bytes_for(const kivi_cache* c, int hq, int n_split) {
   return (size_t)c->cfg.batch * hq * n_split * (c->cfg.head_dim + 2) * sizeof(float);
 }
 
+// Largest split count a decode launch can use: the kernels split the token
+// axis into 32-token streams (a block of G = 32, or half a block of G = 64),
+// the packed ones plus the window's.
 int max_items(const kivi_cache* c) {
-  return c->cap / c->cfg.group_size + c->cfg.residual_length / c->cfg.group_size;
+  return c->cap / kivi::kStream + c->cfg.residual_length / kivi::kStream;
 }
 
 }  // namespace
@@ -562,8 +565,6 @@ kivi_status check_decode_args(const kivi_cache* c, const void* q, int32_t num_q_
   const int gq = num_q_heads / c->cfg.num_kv_heads;
   if (gq != 1 && gq != 2 && gq != 4 && gq != 8)
     return fail(KIVI_ERR_UNSUPPORTED, "query heads per kv head must be 1, 2, 4 or 8 (got %d)", gq);
-  if (gq == 8 && c->cfg.group_size != kivi::kGroup)
-    return fail(KIVI_ERR_UNSUPPORTED, "8 query heads per kv head need group_size %d", kivi::kGroup);
   size_t need = 0;
   kivi_decode_attn_workspace_bytes(c, num_q_heads, &need);
   if (ws_bytes < need)
@@ -690,6 +691,10 @@ kivi_status decode_launch(kivi_cache* c, const void* q, int32_t num_q_heads, flo
     n_split = (n_items + per - 1) / per;
   }
 
+  // the workspace query sized the partials for at most this many splits
+  if (n_split > std::min(kivi::kMaxSplits, max_items(c)))
+    return fail(KIVI_ERR_UNSUPPORTED, "internal: %d planned splits exceed the workspace bound %d", n_split,
+                std::min(kivi::kMaxSplits, max_items(c)));
   kivi::DecodeArgs a{};
   a.blocks = c->blocks;
   a.k_resid = c->k_resid;

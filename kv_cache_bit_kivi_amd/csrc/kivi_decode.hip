@@ -46,16 +46,20 @@ __device__ __forceinline__ uint32_t code_at(uint32_t word, int i) {
 
 // ---------------------------------------------------------------------------
 // Reference-structured VALU kernel: every element is dequantized in fp32 and
-// both products run on the vector ALUs.
-template <int KB, int VB, bool BF16, int GQ>
+// both products run on the vector ALUs.  Work items are 32-token streams: a
+// block of GT = 32 tokens, or half of a block of GT = 64 (whose key scale and
+// zero both halves share; its key rows, value word rows and value scale/zero
+// rows of the half start at row 32 * half).
+template <int KB, int VB, bool BF16, int GQ, int GT>
 __global__ __launch_bounds__(256) void decode_split_valu(DecodeArgs a) {
   constexpr int PK = 32 / KB, KW = D / PK;
   constexpr int PV = 32 / VB;
-  constexpr BlockLayout BL = block_layout(KB, VB);
+  constexpr BlockLayout BL = block_layout(KB, VB, GT);
+  constexpr int SPB = GT / kStream;  // streams per block
 
   __shared__ float qs[GQ][D];
   __shared__ float kS[D], kZ[D];
-  __shared__ float vS[4 * G], vZ[4 * G];  // [m][row]
+  __shared__ float vS[D], vZ[D];          // [channel group of GT][row of the block]
   __shared__ float sc[GQ][G];             // scores, then probabilities
   __shared__ float st_m[GQ], st_l[GQ], st_a[GQ];
   __shared__ float ored[GQ][D];
@@ -85,7 +89,7 @@ __global__ __launch_bounds__(256) void decode_split_valu(DecodeArgs a) {
 #pragma unroll
   for (int j = 0; j < GQ; ++j) o[j] = 0.0f;
 
-  const int nqb = nq / G;
+  const int nqb = nq / kStream;  // packed streams
   const int n_items = nqb + (nr + G - 1) / G;
   const int i0 = split * a.items_per_split;
   const int i1 = min(n_items, i0 + a.items_per_split);
@@ -95,10 +99,11 @@ __global__ __launch_bounds__(256) void decode_split_valu(DecodeArgs a) {
     const bool packed = it < nqb;
     const int rc = it - nqb;  // window chunk index when !packed
     const int ntok = packed ? G : min(G, nr - rc * G);
+    const int r0 = packed ? (it % SPB) * kStream : 0;  // first row of the stream in its block
     const uint8_t* const rec =
-        a.blocks + record_index(a.page_table, a.page_stride, a.num_pages, a.nb, a.H, u, packed ? it : 0) * BL.bytes;
+        a.blocks + record_index(a.page_table, a.page_stride, a.num_pages, a.nb, a.H, u, packed ? it / SPB : 0) * BL.bytes;
     if (packed) {
-      // key meta [d]; value meta [m][row], 4 * 32 = D entries
+      // key meta [d]; value meta [m][row], (D / GT) * GT = D entries
       if (tid < D) {
         kS[tid] = h2f(reinterpret_cast<const uint16_t*>(rec + BL.k_scale)[tid]);
         vS[tid] = h2f(reinterpret_cast<const uint16_t*>(rec + BL.v_scale)[tid]);
@@ -117,7 +122,7 @@ __global__ __launch_bounds__(256) void decode_split_valu(DecodeArgs a) {
       for (int j = 0; j < GQ; ++j) acc[j] = 0.0f;
       if (t < ntok) {
         if (packed) {
-          const uint32_t* kw = reinterpret_cast<const uint32_t*>(rec + BL.k_codes) + t * KW;
+          const uint32_t* kw = reinterpret_cast<const uint32_t*>(rec + BL.k_codes) + (r0 + t) * KW;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int d = sl * 16 + i;
@@ -173,16 +178,16 @@ __global__ __launch_bounds__(256) void decode_split_valu(DecodeArgs a) {
 
     // ---- values: channel d = tid % 128, rows 16*half .. 16*half+15
     {
-      const int d = tid & (D - 1), half = tid >> 7, m = d / G;
+      const int d = tid & (D - 1), half = tid >> 7, m = d / GT;
 #pragma unroll
       for (int j = 0; j < GQ; ++j) o[j] *= st_a[j];
       if (packed) {
         const uint32_t* vw = reinterpret_cast<const uint32_t*>(rec + BL.v_codes) + d;  // word w at vw[w * D]
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int row = half * 16 + i;
-          const uint32_t c = code_at<VB>(vw[(row / PV) * D], row % PV);
-          const float vh = fmaf(static_cast<float>(c), vS[m * G + row], vZ[m * G + row]);
+          const int row = half * 16 + i, br = r0 + row;  // row of the stream, of the block
+          const uint32_t c = code_at<VB>(vw[(br / PV) * D], br % PV);
+          const float vh = fmaf(static_cast<float>(c), vS[m * GT + br], vZ[m * GT + br]);
 #pragma unroll
           for (int j = 0; j < GQ; ++j) o[j] = fmaf(sc[j][row], vh, o[j]);
         }
@@ -296,7 +301,11 @@ __global__ __launch_bounds__(D) void decode_merge(DecodeArgs a) {
 template <int KB, int VB, bool BF16, int GQ>
 hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
   dim3 grid(a.n_split, a.B * a.H);
-  hipLaunchKernelGGL((decode_split_valu<KB, VB, BF16, GQ>), grid, dim3(256), 0, stream, a);
+  if (a.G == 64) {
+    hipLaunchKernelGGL((decode_split_valu<KB, VB, BF16, GQ, 64>), grid, dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((decode_split_valu<KB, VB, BF16, GQ, 32>), grid, dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

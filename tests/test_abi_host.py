@@ -166,3 +166,16 @@ def test_null_handles():
     assert kivi.lib.kivi_cache_bytes(None, ctypes.byref(n)) == kivi.KIVI_ERR_INVALID_ARG
     assert kivi.lib.kivi_append(None, None, None, 1, None) == kivi.KIVI_ERR_INVALID_ARG
     assert kivi.lib.kivi_cache_get_view(None, None) == kivi.KIVI_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("G,R,max_tokens", [(32, 128, 300), (64, 128, 300), (64, 64, 1000), (64, 1024, 5000)])
+def test_workspace_covers_32_token_streams(G, R, max_tokens):
+    # the decode kernels split the token axis into 32-token streams (half a
+    # block when G = 64), so the workspace holds one partial per stream of the
+    # capacity and of the window, up to 256 splits, whatever the group size
+    h = _make(cfg(group_size=G, residual_length=R, max_tokens=max_tokens))
+    cap = -(-max_tokens // R) * R
+    splits = min(256, cap // 32 + R // 32)
+    for hq in (2, 4, 8, 16):
+        assert kivi.kivi_decode_attn_workspace_bytes(h, hq) == 2 * hq * splits * 130 * 4
+    kivi.kivi_cache_destroy(h)
