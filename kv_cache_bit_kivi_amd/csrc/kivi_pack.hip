@@ -17,6 +17,8 @@
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "kivi_internal.h"
 
 namespace kivi {
@@ -74,24 +76,48 @@ __device__ __forceinline__ bool group_consts(float mn, float mx, float& s, float
 // of RN(d / s).  Rounding y to an integer therefore gives the same result
 // unless y lies within 2^-17 of a half-integer.
 //
-// The fast pass (CAREFUL false) only keeps in `dev` the largest |y - rint(y)|
-// seen (one v_max per code, no per-code compare).  A thread whose dev exceeds
-// 0.5 - 2^-17, or any thread of a block with a tiny scale, runs the careful
-// pass: the same loop, in which only the codes near a tie (all codes, in a
-// tiny-scale block) take the IEEE division of the definition.  Exact ties
-// are common with 16-bit inputs (an element at the midpoint of its group),
-// so the careful pass must stay cheap.
+// Near ties are repaired in one of two ways (Tie::kMask for bf16 inputs with
+// 32-token blocks, whose coarse grid makes ties about ten times as frequent,
+// Tie::kDev otherwise; with 64-token blocks the mask's registers would cost
+// more resident workgroups than the repair saves):
+//   kDev:  the fast pass only keeps the largest |y - rint(y)| of the thread
+//          (one v_max per code).  A thread above 0.5 - 2^-17 runs the careful
+//          pass: the same loop, in which the codes near a tie take the IEEE
+//          division of the definition.  Cheapest in registers.
+//   kMask: the fast pass sets the bit of every code near a tie in a per-thread
+//          mask; only those codes are recomputed by the definition and patched
+//          into their words (key_fix, value_fix).  Cheapest when most waves
+//          hold a tie (bf16 with 4-bit codes: 98% of the waves), at the price
+//          of more registers (fewer resident workgroups).
+// A block with a tiny scale runs the careful pass (every code divides).
 constexpr float kTieMargin = 0.49999237060546875f;  // 0.5 - 2^-17
-template <bool CAREFUL>
-__device__ __forceinline__ float code_of(float d, float rcp, float s, bool tiny, float& dev) {
+enum class Tie { kDev, kMask, kCareful };
+// one bit per code of a thread: G codes
+template <int G>
+using TieMask = typename std::conditional<G == 32, uint32_t, uint64_t>::type;
+// per-thread tie state of the fast pass: the largest deviation, or the mask
+template <Tie T, int G>
+using TieState = typename std::conditional<T == Tie::kMask, TieMask<G>, float>::type;
+template <Tie T, typename M>
+__device__ __forceinline__ float code_of(float d, float rcp, float s, bool tiny, M& st, M bit) {
   const float y = d * rcp;
   float r = rintf(y);
-  if constexpr (CAREFUL) {
+  if constexpr (T == Tie::kCareful) {
     if (tiny || !(fabsf(y - r) <= kTieMargin)) r = s == 0.0f ? 0.0f : rintf(d / s);
+  } else if constexpr (T == Tie::kMask) {
+    if (!(fabsf(y - r) <= kTieMargin)) st |= bit;
   } else {
-    dev = fmaxf(dev, fabsf(y - r));
+    st = fmaxf(st, fabsf(y - r));
   }
   return r;
+}
+
+// The code of element x of a group (minimum mn, scale s) by the definition:
+// rne(RN(RN(x - mn) / s)), 0 when s == 0.
+template <bool BF16>
+__device__ __forceinline__ uint32_t exact_code(uint16_t xb, float mn, float s) {
+  const float x = BF16 ? __uint_as_float(static_cast<uint32_t>(xb) << 16) : __half2float(__ushort_as_half(xb));
+  return s == 0.0f ? 0u : static_cast<uint32_t>(rintf((x - mn) / s));
 }
 
 // d = RN(x - mn) for element SEL (0: low, 1: high half) of a packed pair.
@@ -157,10 +183,10 @@ __device__ __forceinline__ void lds_barrier() {
 // tokens tg, tg + TS, ...; the channels are taken 8 at a time (fewer live
 // registers).  kt: the staged key tile; kmn, krc, ksc: per channel minimum,
 // reciprocal and scale.
-template <int KB, int G, bool BF16, bool CAREFUL>
+template <int KB, int G, bool BF16, Tie T>
 __device__ __forceinline__ void key_words(const uint16_t* kt, const float* kmn, const float* krc,
                                           const float* ksc, int w, int tg, bool tiny,
-                                          uint32_t* word, float& dev) {
+                                          uint32_t* word, TieState<T, G>& st) {
   constexpr int PK = 32 / KB, KW = D / PK, TS = 128 / KW, NT = G / TS;
   float wlo[NT], whi[NT];  // the word's even / odd codes as exact integers
 #pragma unroll
@@ -175,7 +201,7 @@ __device__ __forceinline__ void key_words(const uint16_t* kt, const float* kmn, 
       const float4 c4 = *reinterpret_cast<const float4*>(&krc[d0 + i]);
       mn[i] = a4.x; mn[i + 1] = a4.y; mn[i + 2] = a4.z; mn[i + 3] = a4.w;
       rc[i] = c4.x; rc[i + 1] = c4.y; rc[i + 2] = c4.z; rc[i + 3] = c4.w;
-      if constexpr (CAREFUL) {
+      if constexpr (T == Tie::kCareful) {
         const float4 s4 = *reinterpret_cast<const float4*>(&ksc[d0 + i]);
         sc[i] = s4.x; sc[i + 1] = s4.y; sc[i + 2] = s4.z; sc[i + 3] = s4.w;
       } else {
@@ -190,9 +216,12 @@ __device__ __forceinline__ void key_words(const uint16_t* kt, const float* kmn, 
       for (int i = 0; i < 8; i += 2) {
         // codes c8 + i (even: low half) and c8 + i + 1 (odd: high half),
         // both at bit KB * (c8 + i) / 2 of their half
+        // (mask bit of code n of token slot j: j * PK + n)
         const float wt = static_cast<float>(1 << (KB * ((c8 + i) >> 1)));
-        wlo[j] = fmaf(code_of<CAREFUL>(diff<BF16, 0>(xw[i >> 1], mn[i]), rc[i], sc[i], tiny, dev), wt, wlo[j]);
-        whi[j] = fmaf(code_of<CAREFUL>(diff<BF16, 1>(xw[i >> 1], mn[i + 1]), rc[i + 1], sc[i + 1], tiny, dev),
+        const TieState<T, G> bit = T == Tie::kMask ? TieState<T, G>(TieMask<G>(1) << (j * PK + c8 + i)) : 0;
+        wlo[j] = fmaf(code_of<T>(diff<BF16, 0>(xw[i >> 1], mn[i]), rc[i], sc[i], tiny, st, bit), wt, wlo[j]);
+        whi[j] = fmaf(code_of<T>(diff<BF16, 1>(xw[i >> 1], mn[i + 1]), rc[i + 1], sc[i + 1], tiny, st,
+                                 T == Tie::kMask ? TieState<T, G>(TieMask<G>(bit) << 1) : bit),
                       wt, whi[j]);
       }
     }
@@ -204,10 +233,10 @@ __device__ __forceinline__ void key_words(const uint16_t* kt, const float* kmn, 
 // Value code words of one thread: channels d0, d0 + 1 (one channel group) and
 // rows (G/2)*h .. (G/2)*h + G/2 - 1, taken 8 rows at a time.  vt: the staged
 // value tile; vmn, vrc, vsc: per (group, row) minimum, reciprocal and scale.
-template <int VB, int G, bool BF16, bool CAREFUL>
+template <int VB, int G, bool BF16, Tie T>
 __device__ __forceinline__ void value_words(const uint16_t* vt, const float* vmn, const float* vrc,
                                             const float* vsc, int d0, int h, bool tiny,
-                                            uint32_t* w0, uint32_t* w1, float& dev) {
+                                            uint32_t* w0, uint32_t* w1, TieState<T, G>& st) {
   constexpr int PV = 32 / VB, HR = G / 2, NW = HR / PV;
   const int m = d0 / G;
   float l0[NW], h0[NW], l1[NW], h1[NW];  // even / odd codes of channels d0, d0+1
@@ -223,7 +252,7 @@ __device__ __forceinline__ void value_words(const uint16_t* vt, const float* vmn
       const float4 c4 = *reinterpret_cast<const float4*>(&vrc[sbase + j]);
       mn[j] = a4.x; mn[j + 1] = a4.y; mn[j + 2] = a4.z; mn[j + 3] = a4.w;
       rc[j] = c4.x; rc[j + 1] = c4.y; rc[j + 2] = c4.z; rc[j + 3] = c4.w;
-      if constexpr (CAREFUL) {
+      if constexpr (T == Tie::kCareful) {
         const float4 s4 = *reinterpret_cast<const float4*>(&vsc[sbase + j]);
         sc[j] = s4.x; sc[j + 1] = s4.y; sc[j + 2] = s4.z; sc[j + 3] = s4.w;
       } else {
@@ -236,8 +265,11 @@ __device__ __forceinline__ void value_words(const uint16_t* vt, const float* vmn
       const uint32_t xw = *reinterpret_cast<const uint32_t*>(&vt[(HR * h + r) * RS + d0]);
       const int k = r / PV, pos = r % PV;
       const float wt = static_cast<float>(1 << (VB * (pos >> 1)));
-      const float c0 = code_of<CAREFUL>(diff<BF16, 0>(xw, mn[j]), rc[j], sc[j], tiny, dev);  // channel d0
-      const float c1 = code_of<CAREFUL>(diff<BF16, 1>(xw, mn[j]), rc[j], sc[j], tiny, dev);  // channel d0 + 1
+      // (mask bits of row r: 2 r for channel d0, 2 r + 1 for channel d0 + 1)
+      const TieState<T, G> bit = T == Tie::kMask ? TieState<T, G>(TieMask<G>(1) << (2 * r)) : 0;
+      const float c0 = code_of<T>(diff<BF16, 0>(xw, mn[j]), rc[j], sc[j], tiny, st, bit);
+      const float c1 = code_of<T>(diff<BF16, 1>(xw, mn[j]), rc[j], sc[j], tiny, st,
+                                  T == Tie::kMask ? TieState<T, G>(TieMask<G>(bit) << 1) : bit);
       if (pos & 1) {
         h0[k] = fmaf(c0, wt, h0[k]);
         h1[k] = fmaf(c1, wt, h1[k]);
@@ -251,6 +283,49 @@ __device__ __forceinline__ void value_words(const uint16_t* vt, const float* vmn
   for (int k = 0; k < NW; ++k) {
     w0[k] = halves_to_word(l0[k], h0[k]);
     w1[k] = halves_to_word(l1[k], h1[k]);
+  }
+}
+
+// Recomputes the key codes flagged in `mask` (bit j * PK + n: code n of the
+// word of token slot j) by the definition and patches them into `word`.
+template <int KB, int G, bool BF16>
+__device__ __forceinline__ void key_fix(const uint16_t* kt, const float* kmn, const float* ksc, int w, int tg,
+                                     TieMask<G> mask, uint32_t* word) {
+  constexpr int PK = 32 / KB, KW = D / PK, TS = 128 / KW, NT = G / TS;
+  while (mask) {
+    const int bit = __builtin_ctzll(static_cast<uint64_t>(mask));
+    mask &= mask - 1;
+    const int j = bit / PK, n = bit % PK, d = w * PK + n;
+    const uint32_t c = exact_code<BF16>(kt[(tg + j * TS) * RS + d], kmn[d], ksc[d]);
+    const int pos = KB * (n >> 1) + 16 * (n & 1);
+    const uint32_t keep = ~(((1u << KB) - 1u) << pos);
+#pragma unroll
+    for (int jj = 0; jj < NT; ++jj)
+      if (jj == j) word[jj] = (word[jj] & keep) | (c << pos);
+  }
+}
+
+// Recomputes the value codes flagged in `mask` (bit 2 r + e: row r of the
+// thread's rows, channel d0 + e) and patches them into w0 / w1.
+template <int VB, int G, bool BF16>
+__device__ __forceinline__ void value_fix(const uint16_t* vt, const float* vmn, const float* vsc, int d0, int h,
+                                       TieMask<G> mask, uint32_t* w0, uint32_t* w1) {
+  constexpr int PV = 32 / VB, HR = G / 2, NW = HR / PV;
+  const int m = d0 / G;
+  while (mask) {
+    const int bit = __builtin_ctzll(static_cast<uint64_t>(mask));
+    mask &= mask - 1;
+    const int r = bit >> 1, e = bit & 1;
+    const int gi = m * G + HR * h + r;  // the row's group constants
+    const uint32_t c = exact_code<BF16>(vt[(HR * h + r) * RS + d0 + e], vmn[gi], vsc[gi]);
+    const int k = r / PV, p = r % PV;
+    const int pos = VB * (p >> 1) + 16 * (p & 1);
+    const uint32_t keep = ~(((1u << VB) - 1u) << pos);
+#pragma unroll
+    for (int kk = 0; kk < NW; ++kk) {
+      if (kk == k && e == 0) w0[kk] = (w0[kk] & keep) | (c << pos);
+      if (kk == k && e == 1) w1[kk] = (w1[kk] & keep) | (c << pos);
+    }
   }
 }
 
@@ -421,11 +496,15 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
     constexpr int TS = 128 / KW, NT = G / TS;
     const int w = tid % KW, tg = tid / KW;
     uint32_t word[NT];
-    float dev = 0.0f;
-    key_words<KB, G, BF16, false>(kt, kmn, krc, ksc, w, tg, false, word, dev);
-    if (dev > kTieMargin || tiny) {
+    constexpr Tie TF = (BF16 && G == 32) ? Tie::kMask : Tie::kDev;
+    TieState<TF, G> st = 0;
+    key_words<KB, G, BF16, TF>(kt, kmn, krc, ksc, w, tg, false, word, st);
+    float unused = 0.0f;
+    if (tiny || (TF == Tie::kDev && st > kTieMargin)) {
       asm volatile("" ::: "memory");  // reload the tile: nothing kept live across the passes
-      key_words<KB, G, BF16, true>(kt, kmn, krc, ksc, w, tg, tiny, word, dev);
+      key_words<KB, G, BF16, Tie::kCareful>(kt, kmn, krc, ksc, w, tg, tiny, word, unused);
+    } else if constexpr (TF == Tie::kMask) {
+      if (st) key_fix<KB, G, BF16>(kt, kmn, ksc, w, tg, st, word);
     }
     uint32_t* const kc = reinterpret_cast<uint32_t*>(rec + BL.k_codes);
 #pragma unroll
@@ -438,11 +517,15 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
     const int d0 = 2 * (i0 % 64), h = i0 / 64;
     constexpr int NW = (G / 2) / PV;
     uint32_t w0[NW], w1[NW];
-    float dev = 0.0f;
-    value_words<VB, G, BF16, false>(vt, vmn, vrc, vsc, d0, h, false, w0, w1, dev);
-    if (dev > kTieMargin || tiny) {
+    constexpr Tie TF = (BF16 && G == 32) ? Tie::kMask : Tie::kDev;
+    TieState<TF, G> st = 0;
+    value_words<VB, G, BF16, TF>(vt, vmn, vrc, vsc, d0, h, false, w0, w1, st);
+    float unused = 0.0f;
+    if (tiny || (TF == Tie::kDev && st > kTieMargin)) {
       asm volatile("" ::: "memory");  // reload the tile: nothing kept live across the passes
-      value_words<VB, G, BF16, true>(vt, vmn, vrc, vsc, d0, h, tiny, w0, w1, dev);
+      value_words<VB, G, BF16, Tie::kCareful>(vt, vmn, vrc, vsc, d0, h, tiny, w0, w1, unused);
+    } else if constexpr (TF == Tie::kMask) {
+      if (st) value_fix<VB, G, BF16>(vt, vmn, vsc, d0, h, st, w0, w1);
     }
     uint32_t* const vc = reinterpret_cast<uint32_t*>(rec + BL.v_codes);
 #pragma unroll
