@@ -329,7 +329,8 @@ __device__ __forceinline__ void value_fix(const uint16_t* vt, const float* vmn, 
   }
 }
 
-template <int KB, int VB, bool BF16, int G>
+// TF: how near ties are repaired (Tie::kMask or Tie::kDev, see code_of).
+template <int KB, int VB, bool BF16, int G, Tie TF>
 __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
   constexpr int QK = (1 << KB) - 1, QV = (1 << VB) - 1;
   constexpr int PK = 32 / KB;  // key codes (channels) per word
@@ -496,7 +497,6 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
     constexpr int TS = 128 / KW, NT = G / TS;
     const int w = tid % KW, tg = tid / KW;
     uint32_t word[NT];
-    constexpr Tie TF = (BF16 && G == 32) ? Tie::kMask : Tie::kDev;
     TieState<TF, G> st = 0;
     key_words<KB, G, BF16, TF>(kt, kmn, krc, ksc, w, tg, false, word, st);
     float unused = 0.0f;
@@ -517,7 +517,6 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
     const int d0 = 2 * (i0 % 64), h = i0 / 64;
     constexpr int NW = (G / 2) / PV;
     uint32_t w0[NW], w1[NW];
-    constexpr Tie TF = (BF16 && G == 32) ? Tie::kMask : Tie::kDev;
     TieState<TF, G> st = 0;
     value_words<VB, G, BF16, TF>(vt, vmn, vrc, vsc, d0, h, false, w0, w1, st);
     float unused = 0.0f;
@@ -544,10 +543,18 @@ hipError_t launch_pack_t(const PackArgs& a, hipStream_t stream) {
   }
   if (items == 0 || a.units == 0) return hipSuccess;
   dim3 grid(items, a.units);
+  // The tie repair by mask costs registers (fewer resident workgroups) and
+  // saves vector work: it pays for bf16 inputs (frequent ties) and for
+  // launches of at most one round of workgroups (a window flush), whose time
+  // is one workgroup's latency; big fp16 launches are bound by memory and
+  // keep the careful pass.  64-token blocks keep it too.
+  const bool one_round = (long long)items * a.units <= 256LL * 8;
   if (a.G == 64) {
-    hipLaunchKernelGGL((pack_kernel<KB, VB, BF16, 64>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((pack_kernel<KB, VB, BF16, 64, Tie::kDev>), grid, dim3(256), 0, stream, a);
+  } else if (BF16 || one_round) {
+    hipLaunchKernelGGL((pack_kernel<KB, VB, BF16, 32, Tie::kMask>), grid, dim3(256), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((pack_kernel<KB, VB, BF16, 32>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((pack_kernel<KB, VB, BF16, 32, Tie::kDev>), grid, dim3(256), 0, stream, a);
   }
   return hipGetLastError();
 }
