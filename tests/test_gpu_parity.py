@@ -199,7 +199,11 @@ def _hard_triples(bits, count, seed):
 
 
 @pytest.mark.parametrize("bits", [2, 4])
-def test_quantizer_hard_cases_bitexact(bits):
+@pytest.mark.parametrize("heads,blocks", [(1, 1), (72, 30)], ids=["one_round", "many_rounds"])
+def test_quantizer_hard_cases_bitexact(bits, heads, blocks):
+    # one launch of at most one round of workgroups repairs near ties by mask,
+    # a bigger one by the careful pass: the same hard block, tiled over
+    # `heads` kv heads and `blocks` blocks, reaches both
     mn, mx, xv = _hard_triples(bits, 128, 17 + bits)
     n = mn.size
     # keys: channel d of block 0 holds [mn, mx, x, x, ...] over its 32 tokens;
@@ -216,16 +220,17 @@ def test_quantizer_hard_cases_bitexact(bits):
             i = (t * 4 + m) % n
             V[t, m * 32:(m + 1) * 32] = xv[i]
             V[t, m * 32], V[t, m * 32 + 1] = mn[i], mx[i]
-    k = torch.from_numpy(K.astype(np.float16))[None, None]
-    v = torch.from_numpy(V.astype(np.float16))[None, None]
-    kk = torch.cat([k, k[:, :, :1]], 2)  # one more token flushes the block
+    k = torch.from_numpy(K.astype(np.float16))[None, None].repeat(1, heads, blocks, 1)
+    v = torch.from_numpy(V.astype(np.float16))[None, None].repeat(1, heads, blocks, 1)
+    kk = torch.cat([k, k[:, :, :1]], 2)  # one more token flushes the last block
     vv = torch.cat([v, v[:, :, :1]], 2)
-    w = small("hard", 1, 1, 1, T + 1, bits, bits, torch.float16, residual_length=32)
-    cache = _gpu_cache(w, T + 1)
+    Tn = T * blocks + 1
+    w = small("hard", 1, heads, heads, Tn, bits, bits, torch.float16, residual_length=32)
+    cache = _gpu_cache(w, Tn)
     cache.append(kk.contiguous().to(DEV), vv.contiguous().to(DEV))
-    ref = oracle.OracleCache(1, 1, 128, T + 1, bits, bits, 32, 32)
+    ref = oracle.OracleCache(1, heads, 128, Tn, bits, bits, 32, 32)
     ref.append(bits16(kk), bits16(vv))
-    assert ref.n_quant == 32
+    assert ref.n_quant == 32 * blocks
     _compare(cache, ref)
 
 
