@@ -299,9 +299,13 @@ def main():
     for k in ("pack", "flush", "decode"):
         g = ab[k] / avg[k] / 1e9
         phases[k] = {"bytes": ab[k], "us_mean": avg[k] * 1e6, "us_median": med[k] * 1e6,
+                     "us_p10": float(np.percentile(phase[k], 10)) * 1e6,
+                     "us_p90": float(np.percentile(phase[k], 90)) * 1e6, "samples": len(phase[k]),
                      "gbps": g, "frac": g / PEAK_GBPS, "launches": PHASE_KERNEL[k][2]}
     cold_med = float(np.median(cold))
     phases["decode_cold_llc"] = {"bytes": ab["decode"], "us_median": cold_med * 1e6,
+                                 "us_p10": float(np.percentile(cold, 10)) * 1e6,
+                                 "us_p90": float(np.percentile(cold, 90)) * 1e6, "samples": len(cold),
                                  "gbps": ab["decode"] / cold_med / 1e9,
                                  "frac": ab["decode"] / cold_med / 1e9 / PEAK_GBPS}
     # roofline of the phase that takes the most time (pack and decode are one
