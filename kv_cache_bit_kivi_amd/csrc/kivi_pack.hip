@@ -499,10 +499,10 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
     uint32_t word[NT];
     TieState<TF, G> st = 0;
     key_words<KB, G, BF16, TF>(kt, kmn, krc, ksc, w, tg, false, word, st);
-    float unused = 0.0f;
+    float no_state = 0.0f;  // the careful pass keeps no tie state
     if (tiny || (TF == Tie::kDev && st > kTieMargin)) {
       asm volatile("" ::: "memory");  // reload the tile: nothing kept live across the passes
-      key_words<KB, G, BF16, Tie::kCareful>(kt, kmn, krc, ksc, w, tg, tiny, word, unused);
+      key_words<KB, G, BF16, Tie::kCareful>(kt, kmn, krc, ksc, w, tg, tiny, word, no_state);
     } else if constexpr (TF == Tie::kMask) {
       if (st) key_fix<KB, G, BF16>(kt, kmn, ksc, w, tg, st, word);
     }
@@ -519,10 +519,10 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
     uint32_t w0[NW], w1[NW];
     TieState<TF, G> st = 0;
     value_words<VB, G, BF16, TF>(vt, vmn, vrc, vsc, d0, h, false, w0, w1, st);
-    float unused = 0.0f;
+    float no_state = 0.0f;  // the careful pass keeps no tie state
     if (tiny || (TF == Tie::kDev && st > kTieMargin)) {
       asm volatile("" ::: "memory");  // reload the tile: nothing kept live across the passes
-      value_words<VB, G, BF16, Tie::kCareful>(vt, vmn, vrc, vsc, d0, h, tiny, w0, w1, unused);
+      value_words<VB, G, BF16, Tie::kCareful>(vt, vmn, vrc, vsc, d0, h, tiny, w0, w1, no_state);
     } else if constexpr (TF == Tie::kMask) {
       if (st) value_fix<VB, G, BF16>(vt, vmn, vsc, d0, h, st, w0, w1);
     }
