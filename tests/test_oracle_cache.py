@@ -68,6 +68,44 @@ def test_layout_4bit_hand_words(oracle_mod):
     assert vc[:, 8].tolist() == [0xFDB9ECA8, 0x75316420, 0xFDB9ECA8, 0x75316420]
 
 
+def test_layout_group64_hand_words(oracle_mod):
+    # G = D = R = 64, 2-bit codes, 65 tokens.  Keys: K[t][d] = (t + d) mod 4,
+    # times 3 for tokens 32..63; values: V[t][d] = (t + d) mod 4, times 3 for
+    # channels 32..63.  Every group of 64 then spans 0..9, so s = 3 (0x4200)
+    # and zero-point 0; a group of 32 would give s = 1 on the unscaled half.
+    # Unscaled inputs 0,1,2,3 become codes 0,0,1,1 (thirds round to the
+    # nearest integer); scaled ones 0,3,6,9 become 0,1,2,3.
+    D, T = 64, 65
+    t = np.arange(T)[:, None]
+    d = np.arange(D)[None, :]
+    base = (t + d) % 4
+    K = (base * np.where((t >= 32) & (t < 64), 3, 1)).astype(np.float16)[None, None]
+    V = (base * np.where(d >= 32, 3, 1)).astype(np.float16)[None, None]
+    c = oracle_mod.OracleCache(1, 1, D, 128, 2, 2, 64, 64)
+    c.append(K.view(np.uint16), V.view(np.uint16))
+    assert (c.n_quant, c.n_resid) == (64, 1)
+    # Codes 0,0,1,1 by (t + d) mod 4, packed as in the 32-group pin (even
+    # channels in the low half-word, odd in the high, 2 bits each): token
+    # t = 0 mod 4 -> even 0,1,0,1.. = 0x4444, odd 0x4444; t = 1 -> 0x4444
+    # and 0x1111; t = 2 -> 0x1111 both; t = 3 -> 0x1111 and 0x4444.
+    thirds = [0x44444444, 0x11114444, 0x11111111, 0x44441111]
+    plain = [0xDDDD8888, 0x2222DDDD, 0x77772222, 0x88887777]
+    kc = c.array("k_codes").reshape(-1, 4)  # [token][word], 16 channels a word
+    for tok in range(64):
+        want = thirds[tok % 4] if tok < 32 else plain[tok % 4]
+        assert kc[tok].tolist() == [want] * 4, tok
+    # value words: word w of channel d holds rows 16w..16w+15, [word][channel]
+    vc = c.array("v_codes").reshape(-1, 4, D)[0]
+    for ch in range(D):
+        want = thirds[ch % 4] if ch < 32 else plain[ch % 4]
+        assert vc[:, ch].tolist() == [want] * 4, ch
+    assert set(c.array("k_scale")[:D].tolist()) == {0x4200}
+    assert set(c.array("k_zero")[:D].tolist()) == {0}
+    assert set(c.array("v_scale")[:64].tolist()) == {0x4200}
+    assert set(c.array("v_zero")[:64].tolist()) == {0}
+    assert c.array("k_resid")[:D].tolist() == K[0, 0, 64].view(np.uint16).tolist()
+
+
 def _random_bits(rng, shape):
     x = (rng.standard_normal(shape) * 2 + rng.standard_normal(shape[-1])).astype(np.float16)
     return x.view(np.uint16)
