@@ -279,3 +279,64 @@ def test_binding_rejects_malformed_tensors():
     with pytest.raises(ValueError):
         cache.decode_attn(torch.zeros(2, 4, 64, dtype=torch.float16, device=DEV), 0.1)
     assert (cache.n_quant, cache.n_resid) == (0, 8)
+
+
+def _degenerate_layer(G, H, T, extremes, seed):
+    # Ordinary data with degenerate groups planted in the first three blocks:
+    # constant key channels and value groups (scale 0, zero-point = the value),
+    # all-zero groups mixing +0 and -0 (zero-point +0), two-valued groups and,
+    # with `extremes`, groups spanning -65280 .. 65280 (the widest span whose
+    # ends both fp16 and bf16 hold).  Values are exact in fp16 and bf16.
+    rng = np.random.default_rng(seed)
+    big = 65280.0 if extremes else 5.0
+    K = (rng.standard_normal((H, T, 128)) * 2).astype(np.float32)
+    V = (rng.standard_normal((H, T, 128)) * 2).astype(np.float32)
+    signed_zeros = lambda shape: np.where(rng.random(shape) < 0.5, 0.0, -0.0).astype(np.float32)
+    consts = [0.0, 1.25, -2.0, 3.5, -0.0, 7.0, -big, big]
+    for c in range(8):  # block 0: constant key channels 0..7
+        K[:, :G, c] = consts[c]
+    K[:, :G, 8:16] = signed_zeros((H, G, 8))
+    K[:, :G, 16:24] = np.where(rng.random((H, G, 8)) < 0.5, -1.5, 2.25)
+    K[:, :G, 24] = np.where(np.arange(G) % 2 == 0, -big, big)
+    K[:, G:2 * G] = signed_zeros((H, G, 128))  # block 1: every key group zero
+    K[:, 2 * G:3 * G, 100] = 0.5
+    nv = 128 // G  # value groups per token
+    for m in range(nv):  # token 0: every value group constant
+        V[:, 0, m * G:(m + 1) * G] = consts[m + 1]
+    V[:, 1] = signed_zeros((H, 128))
+    V[:, 2, :G] = np.where(np.arange(G) % 2 == 0, -big, big)
+    V[:, 2, G:2 * G] = np.where(rng.random((H, G)) < 0.5, -1.5, 2.25)
+    V[:, G + 5] = big
+    return torch.from_numpy(K)[None], torch.from_numpy(V)[None]
+
+
+@pytest.mark.parametrize("extremes", [False, True], ids=["plain", "extremes"])
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("dt", [torch.float16, torch.bfloat16], ids=["f16", "bf16"])
+@pytest.mark.parametrize("G", [32, 64])
+def test_degenerate_groups_bitexact(G, dt, bits, extremes):
+    # codes, scales, zero-points and window bit-exact on degenerate groups; the
+    # attention check runs where the scales stay inside the documented range
+    # of the matrix-core products (no extremes)
+    H, gq = 2, (4 if bits == 2 else 8)
+    T = 3 * G + 1
+    print(f"degenerate G={G} {dt} bits={bits} extremes={extremes}", flush=True)
+    K, V = _degenerate_layer(G, H, T, extremes, seed=G + bits)
+    k, v = K.to(dt), V.to(dt)
+    cache = kivi.KiviCache(1, H, T, k_bits=bits, v_bits=bits, group_size=G, residual_length=G,
+                           dtype=dt, device=DEV)
+    cache.append(k.contiguous().to(DEV), v.contiguous().to(DEV))
+    ref = oracle.OracleCache(1, H, 128, T, bits, bits, G, G,
+                             oracle.BF16 if dt == torch.bfloat16 else oracle.F16)
+    ref.append(bits16(k), bits16(v))
+    assert (ref.n_quant, ref.n_resid) == (3 * G, 1)
+    torch.cuda.synchronize()
+    assert (cache.n_quant, cache.n_resid) == (ref.n_quant, ref.n_resid)
+    assert_cache_equal(gpu_arrays(cache), oracle_arrays(ref), ref.n_quant, ref.n_resid,
+                       ref.capacity, ref.num_blocks, G=G)
+    if not extremes:
+        q = torch.randn(1, H * gq, 128, generator=torch.Generator().manual_seed(bits)).to(dt)
+        scale = 1.0 / np.sqrt(128)
+        out = cache.decode_attn(q.to(DEV), scale).cpu().numpy().astype(np.float64)
+        err = float(np.abs(out - ref.decode_attn(bits16(q), scale)).max())
+        assert err <= TOL, f"attention error {err:.3e}"
