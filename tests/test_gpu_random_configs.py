@@ -69,7 +69,7 @@ def paged_arrays(cache, table):
     return out
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(128))
 def test_random_configuration(seed):
     c = draw(seed)
     G, R, B, H, gq, kb, vb, dt = (c[k] for k in ("G", "R", "B", "H", "gq", "kb", "vb", "dt"))
