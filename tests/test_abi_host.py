@@ -4,6 +4,9 @@ include/kivi.h declares, and rejects bad arguments before enqueuing anything
 import ctypes
 import os
 import re
+import shutil
+import subprocess
+import sys
 
 import pytest
 
@@ -179,3 +182,19 @@ def test_workspace_covers_32_token_streams(G, R, max_tokens):
     for hq in (2, 4, 8, 16):
         assert kivi.kivi_decode_attn_workspace_bytes(h, hq) == 2 * hq * splits * 130 * 4
     kivi.kivi_cache_destroy(h)
+
+
+def test_binding_without_library_fails_loudly(tmp_path):
+    # a copy of the package without libkivi.so: importing the binding raises
+    # ImportError naming the missing library (there is no CPU fallback)
+    src = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                       "kv_cache_bit_kivi_amd")
+    dst = tmp_path / "kv_cache_bit_kivi_amd"
+    dst.mkdir()
+    for f in ("__init__.py", "kivi.py", "inputs.py"):
+        shutil.copy(os.path.join(src, f), dst / f)
+    r = subprocess.run([sys.executable, "-c", "import kv_cache_bit_kivi_amd.kivi"], cwd=tmp_path,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "libkivi.so is missing" in r.stderr
+    assert "no CPU fallback" in r.stderr
