@@ -3,8 +3,8 @@ I Ran the Experiments So You Don't Have To" and the config knobs of page
 "KIVI: Asymmetric 2-Bit KV Cache Quantization Guide"): bulk and single-token
 appends bit-exact against the oracle at G = 64, decode attention within
 2e-3, and the same through sequences of different lengths, paged records and
-the fused decode step.  With 8 query heads per kv head decode attention is
-not built for G = 64 and must say so before enqueuing anything."""
+the fused decode step, for 1, 2, 4 and 8 query heads per kv head.  A ratio
+that is not built (16) must be rejected before anything is enqueued."""
 import dataclasses
 
 import numpy as np
