@@ -587,8 +587,8 @@ kivi_status decode_launch(kivi_cache* c, const void* q, int32_t num_q_heads, flo
     c->cu_count = cus;
   }
 
-  // the kernels walk the packed tokens in streams of 32 (a block of G = 32,
-  // or half a block of G = 64; the vector kernel only takes G = 32)
+  // both decode kernels walk the packed tokens in streams of 32 (a block of
+  // G = 32, or half a block of G = 64)
   const int G = kivi::kStream;
   const int units = c->cfg.batch * c->cfg.num_kv_heads;
   const int nqg = c->n_quant / G;
