@@ -1,0 +1,52 @@
+"""The benchmark's output line on the GPU, from a short run of the default
+workload (c1): one JSON line with the fields the contract names, and their
+relations: value is the algorithmic bytes of a step over its time, the
+roofline's achieved rate is the dominant kernel's bytes over its launch time,
+and frac is achieved over the 8 TB/s HBM peak."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from kv_cache_bit_kivi_amd.inputs import WORKLOADS  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def test_bench_line_contract():
+    print("bench: c1, 3 steps, 1 warm-up, no CPU baseline", flush=True)
+    r = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--steps", "3",
+                        "--warmup", "1", "--cold-iters", "2", "--no-cpu-baseline"],
+                       capture_output=True, text=True, timeout=240, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-3000:]
+    lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
+    assert len(lines) == 1, r.stdout[-3000:]
+    j = json.loads(lines[0])
+    for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+              "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+              "roofline", "cpu_baseline"):
+        assert k in j, k
+    assert (j["n_gpus"], j["steps"], j["warmup"]) == (1, 3, 1)
+    assert j["unit"] == "GB/s" and j["higher_is_better"] is True and j["data"] == "synthetic"
+    assert j["vs_baseline"] is None and j["cpu_baseline"] is None
+    assert j["config"]["workload"].startswith("c1:")
+    step_bytes = sum(bench.algorithmic_bytes(WORKLOADS["c1"]).values())
+    assert j["value"] == pytest.approx(step_bytes / (j["ms_per_step"] * 1e-3) / 1e9, rel=1e-9)
+    rf = j["roofline"]
+    for k in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
+        assert k in rf, k
+    assert (rf["bound"], rf["peak"], rf["unit"]) == ("hbm", 8000.0, "GB/s")
+    assert rf["achieved"] == pytest.approx(rf["bytes_per_launch"] / (rf["us_per_launch"] * 1e-6) / 1e9,
+                                           rel=1e-9)
+    assert rf["frac"] == pytest.approx(rf["achieved"] / rf["peak"], rel=1e-12)
+    assert 0.0 < rf["frac"] < 1.0
+    # null when the kernel source changed after the counters were taken;
+    # otherwise the measured HBM bytes are close to the algorithmic ones
+    if rf["traffic"] is not None:
+        assert 0.95 <= rf["traffic"] / rf["bytes_per_launch"] <= 1.2
