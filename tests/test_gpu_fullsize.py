@@ -7,6 +7,8 @@ planner.
 The oracle runs on sampled (batch, kv head) units alone; their packed arrays
 must match bit for bit and the attention outputs of their query heads must be
 within 2e-3 of the oracle's."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -23,7 +25,20 @@ TOL = 2e-3
 
 @pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
 def test_fullsize_sampled_units(name):
-    w = WORKLOADS[name]
+    _sampled_parity(WORKLOADS[name], name)
+
+
+def test_cache_beyond_4gib_sampled_units():
+    # 1024 units of 32768 tokens at 4/4 bits: 160 B per token and unit, 5.4 GB
+    # of records, so the last unit's records lie beyond 2^32 bytes; every
+    # record, window and partial offset must be formed in 64 bits
+    w = dataclasses.replace(WORKLOADS["c2"], name="c2x4", kv_heads=32, q_heads=128, k_bits=4,
+                            v_bits=4, description="c2 with 32 kv heads and 4-bit codes")
+    assert w.batch * w.kv_heads * w.tokens * 160 > 1 << 32
+    _sampled_parity(w, w.name)
+
+
+def _sampled_parity(w, name):
     T = w.tokens
     U = w.batch * w.kv_heads
     print(f"workload {name}: B={w.batch} H={w.kv_heads} Hq={w.q_heads} T={T} "
