@@ -23,6 +23,39 @@ def gpu_arrays(cache, units=None):
     return out
 
 
+def paged_arrays(cache, table, units=None):
+    """Host copies of the packed fields per unit of a paged cache, gathering
+    each unit's blocks through the page table (block g of sequence b, kv head
+    h is record table[b][g] * H + h), plus the window arrays; optionally only
+    the listed units."""
+    import torch
+    v, cfg = cache.view(), cache.cfg
+    H, U, nb, bb = cfg.num_kv_heads, cfg.batch * cfg.num_kv_heads, v.num_blocks, v.block_bytes
+    units = list(range(U)) if units is None else list(units)
+    ob = v.blocks - cache.buffer.data_ptr()
+    flat = cache.buffer[ob:ob + U * nb * bb].view(U * nb, bb)
+    idx = torch.tensor([[int(table[u // H][g]) * H + u % H for g in range(nb)] for u in units],
+                       device=flat.device)
+    recs = flat[idx]  # [units][nb][block_bytes]
+    G, D, n = cfg.group_size, cfg.head_dim, len(units)
+
+    def field(off, nbytes, as_words):
+        a = recs[:, :, off:off + nbytes].contiguous().view(n, -1).cpu().numpy()
+        return a.view(np.uint32) if as_words else a.view(np.uint16)
+
+    out = {
+        "k_codes": field(v.off_k_codes, G * D * cfg.k_bits // 8, True),
+        "k_scale": field(v.off_k_scale, 2 * D, False),
+        "k_zero": field(v.off_k_zero, 2 * D, False),
+        "v_codes": field(v.off_v_codes, G * D * cfg.v_bits // 8, True),
+        "v_scale": field(v.off_v_scale, 2 * D, False),
+        "v_zero": field(v.off_v_zero, 2 * D, False),
+    }
+    win = gpu_arrays(cache, units)
+    out["k_resid"], out["v_resid"] = win["k_resid"], win["v_resid"]
+    return out
+
+
 def oracle_arrays(ref):
     U = ref.B * ref.H
     return {n: a.reshape(U, -1) for n, a in ref.arrays().items()}

@@ -16,7 +16,7 @@ import torch
 import oracle
 from kv_cache_bit_kivi_amd import kivi
 from kv_cache_bit_kivi_amd.inputs import WORKLOADS, bits16, make_layer
-from tests.gpu_helpers import assert_cache_equal, gpu_arrays, oracle_arrays, unit_oracle
+from tests.gpu_helpers import assert_cache_equal, gpu_arrays, oracle_arrays, paged_arrays, unit_oracle
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -28,17 +28,19 @@ def test_fullsize_sampled_units(name):
     _sampled_parity(WORKLOADS[name], name)
 
 
-def test_cache_beyond_4gib_sampled_units():
+@pytest.mark.parametrize("paged", [False, True], ids=["unit_major", "paged"])
+def test_cache_beyond_4gib_sampled_units(paged):
     # 1024 units of 32768 tokens at 4/4 bits: 160 B per token and unit, 5.4 GB
-    # of records, so the last unit's records lie beyond 2^32 bytes; every
-    # record, window and partial offset must be formed in 64 bits
+    # of records, so the last unit's records lie beyond 2^32 bytes (paged: a
+    # seeded permutation of the records spreads every unit over the pool);
+    # every record, window and partial offset must be formed in 64 bits
     w = dataclasses.replace(WORKLOADS["c2"], name="c2x4", kv_heads=32, q_heads=128, k_bits=4,
                             v_bits=4, description="c2 with 32 kv heads and 4-bit codes")
     assert w.batch * w.kv_heads * w.tokens * 160 > 1 << 32
-    _sampled_parity(w, w.name)
+    _sampled_parity(w, w.name + (" paged" if paged else ""), paged=paged)
 
 
-def _sampled_parity(w, name):
+def _sampled_parity(w, name, paged=False):
     T = w.tokens
     U = w.batch * w.kv_heads
     print(f"workload {name}: B={w.batch} H={w.kv_heads} Hq={w.q_heads} T={T} "
@@ -47,6 +49,11 @@ def _sampled_parity(w, name):
     cache = kivi.KiviCache(w.batch, w.kv_heads, T + 1, k_bits=w.k_bits, v_bits=w.v_bits,
                            group_size=w.group_size, residual_length=w.residual_length,
                            dtype=w.dtype, device=DEV)
+    table = None
+    if paged:
+        nb = cache.view().num_blocks
+        table = np.random.default_rng(7).permutation(w.batch * nb).astype(np.int32).reshape(w.batch, nb)
+        cache.set_page_table(torch.from_numpy(table).to(DEV), w.batch * nb)
     cache.append(x.k[:, :, :T].contiguous(), x.v[:, :, :T].contiguous())
     cache.flush()
     scale = 1.0 / np.sqrt(w.head_dim)
@@ -58,7 +65,7 @@ def _sampled_parity(w, name):
 
     rng = np.random.default_rng(U)
     units = sorted({0, U - 1, int(rng.integers(1, U - 1))})
-    got = gpu_arrays(cache, units)
+    got = gpu_arrays(cache, units) if table is None else paged_arrays(cache, table, units)
     dt = oracle.BF16 if w.dtype == torch.bfloat16 else oracle.F16
     for i, u in enumerate(units):
         b, h = divmod(u, w.kv_heads)

@@ -15,7 +15,7 @@ import torch
 import oracle
 from kv_cache_bit_kivi_amd import kivi
 from kv_cache_bit_kivi_amd.inputs import bits16, make_layer, small
-from tests.gpu_helpers import assert_cache_equal, gpu_arrays, oracle_arrays
+from tests.gpu_helpers import assert_cache_equal, gpu_arrays, oracle_arrays, paged_arrays
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -37,36 +37,6 @@ def draw(seed):
     paged = bool(rng.random() < 0.5)
     return dict(G=G, R=R, B=B, H=H, gq=gq, kb=kb, vb=vb, dt=dt, lens=lens, steps=steps,
                 paged=paged)
-
-
-def paged_arrays(cache, table):
-    """Host copies of the packed fields per unit, gathering each unit's blocks
-    through the page table (block g of sequence b, kv head h is record
-    table[b][g] * H + h), plus the window arrays."""
-    v, cfg = cache.view(), cache.cfg
-    H, U, nb, bb = cfg.num_kv_heads, cfg.batch * cfg.num_kv_heads, v.num_blocks, v.block_bytes
-    ob = v.blocks - cache.buffer.data_ptr()
-    flat = cache.buffer[ob:ob + U * nb * bb].view(U * nb, bb)
-    idx = torch.tensor([[int(table[u // H][g]) * H + u % H for g in range(nb)] for u in range(U)],
-                       device=flat.device)
-    recs = flat[idx]  # [U][nb][block_bytes], unit-major
-    G, D = cfg.group_size, cfg.head_dim
-
-    def field(off, nbytes, as_words):
-        a = recs[:, :, off:off + nbytes].contiguous().view(U, -1).cpu().numpy()
-        return a.view(np.uint32) if as_words else a.view(np.uint16)
-
-    out = {
-        "k_codes": field(v.off_k_codes, G * D * cfg.k_bits // 8, True),
-        "k_scale": field(v.off_k_scale, 2 * D, False),
-        "k_zero": field(v.off_k_zero, 2 * D, False),
-        "v_codes": field(v.off_v_codes, G * D * cfg.v_bits // 8, True),
-        "v_scale": field(v.off_v_scale, 2 * D, False),
-        "v_zero": field(v.off_v_zero, 2 * D, False),
-    }
-    win = gpu_arrays(cache)
-    out["k_resid"], out["v_resid"] = win["k_resid"], win["v_resid"]
-    return out
 
 
 @pytest.mark.parametrize("seed", range(128))
