@@ -62,6 +62,11 @@
  * The residual window is stored apart:
  *   k_resid, v_resid  kv_dtype [B*H][R][D]  slot i holds the token
  *                                          n_quant + i
+ * and so is one 32-bit word per block record, at the record's index:
+ *   scale_max  uint32 [B*H*NB]  bits 0-15: the largest k_scale of the
+ *                               record, bits 16-31: the largest v_scale
+ *                               (fp16 bit patterns; scales are >= 0)
+ * The decode reads these maxima to keep its fp16 matrix operands in range.
  * Tokens [0, n_quant) are packed, tokens [n_quant, n_quant + n_resid) are in
  * the residual window.  Entries beyond those are unspecified.
  *
@@ -81,8 +86,9 @@
  *     launch returns KIVI_ERR_HIP and poisons the handle (later calls return
  *     KIVI_ERR_HIP).  Device faults surface at the caller's next
  *     synchronization.  kivi_last_error_message() gives a thread-local text.
- *   - Inputs must be finite and within +-65504 (the fp16 range of S and Z);
- *     results for other inputs are unspecified.
+ *   - Inputs (k, v and q) must be finite and within +-65504, the fp16 range
+ *     of the stored scale S and zero-point Z; results for other inputs are
+ *     unspecified.
  */
 #ifndef KIVI_H_
 #define KIVI_H_
@@ -137,16 +143,27 @@ typedef struct {
   int32_t off_k_codes, off_v_codes, off_k_scale, off_k_zero, off_v_scale, off_v_zero;
   void* blocks;        /* [B*H][NB] block records */
   void *k_resid, *v_resid; /* kv_dtype */
+  void* scale_max;     /* uint32 [B*H*NB]: per record, largest key scale
+                          (low half) and value scale (high half) */
 } kivi_cache_view;
 
-/* Bytes of device memory the cache for `cfg` needs (the block records and
- * the two window arrays, each 256-byte aligned).  Pure arithmetic; no device is touched. */
+/* Bytes of device memory the cache for `cfg` needs (the block records, the
+ * two window arrays and the per-record scale maxima, each 256-byte aligned).
+ * Pure arithmetic; no device is touched. */
 kivi_status kivi_cache_bytes(const kivi_config* cfg, size_t* bytes);
 
-/* Creates an empty cache (n_quant = n_resid = 0) over the caller's device
- * buffer `dev_buf` of `dev_bytes` bytes (>= kivi_cache_bytes, 256-byte
- * aligned).  The buffer content is not read or written here.  On success
- * *out receives a handle the caller frees with kivi_cache_destroy. */
+/* Creates an empty cache (n_quant = n_resid = 0) for one attention layer
+ * over the caller's device buffer `dev_buf` of `dev_bytes` bytes
+ * (>= kivi_cache_bytes, 256-byte aligned): the per-layer store of packed
+ * keys and values plus the full-precision window that the cache manager of
+ * page "KIVI: Asymmetric 2-Bit KV Cache Quantization Guide", "Step 3:
+ * Implement the KIVI KV Cache Manager with Rolling Window", keeps.  The
+ * buffer content is not read or written here; the current device's
+ * compute-unit count is queried (a failed query is repeated by the first
+ * decode).  On success *out receives a handle the caller frees with
+ * kivi_cache_destroy.
+ * Errors: those of kivi_cache_bytes, INVALID_ARG (null dev_buf or out,
+ * unaligned dev_buf), BUFFER_TOO_SMALL. */
 kivi_status kivi_cache_create(const kivi_config* cfg, void* dev_buf,
                               size_t dev_bytes, kivi_cache** out);
 
@@ -220,16 +237,36 @@ kivi_status kivi_cache_set_page_table(kivi_cache* cache, const int32_t* table,
 kivi_status kivi_cache_get_lengths(const kivi_cache* cache, int32_t* n_quant, int32_t* n_resid);
 
 /* Packs the residual window of every sequence whose window holds exactly R
- * tokens (n_quant += R, n_resid = 0); the others are left alone. */
+ * tokens (n_quant += R, n_resid = 0); the others are left alone.  This is
+ * the step of page "KIVI: Asymmetric 2-Bit KV Cache Quantization Guide",
+ * item 3 of "The Three Structural Innovations of KIVI" (tokens that leave
+ * the streaming window are grouped and packed) and "Step 3", done for the
+ * whole window at once, with the quantizer of "Step 1".  kivi_append runs
+ * it by itself before a token enters a full window; calling it early only
+ * moves that launch.
+ * Errors: INVALID_ARG (null cache), HIP. */
 kivi_status kivi_flush_residual(kivi_cache* cache, void* stream);
 
 /* Workspace bytes kivi_decode_attn needs for num_q_heads query heads at any
- * fill level of this cache.  Pure arithmetic. */
+ * fill level of this cache: the per-split partial softmax states (m, l,
+ * o[D]) in fp32 of the split-K decode that reads the whole cache for every
+ * generated token (page "KV-Cache Quantization: I Ran the Experiments So
+ * You Don't Have To", "Component 1 - The cache is a tax that scales with
+ * tokens").  Pure arithmetic.
+ * Errors: INVALID_ARG (null cache or bytes, num_q_heads not a positive
+ * multiple of num_kv_heads). */
 kivi_status kivi_decode_attn_workspace_bytes(const kivi_cache* cache,
                                              int32_t num_q_heads,
                                              size_t* bytes);
 
-/* One decode step of attention for every sequence:
+/* One decode step of attention for every sequence (page "KIVI: Asymmetric
+ * 2-Bit KV Cache Quantization Guide", "Step 2: Implement Dequantization for
+ * Attention Computation", with the dequantization fused into the attention
+ * kernel as its "Production Serving and vLLM Deployment Trade-offs" section
+ * and page "KV-Cache Quantization: I Ran the Experiments", "Where it still
+ * breaks", item 3, require; the paper abstract, "KIVI: A Tuning-Free
+ * Asymmetric 2bit Quantization for KV Cache", for the loading of the cache
+ * as what bounds the speed):
  *   out[b][j] = sum_t softmax_t(softmax_scale * q[b][j] . k^_t) v^_t
  * over the T = n_quant + n_resid cached tokens of kv head h = j / (Hq / H)
  * (consecutive query heads share a kv head), where k^ and v^ are the
@@ -240,19 +277,20 @@ kivi_status kivi_decode_attn_workspace_bytes(const kivi_cache* cache,
  * softmax states are merged exactly (log-sum-exp) in a second kernel; the
  * workspace holds those partials.
  * With 1, 2 or 4 query heads per kv head the products run on the matrix
- * cores with fp16 operands (hi + lo pairs, about 22 significant bits).  Their
- * range needs, besides finite inputs, |q| * S < 8188 for every key scale S
- * (2-bit keys; 32752 for 4-bit keys) and S < 1023 for every value scale
- * (2-bit values; 4094 for 4-bit), i.e. value groups spanning less than about
- * 3000 (2-bit) or 61000 (4-bit); results beyond that are unspecified.
+ * cores with fp16 operands (hi + lo pairs, about 22 significant bits).  Each
+ * workgroup scales its folded operands q*S and p*S by powers of two chosen
+ * from the largest |q| of each head and the scale maxima of the records it
+ * reads, so every input in the domain stated above stays in the operands'
+ * range; the scaling is exact and undone in fp32.
  * Sequences of different lengths each attend over their own tokens; a
  * sequence without tokens gets zeros.  The splits are then planned for the
  * longest sequence, and each launch pair covers 64 sequences.
  * Errors: INVALID_ARG (nulls, Hq not a positive multiple of H, bad dtype),
  * UNSUPPORTED (a ratio Hq / H other than 1, 2, 4 or 8),
  * EMPTY (no sequence holds a token), BUFFER_TOO_SMALL (ws_bytes below the
- * workspace query), HIP. */
-kivi_status kivi_decode_attn(const kivi_cache* cache, const void* q,
+ * workspace query), HIP (the compute-unit query failed: nothing enqueued,
+ * cache unchanged; or the launch failed: the handle is poisoned). */
+kivi_status kivi_decode_attn(kivi_cache* cache, const void* q,
                              int32_t num_q_heads, float softmax_scale,
                              void* out, int32_t out_dtype, void* workspace,
                              size_t ws_bytes, void* stream);
@@ -267,7 +305,10 @@ kivi_status kivi_decode_attn(const kivi_cache* cache, const void* q,
  * than the two calls.  A full window is still packed first, in a launch of
  * its own.  With 8 query heads per kv head it runs the two calls.
  * Errors: those of kivi_decode_attn and kivi_append (INVALID_ARG for null or
- * unaligned k_new / v_new, CAPACITY), all before anything is enqueued. */
+ * unaligned k_new / v_new, CAPACITY).  The argument checks, the device query
+ * and the split plan of the state after the append all come before anything
+ * is enqueued or counted, so these errors leave the cache unchanged; a failed
+ * launch poisons the handle. */
 kivi_status kivi_append_decode_attn(kivi_cache* cache, const void* k_new, const void* v_new,
                                     const void* q, int32_t num_q_heads, float softmax_scale,
                                     void* out, int32_t out_dtype, void* workspace,

@@ -40,9 +40,10 @@ struct kivi_cache {
   const int32_t* page_table;
   int page_stride, num_pages;
   int forced_splits;
-  int cu_count;  // queried on first decode
+  int cu_count;  // compute units of the device (0: not known yet)
   bool poisoned;
   uint8_t* blocks;  // [B*H][nb] block records
+  uint32_t* scale_max;  // one entry per block record (same index)
   uint16_t* k_resid;
   uint16_t* v_resid;
 };
@@ -66,7 +67,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t off[3];  // blocks, k_resid, v_resid
+  size_t off[4];  // blocks, k_resid, v_resid, scale_max
   size_t total;
   int cap, nb;
 };
@@ -105,13 +106,14 @@ Layout layout_of(const kivi_config* c) {
   L.cap = (int)(((size_t)c->max_tokens + R - 1) / R * R);
   L.nb = (int)(L.cap / G);
   const size_t block_bytes = G * D * (c->k_bits + c->v_bits) / 8 + 8 * D;
-  const size_t sizes[3] = {
+  const size_t sizes[4] = {
       U * L.nb * block_bytes,  // block records
       U * R * D * 2,           // k_resid
       U * R * D * 2,           // v_resid
+      U * L.nb * 4,            // scale_max: one u32 per block record
   };
   size_t o = 0;
-  for (int i = 0; i < 3; ++i) {
+  for (int i = 0; i < 4; ++i) {
     L.off[i] = o;
     o = align_up(o + sizes[i]);
   }
@@ -124,6 +126,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 kivi::PackArgs base_pack_args(const kivi_cache* c) {
   kivi::PackArgs a{};
   a.blocks = c->blocks;
+  a.scale_max = c->scale_max;
   a.k_resid = c->k_resid;
   a.v_resid = c->v_resid;
   a.cap = c->cap;
@@ -364,6 +367,13 @@ kivi_status kivi_cache_create(const kivi_config* cfg, void* dev_buf, size_t dev_
   c->blocks = reinterpret_cast<uint8_t*>(base + L.off[0]);
   c->k_resid = reinterpret_cast<uint16_t*>(base + L.off[1]);
   c->v_resid = reinterpret_cast<uint16_t*>(base + L.off[2]);
+  c->scale_max = reinterpret_cast<uint32_t*>(base + L.off[3]);
+  // the decode's split planner needs the compute-unit count; a failed
+  // query is repeated by the first decode call
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+    c->cu_count = cus;
   *out = c;
   return KIVI_OK;
 }
@@ -572,26 +582,85 @@ kivi_status check_decode_args(const kivi_cache* c, const void* q, int32_t num_q_
   return KIVI_OK;
 }
 
-// Plans and launches decode attention over the current state.  With k_new
-// (matrix-core kernel only) each unit's newest window token is read from
-// k_new / v_new and stored into the window by the same launch.
-kivi_status decode_launch(kivi_cache* c, const void* q, int32_t num_q_heads, float softmax_scale,
-                          void* out, int32_t out_dtype, void* workspace, void* stream,
-                          const void* k_new, const void* v_new) {
-  const int gq = num_q_heads / c->cfg.num_kv_heads;
-  if (c->cu_count == 0) {
-    int dev = 0, cus = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess || cus < 1) return hip_fail(c, e, "querying the compute-unit count");
-    c->cu_count = cus;
-  }
+// Lengths of every sequence: the cache's, or the state a decode step will
+// see after its token append.
+struct DecodeState {
+  bool ragged;
+  int n_quant, n_resid;     // every sequence's, or the largest (ragged)
+  std::vector<int> sq, sr;  // per sequence (ragged)
+};
 
+DecodeState state_of(const kivi_cache* c) {
+  DecodeState st{c->ragged, c->n_quant, c->n_resid, {}, {}};
+  if (c->ragged) {
+    st.sq = c->sq;
+    st.sr = c->sr;
+  }
+  return st;
+}
+
+// The state after one token per sequence: a full window is packed first
+// (n_quant += R, n_resid = 0), then the token enters the window.
+DecodeState after_token(const kivi_cache* c) {
+  const int R = c->cfg.residual_length;
+  DecodeState st = state_of(c);
+  if (!st.ragged) {
+    if (st.n_resid == R) {
+      st.n_quant += R;
+      st.n_resid = 0;
+    }
+    st.n_resid += 1;
+    return st;
+  }
+  st.n_quant = st.n_resid = 0;
+  bool same = true;
+  for (int b = 0; b < c->cfg.batch; ++b) {
+    if (st.sr[b] == R) {
+      st.sq[b] += R;
+      st.sr[b] = 0;
+    }
+    st.sr[b] += 1;
+    st.n_quant = std::max(st.n_quant, st.sq[b]);
+    st.n_resid = std::max(st.n_resid, st.sr[b]);
+    same = same && st.sq[b] == st.sq[0] && st.sr[b] == st.sr[0];
+  }
+  if (same) {  // as settle(): equal lengths go back to the uniform state
+    st.ragged = false;
+    st.sq.clear();
+    st.sr.clear();
+  }
+  return st;
+}
+
+// The compute-unit count of the current device (queried at creation, or
+// here when that failed).  Nothing is enqueued; a failure leaves the cache
+// unchanged.
+kivi_status ensure_cu_count(kivi_cache* c) {
+  if (c->cu_count > 0) return KIVI_OK;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess || cus < 1)
+    return fail(KIVI_ERR_HIP, "querying the compute-unit count: %s",
+                e != hipSuccess ? hipGetErrorString(e) : "no compute units");
+  c->cu_count = cus;
+  return KIVI_OK;
+}
+
+// How a decode launch splits the token axis.
+struct DecodePlan {
+  bool use_mfma;
+  int n_split, per, n_split_packed, gps;
+};
+
+// Plans the decode launches over state `st` for gq query heads per kv head
+// (pure host arithmetic: no device access, no change of the cache).
+kivi_status plan_decode(const kivi_cache* c, const DecodeState& st, int gq, DecodePlan& out) {
   // both decode kernels walk the packed tokens in streams of 32 (a block of
   // G = 32, or half a block of G = 64)
   const int G = kivi::kStream;
   const int units = c->cfg.batch * c->cfg.num_kv_heads;
-  const int nqg = c->n_quant / G;
+  const int nqg = st.n_quant / G;
   // matrix-core kernel: up to 4 query heads per kv head share one wave
   const bool use_mfma = gq == 1 || gq == 2 || gq == 4;
   int n_split, per = 0, n_split_packed = 0, gps = 0;
@@ -622,7 +691,7 @@ kivi_status decode_launch(kivi_cache* c, const void* q, int32_t num_q_heads, flo
         // (the divisions of the longest sequence alone are too coarse to
         // fill a round with the shorter ones).
         long long best = -1;
-        const int n_cand = c->ragged ? (nqg + 3) / 4 : max_split;
+        const int n_cand = st.ragged ? (nqg + 3) / 4 : max_split;
         // Ragged caches: the plans whose whole grid (the splits past a short
         // sequence's end included) fits in one round of resident slots are
         // preferred (a second round, even of short or empty splits, was
@@ -642,7 +711,7 @@ kivi_status decode_launch(kivi_cache* c, const void* q, int32_t num_q_heads, flo
         double best1 = -1.0;
         for (int i = 1; i <= n_cand; ++i) {
           int g, np;
-          if (c->ragged) {
+          if (st.ragged) {
             g = 4 * i;
             np = (nqg + g - 1) / g;
             if (np > kivi::kMaxSplits - 1) continue;
@@ -650,9 +719,9 @@ kivi_status decode_launch(kivi_cache* c, const void* q, int32_t num_q_heads, flo
             plan(i, g, np);
           }
           long long work = (long long)units * np;
-          if (c->ragged) {
+          if (st.ragged) {
             work = 0;
-            for (int b = 0; b < c->cfg.batch; ++b) work += (c->sq[b] / G + g - 1) / g;
+            for (int b = 0; b < c->cfg.batch; ++b) work += (st.sq[b] / G + g - 1) / g;
             work *= c->cfg.num_kv_heads;
             // (a ragged launch covers at most kDecodeChunk sequences)
             const long long grid = (long long)np * std::min(c->cfg.batch, kivi::kDecodeChunk) * c->cfg.num_kv_heads;
@@ -677,9 +746,9 @@ kivi_status decode_launch(kivi_cache* c, const void* q, int32_t num_q_heads, flo
         }
       }
     }
-    n_split = n_split_packed + (c->n_resid > 0 ? 1 : 0);
+    n_split = n_split_packed + (st.n_resid > 0 ? 1 : 0);
   } else {
-    const int n_items = nqg + (c->n_resid + G - 1) / G;
+    const int n_items = nqg + (st.n_resid + G - 1) / G;
     if (c->forced_splits > 0) {
       n_split = c->forced_splits;
     } else {
@@ -695,8 +764,20 @@ kivi_status decode_launch(kivi_cache* c, const void* q, int32_t num_q_heads, flo
   if (n_split > std::min(kivi::kMaxSplits, max_items(c)))
     return fail(KIVI_ERR_UNSUPPORTED, "internal: %d planned splits exceed the workspace bound %d", n_split,
                 std::min(kivi::kMaxSplits, max_items(c)));
+  out = DecodePlan{use_mfma, n_split, per, n_split_packed, gps};
+  return KIVI_OK;
+}
+
+// Launches decode attention over the cache's current state with a plan made
+// for that state.  With k_new (matrix-core kernel only) each unit's newest
+// window token is read from k_new / v_new and stored into the window by the
+// same launch.
+kivi_status decode_launch(kivi_cache* c, const DecodePlan& plan, const void* q, int32_t num_q_heads,
+                          float softmax_scale, void* out, int32_t out_dtype, void* workspace, void* stream,
+                          const void* k_new, const void* v_new) {
   kivi::DecodeArgs a{};
   a.blocks = c->blocks;
+  a.scale_max = c->scale_max;
   a.k_resid = c->k_resid;
   a.v_resid = c->v_resid;
   a.q = static_cast<const uint16_t*>(q);
@@ -705,17 +786,17 @@ kivi_status decode_launch(kivi_cache* c, const void* q, int32_t num_q_heads, flo
   a.B = c->cfg.batch;
   a.H = c->cfg.num_kv_heads;
   a.Hq = num_q_heads;
-  a.gq = gq;
+  a.gq = num_q_heads / c->cfg.num_kv_heads;
   a.cap = c->cap;
   a.nb = c->nb;
   a.G = c->cfg.group_size;
   a.R = c->cfg.residual_length;
   a.n_quant = c->n_quant;
   a.n_resid = c->n_resid;
-  a.n_split = n_split;
-  a.items_per_split = per;
-  a.n_split_packed = n_split_packed;
-  a.groups_per_split = gps;
+  a.n_split = plan.n_split;
+  a.items_per_split = plan.per;
+  a.n_split_packed = plan.n_split_packed;
+  a.groups_per_split = plan.gps;
   a.qscale = softmax_scale * 1.4426950408889634f;  // log2(e): base-2 softmax
   a.page_table = c->page_table;
   a.page_stride = c->page_stride;
@@ -726,7 +807,7 @@ kivi_status decode_launch(kivi_cache* c, const void* q, int32_t num_q_heads, flo
   a.v_resid_w = c->v_resid;
   if (!c->ragged) {
     hipError_t e = kivi::launch_decode(a, c->cfg.k_bits, c->cfg.v_bits, c->cfg.kv_dtype, out_dtype,
-                                       use_mfma, static_cast<hipStream_t>(stream));
+                                       plan.use_mfma, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(c, e, "decode launch");
     return KIVI_OK;
   }
@@ -744,7 +825,7 @@ kivi_status decode_launch(kivi_cache* c, const void* q, int32_t num_q_heads, flo
       a.seq_len[i][1] = c->sr[b0 + i];
     }
     hipError_t e = kivi::launch_decode(a, c->cfg.k_bits, c->cfg.v_bits, c->cfg.kv_dtype, out_dtype,
-                                       use_mfma, static_cast<hipStream_t>(stream));
+                                       plan.use_mfma, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(c, e, "decode launch (sequences of different lengths)");
   }
   return KIVI_OK;
@@ -754,14 +835,16 @@ kivi_status decode_launch(kivi_cache* c, const void* q, int32_t num_q_heads, flo
 
 extern "C" {
 
-kivi_status kivi_decode_attn(const kivi_cache* cc, const void* q, int32_t num_q_heads,
-                             float softmax_scale, void* out, int32_t out_dtype, void* workspace,
-                             size_t ws_bytes, void* stream) {
-  kivi_cache* c = const_cast<kivi_cache*>(cc);
+kivi_status kivi_decode_attn(kivi_cache* c, const void* q, int32_t num_q_heads, float softmax_scale,
+                             void* out, int32_t out_dtype, void* workspace, size_t ws_bytes,
+                             void* stream) {
   kivi_status st = check_decode_args(c, q, num_q_heads, out, out_dtype, workspace, ws_bytes);
   if (st != KIVI_OK) return st;
   if (c->n_quant + c->n_resid < 1) return fail(KIVI_ERR_EMPTY, "decode on an empty cache");
-  return decode_launch(c, q, num_q_heads, softmax_scale, out, out_dtype, workspace, stream, nullptr,
+  if ((st = ensure_cu_count(c)) != KIVI_OK) return st;
+  DecodePlan plan;
+  if ((st = plan_decode(c, state_of(c), num_q_heads / c->cfg.num_kv_heads, plan)) != KIVI_OK) return st;
+  return decode_launch(c, plan, q, num_q_heads, softmax_scale, out, out_dtype, workspace, stream, nullptr,
                        nullptr);
 }
 
@@ -782,11 +865,17 @@ kivi_status kivi_append_decode_attn(kivi_cache* c, const void* k_new, const void
   if ((long long)longest + 1 > c->cfg.max_tokens)
     return fail(KIVI_ERR_CAPACITY, "appending a token to %d exceeds max_tokens %d", longest,
                 c->cfg.max_tokens);
+  // everything that can fail without a launch failing is settled before the
+  // first launch: the device query and the split plan of the state after the
+  // token append
+  if ((st = ensure_cu_count(c)) != KIVI_OK) return st;
   const int gq = num_q_heads / c->cfg.num_kv_heads;
+  DecodePlan plan;
+  if ((st = plan_decode(c, after_token(c), gq, plan)) != KIVI_OK) return st;
   if (gq == 8) {  // vector-ALU decode: the append stays a launch of its own
     if ((st = kivi_append(c, k_new, v_new, 1, stream)) != KIVI_OK) return st;
-    return decode_launch(c, q, num_q_heads, softmax_scale, out, out_dtype, workspace, stream, nullptr,
-                         nullptr);
+    return decode_launch(c, plan, q, num_q_heads, softmax_scale, out, out_dtype, workspace, stream,
+                         nullptr, nullptr);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int R = c->cfg.residual_length;
@@ -802,7 +891,7 @@ kivi_status kivi_append_decode_attn(kivi_cache* c, const void* k_new, const void
     if (c->n_resid == R && (st = flush_window(c, s)) != KIVI_OK) return st;
     c->n_resid += 1;
   }
-  return decode_launch(c, q, num_q_heads, softmax_scale, out, out_dtype, workspace, stream, k_new,
+  return decode_launch(c, plan, q, num_q_heads, softmax_scale, out, out_dtype, workspace, stream, k_new,
                        v_new);
 }
 
@@ -830,6 +919,7 @@ kivi_status kivi_cache_get_view(const kivi_cache* c, kivi_cache_view* v) {
   v->blocks = c->blocks;
   v->k_resid = c->k_resid;
   v->v_resid = c->v_resid;
+  v->scale_max = c->scale_max;
   return KIVI_OK;
 }
 

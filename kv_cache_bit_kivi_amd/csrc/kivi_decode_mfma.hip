@@ -456,6 +456,59 @@ __device__ __forceinline__ void issue_vstage(const DecodeArgs& a, long long u, i
 }
 
 // ---------------------------------------------------------------------------
+// Operand range.  The folded operands q''*S (keys) and p'*S (values) are fp16
+// hi + lo pairs, so they must stay below 65504.  Each workgroup scales them by
+// powers of two: q'' by 2^-Ek (one exponent per head, from the head's largest
+// |q| and the largest key scale of the records the split reads) and p' by
+// 2^-Ev (one per split, from the largest value scale), such that every
+// product stays below 2^15.  Scaling by a power of two is exact; the scores
+// take 2^Ek back in fp32, and the partial's (m, l, o) carry 2^-Ev in l and o,
+// which the partial's m + Ev compensates in the merge's weights 2^(m - M).
+// Ordinary inputs get Ek = Ev = 0.
+
+// Largest stored key scale and value scale over the block records of
+// streams [gb, ge) of unit u (the same on every lane of the wave).
+template <int GT, bool PAGED>
+__device__ __forceinline__ void split_scale_max(const DecodeArgs& a, long long u, int gb, int ge, float& sk,
+                                                float& sv) {
+  constexpr int SPB = GT / kStream;
+  const int lane = threadIdx.x & 63;
+  const int blk0 = gb / SPB, blk1 = (ge - 1) / SPB;
+  uint32_t mk = 0, mv = 0;
+  for (int base = blk0; base <= blk1; base += 256) {
+    uint32_t e[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // four independent loads in flight per lane
+      const int blk = base + lane + 64 * i;
+      long long r = 0;
+      if (blk <= blk1) {
+        if constexpr (PAGED) {
+          r = record_index(a.page_table, a.page_stride, a.num_pages, a.nb, a.H, u, blk);
+        } else {
+          r = u * a.nb + blk;
+        }
+      }
+      e[i] = blk <= blk1 ? a.scale_max[r] : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      mk = max(mk, e[i] & 0xffffu);
+      mv = max(mv, e[i] >> 16);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    mk = max(mk, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mk), off)));
+    mv = max(mv, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mv), off)));
+  }
+  sk = __half2float(__ushort_as_half(static_cast<uint16_t>(mk)));
+  sv = __half2float(__ushort_as_half(static_cast<uint16_t>(mv)));
+}
+
+// Smallest E >= 0 with x * 2^-E < 2^15 (x >= 0 finite).
+__device__ __forceinline__ int range_exp(float x) { return max(0, __builtin_amdgcn_frexp_expf(x) - 15); }
+
+// ---------------------------------------------------------------------------
 // Key wave: scores of each step on the matrix cores, online softmax, and the
 // probabilities handed to the value wave.  Writes m and l of the partial.
 template <int KB, int VB, bool BF16, int NQ, int GT, bool PAGED>
@@ -475,13 +528,8 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
   __builtin_amdgcn_s_setprio(1);
   // the first stage's loads go out before q is read: their latencies overlap
   issue_kstage<KB, VB, GT, PAGED>(a, u, gb, min(4, ge - gb), smem, smem + S::offKM0);
-  // q'' = q * 2^(lf(e) - 3) as fp16 pairs for head hq, channels 32*lk ..
-  // 32*lk+31 (pair p: channels 2p, 2p+1; e = p & 3 its pair class in the run
-  // of 8): the code-position factor of the key codes it multiplies, over 8.
-  // Power-of-two factors keep q'' exact (a bf16 q is rounded to fp16 once).
-  // softmax_scale * log2(e) multiplies the scores afterwards.  Head slots
-  // hq >= NQ carry q'' = 0 and are masked out of the softmax.
-  uint32_t q2[16];
+  // q of head hq, channels 32*lk .. 32*lk+31 (head slots hq >= NQ: zeros)
+  float qf[32];
   if (hq < NQ) {
     const uint16_t* qp = a.q + ((long long)b * a.Hq + kvh * NQ + hq) * D + 32 * lk;
 #pragma unroll
@@ -490,18 +538,46 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
       const uint32_t ww[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float f = KS::lf(e) >= 3 ? static_cast<float>(1 << (KS::lf(e) - 3))
-                                       : 1.0f / static_cast<float>(1 << (3 - KS::lf(e)));
-        q2[i / 2 + e] = pk_rne(to_f32<BF16>(static_cast<uint16_t>(ww[e])) * f,
-                               to_f32<BF16>(static_cast<uint16_t>(ww[e] >> 16)) * f);
+        qf[i + 2 * e] = to_f32<BF16>(static_cast<uint16_t>(ww[e]));
+        qf[i + 2 * e + 1] = to_f32<BF16>(static_cast<uint16_t>(ww[e] >> 16));
       }
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) q2[i] = 0u;
+    for (int i = 0; i < 32; ++i) qf[i] = 0.0f;
   }
-  // raw product -> score: products are c q S 2^(F-27)
-  const float k_unscale = a.qscale * static_cast<float>(1 << (27 - KS::F));
+  // operand range exponents: Ek for head hq, Ev for the split
+  float sk_max, sv_max;
+  split_scale_max<GT, PAGED>(a, u, gb, ge, sk_max, sv_max);
+  float qabs = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) qabs = fmaxf(qabs, fabsf(qf[i]));
+  qabs = swap_max<16>(qabs);
+  qabs = swap_max<32>(qabs);  // the 128 channels of head hq
+  const int ek = range_exp(static_cast<float>(1 << (KS::F - 3)) * qabs * fmaxf(sk_max, 1.0f));
+  const int ev = range_exp(static_cast<float>(1 << VS::F) * sv_max);
+  // q'' = q * 2^(lf(e) - 3 - Ek) as fp16 pairs (pair p: channels 2p, 2p+1;
+  // e = p & 3 its pair class in the run of 8): the code-position factor of
+  // the key codes it multiplies, over 8, and the range exponent.
+  // Power-of-two factors keep q'' exact (a bf16 q is rounded to fp16 once).
+  // softmax_scale * log2(e) * 2^Ek multiplies the scores afterwards.  Head
+  // slots hq >= NQ carry q'' = 0 and are masked out of the softmax.
+  uint32_t q2[16];
+#pragma unroll
+  for (int i = 0; i < 32; i += 8) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int x = KS::lf(e) - 3 - ek;
+      q2[i / 2 + e] = pk_rne(__builtin_amdgcn_ldexpf(qf[i + 2 * e], x), __builtin_amdgcn_ldexpf(qf[i + 2 * e + 1], x));
+    }
+  }
+  // raw product -> score: products are c q S 2^(F-27-Ek)
+  const float k_unscale = __builtin_amdgcn_ldexpf(a.qscale, 27 - KS::F + ek);
+  const float z_unscale = __builtin_amdgcn_ldexpf(a.qscale, ek);
+  // p' = p * 2^(lf(e') - Ev): the value-code factor of its token position
+  float p_exp[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) p_exp[e] = static_cast<float>(VS::lf(e) - ev);
 
   const bool diag = (lc & 3) == lk;  // lane holds scores (stream lk)
   float m_run = -INFINITY;           // running max of head hq (base 2)
@@ -578,7 +654,7 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
       bias = fmaf(bcls[e], KS::lf(e) >= 3 ? 1.0f / static_cast<float>(1 << (KS::lf(e) - 3))
                                           : static_cast<float>(1 << (3 - KS::lf(e))), bias);
     bias = swap_sum<16>(bias);
-    bias = swap_sum<32>(bias) * a.qscale;  // all 128 channels: head hq, group g0 + (lc & 3)
+    bias = swap_sum<32>(bias) * z_unscale;  // all 128 channels: head hq, group g0 + (lc & 3)
 
     // ------------------------------------------------------------- softmax
     // The 16 diagonal lanes hold the step's 512 scores (head hq, stream lk,
@@ -623,13 +699,13 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
     m_run = m_new;
 #pragma unroll
     for (int e = 0; e < 4; ++e) lcls[e] *= alpha;
-    // p scaled by the value-code factor of its token position: token t sits
-    // in pair class e'(t) = (t mod 8) / 2 of its run of 8
+    // p scaled by the value-code factor of its token position and 2^-Ev:
+    // token t sits in pair class e'(t) = (t mod 8) / 2 of its run of 8
     f32x4 p0, p1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      p0[i] = fast_exp2(x[i] + (static_cast<float>(VS::lf(i >> 1)) - m_run));
-      p1[i] = fast_exp2(x[4 + i] + (static_cast<float>(VS::lf(2 + (i >> 1))) - m_run));
+      p0[i] = fast_exp2(x[i] + (p_exp[i >> 1] - m_run));
+      p1[i] = fast_exp2(x[4 + i] + (p_exp[2 + (i >> 1)] - m_run));
     }
     lcls[0] += p0[0] + p0[1];
     lcls[1] += p0[2] + p0[3];
@@ -649,8 +725,9 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
   l = swap_sum<16>(l);
   l = swap_sum<32>(l);  // the 16 lanes of head hq
   if (lk == 0 && jt == 0 && hq < NQ) {
+    // l and the value wave's o carry 2^-Ev; m + Ev restores their weight
     float* P = a.partial + (((long long)b * a.Hq + kvh * NQ + hq) * a.n_split + split) * (D + 2);
-    P[0] = m_run;
+    P[0] = m_run + static_cast<float>(ev);
     P[1] = l;
   }
 }

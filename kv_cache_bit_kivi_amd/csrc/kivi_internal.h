@@ -69,6 +69,9 @@ struct PackArgs {
   int r_dst_slot0;
   // cache arrays
   uint8_t* blocks;  // [units][nb] block records
+  // per block record (same index as the record): the largest stored key
+  // scale (fp16 bits, low half) and value scale (high half) of the record
+  uint32_t* scale_max;
   uint16_t* k_resid;
   uint16_t* v_resid;
   int cap;    // token capacity per unit
@@ -87,6 +90,7 @@ struct PackArgs {
 // One decode-attention launch (split kernel + merge kernel).
 struct DecodeArgs {
   const uint8_t* blocks;  // [B*H][nb] block records
+  const uint32_t* scale_max;  // per record: largest key scale | largest value scale << 16
   const uint16_t* k_resid;
   const uint16_t* v_resid;
   const uint16_t* q;   // [B][Hq][D] kv dtype

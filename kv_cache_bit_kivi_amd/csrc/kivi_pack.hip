@@ -173,6 +173,13 @@ __device__ __forceinline__ float max3_f32(float a, float b, float c) {
   return r;
 }
 
+// Largest value over the 64 lanes of the wave.
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = max(x, static_cast<uint32_t>(__shfl_xor(static_cast<int>(x), off)));
+  return x;
+}
+
 // Orders this workgroup's LDS traffic; unlike __syncthreads it does not wait
 // for the scale/zero stores just issued to complete.
 __device__ __forceinline__ void lds_barrier() {
@@ -342,8 +349,12 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
   __shared__ __align__(16) float kmn[D], ksc[D], krc[D];
   __shared__ __align__(16) float vmn[D], vsc[D], vrc[D];  // index m * G + row (D / G groups per row)
   // set when some group of the block has a scale below 2^-100; kept in the
-  // padding of the first key row (the LDS total stays at 20 KiB)
+  // padding of the first key row (the LDS total stays at 20 KiB), next to
+  // the largest stored key and value scale of the block (fp16 bit patterns:
+  // scales are >= 0, so their bit patterns order like their values)
   int& tiny_scale = *reinterpret_cast<int*>(&kt[D]);
+  uint32_t& smax_k = *reinterpret_cast<uint32_t*>(&kt[D + 2]);
+  uint32_t& smax_v = *reinterpret_cast<uint32_t*>(&kt[D + 4]);
 
   const int tid = threadIdx.x;
   const int item = blockIdx.x;
@@ -381,8 +392,8 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
   constexpr BlockLayout BL = block_layout(KB, VB, G);
   const int blk = item;
   const int gblk = dst_blk0 + blk;
-  uint8_t* const rec =  // this block's record
-      a.blocks + record_index(a.page_table, a.page_stride, a.num_pages, a.nb, a.H, u, gblk) * BL.bytes;
+  const long long ri = record_index(a.page_table, a.page_stride, a.num_pages, a.nb, a.H, u, gblk);
+  uint8_t* const rec = a.blocks + ri * BL.bytes;  // this block's record
   {
     // 16-byte pieces tid, tid + 256, ... of the G x 128 tiles (rows 16
     // apart), all loads issued before the first LDS store
@@ -400,7 +411,10 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
       *reinterpret_cast<uint4*>(&kt[(row + 16 * i) * RS + col]) = kx[i];
       *reinterpret_cast<uint4*>(&vt[(row + 16 * i) * RS + col]) = vx[i];
     }
-    if (tid == 0) tiny_scale = 0;
+    if (tid == 0) {
+      tiny_scale = 0;
+      smax_k = smax_v = 0u;
+    }
   }
   __syncthreads();
 
@@ -440,8 +454,10 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
     if (t0 || t1) tiny_scale = 1;
     kmn[p2] = mn0; ksc[p2] = s0; krc[p2] = r0;
     kmn[p2 + 1] = mn1; ksc[p2 + 1] = s1; krc[p2 + 1] = r1;
-    store_stream(reinterpret_cast<uint32_t*>(rec + BL.k_scale) + tid,
-                 f16_bits_canon(s0) | (static_cast<uint32_t>(f16_bits_canon(s1)) << 16));
+    const uint32_t sb0 = f16_bits_canon(s0), sb1 = f16_bits_canon(s1);
+    const uint32_t top = wave_max(max(sb0, sb1));  // wave 0: all 128 key channels
+    if (tid == 0) atomicMax(&smax_k, top);
+    store_stream(reinterpret_cast<uint32_t*>(rec + BL.k_scale) + tid, sb0 | (sb1 << 16));
     store_stream(reinterpret_cast<uint32_t*>(rec + BL.k_zero) + tid,
                  f16_bits_canon(mn0) | (static_cast<uint32_t>(f16_bits_canon(mn1)) << 16));
   } else if (tid < D / 2 + D) {
@@ -485,11 +501,16 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
     vmn[i] = mn;
     vsc[i] = s;
     vrc[i] = rcp;
-    store_stream(reinterpret_cast<uint16_t*>(rec + BL.v_scale) + i, f16_bits_canon(s));  // [m][row]
+    const uint32_t sb = f16_bits_canon(s);
+    const uint32_t top = wave_max(sb);  // waves 1 and 2: 64 value groups each
+    if ((tid & 63) == 0) atomicMax(&smax_v, top);
+    store_stream(reinterpret_cast<uint16_t*>(rec + BL.v_scale) + i, static_cast<uint16_t>(sb));  // [m][row]
     store_stream(reinterpret_cast<uint16_t*>(rec + BL.v_zero) + i, f16_bits_canon(mn));
   }
   lds_barrier();
 
+  // the record's largest key and value scale, for the decode's operand range
+  if (tid == 0) store_stream(a.scale_max + ri, smax_k | (smax_v << 16));
   const bool tiny = tiny_scale != 0;
   if (tid < 128) {
     // ---- key code words: word w of token t holds channels w*PK .. w*PK+PK-1.

@@ -52,6 +52,7 @@ class kivi_cache_view(ctypes.Structure):
         ("off_v_scale", ctypes.c_int32), ("off_v_zero", ctypes.c_int32),
         ("blocks", ctypes.c_void_p),
         ("k_resid", ctypes.c_void_p), ("v_resid", ctypes.c_void_p),
+        ("scale_max", ctypes.c_void_p),
     ]
 
 
@@ -360,7 +361,8 @@ class KiviCache:
     def arrays(self):
         """Device tensors aliasing the cache fields, shaped [B*H][...] per unit.
         The packed fields are strided views into the block records: unit u,
-        block g, field f lies at blocks + (u * NB + g) * block_bytes + off_f."""
+        block g, field f lies at blocks + (u * NB + g) * block_bytes + off_f;
+        "scale_max" holds one word per record index ([B*H][NB] unit-major)."""
         torch = self.torch
         v = self.view()
         c = self.cfg
@@ -386,4 +388,6 @@ class KiviCache:
             "v_zero": field(v.off_v_zero, 2 * D, torch.int16),
             "k_resid": sub(v.k_resid, U * R * D, torch.int16, 2),
             "v_resid": sub(v.v_resid, U * R * D, torch.int16, 2),
+            # one word per block record, at the record's index
+            "scale_max": sub(v.scale_max, U * nb, torch.int32, 4),
         }

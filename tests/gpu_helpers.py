@@ -19,7 +19,7 @@ def gpu_arrays(cache, units=None):
         if units is not None:
             t = t[torch.as_tensor(units, device=t.device)]
         a = t.contiguous().view(t.shape[0], -1).cpu().numpy()
-        out[name] = a.view(np.uint32) if "codes" in name else a.view(np.uint16)
+        out[name] = a.view(np.uint32) if ("codes" in name or name == "scale_max") else a.view(np.uint16)
     return out
 
 
@@ -54,6 +54,44 @@ def paged_arrays(cache, table, units=None):
     win = gpu_arrays(cache, units)
     out["k_resid"], out["v_resid"] = win["k_resid"], win["v_resid"]
     return out
+
+
+def expected_scale_max(ref):
+    """Per unit and packed block of the oracle cache: the largest key scale
+    (low half) and value scale (high half) as fp16 bit patterns, uint32
+    [U][n_quant / G].  Scales are >= 0, so the largest bit pattern is the
+    largest value."""
+    U, D, nb = ref.B * ref.H, ref.D, ref.num_blocks
+    nblk = ref.n_quant // ref.G
+    ks = ref.array("k_scale").reshape(U, nb, D)[:, :nblk].max(-1, initial=0).astype(np.uint32)
+    vs = ref.array("v_scale").reshape(U, nb, D)[:, :nblk].max(-1, initial=0).astype(np.uint32)
+    return ks | (vs << 16)
+
+
+def assert_scale_max(cache, ref, units=None, table=None):
+    """The GPU cache's per-record scale maxima equal the oracle's, for the
+    packed blocks of the listed units (all by default; the oracle cache holds
+    every unit of the GPU cache); paged caches give their table (record of
+    unit u, block g: table[u // H][g] * H + u % H)."""
+    import torch
+    want = expected_scale_max(ref)
+    H = cache.cfg.num_kv_heads
+    flat = cache.arrays()["scale_max"].reshape(-1)
+    units = range(want.shape[0]) if units is None else units
+    nb = cache.view().num_blocks
+    n = want.shape[1]
+    if n == 0:
+        return
+    for u in units:
+        if table is None:
+            idx = torch.arange(u * nb, u * nb + n, device=flat.device)
+        else:
+            idx = torch.as_tensor([int(table[u // H][g]) * H + u % H for g in range(n)], device=flat.device)
+        got = flat[idx].cpu().numpy().view(np.uint32)
+        row = want[u]
+        bad = np.nonzero(got != row)[0]
+        assert bad.size == 0, (f"scale_max: {bad.size} mismatches, unit {u} block {bad[0]}: "
+                               f"gpu {got[bad[0]]:#010x} oracle {row[bad[0]]:#010x}")
 
 
 def oracle_arrays(ref):

@@ -75,7 +75,8 @@ def test_cache_bytes_closed_form():
     U, D = 256, 128
     expect = (U * cap * D * 2 // 8 * 2  # k and v codes
               + 4 * U * (cap // 32) * D * 2  # k/v scale and zero
-              + 2 * U * 128 * D * 2)  # windows
+              + 2 * U * 128 * D * 2  # windows
+              + U * (cap // 32) * 4)  # one scale-maximum word per block record
     assert kivi.kivi_cache_bytes(c) == expect  # every array is a multiple of 256 B
 
 
