@@ -1,24 +1,32 @@
 """Benchmark of the KIVI hot path on one MI355X.
 
-One step = one pass of the whole hot path over one layer's synthetic batch:
-  1. bulk append of the T-token prefix: quantize + bit-pack every full
-     window straight from the input, copy the last R tokens to the window
-     (one pack launch);
-  2. the full window is packed before the decode token enters it (flush,
-     one launch);
-  3. the decode step: the token is appended and split-K decode attention
-     runs over the packed cache plus the window in the same launch, then the
-     cross-split merge (kivi_append_decode_attn, two launches).
-The cache is reset (host counters only) at the start of each step.
+One step = one decode step of every layer of the workload, from the state
+the prefix leaves (n_quant = T - R packed tokens, n_resid = R window tokens):
+  1. the full window is packed before the new token enters it (flush, one
+     pack launch);
+  2. the token is appended and split-K decode attention runs over the packed
+     cache plus the window in the same launch (the decode kernel), then the
+     cross-split merge (kivi_append_decode_attn: the flush, decode and merge
+     launches);
+  3. the lengths return to (T - R, R) on the host (kivi_cache_set_lengths).
+     The new token is a copy of window slot 0's, so the flush packs the same
+     window every step and the step's work and results repeat exactly.
+The prefix pack (quantize + bit-pack T tokens per unit, the bulk prefill) is
+timed on its own after the timed steps, as the "pack" phase.
 
-Default workload: Llama-2-7B-shaped MHA layer, batch 8, 32 heads, T = 4096,
-2-bit, G = 32, R = 128, fp16 (--workload c1).  `value` is the step's
-algorithmic bytes (fp16 K/V read by the pack, codes + scale/zero + window
-written and read back, q, out) divided by the step time, in GB/s.
+Default workload: Llama-3-8B-shaped GQA layer, batch 32, 32 query / 8 kv
+heads, T = 32768, 2-bit, G = 32, R = 128, fp16 (--workload c2).  `value` is
+the step's algorithmic bytes (window read, codes + scale/zero written by the
+flush, the token read and written, codes + scale/zero + window + q read by
+the decode, out written by the merge) divided by the step time, in GB/s.
+The roofline describes the decode kernel: its algorithmic bytes per launch
+over its mean launch time, from HIP events recorded by the library right
+around the kernel on the stream it runs on (kivi_set_timing_events).
 
 Prints one JSON line.  Inputs are resident in HBM before timing starts.
 """
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -35,14 +43,16 @@ METRIC = "fused 2-bit dequant decode-attn effective HBM GB/s + % peak; pack GB/s
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="c1", choices=["c0", "c1", "c2", "c3", "c4"])
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="c2", choices=["c0", "c1", "c2", "c3", "c4"])
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--phase-every", type=int, default=4,
-                   help="bracket the phases with HIP events on every N-th timed step")
-    p.add_argument("--cold-iters", type=int, default=20,
-                   help="decode-only iterations with the last-level cache scrubbed")
+    p.add_argument("--phase-every", type=int, default=2,
+                   help="bracket the launches with HIP events on every N-th timed step")
+    p.add_argument("--pack-iters", type=int, default=20, help="timed prefix packs (all layers each)")
+    p.add_argument("--cold-iters", type=int, default=50,
+                   help="decode-only launches with the last-level cache scrubbed before each")
+    p.add_argument("--probe-iters", type=int, default=20, help="streaming-read probe launches")
     p.add_argument("--ragged", action="store_true",
                    help="sequences of different lengths: sequence b's prefix has T_b tokens, "
                         "drawn uniformly from [T/2, T] (seed 0)")
@@ -55,14 +65,20 @@ def parse():
 # ------------------------------------------------------------ byte accounting
 
 def algorithmic_bytes(w, lens=None):
-    """Bytes the method must move per step, per phase (whole batch), with
+    """Bytes the method must move per layer, per phase (whole batch), with
     every sequence's prefix T tokens long or sequence b's lens[b] long.
-    Codes: bits/8 per element; scale + zero: 4 bytes per group of G."""
+    Codes: bits/8 per element; scale + zero: 4 bytes per group of G.
+      pack   : the prefix pack (read T tokens of K and V, write codes,
+               scale/zero and the last r tokens into the window)
+      flush  : a full window packed (read R tokens, write codes, scale/zero)
+      decode : the decode kernel (the token read and written into the
+               window; codes, scale/zero and window tokens read; q read)
+      merge  : the merge kernel (out written, fp32; partials excluded)"""
     D, G, R = w.head_dim, w.group_size, w.residual_length
     e = 2  # fp16 / bf16
     codes = lambda n: n * D * (w.k_bits + w.v_bits) // 8
     meta = lambda n: (n // G) * D * 4 + n * (D // G) * 4
-    tot = {"pack": 0, "flush": 0, "decode": 0}
+    tot = {"pack": 0, "flush": 0, "decode": 0, "merge": 0}
     for T in (lens if lens is not None else [w.tokens] * w.batch):
         r = (T - 1) % R + 1
         nq = T - r
@@ -73,9 +89,14 @@ def algorithmic_bytes(w, lens=None):
         else:
             nq2, r2 = nq, r + 1
         token = 2 * (2 * D * e)  # the appended token, read and written into the window
-        tot["decode"] += (token + codes(nq2) + meta(nq2) + 2 * r2 * D * e + w.gq * D * e
-                          + w.gq * D * 4)
+        tot["decode"] += token + codes(nq2) + meta(nq2) + 2 * r2 * D * e + w.gq * D * e
+        tot["merge"] += w.gq * D * 4
     return {k: w.kv_heads * v for k, v in tot.items()}
+
+
+def step_bytes(ab):
+    """Bytes of one decode step (flush + decode + merge) of one layer."""
+    return ab["flush"] + ab["decode"] + ab["merge"]
 
 
 def ragged_lengths(w):
@@ -84,18 +105,11 @@ def ragged_lengths(w):
     return [int(x) for x in np.random.default_rng(0).integers(w.tokens // 2, w.tokens + 1, w.batch)]
 
 
-# the kernel each phase's roofline describes, and the source it is built from
-PHASE_KERNEL = {
-    "pack": ("pack_kernel", "kivi_pack.hip", "one launch: quantize + bit-pack the prefix, "
-             "copy the last window"),
-    "flush": ("pack_kernel", "kivi_pack.hip", "one launch: window flush"),
-    "decode": ("decode split + merge", None, "two launches: token append + split-K attention, "
-               "merge"),
-}
-
-
-def decode_source(w):
-    return "kivi_decode_mfma.hip" if w.gq in (1, 2, 4) else "kivi_decode.hip"
+def decode_kernel(w):
+    """Name and source of the split-K decode kernel that serves the workload."""
+    if w.gq in (1, 2, 4):
+        return "decode_mfma", "kivi_decode_mfma.hip"
+    return "decode_split_valu", "kivi_decode.hip"
 
 
 def traffic_from_profile(kernel, workload, kernel_src):
@@ -119,6 +133,15 @@ def traffic_from_profile(kernel, workload, kernel_src):
         return None
 
 
+def stats(samples_s):
+    """mean, median, p10, p90 (microseconds) and count of durations in seconds."""
+    import numpy as np
+    a = np.asarray(samples_s) * 1e6
+    return {"us_mean": float(a.mean()), "us_median": float(np.median(a)),
+            "us_p10": float(np.percentile(a, 10)), "us_p90": float(np.percentile(a, 90)),
+            "samples": int(a.size)}
+
+
 # ---------------------------------------------------------------- GPU run
 
 def run(args):
@@ -130,55 +153,74 @@ def run(args):
 
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
-    T = w.tokens
+    T, R, B = w.tokens, w.residual_length, w.batch
     scale = 1.0 / np.sqrt(w.head_dim)
-    lens = ragged_lengths(w) if args.ragged else None
-    layers = []
-    for layer in range(w.layers):
-        x = make_layer(w, seed=layer, device=dev, n_new=1)
-        layers.append(dict(
-            kp=x.k[:, :, :T].contiguous(), vp=x.v[:, :, :T].contiguous(),
-            kn=x.k[:, :, T:].contiguous(), vn=x.v[:, :, T:].contiguous(), q=x.q,
-            cache=kivi.KiviCache(w.batch, w.kv_heads, T + 1, k_bits=w.k_bits, v_bits=w.v_bits,
-                                 group_size=w.group_size, residual_length=w.residual_length,
-                                 dtype=w.dtype, device=dev),
-            out=torch.empty(w.batch, w.q_heads, w.head_dim, dtype=torch.float32, device=dev)))
-        del x
+    lens = ragged_lengths(w) if args.ragged else [T] * B
+    r0 = [(t - 1) % R + 1 for t in lens]  # window tokens of each prefix
+    q0 = [t - r for t, r in zip(lens, r0)]
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
-    for L in layers:
-        c = L["cache"]
-        ws = c.workspace(w.q_heads)  # allocated before timing
-        # the C-ABI calls of one step with their arguments resolved once: the
-        # step then costs the host a few microseconds per call (the checks
-        # of the KiviCache convenience methods take longer than a c1 step on
-        # the GPU)
-        L["append"] = (c.handle, L["kp"].data_ptr(), L["vp"].data_ptr(), T, sp)
-        L["decode"] = (c.handle, L["kn"].data_ptr(), L["vn"].data_ptr(), L["q"].data_ptr(),
-                       w.q_heads, float(scale), L["out"].data_ptr(), kivi.KIVI_F32,
-                       ws.data_ptr(), ws.numel(), sp)
+    layers = []
+    for layer in range(w.layers):
+        x = make_layer(w, seed=layer, device=dev, n_new=0)
+        cache = kivi.KiviCache(B, w.kv_heads, T + 1, k_bits=w.k_bits, v_bits=w.v_bits,
+                               group_size=w.group_size, residual_length=w.residual_length,
+                               dtype=w.dtype, device=dev)
+        kp, vp = x.k.contiguous(), x.v.contiguous()
+        if args.ragged:
+            cache.append_varlen(kp, vp, lens)
+        else:
+            cache.append(kp, vp)
+        # the decode token of sequence b: a copy of its window slot 0 (token
+        # T_b - r_b), so that the flush packs the same window every step
+        idx = torch.tensor(q0, device=dev)
+        kn = kp[torch.arange(B, device=dev), :, idx].contiguous()  # [B][H][D]
+        vn = vp[torch.arange(B, device=dev), :, idx].contiguous()
+        L = dict(cache=cache, kp=kp, vp=vp, kn=kn, vn=vn, q=x.q.contiguous(),
+                 out=torch.empty(B, w.q_heads, w.head_dim, dtype=torch.float32, device=dev))
+        ws = cache.workspace(w.q_heads)  # allocated before timing
+        # the C-ABI calls of one step with their arguments resolved once (the
+        # checks of the KiviCache convenience methods cost the host more than
+        # a small step costs the GPU)
+        L["lengths"] = ((ctypes.c_int32 * B)(*q0), (ctypes.c_int32 * B)(*r0))
+        L["decode"] = (cache.handle, kn.data_ptr(), vn.data_ptr(), L["q"].data_ptr(), w.q_heads,
+                       ctypes.c_float(scale), L["out"].data_ptr(), kivi.KIVI_F32, ws.data_ptr(),
+                       ws.numel(), ctypes.c_void_p(sp))
+        layers.append(L)
+        del x
+    # events of the marked steps: [0] before the call, [1] and [2] recorded by
+    # the library right around the decode kernel, [3] after the call
+    every = max(1, args.phase_every)
+    marked = list(range(0, args.steps, every))[:64]
+    events = {k: [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in layers] for k in marked}
+    for evs in events.values():
+        for ev in evs:
+            for e in ev:
+                e.record(stream)  # creates the event
     torch.cuda.synchronize()
+    lib = kivi.lib
+    new_tok = [(ctypes.c_void_p(L["kn"].data_ptr()), ctypes.c_void_p(L["vn"].data_ptr())) for L in layers]
+    null = ctypes.c_void_p(0)
 
-    def step(ev=None):
-        # one pass of the hot path over every layer, phase by phase: the prefix
-        # of every layer packed, then every layer's decode token appended, then
-        # decode attention for every layer.  ev: four HIP events bracketing the
-        # three phase groups, recorded on the stream every kernel is launched on.
-        rec = (lambda n: ev[n].record(stream)) if ev is not None else (lambda n: None)
-        rec(0)
-        for L in layers:
-            kivi.kivi_cache_reset(L["cache"].handle)
-            if lens is None:
-                kivi.kivi_append(*L["append"])
-            else:  # sequence b takes the first lens[b] tokens of the prefix
-                L["cache"].append_varlen(L["kp"], L["vp"], lens, stream=stream)
-        rec(1)
-        for L in layers:
-            kivi.kivi_flush_residual(L["cache"].handle, sp)
-        rec(2)
-        for L in layers:
-            kivi.kivi_append_decode_attn(*L["decode"])
-        rec(3)
+    def step(evs=None):
+        # one decode step of every layer
+        for i, L in enumerate(layers):
+            h = L["cache"].handle
+            if lib.kivi_cache_set_lengths(h, *L["lengths"]) != kivi.KIVI_OK:
+                raise kivi.KiviError(kivi.KIVI_ERR_INVALID_ARG, kivi.last_error_message())
+            if evs is not None:
+                ev = evs[i]
+                lib.kivi_set_timing_events(h, ctypes.c_void_p(ev[1].cuda_event), ctypes.c_void_p(ev[2].cuda_event))
+                ev[0].record(stream)
+            a = L["decode"]
+            st = lib.kivi_append_decode_attn(a[0], new_tok[i][0], new_tok[i][1], ctypes.c_void_p(a[3]), a[4],
+                                             a[5], ctypes.c_void_p(a[6]), a[7], ctypes.c_void_p(a[8]), a[9],
+                                             a[10])
+            if st != kivi.KIVI_OK:
+                raise kivi.KiviError(st, kivi.last_error_message())
+            if evs is not None:
+                ev[3].record(stream)
+                lib.kivi_set_timing_events(h, null, null)
 
     if args.copy_calibration:
         # a plain copy of known size: 1 GiB read + 1 GiB written
@@ -192,50 +234,78 @@ def run(args):
         step()
     torch.cuda.synchronize()
 
-    # Each event record is a marker that the next launch waits for (about
-    # 6.5 us between kernels, against no gap between two launches of one
-    # call), so the phases are bracketed on every `phase_every`-th timed step
-    # only; the other steps run as a serving loop would, without markers.
-    # `value` counts every timed step, marked or not.
-    marked = list(range(0, args.steps, max(1, args.phase_every)))
-    events = {k: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for k in marked}
-    # timed region: exactly `steps` steps between two synchronizations
+    # Each event record is a stream marker that the next launch waits for, so
+    # the launches are bracketed on every `phase_every`-th timed step only (at
+    # most 64 of them); the other steps run back to back as a serving loop
+    # would.  `value` counts every timed step, marked or not.
     t0 = time.perf_counter()
     for k in range(args.steps):
         step(events.get(k))
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps
+    phase = {"flush": [], "decode": [], "merge": []}
+    for evs in events.values():
+        for ev in evs:
+            phase["flush"].append(ev[0].elapsed_time(ev[1]) * 1e-3)
+            phase["decode"].append(ev[1].elapsed_time(ev[2]) * 1e-3)
+            phase["merge"].append(ev[2].elapsed_time(ev[3]) * 1e-3)
 
-    # per step, the average duration of one layer's launches of each phase
-    phase = {"pack": [], "flush": [], "decode": []}
-    n = len(layers)
-    for ev in events.values():
-        phase["pack"].append(ev[0].elapsed_time(ev[1]) * 1e-3 / n)
-        phase["flush"].append(ev[1].elapsed_time(ev[2]) * 1e-3 / n)
-        phase["decode"].append(ev[2].elapsed_time(ev[3]) * 1e-3 / n)
-
-    # decode alone with the 256 MB last-level cache scrubbed before each call
+    # decode alone (the state after the step, kivi_decode_attn) with the
+    # 256 MB last-level cache scrubbed before each launch pair
     scrub = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     cold = []
     L0 = layers[0]
+    c0 = L0["cache"]
     for _ in range(args.cold_iters):
         scrub.fill_(1)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        L0["cache"].decode_attn(L0["q"], scale, out=L0["out"])
+        c0.decode_attn(L0["q"], scale, out=L0["out"])
         e1.record(stream)
         torch.cuda.synchronize()
         cold.append(e0.elapsed_time(e1) * 1e-3)
-    del scrub
-    return w, wall, phase, cold, layers, lens
+
+    # streaming-read probe: 4 GiB read once per launch
+    probe = []
+    nbytes = 4 << 30
+    src = scrub.new_empty(nbytes)
+    src.fill_(3)
+    wgs = 8 * torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty(wgs * 256, dtype=torch.int32, device=dev)
+    for _ in range(args.probe_iters):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        kivi.kivi_stream_read_probe(src.data_ptr(), nbytes, sink.data_ptr(), sink.numel() * 4, wgs, sp)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        probe.append(e0.elapsed_time(e1) * 1e-3)
+    del src, sink, scrub
+
+    # the prefix pack (bulk prefill), every layer per iteration
+    pack = []
+    for _ in range(args.pack_iters):
+        for L in layers:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c = L["cache"]
+            c.reset()
+            e0.record(stream)
+            if args.ragged:
+                c.append_varlen(L["kp"], L["vp"], lens)
+            else:
+                kivi.kivi_append(c.handle, L["kp"].data_ptr(), L["vp"].data_ptr(), T, sp)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            pack.append(e0.elapsed_time(e1) * 1e-3)
+    return w, wall, phase, cold, probe, nbytes, pack, layers, (lens if args.ragged else None)
 
 
 def cpu_baseline(w, layers, lens=None):
-    """The oracle, as it stands, on a bounded sample of the same workload: one
-    step (prefix pack, decode-token append, decode attention for every query
-    head) on one batch row of the first layer at a time (row b's prefix cut to
-    lens[b] tokens when given), cycling through the rows until about ten
-    seconds of CPU work are done."""
+    """The oracle, as it stands, on a bounded sample of the same workload: the
+    decode step (token append, which packs the full window first, then decode
+    attention for every query head) on one batch row of the first layer at a
+    time, cycling through the rows; each row's oracle cache is first filled
+    with its prefix (untimed).  Stops after about ten seconds of timed oracle
+    work or 40 s in all."""
     import numpy as np
 
     import oracle
@@ -243,29 +313,28 @@ def cpu_baseline(w, layers, lens=None):
 
     L = layers[0]
     dt = oracle.BF16 if "bfloat" in str(w.dtype) else oracle.F16
-    done, t, nbytes = 0, 0.0, 0
-    while t < 10.0:
+    done, t, nbytes, t_all = 0, 0.0, 0, time.perf_counter()
+    while t < 10.0 and time.perf_counter() - t_all < 40.0:
         r = done % w.batch
         rows = slice(r, r + 1)
         T = w.tokens if lens is None else lens[r]
-        k, v = bits16(L["kp"][rows, :, :T]), bits16(L["vp"][rows, :, :T])
-        kn, vn = bits16(L["kn"][rows]), bits16(L["vn"][rows])
+        ref = oracle.OracleCache(1, w.kv_heads, w.head_dim, w.tokens + 1, w.k_bits, w.v_bits,
+                                 w.group_size, w.residual_length, dt)
+        ref.append(bits16(L["kp"][rows, :, :T]), bits16(L["vp"][rows, :, :T]))
+        kn, vn = bits16(L["kn"][rows, :, None]), bits16(L["vn"][rows, :, None])
         q = bits16(L["q"][rows])
         t0 = time.perf_counter()
-        ref = oracle.OracleCache(1, w.kv_heads, w.head_dim, w.tokens + 1, w.k_bits,
-                                 w.v_bits, w.group_size, w.residual_length, dt)
-        ref.append(k, v)
         ref.append(kn, vn)
         ref.decode_attn(q, 1.0 / np.sqrt(w.head_dim))
         t += time.perf_counter() - t0
         done += 1
-        nbytes += sum(algorithmic_bytes(w, [T]).values())
-    b = nbytes
-    return {"value": b / t / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+        nbytes += step_bytes(algorithmic_bytes(w, [T]))
+    return {"value": nbytes / t / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{done} batch rows (all {w.kv_heads} kv heads each, cycling through the "
-                      f"{w.batch} rows of layer 0), one step each (prefix pack, decode-token "
-                      f"append, decode attention); {t:.1f} s of oracle time; host CPU: "
-                      f"{cpu_model()}, {os.cpu_count()} logical CPUs visible"}
+                      f"{w.batch} rows of layer 0), one decode step each (the token append that "
+                      f"packs the full window, then decode attention for every query head; the "
+                      f"prefix pack that builds each row's cache is not timed); {t:.1f} s of "
+                      f"oracle time; host CPU: {cpu_model()}, {os.cpu_count()} logical CPUs visible"}
 
 
 def cpu_model():
@@ -288,41 +357,44 @@ def main():
         sys.exit(2)
     import numpy as np
 
-    w, wall, phase, cold, layers, lens = run(args)
+    w, wall, phase, cold, probe, probe_bytes, pack, layers, lens = run(args)
     ab = algorithmic_bytes(w, lens)
-    layers_n = w.layers
-    step_bytes = sum(ab.values()) * layers_n
-    # average launch-sequence duration per phase (HIP events in the timed steps)
-    avg = {k: float(np.mean(v)) for k, v in phase.items()}
-    med = {k: float(np.median(v)) for k, v in phase.items()}
+    kname, ksrc = decode_kernel(w)
     phases = {}
-    for k in ("pack", "flush", "decode"):
-        g = ab[k] / avg[k] / 1e9
-        phases[k] = {"bytes": ab[k], "us_mean": avg[k] * 1e6, "us_median": med[k] * 1e6,
-                     "us_p10": float(np.percentile(phase[k], 10)) * 1e6,
-                     "us_p90": float(np.percentile(phase[k], 90)) * 1e6, "samples": len(phase[k]),
-                     "gbps": g, "frac": g / PEAK_GBPS, "launches": PHASE_KERNEL[k][2]}
-    cold_med = float(np.median(cold))
-    phases["decode_cold_llc"] = {"bytes": ab["decode"], "us_median": cold_med * 1e6,
-                                 "us_p10": float(np.percentile(cold, 10)) * 1e6,
-                                 "us_p90": float(np.percentile(cold, 90)) * 1e6, "samples": len(cold),
-                                 "gbps": ab["decode"] / cold_med / 1e9,
-                                 "frac": ab["decode"] / cold_med / 1e9 / PEAK_GBPS}
-    # roofline of the phase that takes the most time (pack and decode are one
-    # dominant kernel each)
-    dom = max(("pack", "decode"), key=lambda k: avg[k])
-    kname, ksrc, _ = PHASE_KERNEL[dom]
-    if dom == "decode":
-        kname = "decode_mfma" if w.gq in (1, 2, 4) else "decode_split_valu"
-        ksrc = decode_source(w)
-    # (the committed counters describe the workload with every sequence T long)
+    for k, desc in (("flush", "window flush (pack kernel), before the decode kernel"),
+                    ("decode", f"{kname}: token append + split-K attention"),
+                    ("merge", "decode_merge: cross-split merge, out written")):
+        s = stats(phase[k])
+        g = ab[k] / (s["us_mean"] * 1e-6) / 1e9
+        phases[k] = dict(bytes=ab[k], **s, gbps=g, frac=g / PEAK_GBPS, launch=desc)
+    s = stats(pack)
+    phases["pack"] = dict(bytes=ab["pack"], **s, gbps=ab["pack"] / (s["us_median"] * 1e-6) / 1e9,
+                          frac=ab["pack"] / (s["us_median"] * 1e-6) / 1e9 / PEAK_GBPS,
+                          launch="prefix pack (prefill): quantize + bit-pack T tokens, copy the window")
+    # decode alone reads no new token: the token's 4 D e bytes per unit less
+    dec_bytes = ab["decode"] + ab["merge"] - 4 * w.head_dim * 2 * w.kv_heads * w.batch
+    s = stats(cold)
+    phases["decode_cold_llc"] = dict(bytes=dec_bytes, **s,
+                                     gbps=dec_bytes / (s["us_median"] * 1e-6) / 1e9,
+                                     frac=dec_bytes / (s["us_median"] * 1e-6) / 1e9 / PEAK_GBPS,
+                                     launch="kivi_decode_attn alone (decode kernel + merge), "
+                                            "last-level cache scrubbed before each")
+    s = stats(probe)
+    probe_gbps = probe_bytes / (s["us_median"] * 1e-6) / 1e9
+    phases["stream_read_probe"] = dict(bytes=probe_bytes, **s, gbps=probe_gbps, frac=probe_gbps / PEAK_GBPS,
+                                       launch="kivi_stream_read_probe: 4 GiB read once, 16-byte loads")
+    # the roofline of the decode kernel: algorithmic bytes per launch over the
+    # mean launch duration measured by the library's events in the timed steps
+    dec = phases["decode"]
+    achieved = dec["gbps"]
+    dec["frac_of_stream_read"] = achieved / probe_gbps
     traffic = None if lens is not None else traffic_from_profile(
         kname, w.name, os.path.join(ROOT, "kv_cache_bit_kivi_amd", "csrc", ksrc))
-    achieved = ab[dom] / avg[dom] / 1e9
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, layers, lens)
+    per_step = step_bytes(ab) * w.layers
     res = {
         "metric": METRIC,
-        "value": step_bytes / wall / 1e9,
+        "value": per_step / wall / 1e9,
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -331,19 +403,22 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": ("f16 hi+lo matrix operands x 2/4-bit codes, f32 accumulation" if w.gq in (1, 2, 4)
+                  else "f32"),
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.description}", "batch": w.batch,
                    "kv_heads": w.kv_heads, "q_heads": w.q_heads, "head_dim": w.head_dim,
                    "tokens": w.tokens, "k_bits": w.k_bits, "v_bits": w.v_bits,
                    "group_size": w.group_size, "residual_length": w.residual_length,
                    "kv_dtype": str(w.dtype).replace("torch.", ""), "layers": w.layers,
+                   "step": "per layer: window flush + token append + split-K decode + merge, "
+                           "from (T - R packed, R window)",
                    "lengths": ("every sequence T" if lens is None else
                                f"per sequence uniform in [T/2, T], seed 0 (mean {np.mean(lens):.0f})")},
-        "roofline": {"bound": "hbm", "kernel": f"{kname} ({dom})",
-                     "achieved": achieved, "peak": PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / PEAK_GBPS, "traffic": traffic,
-                     "bytes_per_launch": ab[dom], "us_per_launch": avg[dom] * 1e6},
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved, "peak": PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / PEAK_GBPS, "traffic": traffic,
+                     "bytes_per_launch": ab["decode"], "us_per_launch": dec["us_mean"],
+                     "frac_of_stream_read": achieved / probe_gbps},
         "cpu_baseline": cpu,
         "phases": phases,
     }

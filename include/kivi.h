@@ -314,6 +314,18 @@ kivi_status kivi_append_decode_attn(kivi_cache* cache, const void* k_new, const 
                                     void* out, int32_t out_dtype, void* workspace,
                                     size_t ws_bytes, void* stream);
 
+/* Declares that the cache buffer holds, for every sequence b, n_quant[b]
+ * packed tokens and n_resid[b] window tokens (host arrays of `batch`
+ * entries), without touching device memory: a buffer restored from a
+ * snapshot of this cache (its bytes copied back, or saved and reloaded)
+ * resumes at the lengths it had, the same state kivi_cache_get_lengths
+ * reported when the snapshot was taken.  The contents are not checked.
+ * Errors: INVALID_ARG (nulls; n_quant[b] not a non-negative multiple of R,
+ * n_resid[b] outside [0, R], or n_quant[b] + n_resid[b] > max_tokens), HIP
+ * (poisoned handle). */
+kivi_status kivi_cache_set_lengths(kivi_cache* cache, const int32_t* n_quant,
+                                   const int32_t* n_resid);
+
 /* Fixes the number of token splits used by kivi_decode_attn (0 restores the
  * automatic choice).  The value is clamped to [1, blocks + 1]. For tests of
  * split invariance and for tuning. */
@@ -321,6 +333,32 @@ kivi_status kivi_set_decode_splits(kivi_cache* cache, int32_t n_split);
 
 /* Fills *view with the device pointers and counters of the cache. */
 kivi_status kivi_cache_get_view(const kivi_cache* cache, kivi_cache_view* view);
+
+/* ------------------------------------------------------------------------
+ * Measurement helpers (for benchmarks and profiling; not part of the path).
+ */
+
+/* Timing hook: with events set, every decode launch on this cache records
+ * split_begin on its stream right before the split-K attention kernel and
+ * split_end right after it, before the merge (hipEvent_t handles passed as
+ * void*, created by the caller; both or neither; NULL, NULL removes them).
+ * Each record is a stream marker, so a marked launch starts a little later
+ * than an unmarked one.  For caches of more than 64 sequences of different
+ * lengths the events bracket the last launch pair's split kernel.
+ * Errors: INVALID_ARG (null cache, only one event given). */
+kivi_status kivi_set_timing_events(kivi_cache* cache, void* split_begin, void* split_end);
+
+/* Streaming-read probe: reads `bytes` (a positive multiple of 16) of device
+ * memory at src (16-byte aligned) once with 16-byte non-temporal loads, by
+ * `workgroups` workgroups of 256 threads each reading one contiguous chunk,
+ * and writes one word per thread to the device array sink (at least
+ * workgroups * 1024 bytes).  Timed by the caller, it gives the HBM read rate
+ * a plain streaming kernel reaches: the practical ceiling for the decode,
+ * which streams the packed cache once per generated token (page "KV-Cache
+ * Quantization: I Ran the Experiments So You Don't Have To", "Component 1").
+ * Errors: INVALID_ARG, BUFFER_TOO_SMALL (sink), HIP (launch failure). */
+kivi_status kivi_stream_read_probe(const void* src, size_t bytes, void* sink, size_t sink_bytes,
+                                   int32_t workgroups, void* stream);
 
 /* Static text for a status code. */
 const char* kivi_status_string(kivi_status status);

@@ -26,6 +26,7 @@ UNITS = {
     "kivi_pack.hip": ["-ffp-contract=off"],
     "kivi_decode.hip": [],
     "kivi_decode_mfma.hip": [],
+    "kivi_probe.hip": [],
     "kivi_api.cpp": ["-x", "hip"],
 }
 

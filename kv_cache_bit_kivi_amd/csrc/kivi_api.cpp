@@ -42,6 +42,8 @@ struct kivi_cache {
   int forced_splits;
   int cu_count;  // compute units of the device (0: not known yet)
   bool poisoned;
+  // measurement: events recorded around each split-kernel launch (or null)
+  hipEvent_t ev_split_begin, ev_split_end;
   uint8_t* blocks;  // [B*H][nb] block records
   uint32_t* scale_max;  // one entry per block record (same index)
   uint16_t* k_resid;
@@ -807,7 +809,8 @@ kivi_status decode_launch(kivi_cache* c, const DecodePlan& plan, const void* q, 
   a.v_resid_w = c->v_resid;
   if (!c->ragged) {
     hipError_t e = kivi::launch_decode(a, c->cfg.k_bits, c->cfg.v_bits, c->cfg.kv_dtype, out_dtype,
-                                       plan.use_mfma, static_cast<hipStream_t>(stream));
+                                       plan.use_mfma, static_cast<hipStream_t>(stream), c->ev_split_begin,
+                                       c->ev_split_end);
     if (e != hipSuccess) return hip_fail(c, e, "decode launch");
     return KIVI_OK;
   }
@@ -825,7 +828,8 @@ kivi_status decode_launch(kivi_cache* c, const DecodePlan& plan, const void* q, 
       a.seq_len[i][1] = c->sr[b0 + i];
     }
     hipError_t e = kivi::launch_decode(a, c->cfg.k_bits, c->cfg.v_bits, c->cfg.kv_dtype, out_dtype,
-                                       plan.use_mfma, static_cast<hipStream_t>(stream));
+                                       plan.use_mfma, static_cast<hipStream_t>(stream), c->ev_split_begin,
+                                       c->ev_split_end);
     if (e != hipSuccess) return hip_fail(c, e, "decode launch (sequences of different lengths)");
   }
   return KIVI_OK;
@@ -893,6 +897,48 @@ kivi_status kivi_append_decode_attn(kivi_cache* c, const void* k_new, const void
   }
   return decode_launch(c, plan, q, num_q_heads, softmax_scale, out, out_dtype, workspace, stream, k_new,
                        v_new);
+}
+
+kivi_status kivi_cache_set_lengths(kivi_cache* c, const int32_t* n_quant, const int32_t* n_resid) {
+  if (!c || !n_quant || !n_resid) return fail(KIVI_ERR_INVALID_ARG, "cache and lengths must not be NULL");
+  if (c->poisoned) return fail(KIVI_ERR_HIP, "cache handle is poisoned by an earlier HIP error");
+  const int B = c->cfg.batch, R = c->cfg.residual_length;
+  for (int b = 0; b < B; ++b) {
+    if (n_quant[b] < 0 || n_quant[b] % R != 0 || n_resid[b] < 0 || n_resid[b] > R ||
+        (long long)n_quant[b] + n_resid[b] > c->cfg.max_tokens)
+      return fail(KIVI_ERR_INVALID_ARG,
+                  "sequence %d: lengths (%d, %d) need n_quant a multiple of R = %d, 0 <= n_resid <= R and "
+                  "n_quant + n_resid <= max_tokens = %d", b, n_quant[b], n_resid[b], R, c->cfg.max_tokens);
+  }
+  c->ragged = true;
+  c->sq.assign(n_quant, n_quant + B);
+  c->sr.assign(n_resid, n_resid + B);
+  settle(c);
+  return KIVI_OK;
+}
+
+kivi_status kivi_set_timing_events(kivi_cache* c, void* split_begin, void* split_end) {
+  if (!c) return fail(KIVI_ERR_INVALID_ARG, "cache is NULL");
+  if ((split_begin == nullptr) != (split_end == nullptr))
+    return fail(KIVI_ERR_INVALID_ARG, "give both events or neither");
+  c->ev_split_begin = static_cast<hipEvent_t>(split_begin);
+  c->ev_split_end = static_cast<hipEvent_t>(split_end);
+  return KIVI_OK;
+}
+
+kivi_status kivi_stream_read_probe(const void* src, size_t bytes, void* sink, size_t sink_bytes,
+                                   int32_t workgroups, void* stream) {
+  if (!src || !sink) return fail(KIVI_ERR_INVALID_ARG, "src and sink must not be NULL");
+  if (bytes == 0 || bytes % 16 || reinterpret_cast<uintptr_t>(src) % 16)
+    return fail(KIVI_ERR_INVALID_ARG, "bytes must be a positive multiple of 16 and src 16-byte aligned");
+  if (workgroups < 1 || workgroups > (1 << 20))
+    return fail(KIVI_ERR_INVALID_ARG, "workgroups must be in [1, 2^20]");
+  if (sink_bytes < (size_t)workgroups * 256 * 4)
+    return fail(KIVI_ERR_BUFFER_TOO_SMALL, "sink needs %zu bytes", (size_t)workgroups * 256 * 4);
+  hipError_t e = kivi::launch_stream_read(src, bytes, static_cast<uint32_t*>(sink), workgroups,
+                                          static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KIVI_ERR_HIP, "stream read launch: %s", hipGetErrorString(e));
+  return KIVI_OK;
 }
 
 kivi_status kivi_set_decode_splits(kivi_cache* c, int32_t n_split) {

@@ -323,9 +323,15 @@ hipError_t launch_split_gq(const DecodeArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, int k_bits, int v_bits, int kv_dtype,
-                         int out_dtype, bool use_mfma, hipStream_t stream) {
+                         int out_dtype, bool use_mfma, hipStream_t stream,
+                         hipEvent_t split_begin, hipEvent_t split_end) {
   const bool bf = kv_dtype == 1;
   hipError_t e = hipErrorInvalidValue;
+  if (split_begin) {
+    e = hipEventRecord(split_begin, stream);
+    if (e != hipSuccess) return e;
+    e = hipErrorInvalidValue;
+  }
   if (use_mfma) {
     e = launch_decode_mfma(a, k_bits, v_bits, kv_dtype, stream);
   } else {
@@ -339,6 +345,7 @@ hipError_t launch_decode(const DecodeArgs& a, int k_bits, int v_bits, int kv_dty
 #undef KIVI_SPLIT_CASE
   }
   if (e != hipSuccess) return e;
+  if (split_end && (e = hipEventRecord(split_end, stream)) != hipSuccess) return e;
   dim3 grid(a.B * a.Hq);
   switch (out_dtype) {
     case 0: hipLaunchKernelGGL(decode_merge<0>, grid, dim3(D), 0, stream, a); break;

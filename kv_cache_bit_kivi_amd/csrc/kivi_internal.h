@@ -137,9 +137,16 @@ hipError_t launch_pack(const PackArgs& a, int k_bits, int v_bits, int kv_dtype,
                        hipStream_t stream);
 hipError_t launch_resid_copy(const PackArgs& a, int kv_dtype, hipStream_t stream);
 // use_mfma selects the matrix-core kernel (1, 2 or 4 query heads per kv head).
+// split_begin / split_end (may be null): events recorded on the stream right
+// before and right after the split kernel (before the merge).
 hipError_t launch_decode(const DecodeArgs& a, int k_bits, int v_bits, int kv_dtype,
-                         int out_dtype, bool use_mfma, hipStream_t stream);
+                         int out_dtype, bool use_mfma, hipStream_t stream,
+                         hipEvent_t split_begin, hipEvent_t split_end);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int k_bits, int v_bits, int kv_dtype,
                                   hipStream_t stream);
+// Streaming read of `bytes` (a multiple of 16) from src by `workgroups`
+// workgroups of 256 threads; each thread writes one word of its XOR to sink.
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int workgroups,
+                              hipStream_t stream);
 
 }  // namespace kivi

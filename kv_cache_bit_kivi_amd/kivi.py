@@ -32,7 +32,8 @@ EXPORTED = (
     "kivi_decode_attn", "kivi_set_decode_splits", "kivi_cache_get_view",
     "kivi_status_string", "kivi_last_error_message",
     "kivi_append_varlen", "kivi_cache_reset_sequences", "kivi_cache_get_lengths",
-    "kivi_append_decode_attn", "kivi_cache_set_page_table",
+    "kivi_append_decode_attn", "kivi_cache_set_page_table", "kivi_cache_set_lengths",
+    "kivi_set_timing_events", "kivi_stream_read_probe",
 )
 
 
@@ -84,6 +85,9 @@ def _load():
         "kivi_decode_attn": ([vp, vp, i32, ctypes.c_float, vp, i32, vp, sz, vp], i32),
         "kivi_append_decode_attn": ([vp, vp, vp, vp, i32, ctypes.c_float, vp, i32, vp, sz, vp], i32),
         "kivi_set_decode_splits": ([vp, i32], i32),
+        "kivi_cache_set_lengths": ([vp, ctypes.POINTER(i32), ctypes.POINTER(i32)], i32),
+        "kivi_set_timing_events": ([vp, vp, vp], i32),
+        "kivi_stream_read_probe": ([vp, sz, vp, sz, i32, vp], i32),
         "kivi_cache_get_view": ([vp, ctypes.POINTER(kivi_cache_view)], i32),
         "kivi_status_string": ([i32], ctypes.c_char_p),
         "kivi_last_error_message": ([], ctypes.c_char_p),
@@ -195,6 +199,21 @@ def kivi_set_decode_splits(h, n_split):
     _check(lib.kivi_set_decode_splits(h, n_split))
 
 
+def kivi_cache_set_lengths(h, n_quant, n_resid):
+    nq, _ = _i32_array(n_quant)
+    nr, _ = _i32_array(n_resid)
+    _check(lib.kivi_cache_set_lengths(h, nq, nr))
+
+
+def kivi_set_timing_events(h, split_begin, split_end):
+    _check(lib.kivi_set_timing_events(h, ctypes.c_void_p(split_begin), ctypes.c_void_p(split_end)))
+
+
+def kivi_stream_read_probe(src_ptr, nbytes, sink_ptr, sink_bytes, workgroups, stream):
+    _check(lib.kivi_stream_read_probe(ctypes.c_void_p(src_ptr), nbytes, ctypes.c_void_p(sink_ptr),
+                                      sink_bytes, workgroups, ctypes.c_void_p(stream)))
+
+
 def kivi_cache_get_view(h):
     v = kivi_cache_view()
     _check(lib.kivi_cache_get_view(h, ctypes.byref(v)))
@@ -297,6 +316,16 @@ class KiviCache:
     def lengths(self):
         """(n_quant, n_resid) lists, one entry per sequence."""
         return kivi_cache_get_lengths(self.handle, self.cfg.batch)
+
+    def set_lengths(self, n_quant, n_resid):
+        """Declares per-sequence lengths of the buffer's contents (lists or
+        ints for every sequence), e.g. after restoring a snapshot."""
+        B = self.cfg.batch
+        nq = [n_quant] * B if isinstance(n_quant, int) else list(n_quant)
+        nr = [n_resid] * B if isinstance(n_resid, int) else list(n_resid)
+        if len(nq) != B or len(nr) != B:
+            raise ValueError(f"lengths need {B} entries")
+        kivi_cache_set_lengths(self.handle, nq, nr)
 
     def flush(self, stream=None):
         kivi_flush_residual(self.handle, self._stream(stream))

@@ -240,6 +240,35 @@ void ragged_paths() {
   }
   CHECK(kivi_cache_destroy(h) == KIVI_OK);
 }
+// Declared lengths (a restored snapshot): validated per sequence, no launch.
+void set_lengths_rules() {
+  stub_reset();
+  kivi_cache* h = make(config(2, 2, 1000));
+  const int32_t q1[2] = {256, 128}, r1[2] = {5, 128};
+  CHECK(kivi_cache_set_lengths(h, q1, r1) == KIVI_OK);
+  int32_t nq[2], nr[2];
+  CHECK(kivi_cache_get_lengths(h, nq, nr) == KIVI_OK);
+  CHECK(nq[0] == 256 && nr[0] == 5 && nq[1] == 128 && nr[1] == 128);
+  int v_nq, v_nr;
+  lengths(h, v_nq, v_nr);
+  CHECK(v_nq == -1 && v_nr == -1);
+  const int32_t bad[3][2][2] = {{{100, 0}, {0, 0}}, {{0, 0}, {129, 0}}, {{896, 0}, {128, 0}}};
+  for (const auto& b : bad) {
+    CHECK(kivi_cache_set_lengths(h, b[0], b[1]) == KIVI_ERR_INVALID_ARG);
+    CHECK(kivi_cache_get_lengths(h, nq, nr) == KIVI_OK && nq[0] == 256 && nr[0] == 5);
+  }
+  const int32_t q2[2] = {256, 256}, r2[2] = {0, 0};  // equal lengths: the uniform state
+  CHECK(kivi_cache_set_lengths(h, q2, r2) == KIVI_OK);
+  lengths(h, v_nq, v_nr);
+  CHECK(v_nq == 256 && v_nr == 0);
+  CHECK(kivi_append(h, kIn, kIn, 1, nullptr) == KIVI_OK);  // an empty window takes the token
+  lengths(h, v_nq, v_nr);
+  CHECK(v_nq == 256 && v_nr == 1);
+  CHECK(stub_launches() == 1);
+  CHECK(kivi_set_timing_events(h, kDev, nullptr) == KIVI_ERR_INVALID_ARG);
+  CHECK(kivi_set_timing_events(h, nullptr, nullptr) == KIVI_OK);
+  CHECK(kivi_cache_destroy(h) == KIVI_OK);
+}
 }  // namespace
 
 int main() {
@@ -249,6 +278,7 @@ int main() {
   fused_step_plan();
   fused_step_failures();
   ragged_paths();
+  set_lengths_rules();
   std::printf("contract: %d checks passed\n", g_checks);
   return 0;
 }

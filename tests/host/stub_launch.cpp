@@ -16,7 +16,7 @@
 
 namespace {
 struct Launch {
-  int kind;  // 0 pack, 1 window copy, 2 decode (split kernel + merge)
+  int kind;  // 0 pack, 1 window copy, 2 decode (split kernel + merge), 3 read probe
   int nblk, dst_blk0, r_count, r_dst_slot0, ragged;
   int n_quant, n_resid, n_split, n_split_packed, use_mfma, fused_append;
 };
@@ -81,8 +81,12 @@ hipError_t launch_pack(const PackArgs& a, int, int, int, hipStream_t) {
 hipError_t launch_resid_copy(const PackArgs& a, int, hipStream_t) {
   return take(Launch{1, 0, 0, a.r_count, a.r_dst_slot0, a.ragged, 0, 0, 0, 0, 0, 0});
 }
-hipError_t launch_decode(const DecodeArgs& a, int, int, int, int, bool use_mfma, hipStream_t) {
+hipError_t launch_decode(const DecodeArgs& a, int, int, int, int, bool use_mfma, hipStream_t, hipEvent_t,
+                         hipEvent_t) {
   return take(Launch{2, 0, 0, 0, 0, a.ragged, a.n_quant, a.n_resid, a.n_split, a.n_split_packed,
                      use_mfma ? 1 : 0, a.k_new != nullptr ? 1 : 0});
+}
+hipError_t launch_stream_read(const void*, size_t, uint32_t*, int, hipStream_t) {
+  return take(Launch{3, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0});
 }
 }  // namespace kivi

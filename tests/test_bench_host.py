@@ -16,10 +16,10 @@ from kv_cache_bit_kivi_amd.inputs import WORKLOADS  # noqa: E402
 
 
 def unit_bytes_by_field(T, D=128, G=32, R=128, kb=2, vb=2, e=2, gq=1):
-    """Per (batch, kv head) unit, the bytes each phase of one step moves,
-    listed field by field: prefix pack of T tokens (the window keeps the last
-    ((T - 1) mod R) + 1), flush of a full window, then the decode step on the
-    state after the token's append."""
+    """Per (batch, kv head) unit, the bytes each phase moves, listed field by
+    field: prefix pack of T tokens (the window keeps the last
+    ((T - 1) mod R) + 1), flush of a full window, then the decode kernel and
+    the merge on the state after the token's append."""
     r = (T - 1) % R + 1
     nq = T - r
     pack = {
@@ -50,18 +50,18 @@ def unit_bytes_by_field(T, D=128, G=32, R=128, kb=2, vb=2, e=2, gq=1):
         "value scale + zero": nq * (D // G) * 4,
         "window": 2 * r * D * e,
         "q": gq * D * e,
-        "out (fp32)": gq * D * 4,
     }
-    return sum(pack.values()), sum(flush.values()), sum(decode.values())
+    merge = {"out (fp32)": gq * D * 4}
+    return sum(pack.values()), sum(flush.values()), sum(decode.values()), sum(merge.values())
 
 
 @pytest.mark.parametrize("name", ["c0", "c1", "c2", "c3", "c4"])
 def test_algorithmic_bytes_closed_form(name):
     w = WORKLOADS[name]
-    p, f, d = unit_bytes_by_field(w.tokens, w.head_dim, w.group_size, w.residual_length,
-                                  w.k_bits, w.v_bits, 2, w.gq)
+    p, f, d, m = unit_bytes_by_field(w.tokens, w.head_dim, w.group_size, w.residual_length,
+                                     w.k_bits, w.v_bits, 2, w.gq)
     U = w.batch * w.kv_heads
-    assert bench.algorithmic_bytes(w) == {"pack": U * p, "flush": U * f, "decode": U * d}
+    assert bench.algorithmic_bytes(w) == {"pack": U * p, "flush": U * f, "decode": U * d, "merge": U * m}
 
 
 def test_algorithmic_bytes_known_totals():
@@ -69,9 +69,14 @@ def test_algorithmic_bytes_known_totals():
     ab = bench.algorithmic_bytes(WORKLOADS["c1"])
     assert ab["pack"] == 256 * (2 * 4096 * 256 + 3968 * 64 + 124 * 512 + 3968 * 16 + 2 * 128 * 256)
     assert ab["pack"] == 651_165_696
-    # the decode step after the flush reads 4096 packed tokens (96 B each at
+    # the decode kernel after the flush reads 4096 packed tokens (96 B each at
     # 2/2 bits with G = 32) and one window token
-    assert ab["decode"] == 256 * (1024 + 4096 * 96 + 512 + 256 + 512) == 101_253_120
+    assert ab["decode"] + ab["merge"] == 256 * (1024 + 4096 * 96 + 512 + 256 + 512) == 101_253_120
+    # c2, the default: 256 units at gq 4, 32768 packed tokens after the flush
+    ab = bench.algorithmic_bytes(WORKLOADS["c2"])
+    assert ab["decode"] == 256 * (1024 + 32768 * 96 + 512 + 4 * 256) == 805_961_728
+    assert ab["flush"] == 256 * (128 * 512 + 128 * 96) == 19_922_944
+    assert bench.step_bytes(ab) == ab["flush"] + ab["decode"] + 256 * 4 * 512
 
 
 def test_ragged_bytes_are_per_sequence_sums():
@@ -79,13 +84,20 @@ def test_ragged_bytes_are_per_sequence_sums():
     lens = bench.ragged_lengths(w)
     assert len(lens) == w.batch and all(w.tokens // 2 <= t <= w.tokens for t in lens)
     assert lens == bench.ragged_lengths(w)  # seeded
-    tot = {"pack": 0, "flush": 0, "decode": 0}
+    tot = {"pack": 0, "flush": 0, "decode": 0, "merge": 0}
     for t in lens:
-        p, f, d = unit_bytes_by_field(t)
+        p, f, d, m = unit_bytes_by_field(t)
         tot["pack"] += p
         tot["flush"] += f
         tot["decode"] += d
+        tot["merge"] += m
     assert bench.algorithmic_bytes(w, lens) == {k: w.kv_heads * v for k, v in tot.items()}
+
+
+def test_stats_of_durations():
+    s = bench.stats([1e-6 * x for x in range(1, 101)])
+    assert s["samples"] == 100 and s["us_mean"] == pytest.approx(50.5)
+    assert s["us_median"] == pytest.approx(50.5) and s["us_p10"] == pytest.approx(10.9)
 
 
 def test_traffic_lookup_checks_the_source(tmp_path, monkeypatch):
