@@ -326,6 +326,21 @@ kivi_status kivi_append_decode_attn(kivi_cache* cache, const void* k_new, const 
 kivi_status kivi_cache_set_lengths(kivi_cache* cache, const int32_t* n_quant,
                                    const int32_t* n_resid);
 
+/* kivi_decode_attn without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops and
+ * harnesses that forbid allocation.  The split partials go to a fixed 16 MiB
+ * device array inside the library (one per GPU, held until the process
+ * ends; its address is looked up once per device, on the first call with
+ * that device current); the call allocates nothing.  Same kernels, plan and
+ * results as kivi_decode_attn.  Calls on one GPU share the array, so calls
+ * that overlap on one GPU (other streams, other threads) race; issue them in
+ * order on one stream.
+ * Errors: those of kivi_decode_attn except the workspace ones;
+ * BUFFER_TOO_SMALL when the planned partials (batch * num_q_heads * splits *
+ * (head_dim + 2) * 4 bytes) exceed the array, before anything is enqueued. */
+kivi_status kivi_decode_attn_noalloc(kivi_cache* cache, const void* q, int32_t num_q_heads,
+                                     float softmax_scale, void* out, int32_t out_dtype, void* stream);
+
 /* Fixes the number of token splits used by kivi_decode_attn (0 restores the
  * automatic choice).  The value is clamped to [1, blocks + 1]. For tests of
  * split invariance and for tuning. */

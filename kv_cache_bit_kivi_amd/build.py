@@ -27,6 +27,7 @@ UNITS = {
     "kivi_decode.hip": [],
     "kivi_decode_mfma.hip": [],
     "kivi_probe.hip": [],
+    "kivi_noalloc.hip": [],
     "kivi_api.cpp": ["-x", "hip"],
 }
 

@@ -852,6 +852,41 @@ kivi_status kivi_decode_attn(kivi_cache* c, const void* q, int32_t num_q_heads, 
                        nullptr);
 }
 
+}  // extern "C"
+
+kivi_status kivi::report(kivi_status s, const char* message) { return fail(s, "%s", message); }
+
+kivi_status kivi::decode_attn_bounded(kivi_cache* c, const void* q, int32_t num_q_heads, float softmax_scale,
+                                      void* out, int32_t out_dtype, void* scratch, size_t scratch_bytes,
+                                      void* stream) {
+  // the checks of kivi_decode_attn, with the workspace bound by the plan
+  if (!c) return fail(KIVI_ERR_INVALID_ARG, "cache is NULL");
+  if (c->poisoned) return fail(KIVI_ERR_HIP, "cache handle is poisoned by an earlier HIP error");
+  if (!q || !out) return fail(KIVI_ERR_INVALID_ARG, "q and out must not be NULL");
+  if (num_q_heads < 1 || num_q_heads % c->cfg.num_kv_heads)
+    return fail(KIVI_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                num_q_heads, c->cfg.num_kv_heads);
+  if (out_dtype != KIVI_F16 && out_dtype != KIVI_BF16 && out_dtype != KIVI_F32)
+    return fail(KIVI_ERR_INVALID_ARG, "bad out_dtype %d", out_dtype);
+  const int gq = num_q_heads / c->cfg.num_kv_heads;
+  if (gq != 1 && gq != 2 && gq != 4 && gq != 8)
+    return fail(KIVI_ERR_UNSUPPORTED, "query heads per kv head must be 1, 2, 4 or 8 (got %d)", gq);
+  if (c->n_quant + c->n_resid < 1) return fail(KIVI_ERR_EMPTY, "decode on an empty cache");
+  kivi_status st;
+  if ((st = ensure_cu_count(c)) != KIVI_OK) return st;
+  DecodePlan plan;
+  if ((st = plan_decode(c, state_of(c), gq, plan)) != KIVI_OK) return st;
+  const size_t need = workspace_bytes_for(c, num_q_heads, plan.n_split);
+  if (need > scratch_bytes)
+    return fail(KIVI_ERR_BUFFER_TOO_SMALL,
+                "the planned partials need %zu bytes, more than the %zu of the fixed scratch array", need,
+                scratch_bytes);
+  return decode_launch(c, plan, q, num_q_heads, softmax_scale, out, out_dtype, scratch, stream, nullptr,
+                       nullptr);
+}
+
+extern "C" {
+
 kivi_status kivi_append_decode_attn(kivi_cache* c, const void* k_new, const void* v_new,
                                     const void* q, int32_t num_q_heads, float softmax_scale,
                                     void* out, int32_t out_dtype, void* workspace, size_t ws_bytes,

@@ -150,3 +150,17 @@ hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int
                               hipStream_t stream);
 
 }  // namespace kivi
+
+#include "../../include/kivi.h"
+
+namespace kivi {
+// Decode attention over the cache's current state with the partials in
+// `scratch` (scratch_bytes long): the entry point without a workspace
+// argument checks the planned partials, not the worst case, against its
+// fixed array.  Same kernels and plan as kivi_decode_attn.
+kivi_status decode_attn_bounded(kivi_cache* cache, const void* q, int32_t num_q_heads, float softmax_scale,
+                                void* out, int32_t out_dtype, void* scratch, size_t scratch_bytes,
+                                void* stream);
+// Returns `s` and sets the thread's kivi_last_error_message() text.
+kivi_status report(kivi_status s, const char* message);
+}  // namespace kivi

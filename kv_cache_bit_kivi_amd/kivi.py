@@ -33,7 +33,7 @@ EXPORTED = (
     "kivi_status_string", "kivi_last_error_message",
     "kivi_append_varlen", "kivi_cache_reset_sequences", "kivi_cache_get_lengths",
     "kivi_append_decode_attn", "kivi_cache_set_page_table", "kivi_cache_set_lengths",
-    "kivi_set_timing_events", "kivi_stream_read_probe",
+    "kivi_set_timing_events", "kivi_stream_read_probe", "kivi_decode_attn_noalloc",
 )
 
 
@@ -84,6 +84,7 @@ def _load():
         "kivi_decode_attn_workspace_bytes": ([vp, i32, ctypes.POINTER(sz)], i32),
         "kivi_decode_attn": ([vp, vp, i32, ctypes.c_float, vp, i32, vp, sz, vp], i32),
         "kivi_append_decode_attn": ([vp, vp, vp, vp, i32, ctypes.c_float, vp, i32, vp, sz, vp], i32),
+        "kivi_decode_attn_noalloc": ([vp, vp, i32, ctypes.c_float, vp, i32, vp], i32),
         "kivi_set_decode_splits": ([vp, i32], i32),
         "kivi_cache_set_lengths": ([vp, ctypes.POINTER(i32), ctypes.POINTER(i32)], i32),
         "kivi_set_timing_events": ([vp, vp, vp], i32),
@@ -185,6 +186,11 @@ def kivi_decode_attn(h, q_ptr, num_q_heads, softmax_scale, out_ptr, out_dtype, w
     _check(lib.kivi_decode_attn(h, ctypes.c_void_p(q_ptr), num_q_heads,
                                 float(softmax_scale), ctypes.c_void_p(out_ptr), out_dtype,
                                 ctypes.c_void_p(ws_ptr), ws_bytes, ctypes.c_void_p(stream)))
+
+
+def kivi_decode_attn_noalloc(h, q_ptr, num_q_heads, softmax_scale, out_ptr, out_dtype, stream):
+    _check(lib.kivi_decode_attn_noalloc(h, ctypes.c_void_p(q_ptr), num_q_heads, float(softmax_scale),
+                                        ctypes.c_void_p(out_ptr), out_dtype, ctypes.c_void_p(stream)))
 
 
 def kivi_append_decode_attn(h, k_ptr, v_ptr, q_ptr, num_q_heads, softmax_scale, out_ptr,
