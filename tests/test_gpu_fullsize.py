@@ -1,12 +1,15 @@
 """Parity at the full workload sizes, in the launch configuration the benchmark
-times: bulk append of the prefix (one pack launch), flush of the full window
-(one pack launch), then the decode step kivi_append_decode_attn (token append
-and split-K attention in one launch, then the merge) with the default split
+times: bulk append of the prefix (one pack launch), then the decode step
+kivi_append_decode_attn (the full window packed first, then token append and
+split-K attention in one launch, then the merge) with the default split
 planner.
 
-The oracle runs on sampled (batch, kv head) units alone; their packed arrays
-must match bit for bit and the attention outputs of their query heads must be
-within 2e-3 of the oracle's."""
+Every (batch, kv head) unit of every layer is compared with the oracle, run
+over the whole layer: packed arrays, per-record scale maxima and window bit
+for bit, and the attention output of every query head within 2e-3.  The
+workloads c1-c3, c2 with 8 query heads per kv head (the 64q/8kv shape of
+70B-class models), and all 32 layers of c4, one layer's inputs at a time.
+The cache beyond 4 GiB is compared on sampled units."""
 import dataclasses
 
 import numpy as np
@@ -16,16 +19,72 @@ import torch
 import oracle
 from kv_cache_bit_kivi_amd import kivi
 from kv_cache_bit_kivi_amd.inputs import WORKLOADS, bits16, make_layer
-from tests.gpu_helpers import assert_cache_equal, gpu_arrays, oracle_arrays, paged_arrays, unit_oracle
+from tests.gpu_helpers import (assert_cache_equal, assert_scale_max, gpu_arrays, oracle_arrays,
+                               paged_arrays, unit_oracle)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 TOL = 2e-3
 
+C2_GQ8 = dataclasses.replace(WORKLOADS["c2"], name="c2gq8", q_heads=64,
+                             description="c2 with 64 query heads over 8 kv heads")
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
-def test_fullsize_sampled_units(name):
-    _sampled_parity(WORKLOADS[name], name)
+
+def _layer_parity(w, layer, name):
+    """Whole-layer parity of one layer (seed = layer); returns (units, heads, worst error)."""
+    T = w.tokens
+    x = make_layer(w, seed=layer, device=DEV, n_new=1)
+    cache = kivi.KiviCache(w.batch, w.kv_heads, T + 1, k_bits=w.k_bits, v_bits=w.v_bits,
+                           group_size=w.group_size, residual_length=w.residual_length,
+                           dtype=w.dtype, device=DEV)
+    cache.append(x.k[:, :, :T].contiguous(), x.v[:, :, :T].contiguous())
+    scale = 1.0 / np.sqrt(w.head_dim)
+    out = cache.append_decode_attn(x.k[:, :, T:].contiguous(), x.v[:, :, T:].contiguous(),
+                                   x.q.contiguous(), scale)
+    torch.cuda.synchronize()
+    assert (cache.n_quant, cache.n_resid) == (T, 1)  # every workload has T a multiple of R
+    dt = oracle.BF16 if w.dtype == torch.bfloat16 else oracle.F16
+    ref = oracle.OracleCache(w.batch, w.kv_heads, w.head_dim, T + 1, w.k_bits, w.v_bits, w.group_size,
+                             w.residual_length, dt)
+    ref.append(bits16(x.k), bits16(x.v))
+    assert (ref.n_quant, ref.n_resid) == (T, 1)
+    assert_cache_equal(gpu_arrays(cache), oracle_arrays(ref), ref.n_quant, ref.n_resid, ref.capacity,
+                       ref.num_blocks, G=w.group_size)
+    assert_scale_max(cache, ref)
+    o_ref = ref.decode_attn(bits16(x.q), scale)
+    err = np.abs(out.cpu().numpy().astype(np.float64) - o_ref)
+    U, Hq = w.batch * w.kv_heads, w.batch * w.q_heads
+    print(f"workload {name} layer {layer}: {U} units bit-exact, {Hq} query heads, attention max abs "
+          f"error {err.max():.2e}", flush=True)
+    assert err.max() <= TOL, np.unravel_index(np.argmax(err), err.shape)
+    return U, Hq, float(err.max())
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c2gq8"])
+def test_fullsize_every_unit(name):
+    w = C2_GQ8 if name == "c2gq8" else WORKLOADS[name]
+    print(f"workload {name}: B={w.batch} H={w.kv_heads} Hq={w.q_heads} T={w.tokens} "
+          f"bits={w.k_bits}/{w.v_bits} {w.dtype}", flush=True)
+    units, heads, worst = _layer_parity(w, 0, name)
+    print(f"workload {name}: compared {units} units and {heads} query heads of 1 layer "
+          f"(worst {worst:.2e})", flush=True)
+
+
+@pytest.mark.parametrize("first", [0, 8, 16, 24], ids=["layers0-7", "layers8-15", "layers16-23",
+                                                     "layers24-31"])
+def test_fullsize_c4_every_layer(first):
+    # the 32 layers in four tests of eight (the oracle's binary64 attention
+    # over 131072 tokens takes a few seconds per layer)
+    w = WORKLOADS["c4"]
+    print(f"workload c4: B={w.batch} H={w.kv_heads} Hq={w.q_heads} T={w.tokens}, layers {first}.."
+          f"{first + 7} of {w.layers}", flush=True)
+    units = heads = 0
+    worst = 0.0
+    for layer in range(first, first + 8):
+        u, h, e = _layer_parity(w, layer, "c4")
+        units, heads, worst = units + u, heads + h, max(worst, e)
+    print(f"workload c4: compared {units} units and {heads} query heads over 8 layers "
+          f"(worst {worst:.2e})", flush=True)
 
 
 @pytest.mark.parametrize("paged", [False, True], ids=["unit_major", "paged"])
@@ -62,9 +121,9 @@ def _sampled_parity(w, name, paged=False):
     torch.cuda.synchronize()
     v = cache.view()
     assert (v.n_quant, v.n_resid) == (T, 1)  # every workload has T a multiple of R
-
     rng = np.random.default_rng(U)
-    units = sorted({0, U - 1, int(rng.integers(1, U - 1))})
+    units = sorted({0, U - 1, *[int(u) for u in rng.integers(1, U - 1, 6)]})
+    print(f"workload {name}: {len(units)} of {U} units sampled", flush=True)
     got = gpu_arrays(cache, units) if table is None else paged_arrays(cache, table, units)
     dt = oracle.BF16 if w.dtype == torch.bfloat16 else oracle.F16
     for i, u in enumerate(units):
