@@ -53,6 +53,8 @@ def parse():
     p.add_argument("--cold-iters", type=int, default=50,
                    help="decode-only launches with the last-level cache scrubbed before each")
     p.add_argument("--probe-iters", type=int, default=20, help="streaming-read probe launches")
+    p.add_argument("--splits", type=int, default=0,
+                   help="force this many token splits per sequence (0: the library's planner)")
     p.add_argument("--ragged", action="store_true",
                    help="sequences of different lengths: sequence b's prefix has T_b tokens, "
                         "drawn uniformly from [T/2, T] (seed 0)")
@@ -178,6 +180,8 @@ def run(args):
         vn = vp[torch.arange(B, device=dev), :, idx].contiguous()
         L = dict(cache=cache, kp=kp, vp=vp, kn=kn, vn=vn, q=x.q.contiguous(),
                  out=torch.empty(B, w.q_heads, w.head_dim, dtype=torch.float32, device=dev))
+        if args.splits:
+            cache.set_splits(args.splits)
         ws = cache.workspace(w.q_heads)  # allocated before timing
         # the C-ABI calls of one step with their arguments resolved once (the
         # checks of the KiviCache convenience methods cost the host more than
