@@ -172,15 +172,25 @@ __device__ __forceinline__ half8_t codes8(uint32_t x, bool high_byte) {
 // Each returns the value of the partner lane combined with the own value.
 template <int M>
 __device__ __forceinline__ float partner(float v) {
-  const uint32_t x = __float_as_uint(v);
+  const int x = __float_as_int(v);
   if constexpr (M == 1) {
-    return __uint_as_float(__builtin_amdgcn_update_dpp(0u, x, 0xB1, 0xF, 0xF, false));  // [1,0,3,2]
+    return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false));  // [1,0,3,2]
   } else if constexpr (M == 2) {
-    return __uint_as_float(__builtin_amdgcn_update_dpp(0u, x, 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
+    return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
   } else {
     static_assert(M == 16 || M == 32, "exchange");
     return 0.0f;
   }
+}
+
+// max(a, b) as one v_max_f32: the operands are scores or -inf, never NaN, so
+// the NaN quieting the compiler adds to fmaxf (one more instruction per
+// operand that it cannot prove canonical, such as a cross-lane result) is
+// not needed.
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
 // reduce over lanes l ^ 16 / l ^ 32: after the swap the two results hold
 // (own, partner) in some order on every lane, so op(r0, r1) is the pair op
@@ -189,7 +199,7 @@ __device__ __forceinline__ float swap_max(float v) {
   const uint32_t x = __float_as_uint(v);
   auto r = (M == 16) ? __builtin_amdgcn_permlane16_swap(x, x, false, false)
                      : __builtin_amdgcn_permlane32_swap(x, x, false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max_raw(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 template <int M>
 __device__ __forceinline__ float swap_sum(float v) {
@@ -372,12 +382,14 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
 // Records of streams g0 .. g0 + 3 of unit u (unit-major, or through the
 // page table when PAGED).  A stream is 32 tokens: a whole block of G = 32, or
 // half `hf` of a block of G = 64.  Slots past the last valid stream
-// g0 + ns - 1 repeat it (addresses stay inside).
+// g0 + ns - 1 repeat it (addresses stay inside).  ubase: the unit's first
+// record (unit-major); the step's records then lie a few records apart.
 template <int KB, int VB, int GT, bool PAGED>
-__device__ __forceinline__ void step_records(const DecodeArgs& a, long long u, int g0, int ns,
-                                             const uint8_t* (&rp)[4], int (&hf)[4]) {
+__device__ __forceinline__ void step_records(const DecodeArgs& a, long long u, const uint8_t* ubase, int g0,
+                                             int ns, const uint8_t* (&rp)[4], int (&hf)[4]) {
   constexpr BlockLayout BL = block_layout(KB, VB, GT);
   constexpr int SPB = GT / kStream;  // streams per block
+  const uint8_t* const sb = ubase + static_cast<size_t>(g0 / SPB) * BL.bytes;  // (unit-major)
 #pragma unroll
   for (int gi = 0; gi < 4; ++gi) {
     const int g = min(g0 + gi, g0 + ns - 1);
@@ -385,33 +397,42 @@ __device__ __forceinline__ void step_records(const DecodeArgs& a, long long u, i
     if constexpr (PAGED) {
       rp[gi] = a.blocks + record_index(a.page_table, a.page_stride, a.num_pages, a.nb, a.H, u, g / SPB) * BL.bytes;
     } else {
-      rp[gi] = a.blocks + (u * a.nb + g / SPB) * (long long)BL.bytes;
+      rp[gi] = sb + (g / SPB - g0 / SPB) * BL.bytes;
     }
   }
 }
 
 // The record (and half) of this lane's metadata slot (lanes 16 i .. 16 i +
-// 15: stream i).
-__device__ __forceinline__ const uint8_t* lane_record(const uint8_t* const (&rp)[4], int lane) {
+// 15: stream i), selected with arithmetic rather than branches.
+template <int KB, int VB, int GT, bool PAGED>
+__device__ __forceinline__ const uint8_t* lane_record(const uint8_t* const (&rp)[4], int g0, int ns, int lane) {
   const int i = lane >> 4;
-  return i == 0 ? rp[0] : i == 1 ? rp[1] : i == 2 ? rp[2] : rp[3];
+  if constexpr (PAGED) {
+    const uintptr_t r01 = i & 1 ? reinterpret_cast<uintptr_t>(rp[1]) : reinterpret_cast<uintptr_t>(rp[0]);
+    const uintptr_t r23 = i & 1 ? reinterpret_cast<uintptr_t>(rp[3]) : reinterpret_cast<uintptr_t>(rp[2]);
+    return reinterpret_cast<const uint8_t*>(i & 2 ? r23 : r01);
+  } else {
+    constexpr BlockLayout BL = block_layout(KB, VB, GT);
+    constexpr int SPB = GT / kStream;
+    const int g = min(g0 + i, g0 + ns - 1);
+    return rp[0] + (g / SPB - g0 / SPB) * BL.bytes;
+  }
 }
-__device__ __forceinline__ int lane_half(const int (&hf)[4], int lane) {
-  const int i = lane >> 4;
-  return i == 0 ? hf[0] : i == 1 ? hf[1] : i == 2 ? hf[2] : hf[3];
+__device__ __forceinline__ int lane_half(int g0, int ns, int spb, int lane) {
+  return min(g0 + (lane >> 4), g0 + ns - 1) % spb;
 }
 
 // Key stage of streams [g0, g0 + ns): codes to `dst`, scale and zero to
 // `meta`; Stage::kLoads instructions.
 template <int KB, int VB, int GT, bool PAGED>
-__device__ __forceinline__ void issue_kstage(const DecodeArgs& a, long long u, int g0, int ns,
+__device__ __forceinline__ void issue_kstage(const DecodeArgs& a, long long u, const uint8_t* ubase, int g0, int ns,
                                              uint8_t* dst, uint8_t* meta_dst) {
   using S = Stage<KB, VB>;
   constexpr BlockLayout BL = block_layout(KB, VB, GT);
   const int lane = threadIdx.x & 63;
   const uint8_t* rp[4];
   int hf[4];
-  step_records<KB, VB, GT, PAGED>(a, u, g0, ns, rp, hf);
+  step_records<KB, VB, GT, PAGED>(a, u, ubase, g0, ns, rp, hf);
 #pragma unroll
   for (int gi = 0; gi < 4; ++gi) {
 #pragma unroll
@@ -423,21 +444,22 @@ __device__ __forceinline__ void issue_kstage(const DecodeArgs& a, long long u, i
   // lanes per stream.  Stream i's 16-byte chunk j lands in LDS slot
   // (j + 4 i) mod 16 of the stream's 256 bytes: the key wave reads chunk
   // 4 lk + c of four streams at once, which then fall on distinct banks.
-  const uint8_t* const meta = lane_record(rp, lane) + ((lane - 4 * (lane >> 4)) & 15) * 16;
+  const uint8_t* const meta =
+      lane_record<KB, VB, GT, PAGED>(rp, g0, ns, lane) + ((lane - 4 * (lane >> 4)) & 15) * 16;
   dma16(meta + BL.k_scale, meta_dst);
   dma16(meta + BL.k_zero, meta_dst + 4 * D * 2);
 }
 
 // Value stage of groups [g0, g0 + ns): Stage::vLoads instructions.
 template <int KB, int VB, int GT, bool PAGED>
-__device__ __forceinline__ void issue_vstage(const DecodeArgs& a, long long u, int g0, int ns,
+__device__ __forceinline__ void issue_vstage(const DecodeArgs& a, long long u, const uint8_t* ubase, int g0, int ns,
                                              uint8_t* dst) {
   using S = Stage<KB, VB>;
   constexpr BlockLayout BL = block_layout(KB, VB, GT);
   const int lane = threadIdx.x & 63;
   const uint8_t* rp[4];
   int hf[4];
-  step_records<KB, VB, GT, PAGED>(a, u, g0, ns, rp, hf);
+  step_records<KB, VB, GT, PAGED>(a, u, ubase, g0, ns, rp, hf);
 #pragma unroll
   for (int gi = 0; gi < 4; ++gi) {
 #pragma unroll
@@ -449,8 +471,8 @@ __device__ __forceinline__ void issue_vstage(const DecodeArgs& a, long long u, i
   // channel groups of 32 share one stored group.  Lane: stream lane / 16,
   // channel group c / 4 and 8 tokens (c % 4) of c = lane % 16.
   const int c = lane & 15;
-  const int off = ((32 * (c >> 2)) / GT * GT + kStream * lane_half(hf, lane) + 8 * (c & 3)) * 2;
-  const uint8_t* const meta = lane_record(rp, lane) + off;
+  const int off = ((32 * (c >> 2)) / GT * GT + kStream * lane_half(g0, ns, GT / kStream, lane) + 8 * (c & 3)) * 2;
+  const uint8_t* const meta = lane_record<KB, VB, GT, PAGED>(rp, g0, ns, lane) + off;
   dma16(meta + BL.v_scale, dst + S::offVS);
   dma16(meta + BL.v_zero, dst + S::offVZ);
 }
@@ -539,10 +561,12 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
   // The value wave waits at every step's barrier for this wave's softmax, so
   // this wave issues ahead of other workgroups' waves on its SIMD.
   __builtin_amdgcn_s_setprio(1);
+  constexpr BlockLayout BLu = block_layout(KB, VB, GT);
+  const uint8_t* const ubase = a.blocks + static_cast<size_t>(u) * a.nb * BLu.bytes;  // (unit-major)
   // the first stage's loads go out before q is read: their latencies overlap
   {
     const int f0 = step_first(gb, 0, n_steps, rot);
-    issue_kstage<KB, VB, GT, PAGED>(a, u, f0, min(4, ge - f0), smem, smem + S::offKM0);
+    issue_kstage<KB, VB, GT, PAGED>(a, u, ubase, f0, min(4, ge - f0), smem, smem + S::offKM0);
   }
   // q of head hq, channels 32*lk .. 32*lk+31 (head slots hq >= NQ: zeros)
   float qf[32];
@@ -631,7 +655,7 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
     wave_lds_sync();
     if (step + 1 < n_steps) {
       const int g1 = step_first(gb, step + 1, n_steps, rot);
-      issue_kstage<KB, VB, GT, PAGED>(a, u, g1, min(4, ge - g1), smem,
+      issue_kstage<KB, VB, GT, PAGED>(a, u, ubase, g1, min(4, ge - g1), smem,
                                       smem + S::offKM0 + ((step + 1) & 1) * S::kMetaBytes);
     }
     // B = q' * S (hi, lo) for head hq and group g0 + gc, built per block of
@@ -706,9 +730,10 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
         x[4 + i] = valid ? fmaf(x1[i], k_unscale, bz) : -INFINITY;
       }
     }
-    float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-    mx = fmaxf(mx, partner<1>(mx));
-    mx = fmaxf(mx, partner<2>(mx));
+    float mx = max_raw(max_raw(max_raw(x[0], x[1]), max_raw(x[2], x[3])),
+                       max_raw(max_raw(x[4], x[5]), max_raw(x[6], x[7])));
+    mx = max_raw(mx, partner<1>(mx));
+    mx = max_raw(mx, partner<2>(mx));
     mx = swap_max<16>(mx);
     mx = swap_max<32>(mx);  // max over the 4 streams and 32 tokens of head hq
     const float m_new = fmaxf(m_run, mx);
@@ -770,9 +795,11 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
   const int hsrc = kHiLoCols ? hq % NQ : hq;  // head whose probabilities this column takes
   const int part = kHiLoCols ? hq / NQ : 0;   // 0: hi, 1: lo, 2 and 3 (NQ = 1): unused
   uint8_t* const vbase = smem + S::offV0;
+  constexpr BlockLayout BLu = block_layout(KB, VB, GT);
+  const uint8_t* const ubase = a.blocks + static_cast<size_t>(u) * a.nb * BLu.bytes;  // (unit-major)
   {
     const int f0 = step_first(gb, 0, n_steps, rot);
-    issue_vstage<KB, VB, GT, PAGED>(a, u, f0, min(4, ge - f0), vbase);
+    issue_vstage<KB, VB, GT, PAGED>(a, u, ubase, f0, min(4, ge - f0), vbase);
   }
   constexpr float v_unscale = static_cast<float>(1 << (24 - VS::F));  // product -> output
 
@@ -788,7 +815,7 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
     const bool more = step + 1 < n_steps;
     if (more) {
       const int g1 = step_first(gb, step + 1, n_steps, rot);
-      issue_vstage<KB, VB, GT, PAGED>(a, u, g1, min(4, ge - g1), vbase + ((step + 1) & 1) * S::vBytes);
+      issue_vstage<KB, VB, GT, PAGED>(a, u, ubase, g1, min(4, ge - g1), vbase + ((step + 1) & 1) * S::vBytes);
     }
     wg_barrier();  // the key wave has written this step's probabilities
     if (more) {
@@ -817,7 +844,10 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
       const u32x4 vz = *reinterpret_cast<const u32x4*>(vstage + S::offVZ + vmo);
       // p of tokens 8*lk .. 8*lk+7 (pair e: tokens 2e, 2e+1); B = p * S as
       // fp16 hi + lo of the binary32 product (the probabilities are not exact
-      // in fp16, so the product is formed in binary32 and split)
+      // in fp16, so the product is formed in binary32 and split).  (Handing p
+      // over as fp16 hi + lo pairs instead, for packed fp16 products here,
+      // takes 48 fewer instructions in this wave and 16 more in the key
+      // wave, and measured 3% slower: the key wave sets the pace.)
       const float* prow = hp + (gs * GQ + hsrc) * kRowP + 8 * lk;
       const f32x4 p0 = *reinterpret_cast<const f32x4*>(prow);
       const f32x4 p1 = *reinterpret_cast<const f32x4*>(prow + 4);
