@@ -108,10 +108,8 @@ def ragged_lengths(w):
 
 
 def decode_kernel(w):
-    """Name and source of the split-K decode kernel that serves the workload."""
-    if w.gq in (1, 2, 4):
-        return "decode_mfma", "kivi_decode_mfma.hip"
-    return "decode_split_valu", "kivi_decode.hip"
+    """Name and source of the split-K decode kernel (every head ratio)."""
+    return "decode_mfma", "kivi_decode_mfma.hip"
 
 
 def traffic_from_profile(kernel, workload, kernel_src):

@@ -276,9 +276,10 @@ kivi_status kivi_decode_attn_workspace_bytes(const kivi_cache* cache,
  * The token axis is split across workgroups and the per-split partial
  * softmax states are merged exactly (log-sum-exp) in a second kernel; the
  * workspace holds those partials.
- * With 1, 2 or 4 query heads per kv head the products run on the matrix
- * cores with fp16 operands (hi + lo pairs, about 22 significant bits).  Each
- * workgroup scales its folded operands q*S and p*S by powers of two chosen
+ * The products run on the matrix cores with fp16 operands (hi + lo pairs,
+ * about 22 significant bits); one workgroup serves up to 4 query heads of a
+ * kv head per token split, so 8 or 16 query heads per kv head take 2 or 4
+ * workgroups over the same records.  Each workgroup scales its folded operands q*S and p*S by powers of two chosen
  * from the largest |q| of each head and the scale maxima of the records it
  * reads, so every input in the domain stated above stays in the operands'
  * range; the scaling is exact and undone in fp32.
@@ -286,7 +287,7 @@ kivi_status kivi_decode_attn_workspace_bytes(const kivi_cache* cache,
  * sequence without tokens gets zeros.  The splits are then planned for the
  * longest sequence, and each launch pair covers 64 sequences.
  * Errors: INVALID_ARG (nulls, Hq not a positive multiple of H, bad dtype),
- * UNSUPPORTED (a ratio Hq / H other than 1, 2, 4 or 8),
+ * UNSUPPORTED (a ratio Hq / H other than 1, 2, 4, 8 or 16),
  * EMPTY (no sequence holds a token), BUFFER_TOO_SMALL (ws_bytes below the
  * workspace query), HIP (the compute-unit query failed: nothing enqueued,
  * cache unchanged; or the launch failed: the handle is poisoned). */
@@ -299,11 +300,10 @@ kivi_status kivi_decode_attn(kivi_cache* cache, const void* q,
  * arrays of kv_dtype [B][H][D]) exactly as kivi_append with n_tokens = 1,
  * then runs kivi_decode_attn over the cache including that token (the
  * residual-window append and decode attention of one generated token, page
- * "KIVI: Asymmetric 2-Bit KV Cache Quantization Guide", "Step 3").  With 1, 2
- * or 4 query heads per kv head the token is read from k_new / v_new and
- * stored into the window by the attention launch itself: one launch fewer
- * than the two calls.  A full window is still packed first, in a launch of
- * its own.  With 8 query heads per kv head it runs the two calls.
+ * "KIVI: Asymmetric 2-Bit KV Cache Quantization Guide", "Step 3").  The
+ * token is read from k_new / v_new and stored into the window by the
+ * attention launch itself: one launch fewer than the two calls.  A full
+ * window is still packed first, in a launch of its own.
  * Errors: those of kivi_decode_attn and kivi_append (INVALID_ARG for null or
  * unaligned k_new / v_new, CAPACITY).  The argument checks, the device query
  * and the split plan of the state after the append all come before anything

@@ -575,8 +575,8 @@ kivi_status check_decode_args(const kivi_cache* c, const void* q, int32_t num_q_
   if (out_dtype != KIVI_F16 && out_dtype != KIVI_BF16 && out_dtype != KIVI_F32)
     return fail(KIVI_ERR_INVALID_ARG, "bad out_dtype %d", out_dtype);
   const int gq = num_q_heads / c->cfg.num_kv_heads;
-  if (gq != 1 && gq != 2 && gq != 4 && gq != 8)
-    return fail(KIVI_ERR_UNSUPPORTED, "query heads per kv head must be 1, 2, 4 or 8 (got %d)", gq);
+  if (gq != 1 && gq != 2 && gq != 4 && gq != 8 && gq != 16)
+    return fail(KIVI_ERR_UNSUPPORTED, "query heads per kv head must be 1, 2, 4, 8 or 16 (got %d)", gq);
   size_t need = 0;
   kivi_decode_attn_workspace_bytes(c, num_q_heads, &need);
   if (ws_bytes < need)
@@ -651,129 +651,117 @@ kivi_status ensure_cu_count(kivi_cache* c) {
 
 // How a decode launch splits the token axis.
 struct DecodePlan {
-  bool use_mfma;
-  int n_split, per, n_split_packed, gps;
+  int n_split, n_split_packed, gps, hg;
 };
 
 // Plans the decode launches over state `st` for gq query heads per kv head
 // (pure host arithmetic: no device access, no change of the cache).
 kivi_status plan_decode(const kivi_cache* c, const DecodeState& st, int gq, DecodePlan& out) {
-  // both decode kernels walk the packed tokens in streams of 32 (a block of
-  // G = 32, or half a block of G = 64)
+  // the kernel walks the packed tokens in streams of 32 (a block of G = 32,
+  // or half a block of G = 64)
   const int G = kivi::kStream;
   const int units = c->cfg.batch * c->cfg.num_kv_heads;
   const int nqg = st.n_quant / G;
-  // matrix-core kernel: up to 4 query heads per kv head share one wave
-  const bool use_mfma = gq == 1 || gq == 2 || gq == 4;
-  int n_split, per = 0, n_split_packed = 0, gps = 0;
-  if (use_mfma) {
-    // one wave per split; one round of as many waves as fit in LDS on every
-    // CU, each split a multiple of 4 groups; the window is one more partial,
-    // computed by the wave of the last packed split
-    if (nqg > 0) {
-      // resident workgroups (key + value wave) per CU: LDS, and at most 6
-      // (3 waves per SIMD at the kernel's register budget)
-      const int wgs_per_cu = std::max(
-          1, std::min(6, kivi::kLdsPerCu / kivi::mfma_wg_lds_bytes(c->cfg.k_bits, c->cfg.v_bits)));
-      const long long slots = (long long)wgs_per_cu * c->cu_count;
-      const int max_split = std::max(1, std::min((nqg + 3) / 4, kivi::kMaxSplits - 1));
-      auto plan = [&](int want, int& g, int& np) {
-        g = ((nqg + want - 1) / want + 3) / 4 * 4;  // groups per split, whole steps of 4
-        np = (nqg + g - 1) / g;
-      };
-      if (c->forced_splits > 0) {
-        plan(std::min(c->forced_splits, max_split), gps, n_split_packed);
-      } else {
-        // minimise (rounds of resident waves) x (steps per wave): every
-        // split of one launch takes the same time, so a partly filled last
-        // round costs a whole wave duration
-        // (sequences of different lengths: only the splits that hold groups
-        // of their sequence count; the others end at once)
-        // For ragged caches every multiple of 4 is a candidate split size
-        // (the divisions of the longest sequence alone are too coarse to
-        // fill a round with the shorter ones).
-        long long best = -1;
-        const int n_cand = st.ragged ? (nqg + 3) / 4 : max_split;
-        // Ragged caches: the plans whose whole grid (the splits past a short
-        // sequence's end included) fits in one round of resident slots are
-        // preferred (a second round, even of short or empty splits, was
-        // measured slower), and among them the one with the
-        // smallest estimated time (steps per split + set-up) x (time of one
-        // step).  A step takes the time of a lone workgroup or, with k
-        // workgroups sharing a CU, k times the per-workgroup share of a fully
-        // occupied CU, whichever is longer: the split kernel is bound by the
-        // vector and matrix issue of its SIMDs.  In units of that share, a
-        // lone workgroup's step is kLone x (workgroups per CU at full
-        // occupancy): about 2.35 us against 3.7-4.1 us for a step of a full
-        // CU on c2-shaped data.  Interleaved runs on ragged batches: c3 135-139
-        // -> 115-125 us and c1 36.3-36.8 -> 33.0-33.9 us against the rounds
-        // model above; c2 unchanged within noise.
-        constexpr double kSetup = 1.5, kLone = 0.57;
-        const double lone = kLone * wgs_per_cu;
-        double best1 = -1.0;
-        for (int i = 1; i <= n_cand; ++i) {
-          int g, np;
-          if (st.ragged) {
-            g = 4 * i;
-            np = (nqg + g - 1) / g;
-            if (np > kivi::kMaxSplits - 1) continue;
-          } else {
-            plan(i, g, np);
-          }
-          long long work = (long long)units * np;
-          if (st.ragged) {
-            work = 0;
-            for (int b = 0; b < c->cfg.batch; ++b) work += (st.sq[b] / G + g - 1) / g;
-            work *= c->cfg.num_kv_heads;
-            // (a ragged launch covers at most kDecodeChunk sequences)
-            const long long grid = (long long)np * std::min(c->cfg.batch, kivi::kDecodeChunk) * c->cfg.num_kv_heads;
-            if (grid <= slots) {
-              const double cost1 = (g / 4 + kSetup) * std::max(lone, work / (double)c->cu_count);
-              if (best1 < 0.0 || cost1 < best1) {
-                best1 = cost1;
-                gps = g;
-                n_split_packed = np;
-              }
-              continue;
+  // a workgroup serves up to 4 query heads of its kv head; 8 or 16 take 2 or
+  // 4 workgroups (head groups) per split
+  const int hg = gq > 4 ? gq / 4 : 1;
+  int n_split_packed = 0, gps = 0;
+  // one workgroup (key wave + value wave) per split and head group; one
+  // round of as many as fit in LDS on every CU, each split a multiple of 4
+  // groups; the window is one more partial, computed by the workgroup of
+  // the last packed split
+  if (nqg > 0) {
+    // resident workgroups per CU: LDS, and at most 6 (3 waves per SIMD at
+    // the kernel's register budget)
+    const int wgs_per_cu = std::max(
+        1, std::min(6, kivi::kLdsPerCu / kivi::mfma_wg_lds_bytes(c->cfg.k_bits, c->cfg.v_bits)));
+    const long long slots = (long long)wgs_per_cu * c->cu_count;
+    const int max_split = std::max(1, std::min((nqg + 3) / 4, kivi::kMaxSplits - 1));
+    auto plan = [&](int want, int& g, int& np) {
+      g = ((nqg + want - 1) / want + 3) / 4 * 4;  // groups per split, whole steps of 4
+      np = (nqg + g - 1) / g;
+    };
+    if (c->forced_splits > 0) {
+      plan(std::min(c->forced_splits, max_split), gps, n_split_packed);
+    } else {
+      // minimise (rounds of resident workgroups) x (steps per workgroup):
+      // every split of one launch takes the same time, so a partly filled
+      // last round costs a whole workgroup duration
+      // (sequences of different lengths: only the splits that hold groups
+      // of their sequence count; the others end at once)
+      // For ragged caches every multiple of 4 is a candidate split size
+      // (the divisions of the longest sequence alone are too coarse to
+      // fill a round with the shorter ones).
+      long long best = -1;
+      const int n_cand = st.ragged ? (nqg + 3) / 4 : max_split;
+      // Ragged caches: the plans whose whole grid (the splits past a short
+      // sequence's end included) fits in one round of resident slots are
+      // preferred (a second round, even of short or empty splits, was
+      // measured slower), and among them the one with the
+      // smallest estimated time (steps per split + set-up) x (time of one
+      // step).  A step takes the time of a lone workgroup or, with k
+      // workgroups sharing a CU, k times the per-workgroup share of a fully
+      // occupied CU, whichever is longer: the split kernel is bound by the
+      // vector and matrix issue of its SIMDs.  In units of that share, a
+      // lone workgroup's step is kLone x (workgroups per CU at full
+      // occupancy): about 2.35 us against 3.7-4.1 us for a step of a full
+      // CU on c2-shaped data.  Interleaved runs on ragged batches: c3 135-139
+      // -> 115-125 us and c1 36.3-36.8 -> 33.0-33.9 us against the rounds
+      // model above; c2 unchanged within noise.
+      constexpr double kSetup = 1.5, kLone = 0.57;
+      const double lone = kLone * wgs_per_cu;
+      double best1 = -1.0;
+      for (int i = 1; i <= n_cand; ++i) {
+        int g, np;
+        if (st.ragged) {
+          g = 4 * i;
+          np = (nqg + g - 1) / g;
+          if (np > kivi::kMaxSplits - 1) continue;
+        } else {
+          plan(i, g, np);
+        }
+        long long work = (long long)units * np * hg;
+        if (st.ragged) {
+          work = 0;
+          for (int b = 0; b < c->cfg.batch; ++b) work += (st.sq[b] / G + g - 1) / g;
+          work *= (long long)c->cfg.num_kv_heads * hg;
+          // (a ragged launch covers at most kDecodeChunk sequences)
+          const long long grid =
+              (long long)np * std::min(c->cfg.batch, kivi::kDecodeChunk) * c->cfg.num_kv_heads * hg;
+          if (grid <= slots) {
+            const double cost1 = (g / 4 + kSetup) * std::max(lone, work / (double)c->cu_count);
+            if (best1 < 0.0 || cost1 < best1) {
+              best1 = cost1;
+              gps = g;
+              n_split_packed = np;
             }
-            if (best1 >= 0.0) continue;  // a one-round plan exists
+            continue;
           }
-          const long long rounds = (work + slots - 1) / slots;
-          const long long cost = rounds * (g / 4 + 1);  // +1: per-wave set-up and partial
-          if (best1 < 0.0 && (best < 0 || cost < best)) {
-            best = cost;
-            gps = g;
-            n_split_packed = np;
-          }
+          if (best1 >= 0.0) continue;  // a one-round plan exists
+        }
+        const long long rounds = (work + slots - 1) / slots;
+        const long long cost = rounds * (g / 4 + 1);  // +1: per-workgroup set-up and partial
+        if (best1 < 0.0 && (best < 0 || cost < best)) {
+          best = cost;
+          gps = g;
+          n_split_packed = np;
         }
       }
     }
-    n_split = n_split_packed + (st.n_resid > 0 ? 1 : 0);
-  } else {
-    const int n_items = nqg + (st.n_resid + G - 1) / G;
-    if (c->forced_splits > 0) {
-      n_split = c->forced_splits;
-    } else {
-      const int target = 4 * c->cu_count;  // workgroups to keep every CU busy
-      n_split = (target + units - 1) / units;
-    }
-    n_split = std::max(1, std::min({n_split, n_items, kivi::kMaxSplits}));
-    per = (n_items + n_split - 1) / n_split;
-    n_split = (n_items + per - 1) / per;
   }
+  const int n_split = n_split_packed + (st.n_resid > 0 ? 1 : 0);
 
   // the workspace query sized the partials for at most this many splits
   if (n_split > std::min(kivi::kMaxSplits, max_items(c)))
     return fail(KIVI_ERR_UNSUPPORTED, "internal: %d planned splits exceed the workspace bound %d", n_split,
                 std::min(kivi::kMaxSplits, max_items(c)));
-  out = DecodePlan{use_mfma, n_split, per, n_split_packed, gps};
+  out = DecodePlan{n_split, n_split_packed, gps, hg};
   return KIVI_OK;
 }
 
 // Launches decode attention over the cache's current state with a plan made
-// for that state.  With k_new (matrix-core kernel only) each unit's newest
-// window token is read from k_new / v_new and stored into the window by the
-// same launch.
+// for that state.  With k_new each unit's newest window token is read from
+// k_new / v_new and stored into the window by the same launch.
 kivi_status decode_launch(kivi_cache* c, const DecodePlan& plan, const void* q, int32_t num_q_heads,
                           float softmax_scale, void* out, int32_t out_dtype, void* workspace, void* stream,
                           const void* k_new, const void* v_new) {
@@ -796,9 +784,9 @@ kivi_status decode_launch(kivi_cache* c, const DecodePlan& plan, const void* q, 
   a.n_quant = c->n_quant;
   a.n_resid = c->n_resid;
   a.n_split = plan.n_split;
-  a.items_per_split = plan.per;
   a.n_split_packed = plan.n_split_packed;
   a.groups_per_split = plan.gps;
+  a.hg = plan.hg;
   a.qscale = softmax_scale * 1.4426950408889634f;  // log2(e): base-2 softmax
   a.page_table = c->page_table;
   a.page_stride = c->page_stride;
@@ -809,7 +797,7 @@ kivi_status decode_launch(kivi_cache* c, const DecodePlan& plan, const void* q, 
   a.v_resid_w = c->v_resid;
   if (!c->ragged) {
     hipError_t e = kivi::launch_decode(a, c->cfg.k_bits, c->cfg.v_bits, c->cfg.kv_dtype, out_dtype,
-                                       plan.use_mfma, static_cast<hipStream_t>(stream), c->ev_split_begin,
+                                       static_cast<hipStream_t>(stream), c->ev_split_begin,
                                        c->ev_split_end);
     if (e != hipSuccess) return hip_fail(c, e, "decode launch");
     return KIVI_OK;
@@ -828,7 +816,7 @@ kivi_status decode_launch(kivi_cache* c, const DecodePlan& plan, const void* q, 
       a.seq_len[i][1] = c->sr[b0 + i];
     }
     hipError_t e = kivi::launch_decode(a, c->cfg.k_bits, c->cfg.v_bits, c->cfg.kv_dtype, out_dtype,
-                                       plan.use_mfma, static_cast<hipStream_t>(stream), c->ev_split_begin,
+                                       static_cast<hipStream_t>(stream), c->ev_split_begin,
                                        c->ev_split_end);
     if (e != hipSuccess) return hip_fail(c, e, "decode launch (sequences of different lengths)");
   }
@@ -869,8 +857,8 @@ kivi_status kivi::decode_attn_bounded(kivi_cache* c, const void* q, int32_t num_
   if (out_dtype != KIVI_F16 && out_dtype != KIVI_BF16 && out_dtype != KIVI_F32)
     return fail(KIVI_ERR_INVALID_ARG, "bad out_dtype %d", out_dtype);
   const int gq = num_q_heads / c->cfg.num_kv_heads;
-  if (gq != 1 && gq != 2 && gq != 4 && gq != 8)
-    return fail(KIVI_ERR_UNSUPPORTED, "query heads per kv head must be 1, 2, 4 or 8 (got %d)", gq);
+  if (gq != 1 && gq != 2 && gq != 4 && gq != 8 && gq != 16)
+    return fail(KIVI_ERR_UNSUPPORTED, "query heads per kv head must be 1, 2, 4, 8 or 16 (got %d)", gq);
   if (c->n_quant + c->n_resid < 1) return fail(KIVI_ERR_EMPTY, "decode on an empty cache");
   kivi_status st;
   if ((st = ensure_cu_count(c)) != KIVI_OK) return st;
@@ -911,11 +899,6 @@ kivi_status kivi_append_decode_attn(kivi_cache* c, const void* k_new, const void
   const int gq = num_q_heads / c->cfg.num_kv_heads;
   DecodePlan plan;
   if ((st = plan_decode(c, after_token(c), gq, plan)) != KIVI_OK) return st;
-  if (gq == 8) {  // vector-ALU decode: the append stays a launch of its own
-    if ((st = kivi_append(c, k_new, v_new, 1, stream)) != KIVI_OK) return st;
-    return decode_launch(c, plan, q, num_q_heads, softmax_scale, out, out_dtype, workspace, stream,
-                         nullptr, nullptr);
-  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int R = c->cfg.residual_length;
   // a full window is packed before the token enters it (a launch of its

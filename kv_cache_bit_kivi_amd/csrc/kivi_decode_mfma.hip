@@ -1,7 +1,9 @@
 // kivi_decode_mfma.hip - decode attention with both contractions on the
-// matrix cores, for 1, 2 or 4 query heads per kv head (multi-head and
+// matrix cores, for 1, 2, 4, 8 or 16 query heads per kv head (multi-head and
 // grouped-query attention).  The matrix columns hold 4 head slots; with
-// fewer heads the spare slots carry zeros and are masked out.
+// fewer heads the spare slots carry zeros and are masked out, and 8 or 16
+// heads take 2 or 4 workgroups (head groups) per split, launched side by side
+// on one XCD so that the second reads the records from its L2.
 //
 // Method: split-K decode attention over the packed cache (dequantized value =
 // code * scale + zero, page "KIVI: Asymmetric 2-Bit KV Cache Quantization
@@ -16,11 +18,12 @@
 // of each product so that the codes themselves feed the matrix cores:
 //   q . k^_t   = sum_d (q_d S_gd) c_td + sum_d q_d Z_gd         (key group g)
 //   sum_t p_t v^_t,d = sum_t (p_t S_tm) c_td + sum_t p_t Z_tm   (value group m)
-// Codes enter v_mfma_f32_16x16x32_f16 as fp16 subnormals c * 2^-24 (exact),
-// extracted from the split-half words with one shift and one mask per pair.
-// The folded operands q*S and p*S are carried as fp16 hi + lo pairs (two
-// MFMAs), which keeps them within 2^-22 relative; the zero-point term of the keys
-// (one dot product per group and head) runs on the vector ALUs.
+// Codes enter v_mfma_f32_16x16x32_f16 as the normal fp16 numbers c * 2^(F-15)
+// (exact), extracted from the split-half words with one mask and one packed
+// multiply per pair.  The folded operands q*S and p*S are carried as fp16
+// hi + lo pairs (two MFMAs): q*S exactly, p*S within 2^-22 relative; the
+// zero-point term of the keys (one dot product per group and head) runs on
+// the vector ALUs.
 //
 // Key side: four consecutive 32-token groups at once, block-diagonal: A rows
 // are 4 tokens of each of the 4 groups, B columns are the 4 heads x 4 groups,
@@ -134,33 +137,56 @@ __device__ __forceinline__ float dot2_acc(uint32_t a, uint32_t b, float acc) {
 // Code extraction.  Two codes of a split-half word sit at bits [s, s+b) and
 // [16+s, 16+s+b); masking the word (or the word shifted right by 8) in place
 // leaves them as fp16 subnormals c * 2^(t-24), t = 0, 2, 4, 6 (2-bit) or
-// t = 0, 4 (4-bit), exactly.  The dense operand of the product carries the
-// compensating 2^(F-t) (F = 6 for 2-bit, 4 for 4-bit), so every product is
-// c * x * 2^(F-24) and results are rescaled by 2^(24-F) once.
+// t = 0, 4 (4-bit), exactly.  One packed multiply by 2^(F-t+9) (F = 6 for
+// 2-bit, 4 for 4-bit; exact) then makes every code the normal fp16 number
+// c * 2^(F-15) (zero stays zero), the same factor at every position.
+//
+// Normal operands matter for the accuracy of the products: measured on
+// MI355X, a v_mfma_f32_16x16x32_f16 whose A operand holds subnormals adds
+// its products with errors of hundreds of binary32 units relative to the sum
+// of their magnitudes (the subnormal codes with position factors in the
+// other operand: 270 units at 4 bits, 850-1260 at 2 bits, worst over 25600
+// sums of 128 products), while the same products from normal operands come
+// within 5 units.  In attention those errors reached the 2e-3 tolerance
+// where one token holds most of a head's weight and its value is large.
 template <int BITS>
 struct CodeScale {
   static constexpr int F = BITS == 2 ? 6 : 4;
-  // log2 of the factor for pair e' (codes 2e', 2e'+1 of an 8-code run)
-  static constexpr int lf(int ep) { return BITS == 2 ? F - 2 * ep : F - 4 * (ep & 1); }
+  // position t of pair e' (codes 2e', 2e'+1 of an 8-code run) in its half
+  static constexpr int t(int ep) { return BITS == 2 ? 2 * ep : 4 * (ep & 1); }
 };
 
+// 2^k as an fp16 pair, 0 <= k <= 15.
+__device__ __forceinline__ constexpr uint32_t pow2_pair(int k) {
+  return static_cast<uint32_t>((15 + k) << 10) * 0x00010001u;
+}
+
+// a * b for fp16 pairs (v_pk_mul_f16; exact when b is a power of two and the
+// product stays in range).
+__device__ __forceinline__ uint32_t mul_pair(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_pk_mul_f16 %0, %1, %2" : "=v"(r) : "v"(a), "s"(b));
+  return r;
+}
+
 // 8 codes (one run of 8 consecutive entries: positions 8*hb .. 8*hb+7 of
-// word x) as four fp16 pairs c * 2^(t-24).
+// word x) as four fp16 pairs c * 2^(F-15).
 template <int BITS>
 __device__ __forceinline__ half8_t codes8(uint32_t x, bool high_byte) {
+  using CS = CodeScale<BITS>;
   u32x4 r;
   if constexpr (BITS == 2) {
     const uint32_t y = high_byte ? (x >> 8) : x;
-    r[0] = y & 0x00030003u;
-    r[1] = y & 0x000C000Cu;
-    r[2] = y & 0x00300030u;
-    r[3] = y & 0x00C000C0u;
+    r[0] = mul_pair(y & 0x00030003u, pow2_pair(CS::F - CS::t(0) + 9));
+    r[1] = mul_pair(y & 0x000C000Cu, pow2_pair(CS::F - CS::t(1) + 9));
+    r[2] = mul_pair(y & 0x00300030u, pow2_pair(CS::F - CS::t(2) + 9));
+    r[3] = mul_pair(y & 0x00C000C0u, pow2_pair(CS::F - CS::t(3) + 9));
   } else {
     const uint32_t y = x >> 8;
-    r[0] = x & 0x000F000Fu;
-    r[1] = x & 0x00F000F0u;
-    r[2] = y & 0x000F000Fu;
-    r[3] = y & 0x00F000F0u;
+    r[0] = mul_pair(x & 0x000F000Fu, pow2_pair(CS::F - CS::t(0) + 9));
+    r[1] = mul_pair(x & 0x00F000F0u, pow2_pair(CS::F - CS::t(1) + 9));
+    r[2] = mul_pair(y & 0x000F000Fu, pow2_pair(CS::F - CS::t(2) + 9));
+    r[3] = mul_pair(y & 0x00F000F0u, pow2_pair(CS::F - CS::t(3) + 9));
   }
   return as_h8(r);
 }
@@ -244,18 +270,18 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // Residual window on the vector ALUs (one wave, fp32), written as its own
 // partial.  qsh / psh: LDS scratch of this wave.
 template <bool BF16, int NQ>
-__device__ void window_wave(const DecodeArgs& a, long long u, int b, int kvh, int split, int nr,
-                            float (*qsh)[D], float (*psh)[G]) {
+__device__ void window_wave(const DecodeArgs& a, long long u, int b, int h0, int split, int nr,
+                            bool store_token, float (*qsh)[D], float (*psh)[G]) {
   const int lane = threadIdx.x & 63;
   for (int i = lane; i < NQ * D; i += 64) {
     qsh[i / D][i % D] =
-        to_f32<BF16>(a.q[((long long)b * a.Hq + kvh * NQ + i / D) * D + i % D]) * a.qscale;
+        to_f32<BF16>(a.q[((long long)b * a.Hq + h0 + i / D) * D + i % D]) * a.qscale;
   }
   // fused append: the newest token (slot nr - 1) comes from k_new / v_new;
-  // this wave is the only one of the launch that touches the unit's window,
-  // so it also stores the token there
+  // this wave (of the unit's first head group) is the only one of the launch
+  // that writes the unit's window, so it also stores the token there
   const int t_new = a.k_new ? nr - 1 : -1;
-  if (t_new >= 0) {
+  if (t_new >= 0 && store_token) {
     const long long src = u * D + 2 * lane, dst = (u * a.R + t_new) * D + 2 * lane;
     *reinterpret_cast<uint32_t*>(a.k_resid_w + dst) = *reinterpret_cast<const uint32_t*>(a.k_new + src);
     *reinterpret_cast<uint32_t*>(a.v_resid_w + dst) = *reinterpret_cast<const uint32_t*>(a.v_new + src);
@@ -322,7 +348,7 @@ __device__ void window_wave(const DecodeArgs& a, long long u, int b, int kvh, in
   }
 #pragma unroll
   for (int h = 0; h < NQ; ++h) {
-    float* P = a.partial + (((long long)b * a.Hq + kvh * NQ + h) * a.n_split + split) * (D + 2);
+    float* P = a.partial + (((long long)b * a.Hq + h0 + h) * a.n_split + split) * (D + 2);
     P[2 + 2 * lane] = o[h][0];
     P[3 + 2 * lane] = o[h][1];
     if (lane == 0) {
@@ -479,14 +505,17 @@ __device__ __forceinline__ void issue_vstage(const DecodeArgs& a, long long u, c
 
 // ---------------------------------------------------------------------------
 // Operand range.  The folded operands q''*S (keys) and p'*S (values) are fp16
-// hi + lo pairs, so they must stay below 65504.  Each workgroup scales them by
-// powers of two: q'' by 2^-Ek (one exponent per head, from the head's largest
-// |q| and the largest key scale of the records the split reads) and p' by
-// 2^-Ev (one per split, from the largest value scale), such that every
-// product stays below 2^15.  Scaling by a power of two is exact; the scores
-// take 2^Ek back in fp32, and the partial's (m, l, o) carry 2^-Ev in l and o,
-// which the partial's m + Ev compensates in the merge's weights 2^(m - M).
-// Ordinary inputs get Ek = Ev = 0.
+// hi + lo pairs, so they must stay below 65504, and the lo half keeps its
+// precision only while it stays above the fp16 subnormal range.  Each
+// workgroup scales them by powers of two: q'' = q 2^-Ek (one exponent per
+// head, from the head's largest |q| and the largest key scale of the records
+// the split reads) and p' = p 2^-Ev (one per split, from the largest value
+// scale), chosen so that the largest product lies in [2^14, 2^15): Ek and Ev
+// are negative for ordinary inputs (the operands are scaled up) and positive
+// only for scales and queries near the fp16 limit.  Scaling by a power of
+// two is exact; the scores take 2^Ek back in fp32, and the partial's (m, l,
+// o) carry 2^-Ev in l and o, which the partial's m + Ev compensates in the
+// merge's weights 2^(m - M).
 
 // Largest stored key scale and value scale over the block records of
 // streams [gb, ge) of unit u (the same on every lane of the wave).
@@ -540,18 +569,18 @@ __device__ __forceinline__ int step_first(int gb, int step, int n_steps, int rot
   return gb + 4 * k;
 }
 
-// Smallest E >= 0 with x * 2^-E < 2^15 (x >= 0 finite).
-__device__ __forceinline__ int range_exp(float x) { return max(0, __builtin_amdgcn_frexp_expf(x) - 15); }
+// Smallest E with x * 2^-E < 2^15 (x >= 0 finite), at least -30 (x = 0 and
+// tiny x take -30).
+__device__ __forceinline__ int range_exp(float x) { return max(-30, __builtin_amdgcn_frexp_expf(x) - 15); }
 
 // ---------------------------------------------------------------------------
 // Key wave: scores of each step on the matrix cores, online softmax, and the
 // probabilities handed to the value wave.  Writes m and l of the partial.
 template <int KB, int VB, bool BF16, int NQ, int GT, bool PAGED>
-__device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b, int kvh, int split,
+__device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b, int h0, int split,
                                          int gb, int ge, int n_steps, int rot, uint8_t* smem) {
   using S = Stage<KB, VB>;
   using KS = CodeScale<KB>;
-  using VS = CodeScale<VB>;
   constexpr int KL = KB;  // key words per lane (32 channels)
   const int lane = threadIdx.x & 63;
   const int lc = lane & 15, lk = lane >> 4;
@@ -571,7 +600,7 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
   // q of head hq, channels 32*lk .. 32*lk+31 (head slots hq >= NQ: zeros)
   float qf[32];
   if (hq < NQ) {
-    const uint16_t* qp = a.q + ((long long)b * a.Hq + kvh * NQ + hq) * D + 32 * lk;
+    const uint16_t* qp = a.q + ((long long)b * a.Hq + h0 + hq) * D + 32 * lk;
 #pragma unroll
     for (int i = 0; i < 32; i += 8) {
       const uint4 v = *reinterpret_cast<const uint4*>(qp + i);
@@ -594,34 +623,25 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
   for (int i = 0; i < 32; ++i) qabs = fmaxf(qabs, fabsf(qf[i]));
   qabs = swap_max<16>(qabs);
   qabs = swap_max<32>(qabs);  // the 128 channels of head hq
-  const int ek = range_exp(static_cast<float>(1 << (KS::F - 3)) * qabs * fmaxf(sk_max, 1.0f));
-  const int ev = range_exp(static_cast<float>(1 << VS::F) * sv_max);
-  // q'' = q * 2^(lf(e) - 3 - Ek) as fp16 pairs (pair p: channels 2p, 2p+1;
-  // e = p & 3 its pair class in the run of 8): the code-position factor of
-  // the key codes it multiplies, over 8, and the range exponent.
-  // Power-of-two factors keep q'' exact (a bf16 q is rounded to fp16 once).
+  // q'' = q 2^-Ek and q'' S below 2^15 (q'' itself too, when the scales are
+  // below 1); p' = p 2^-Ev <= 2^-Ev and p' S below 2^15
+  const int ek = range_exp(qabs * fmaxf(sk_max, 1.0f));
+  const int ev = range_exp(sv_max);
+  // q'' as fp16 pairs (pair p: channels 2p, 2p+1).  The power-of-two factor
+  // keeps q'' exact (a bf16 q is rounded to fp16 once).
   // softmax_scale * log2(e) * 2^Ek multiplies the scores afterwards.  Head
   // slots hq >= NQ carry q'' = 0 and are masked out of the softmax.
   uint32_t q2[16];
 #pragma unroll
-  for (int i = 0; i < 32; i += 8) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int x = KS::lf(e) - 3 - ek;
-      q2[i / 2 + e] = pk_rne(__builtin_amdgcn_ldexpf(qf[i + 2 * e], x), __builtin_amdgcn_ldexpf(qf[i + 2 * e + 1], x));
-    }
-  }
-  // raw product -> score: products are c q S 2^(F-27-Ek)
-  const float k_unscale = __builtin_amdgcn_ldexpf(a.qscale, 27 - KS::F + ek);
+  for (int i = 0; i < 16; ++i)
+    q2[i] = pk_rne(__builtin_amdgcn_ldexpf(qf[2 * i], -ek), __builtin_amdgcn_ldexpf(qf[2 * i + 1], -ek));
+  // raw product -> score: products are c q S 2^(F-15-Ek)
+  const float k_unscale = __builtin_amdgcn_ldexpf(a.qscale, 15 - KS::F + ek);
   const float z_unscale = __builtin_amdgcn_ldexpf(a.qscale, ek);
-  // p' = p * 2^(lf(e') - Ev): the value-code factor of its token position
-  float p_exp[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) p_exp[e] = static_cast<float>(VS::lf(e) - ev);
 
   const bool diag = (lc & 3) == lk;  // lane holds scores (stream lk)
   float m_run = -INFINITY;           // running max of head hq (base 2)
-  float lcls[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // sum of scaled p, per pair class e'
+  float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // sum of p' (four partial sums)
 
   for (int step = 0; step < n_steps; ++step) {
     const int g0 = step_first(gb, step, n_steps, rot);
@@ -663,7 +683,7 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
     // overlaps the matrix products of block c); zero-point term
     // sum_d q'_d Z_d of the same (head, group) on the vector ALUs, added to
     // the scores afterwards
-    float bcls[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // per pair class: q'' carries 2^(lf(e) - 3)
+    float bcls[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // four partial sums
     f32x4 sc[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) sc[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -690,11 +710,7 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
 #pragma unroll
       for (int s = 0; s < 8; ++s) sc[s] = mfma(ak[s], bl, sc[s]);
     }
-    float bias = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      bias = fmaf(bcls[e], KS::lf(e) >= 3 ? 1.0f / static_cast<float>(1 << (KS::lf(e) - 3))
-                                          : static_cast<float>(1 << (3 - KS::lf(e))), bias);
+    float bias = (bcls[0] + bcls[1]) + (bcls[2] + bcls[3]);
     bias = swap_sum<16>(bias);
     bias = swap_sum<32>(bias) * z_unscale;  // all 128 channels: head hq, group g0 + (lc & 3)
 
@@ -741,35 +757,33 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
     const float alpha = !(m_new > m_run) ? 1.0f : (m_run == -INFINITY ? 0.0f : fast_exp2(m_run - m_new));
     m_run = m_new;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) lcls[e] *= alpha;
-    // p scaled by the value-code factor of its token position and 2^-Ev:
-    // token t sits in pair class e'(t) = (t mod 8) / 2 of its run of 8
+    for (int e = 0; e < 4; ++e) lsum[e] *= alpha;
+    // p' = p 2^-Ev = 2^(x - (m + Ev))
+    const float mm = m_run + static_cast<float>(ev);
     f32x4 p0, p1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      p0[i] = fast_exp2(x[i] + (p_exp[i >> 1] - m_run));
-      p1[i] = fast_exp2(x[4 + i] + (p_exp[2 + (i >> 1)] - m_run));
+      p0[i] = fast_exp2(x[i] - mm);
+      p1[i] = fast_exp2(x[4 + i] - mm);
     }
-    lcls[0] += p0[0] + p0[1];
-    lcls[1] += p0[2] + p0[3];
-    lcls[2] += p1[0] + p1[1];
-    lcls[3] += p1[2] + p1[3];
+    lsum[0] += p0[0] + p0[1];
+    lsum[1] += p0[2] + p0[3];
+    lsum[2] += p1[0] + p1[1];
+    lsum[3] += p1[2] + p1[3];
     *reinterpret_cast<f32x4*>(sl + row) = p0;
     *reinterpret_cast<f32x4*>(sl + row + 4) = p1;
     if (lk == 0 && jt == 0) sl[S::offAlpha / 4 + hq] = alpha;
     wg_barrier();  // step's probabilities ready
   }
 
-  float l = 0.0f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) l = fmaf(lcls[e], 1.0f / static_cast<float>(1 << VS::lf(e)), l);
+  float l = (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
   l = l + partner<1>(l);
   l = l + partner<2>(l);
   l = swap_sum<16>(l);
   l = swap_sum<32>(l);  // the 16 lanes of head hq
   if (lk == 0 && jt == 0 && hq < NQ) {
     // l and the value wave's o carry 2^-Ev; m + Ev restores their weight
-    float* P = a.partial + (((long long)b * a.Hq + kvh * NQ + hq) * a.n_split + split) * (D + 2);
+    float* P = a.partial + (((long long)b * a.Hq + h0 + hq) * a.n_split + split) * (D + 2);
     P[0] = m_run + static_cast<float>(ev);
     P[1] = l;
   }
@@ -779,7 +793,7 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
 // Value wave: p.V of each step on the matrix cores, one step behind the key
 // wave.  Writes o of the partial; the last split also runs the window.
 template <int KB, int VB, bool BF16, int NQ, int GT, bool PAGED>
-__device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int b, int kvh, int split,
+__device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int b, int h0, int split,
                                            int gb, int ge, int n_steps, int rot, uint8_t* smem) {
   using S = Stage<KB, VB>;
   using VS = CodeScale<VB>;
@@ -801,9 +815,9 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
     const int f0 = step_first(gb, 0, n_steps, rot);
     issue_vstage<KB, VB, GT, PAGED>(a, u, ubase, f0, min(4, ge - f0), vbase);
   }
-  constexpr float v_unscale = static_cast<float>(1 << (24 - VS::F));  // product -> output
+  constexpr float v_unscale = static_cast<float>(1 << (15 - VS::F));  // product -> output
 
-  float zcls[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // sum of scaled p * Z, per pair class e'
+  float zcls[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // sum of p' * Z (four partial sums)
   f32x4 o[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -884,9 +898,7 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
     }
   }
 
-  float z = 0.0f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) z = fmaf(zcls[e], 1.0f / static_cast<float>(1 << VS::lf(e)), z);
+  float z = (zcls[0] + zcls[1]) + (zcls[2] + zcls[3]);
   z = swap_sum<16>(z);
   z = swap_sum<32>(z);  // sum over the 4 row chunks: head hq, channel group lc & 3
   if constexpr (kHiLoCols) {
@@ -901,7 +913,7 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
   // 2 + lk / 2; the lane whose column holds that group writes it.
   const int mh = (lc & 3) == (lk >> 1) ? 0 : (lc & 3) == 2 + (lk >> 1) ? 1 : -1;
   if (mh >= 0 && hq < NQ) {
-    float* P = a.partial + (((long long)b * a.Hq + kvh * NQ + hq) * a.n_split + split) * (D + 2);
+    float* P = a.partial + (((long long)b * a.Hq + h0 + hq) * a.n_split + split) * (D + 2);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       f32x4 x;
@@ -912,21 +924,44 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
   }
 }
 
+// Workgroup w of the launch (a 1-D grid) -> pair index P = split + nx * row
+// over the (split, unit row) pairs, and head group hg.  With one head group
+// P = w.  With hg > 1 head groups (8 or 16 query heads per kv head: 4 heads
+// per workgroup) the workgroups of one pair read the same records; w takes
+// them 8 apart, so they fall on the same XCD (workgroups are dealt to the 8
+// XCDs in turn) at about the same time and the second one reads the records
+// from that XCD's L2:
+//   w = (P / 8) * 8 hg + 8 g + P % 8   (g = 0 .. hg - 1).
+__device__ __forceinline__ unsigned pair_of(unsigned w, int hg, int& g) {
+  if (hg == 1) {
+    g = 0;
+    return w;
+  }
+  g = static_cast<int>((w >> 3) % static_cast<unsigned>(hg));
+  return (w / (8u * hg)) * 8u + (w & 7u);
+}
+
 template <int KB, int VB, bool BF16, int NQ, int GT, bool PAGED>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma(DecodeArgs a) {
   using S = Stage<KB, VB>;
   __shared__ __align__(16) uint8_t smem[S::bytes];
   const int wave = threadIdx.x >> 6;  // 0: key wave, 1: value wave
-  const int split = blockIdx.x;
-  const int kvh = static_cast<int>(blockIdx.y % a.H);
+  const int nx = a.n_split_packed > 0 ? a.n_split_packed : 1;
+  int hgi;
+  const unsigned P = pair_of(blockIdx.x, a.hg, hgi);
+  if (P >= static_cast<unsigned>(nx) * static_cast<unsigned>(a.B * a.H)) return;  // (grid rounding)
+  const int split = static_cast<int>(P % static_cast<unsigned>(nx));
+  const int row = static_cast<int>(P / static_cast<unsigned>(nx));
+  const int kvh = row % a.H;
   // this unit's sequence and lengths: the launch's, or its own in a ragged launch
-  int b = static_cast<int>(blockIdx.y / a.H), nq = a.n_quant, nr = a.n_resid;
+  int b = row / a.H, nq = a.n_quant, nr = a.n_resid;
   if (a.ragged) {
     nq = a.seq_len[b][0];
     nr = a.seq_len[b][1];
     b += a.seq0;
   }
   const long long u = (long long)b * a.H + kvh;
+  const int h0 = kvh * a.gq + hgi * NQ;  // first query head of this workgroup
 
   if (a.n_split_packed > 0) {
     const int nqg = nq / kStream;  // packed streams of 32 tokens
@@ -936,18 +971,19 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
       // (ragged) this sequence ends before this split: an empty partial
       // (m = -inf, l = 0, o = 0)
       for (int i = threadIdx.x; i < NQ * (D + 2); i += 128) {
-        float* P = a.partial + (((long long)b * a.Hq + kvh * NQ + i / (D + 2)) * a.n_split + split) * (D + 2);
-        P[i % (D + 2)] = i % (D + 2) == 0 ? -INFINITY : 0.0f;
+        float* Pp = a.partial + (((long long)b * a.Hq + h0 + i / (D + 2)) * a.n_split + split) * (D + 2);
+        Pp[i % (D + 2)] = i % (D + 2) == 0 ? -INFINITY : 0.0f;
       }
     } else {
       const int n_steps = (ge - gb + 3) / 4;  // >= 1: every split holds a group
-      // the first step of this workgroup's walk (see step_first)
-      const int rot = static_cast<int>((blockIdx.x + gridDim.x * blockIdx.y) % static_cast<unsigned>(n_steps));
+      // the first step of this workgroup's walk (see step_first); the head
+      // groups of one pair take the same walk
+      const int rot = static_cast<int>(P % static_cast<unsigned>(n_steps));
       // Both waves run the same number of steps and meet at one barrier per step.
       if (wave == 0) {
-        key_wave<KB, VB, BF16, NQ, GT, PAGED>(a, u, b, kvh, split, gb, ge, n_steps, rot, smem);
+        key_wave<KB, VB, BF16, NQ, GT, PAGED>(a, u, b, h0, split, gb, ge, n_steps, rot, smem);
       } else {
-        value_wave<KB, VB, BF16, NQ, GT, PAGED>(a, u, b, kvh, split, gb, ge, n_steps, rot, smem);
+        value_wave<KB, VB, BF16, NQ, GT, PAGED>(a, u, b, h0, split, gb, ge, n_steps, rot, smem);
       }
     }
   }
@@ -956,19 +992,24 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
   // packed yet); empty for a sequence without window tokens in a ragged
   // launch.  That wave's stage loads have completed, so its value stages
   // serve as scratch.
-  if (wave == 1 && a.n_split > a.n_split_packed && split == max(a.n_split_packed - 1, 0)) {
+  if (wave == 1 && a.n_split > a.n_split_packed && split == nx - 1) {
     wave_lds_sync();
-    window_wave<BF16, NQ>(a, u, b, kvh, a.n_split_packed, nr, reinterpret_cast<float (*)[D]>(smem + S::offV0),
-                      reinterpret_cast<float (*)[G]>(smem + S::offV0 + GQ * D * 4));
+    window_wave<BF16, NQ>(a, u, b, h0, a.n_split_packed, nr, hgi == 0,
+                          reinterpret_cast<float (*)[D]>(smem + S::offV0),
+                          reinterpret_cast<float (*)[G]>(smem + S::offV0 + GQ * D * 4));
   }
 }
 
 template <int KB, int VB, bool BF16, int NQ, int GT, bool PAGED>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  // one workgroup per packed split; the last one also runs the window.
-  // A ragged launch covers a.B sequences from a.seq0.
-  dim3 grid(a.n_split_packed > 0 ? a.n_split_packed : 1, a.B * a.H);
-  hipLaunchKernelGGL((decode_mfma<KB, VB, BF16, NQ, GT, PAGED>), grid, dim3(128), 0, stream, a);
+  // one workgroup per packed split (per head group), one split when nothing
+  // is packed; the last one also runs the window.  A ragged launch covers
+  // a.B sequences from a.seq0.
+  const long long pairs = (long long)(a.n_split_packed > 0 ? a.n_split_packed : 1) * a.B * a.H;
+  const long long grid = a.hg == 1 ? pairs : (pairs + 7) / 8 * 8 * a.hg;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((decode_mfma<KB, VB, BF16, NQ, GT, PAGED>), dim3(static_cast<unsigned>(grid)), dim3(128), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
@@ -981,10 +1022,14 @@ hipError_t launch_gp(const DecodeArgs& a, hipStream_t stream) {
 
 template <int KB, int VB, bool BF16>
 hipError_t launch_nq(const DecodeArgs& a, hipStream_t stream) {
+  // 8 and 16 query heads per kv head: 2 or 4 head groups of 4 (a.hg)
+  if (a.hg != (a.gq > 4 ? a.gq / 4 : 1)) return hipErrorInvalidValue;
   switch (a.gq) {
     case 1: return launch_gp<KB, VB, BF16, 1>(a, stream);
     case 2: return launch_gp<KB, VB, BF16, 2>(a, stream);
-    case 4: return launch_gp<KB, VB, BF16, 4>(a, stream);
+    case 4:
+    case 8:
+    case 16: return launch_gp<KB, VB, BF16, 4>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -103,9 +103,9 @@ struct DecodeArgs {
   int page_stride, num_pages;
   int n_quant, n_resid;
   int n_split;
-  int items_per_split;  // vector kernel: work items (blocks, then window chunks) per split
-  int n_split_packed;   // matrix kernel: splits over packed groups (window split follows)
-  int groups_per_split; // matrix kernel: packed groups per split, a multiple of 4
+  int n_split_packed;   // splits over packed groups (the window split follows)
+  int groups_per_split; // packed groups per split, a multiple of 4
+  int hg;               // workgroups per (unit, split): query heads per kv head / 4 above 4, else 1
   float qscale;         // softmax_scale * log2(e): scores in base-2 units
   // ragged launches (ragged != 0) cover sequences seq0 .. seq0 + gridDim.y / H
   // - 1 and take each one's lengths from seq_len[][2] = (n_quant, n_resid);
@@ -113,9 +113,9 @@ struct DecodeArgs {
   int ragged;
   int seq0;
   int seq_len[kDecodeChunk][2];
-  // fused append (k_new != nullptr, matrix-core kernel only): each unit's
-  // newest window token, slot n_resid - 1, is read from k_new / v_new
-  // ([B][H][D]) and stored into the window by the wave that runs the window
+  // fused append (k_new != nullptr): each unit's newest window token, slot
+  // n_resid - 1, is read from k_new / v_new ([B][H][D]) and stored into the
+  // window by the wave that runs the window (of the first head group)
   const uint16_t* k_new;
   const uint16_t* v_new;
   uint16_t* k_resid_w;  // the window arrays, writable (fused append)
@@ -136,11 +136,11 @@ constexpr int kLdsPerCu = 160 * 1024;  // MI355X (gfx950)
 hipError_t launch_pack(const PackArgs& a, int k_bits, int v_bits, int kv_dtype,
                        hipStream_t stream);
 hipError_t launch_resid_copy(const PackArgs& a, int kv_dtype, hipStream_t stream);
-// use_mfma selects the matrix-core kernel (1, 2 or 4 query heads per kv head).
-// split_begin / split_end (may be null): events recorded on the stream right
-// before and right after the split kernel (before the merge).
+// Split kernel (matrix cores, 1, 2, 4, 8 or 16 query heads per kv head),
+// then the merge.  split_begin / split_end (may be null): events recorded on
+// the stream right before and right after the split kernel.
 hipError_t launch_decode(const DecodeArgs& a, int k_bits, int v_bits, int kv_dtype,
-                         int out_dtype, bool use_mfma, hipStream_t stream,
+                         int out_dtype, hipStream_t stream,
                          hipEvent_t split_begin, hipEvent_t split_end);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int k_bits, int v_bits, int kv_dtype,
                                   hipStream_t stream);

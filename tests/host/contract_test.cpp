@@ -37,7 +37,7 @@ int g_checks = 0;
     }                                                                                     \
   } while (0)
 
-enum { KIND, NBLK, DST_BLK0, R_COUNT, R_DST, RAGGED, NQ, NR, NSPLIT, NSPLIT_PACKED, MFMA, FUSED };
+enum { KIND, NBLK, DST_BLK0, R_COUNT, R_DST, RAGGED, NQ, NR, NSPLIT, NSPLIT_PACKED, HG, FUSED };
 
 void* const kDev = reinterpret_cast<void*>(uintptr_t{0x7f0000000000});  // never dereferenced
 void* const kIn = reinterpret_cast<void*>(uintptr_t{0x7f1000000000});
@@ -158,14 +158,14 @@ void device_query_failure() {
   CHECK(stub_launches() == launches + 2);
   CHECK(field(launches, KIND) == 0 && field(launches, DST_BLK0) == 4);
   CHECK(field(launches + 1, KIND) == 2 && field(launches + 1, NQ) == 256 && field(launches + 1, NR) == 1 &&
-        field(launches + 1, FUSED) == 1 && field(launches + 1, MFMA) == 1);
+        field(launches + 1, FUSED) == 1 && field(launches + 1, HG) == 1);
   CHECK(kivi_cache_destroy(h) == KIVI_OK);
 }
 
 // The fused step uses the plan of the state after its append: the same
 // split counts as an explicit append followed by a decode.
 void fused_step_plan() {
-  for (int hq : {2, 4, 8, 16}) {
+  for (int hq : {2, 4, 8, 16, 32}) {
     stub_reset();
     kivi_cache* a = make(config(2, 2, 4000));
     kivi_cache* b = make(config(2, 2, 4000));
@@ -182,7 +182,9 @@ void fused_step_plan() {
       const int db = stub_launches() - 1;
       CHECK(field(db, KIND) == 2 && field(da, NQ) == field(db, NQ) && field(da, NR) == field(db, NR));
       CHECK(field(da, NSPLIT) == field(db, NSPLIT) && field(da, NSPLIT_PACKED) == field(db, NSPLIT_PACKED));
-      CHECK(field(da, FUSED) == (hq / 2 != 8 ? 1 : 0) && field(db, FUSED) == 0);  // 2 kv heads
+      CHECK(field(da, FUSED) == 1 && field(db, FUSED) == 0);
+      // 2 kv heads: 8 and 16 query heads per kv head take 2 and 4 head groups
+      CHECK(field(da, HG) == (hq / 2 > 4 ? hq / 8 : 1) && field(db, HG) == field(da, HG));
       (void)n0;
     }
     CHECK(kivi_cache_destroy(a) == KIVI_OK);
@@ -190,8 +192,8 @@ void fused_step_plan() {
   }
 }
 
-// Failures inside the fused step: the flush launch, the decode launch, and
-// (8 query heads per kv head) the append's own launch.
+// Failures inside the fused step: the flush launch and the decode launch (4
+// and 8 query heads per kv head).
 void fused_step_failures() {
   for (int fail_at : {1, 2}) {
     stub_reset();
@@ -202,12 +204,15 @@ void fused_step_failures() {
     expect_poisoned(h, 4);
     CHECK(kivi_cache_destroy(h) == KIVI_OK);
   }
-  for (int fail_at : {1, 2}) {
+  {
+    // window not full, 8 query heads per kv head: the decode launch alone
     stub_reset();
     kivi_cache* h = make(config());
-    CHECK(kivi_append(h, kIn, kIn, 200, nullptr) == KIVI_OK);  // window not full: copy + decode
-    stub_fail_launch(fail_at);
+    CHECK(kivi_append(h, kIn, kIn, 200, nullptr) == KIVI_OK);
+    const int launches = stub_launches();
+    stub_fail_launch(1);
     CHECK(step(h, 16) == KIVI_ERR_HIP);
+    CHECK(stub_launches() == launches);
     expect_poisoned(h, 16);
     CHECK(kivi_cache_destroy(h) == KIVI_OK);
   }

@@ -18,7 +18,7 @@ namespace {
 struct Launch {
   int kind;  // 0 pack, 1 window copy, 2 decode (split kernel + merge), 3 read probe
   int nblk, dst_blk0, r_count, r_dst_slot0, ragged;
-  int n_quant, n_resid, n_split, n_split_packed, use_mfma, fused_append;
+  int n_quant, n_resid, n_split, n_split_packed, hg, fused_append;
 };
 std::vector<Launch> g_log;
 int g_fail_in = 0;       // launches until the failing one (0: none)
@@ -49,11 +49,11 @@ void stub_device(int ok, int cus) {
 int stub_launches(void) { return static_cast<int>(g_log.size()); }
 int stub_device_calls(void) { return g_device_calls; }
 // fields of launch i: kind, nblk, dst_blk0, r_count, r_dst_slot0, ragged,
-// n_quant, n_resid, n_split, n_split_packed, use_mfma, fused_append
+// n_quant, n_resid, n_split, n_split_packed, hg, fused_append
 void stub_launch(int i, int* f) {
   const Launch& l = g_log.at(static_cast<size_t>(i));
   const int v[12] = {l.kind, l.nblk, l.dst_blk0, l.r_count, l.r_dst_slot0, l.ragged,
-                     l.n_quant, l.n_resid, l.n_split, l.n_split_packed, l.use_mfma, l.fused_append};
+                     l.n_quant, l.n_resid, l.n_split, l.n_split_packed, l.hg, l.fused_append};
   std::memcpy(f, v, sizeof v);
 }
 
@@ -81,10 +81,9 @@ hipError_t launch_pack(const PackArgs& a, int, int, int, hipStream_t) {
 hipError_t launch_resid_copy(const PackArgs& a, int, hipStream_t) {
   return take(Launch{1, 0, 0, a.r_count, a.r_dst_slot0, a.ragged, 0, 0, 0, 0, 0, 0});
 }
-hipError_t launch_decode(const DecodeArgs& a, int, int, int, int, bool use_mfma, hipStream_t, hipEvent_t,
-                         hipEvent_t) {
-  return take(Launch{2, 0, 0, 0, 0, a.ragged, a.n_quant, a.n_resid, a.n_split, a.n_split_packed,
-                     use_mfma ? 1 : 0, a.k_new != nullptr ? 1 : 0});
+hipError_t launch_decode(const DecodeArgs& a, int, int, int, int, hipStream_t, hipEvent_t, hipEvent_t) {
+  return take(Launch{2, 0, 0, 0, 0, a.ragged, a.n_quant, a.n_resid, a.n_split, a.n_split_packed, a.hg,
+                     a.k_new != nullptr ? 1 : 0});
 }
 hipError_t launch_stream_read(const void*, size_t, uint32_t*, int, hipStream_t) {
   return take(Launch{3, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0});

@@ -21,8 +21,9 @@ TOL = 2e-3
 CASES = [("mha",          2, 2, 2,  2, 2, torch.float16,  128, None,                       140),
          ("gq4_r32",      2, 2, 8,  2, 2, torch.float16,  32,  None,                       70),
          ("gq2_bf16_4b",  1, 2, 4,  4, 4, torch.bfloat16, 64,  None,                       70),
-         ("gq8_fallback", 1, 1, 8,  2, 2, torch.float16,  32,  None,                       40),
+         ("gq8",          1, 1, 8,  2, 2, torch.float16,  32,  None,                       40),
          ("ragged_gq4",   4, 1, 4,  2, 4, torch.float16,  32,  [0, 31, 32, 100],           70),
+         ("ragged_gq16",  3, 2, 32, 2, 2, torch.bfloat16, 32,  [5, 64, 170],               40),
          ("empty_start",  2, 1, 1,  2, 2, torch.float16,  32,  [0, 0],                     40)]
 
 

@@ -30,11 +30,12 @@ CASES = [("mha",         2, 2, 2,  300,  2, 2, torch.float16,  128),
          ("T1",          1, 1, 1,  1,    2, 2, torch.float16,  64),
          ("r1024_flush", 1, 1, 4,  2048, 2, 2, torch.float16,  1024),
          ("r256_gq4",    2, 1, 4,  900,  2, 2, torch.bfloat16, 256),
-         # 8 query heads per kv head: the vector-ALU kernel reads 64-token
+         # 8 and 16 query heads per kv head: head groups reading 64-token
          # records as two 32-token streams
          ("gq8",         1, 2, 16, 700,  2, 2, torch.float16,  128),
          ("gq8_4b_bf16", 2, 1, 8,  300,  4, 4, torch.bfloat16, 64),
-         ("gq8_k2v4",    1, 1, 8,  200,  2, 4, torch.float16,  64)]
+         ("gq8_k2v4",    1, 1, 8,  200,  2, 4, torch.float16,  64),
+         ("gq16",        1, 1, 16, 333,  2, 2, torch.float16,  64)]
 
 
 def _setup(case, extra=1):
@@ -135,11 +136,11 @@ def test_group64_ragged_paged_fused(Hq):
 
 
 def test_group64_unsupported_head_ratio():
-    # 16 query heads per kv head are not built: rejected before anything is enqueued
+    # 32 query heads per kv head are not built: rejected before anything is enqueued
     c = kivi.KiviCache(1, 1, 200, group_size=G, residual_length=128, device=DEV)
     k = torch.zeros(1, 1, 70, 128, dtype=torch.float16, device=DEV)
     c.append(k, k)
-    q = torch.zeros(1, 16, 128, dtype=torch.float16, device=DEV)
+    q = torch.zeros(1, 32, 128, dtype=torch.float16, device=DEV)
     with pytest.raises(kivi.KiviError) as e:
         c.decode_attn(q, 0.1)
     assert e.value.status == kivi.KIVI_ERR_UNSUPPORTED

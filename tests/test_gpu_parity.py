@@ -26,7 +26,7 @@ CASES = [("c0",            1, 1, 1, 1024, 2, 2, torch.float16, 128),
          ("T32",           1, 1, 1, 32, 2, 2, torch.float16, 128),
          ("T128_fullwin",  1, 2, 2, 128, 2, 2, torch.float16, 128),
          ("T129",          1, 2, 2, 129, 2, 2, torch.bfloat16, 128),
-         # 4 query heads per kv head: the matrix-core kernel
+         # 4 query heads per kv head: every head slot of a workgroup used
          ("gq4_f16",       2, 2, 8, 1000, 2, 2, torch.float16, 128),
          ("gq4_k2v4",      1, 2, 8, 700, 2, 4, torch.float16, 128),
          ("gq4_k4v2_r32",  1, 1, 4, 333, 4, 2, torch.float16, 32),
@@ -38,7 +38,10 @@ CASES = [("c0",            1, 1, 1, 1024, 2, 2, torch.float16, 128),
          ("r1024_window",  1, 2, 8, 1000, 2, 2, torch.float16, 1024),
          ("r1024_flush",   1, 1, 2, 2048, 2, 2, torch.bfloat16, 1024),
          ("r256_mha_4b",   2, 2, 2, 700, 4, 4, torch.float16, 256),
-         ("r1024_gq8",     1, 1, 8, 1500, 2, 2, torch.float16, 1024)]
+         ("r1024_gq8",     1, 1, 8, 1500, 2, 2, torch.float16, 1024),
+         # 16 query heads per kv head: 4 head groups per split
+         ("gq16",          2, 1, 16, 900, 2, 2, torch.float16, 128),
+         ("gq16_bf16_4b",  1, 2, 32, 450, 4, 4, torch.bfloat16, 64)]
 IDS = [c[0] for c in CASES]
 
 
@@ -150,13 +153,11 @@ def test_split_invariance_and_determinism(case):
         print(f"case {case[0]}: n_split {ns}", flush=True)
         cache.set_splits(ns)
         outs[ns] = cache.decode_attn(q, scale).cpu().numpy()
-    # fp32 vector path (8 query heads per kv head): only summation order
-    # changes (1e-5).  Matrix path (1, 2 or 4 heads): q*S and p*S are rounded
-    # to fp16 hi + lo (2^-22 relative each) relative to each split's own
-    # maximum, so changing the split count moves scores by up to
-    # 2^-22 * sum_d |c q' S| (about 3e-5 on these inputs) and outputs by that
-    # times max |v| (about 30).
-    tol = 1e-4 if w.gq in (1, 2, 4) else 1e-5
+    # q*S and p*S are rounded to fp16 hi + lo (2^-22 relative each) relative
+    # to each split's own maximum, so changing the split count moves scores
+    # by up to 2^-22 * sum_d |c q' S| (about 3e-5 on these inputs) and
+    # outputs by that times max |v| (about 30).
+    tol = 1e-4
     for ns, o in outs.items():
         d = np.max(np.abs(o - outs[1]))
         print(f"case {case[0]}: n_split {ns} vs 1: max abs diff {d:.2e}", flush=True)

@@ -24,7 +24,8 @@ CASES = [(64, 64, 1, 1, 4, 4, 2, torch.float16, 525),   # the shape of random co
          (64, 256, 1, 1, 2, 4, 2, torch.float16, 600),  # and of 45
          (32, 128, 2, 2, 4, 2, 2, torch.float16, 1000),
          (32, 128, 2, 2, 1, 2, 2, torch.bfloat16, 1000),
-         (64, 128, 1, 2, 4, 4, 4, torch.float16, 800)]
+         (64, 128, 1, 2, 4, 4, 4, torch.float16, 800),
+         (32, 128, 1, 2, 8, 2, 2, torch.float16, 900)]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"G{c[0]}_R{c[1]}_gq{c[4]}_k{c[5]}v{c[6]}" for c in CASES])

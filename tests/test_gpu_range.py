@@ -45,7 +45,7 @@ CASES = [  # G, k_bits, v_bits, dtype, query heads per kv head
     (32, 2, 2, torch.float16, 4), (32, 2, 2, torch.float16, 1), (32, 2, 2, torch.bfloat16, 2),
     (32, 4, 4, torch.float16, 4), (32, 2, 4, torch.bfloat16, 4), (32, 4, 2, torch.float16, 8),
     (64, 2, 2, torch.float16, 4), (64, 4, 2, torch.bfloat16, 1), (64, 2, 4, torch.float16, 2),
-    (64, 4, 4, torch.bfloat16, 8),
+    (64, 4, 4, torch.bfloat16, 8), (32, 2, 2, torch.float16, 16),
 ]
 
 

@@ -23,7 +23,7 @@ TOL = 2e-3
 #        name           B   H  Hq  kb vb dtype           R    prefill lengths                     steps
 CASES = [("mha_mixed",   6,  2, 2,  2, 2, torch.float16,  128, [0, 1, 33, 128, 129, 300],          140),
          ("gq4_bf16_4b", 5,  2, 8,  4, 4, torch.bfloat16, 32,  [31, 32, 64, 95, 7],                40),
-         ("gq8_valu",    4,  1, 8,  2, 4, torch.float16,  128, [5, 260, 0, 128],                   20),
+         ("gq8",         4,  1, 8,  2, 4, torch.float16,  128, [5, 260, 0, 128],                   20),
          ("k4v2_gq2",    3,  2, 4,  4, 2, torch.float16,  64,  [65, 0, 190],                       70),
          ("chunks",      70, 1, 4,  2, 2, torch.float16,  32,  [(7 * i) % 101 for i in range(70)], 3)]
 
