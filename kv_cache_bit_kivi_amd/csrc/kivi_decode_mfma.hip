@@ -134,61 +134,66 @@ __device__ __forceinline__ float dot2_acc(uint32_t a, uint32_t b, float acc) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), acc, false);
 }
 
-// Code extraction.  Two codes of a split-half word sit at bits [s, s+b) and
-// [16+s, 16+s+b); masking the word (or the word shifted right by 8) in place
-// leaves them as fp16 subnormals c * 2^(t-24), t = 0, 2, 4, 6 (2-bit) or
-// t = 0, 4 (4-bit), exactly.  One packed multiply by 2^(F-t+9) (F = 6 for
-// 2-bit, 4 for 4-bit; exact) then makes every code the normal fp16 number
-// c * 2^(F-15) (zero stays zero), the same factor at every position.
+// Code extraction.  In a split-half word the codes of one byte sit at bit
+// steps of b (the 4 codes of a 2-bit byte, the 2 codes of a 4-bit byte).
+// Masking with 0x33333333 (2-bit; also after a shift by 2) leaves one 2-bit
+// code in the low bits of each nibble, which as an fp4 e2m1 number is c / 2;
+// masking with 0x0F0F0F0F (4-bit; also after a shift by 4) leaves one code per
+// byte, which as an fp8 e4m3 number is c * 2^-9.  The gfx950 conversions
+// v_cvt_scalef32_pk_f16_fp4 (two nibbles of a byte) and _fp8 (two bytes of a
+// half word) turn them into two fp16 numbers times a power-of-two scale,
+// exactly: every code becomes the normal fp16 number c * 2^(F-15) (F = 6 for
+// 2-bit, 4 for 4-bit), zero stays zero.  A conversion pairs the codes of
+// entries a and a + 4 of a run of 8 (a = 0..3), so the dense operand of
+// every product takes the same pairing.
 //
 // Normal operands matter for the accuracy of the products: measured on
-// MI355X, a v_mfma_f32_16x16x32_f16 whose A operand holds subnormals adds
-// its products with errors of hundreds of binary32 units relative to the sum
-// of their magnitudes (the subnormal codes with position factors in the
-// other operand: 270 units at 4 bits, 850-1260 at 2 bits, worst over 25600
-// sums of 128 products), while the same products from normal operands come
-// within 5 units.  In attention those errors reached the 2e-3 tolerance
-// where one token holds most of a head's weight and its value is large.
+// MI355X, a v_mfma_f32_16x16x32_f16 whose A operand holds fp16 subnormals
+// (codes masked in place, c * 2^(t-24) at bit position t, with position
+// factors in the other operand) adds its products with errors of hundreds of
+// binary32 units relative to the sum of their magnitudes (270 at 4 bits,
+// 850-1260 at 2 bits, worst over 25600 sums of 128 products), while the same
+// products from normal operands come within 5 units.  In attention those
+// errors reached the 2e-3 tolerance where one token holds most of a head's
+// weight and its value is large.
 template <int BITS>
 struct CodeScale {
   static constexpr int F = BITS == 2 ? 6 : 4;
-  // position t of pair e' (codes 2e', 2e'+1 of an 8-code run) in its half
-  static constexpr int t(int ep) { return BITS == 2 ? 2 * ep : 4 * (ep & 1); }
 };
 
-// 2^k as an fp16 pair, 0 <= k <= 15.
-__device__ __forceinline__ constexpr uint32_t pow2_pair(int k) {
-  return static_cast<uint32_t>((15 + k) << 10) * 0x00010001u;
-}
-
-// a * b for fp16 pairs (v_pk_mul_f16; exact when b is a power of two and the
-// product stays in range).
-__device__ __forceinline__ uint32_t mul_pair(uint32_t a, uint32_t b) {
-  uint32_t r;
-  asm("v_pk_mul_f16 %0, %1, %2" : "=v"(r) : "v"(a), "s"(b));
-  return r;
-}
-
-// 8 codes (one run of 8 consecutive entries: positions 8*hb .. 8*hb+7 of
-// word x) as four fp16 pairs c * 2^(F-15).
-template <int BITS>
-__device__ __forceinline__ half8_t codes8(uint32_t x, bool high_byte) {
-  using CS = CodeScale<BITS>;
+// 8 codes (one run of 8 consecutive entries: positions 8*HB .. 8*HB+7 of
+// word x; 4-bit words hold one run, HB = 0) as four fp16 pairs c * 2^(F-15):
+// pair a holds entries a and a + 4 of the run.
+template <int BITS, int HB>
+__device__ __forceinline__ half8_t codes8(uint32_t x) {
   u32x4 r;
   if constexpr (BITS == 2) {
-    const uint32_t y = high_byte ? (x >> 8) : x;
-    r[0] = mul_pair(y & 0x00030003u, pow2_pair(CS::F - CS::t(0) + 9));
-    r[1] = mul_pair(y & 0x000C000Cu, pow2_pair(CS::F - CS::t(1) + 9));
-    r[2] = mul_pair(y & 0x00300030u, pow2_pair(CS::F - CS::t(2) + 9));
-    r[3] = mul_pair(y & 0x00C000C0u, pow2_pair(CS::F - CS::t(3) + 9));
+    // the nibbles of y0 hold entries (0, 4), (8, 12), (1, 5), (9, 13) by
+    // byte, those of y1 entries (2, 6), (10, 14), (3, 7), (11, 15)
+    const uint32_t y0 = x & 0x33333333u, y1 = (x >> 2) & 0x33333333u;
+    constexpr float kScale = 0x1p-8f;  // c / 2 -> c * 2^-9
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y0, kScale, HB));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y0, kScale, 2 + HB));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y1, kScale, HB));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y1, kScale, 2 + HB));
   } else {
-    const uint32_t y = x >> 8;
-    r[0] = mul_pair(x & 0x000F000Fu, pow2_pair(CS::F - CS::t(0) + 9));
-    r[1] = mul_pair(x & 0x00F000F0u, pow2_pair(CS::F - CS::t(1) + 9));
-    r[2] = mul_pair(y & 0x000F000Fu, pow2_pair(CS::F - CS::t(2) + 9));
-    r[3] = mul_pair(y & 0x00F000F0u, pow2_pair(CS::F - CS::t(3) + 9));
+    static_assert(HB == 0, "a 4-bit word holds one run");
+    // bytes of z0: entries 0, 4, 1, 5; of z1: 2, 6, 3, 7
+    const uint32_t z0 = x & 0x0F0F0F0Fu, z1 = (x >> 4) & 0x0F0F0F0Fu;
+    constexpr float kScale = 0x1p-2f;  // c * 2^-9 -> c * 2^-11
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(z0, kScale, false));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(z0, kScale, true));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(z1, kScale, false));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(z1, kScale, true));
   }
   return as_h8(r);
+}
+
+// (lo half of a, lo half of b) or (hi half of a, hi half of b) of two fp16
+// pairs, one v_perm_b32.
+template <int SEL>
+__device__ __forceinline__ uint32_t halves(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, SEL == 0 ? 0x05040100u : 0x07060302u);
 }
 
 // Cross-lane exchanges on the vector ALUs (no LDS round trip):
@@ -631,10 +636,14 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
   // keeps q'' exact (a bf16 q is rounded to fp16 once).
   // softmax_scale * log2(e) * 2^Ek multiplies the scores afterwards.  Head
   // slots hq >= NQ carry q'' = 0 and are masked out of the softmax.
+  // Pair 4c + a holds channels 8c + a and 8c + a + 4 of the lane's 32 (a =
+  // 0..3), the pairing of the codes (see codes8).
   uint32_t q2[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
-    q2[i] = pk_rne(__builtin_amdgcn_ldexpf(qf[2 * i], -ek), __builtin_amdgcn_ldexpf(qf[2 * i + 1], -ek));
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+      q2[4 * c + a] = pk_rne(__builtin_amdgcn_ldexpf(qf[8 * c + a], -ek), __builtin_amdgcn_ldexpf(qf[8 * c + a + 4], -ek));
   // raw product -> score: products are c q S 2^(F-15-Ek)
   const float k_unscale = __builtin_amdgcn_ldexpf(a.qscale, 15 - KS::F + ek);
   const float z_unscale = __builtin_amdgcn_ldexpf(a.qscale, ek);
@@ -689,22 +698,29 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
     for (int s = 0; s < 8; ++s) sc[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
+      // scale and zero of channels 8c .. 8c+7 as pairs (2k, 2k+1), re-paired
+      // (a, a + 4) like q2 and the codes
       const u32x4 sB = sBp[c], zB = zBp[c];
+      const uint32_t sx[4] = {halves<0>(sB[0], sB[2]), halves<1>(sB[0], sB[2]), halves<0>(sB[1], sB[3]),
+                              halves<1>(sB[1], sB[3])};
+      const uint32_t zx[4] = {halves<0>(zB[0], zB[2]), halves<1>(zB[0], zB[2]), halves<0>(zB[1], zB[3]),
+                              halves<1>(zB[1], zB[3])};
       u32x4 h4, l4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t qq = q2[4 * c + e];
         uint32_t hi, lo;
-        mul_pair_exact(qq, sB[e], hi, lo);
+        mul_pair_exact(qq, sx[e], hi, lo);
         h4[e] = hi;
         l4[e] = lo;
-        bcls[e] = dot2_acc(qq, zB[e], bcls[e]);
+        bcls[e] = dot2_acc(qq, zx[e], bcls[e]);
       }
       const half8_t bh = as_h8(h4), bl = as_h8(l4);
       half8_t ak[8];
 #pragma unroll
       for (int s = 0; s < 8; ++s)
-        ak[s] = (KB == 2) ? codes8<2>(kw[s][c >> 1], c & 1) : codes8<4>(kw[s][c & (KL - 1)], false);
+        ak[s] = (KB == 4) ? codes8<4, 0>(kw[s][c & (KL - 1)])
+                : (c & 1) ? codes8<2, 1>(kw[s][c >> 1]) : codes8<2, 0>(kw[s][c >> 1]);
 #pragma unroll
       for (int s = 0; s < 8; ++s) sc[s] = mfma(ak[s], bh, sc[s]);
 #pragma unroll
@@ -823,8 +839,6 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
   for (int i = 0; i < 8; ++i) o[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   for (int step = 0; step < n_steps; ++step) {
-    const int g0 = step_first(gb, step, n_steps, rot);
-    const int ns = min(4, ge - g0);
     const uint8_t* vstage = vbase + (step & 1) * S::vBytes;
     const bool more = step + 1 < n_steps;
     if (more) {
@@ -846,42 +860,30 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
 #pragma unroll
       for (int e = 0; e < 4; ++e) zcls[e] *= alpha;
     }
-    for (int gs = 0; gs < ns; ++gs) {
-      const int w = (VB == 2) ? (lk >> 1) : lk;
-      // words of channels 4 lc .. 4 lc + 3 and 64 + 4 lc .. 64 + 4 lc + 3: the
-      // 16 lanes of a read cover 256 contiguous bytes
-      const uint8_t* vrow = vstage + gs * S::vGroup + (w * D + 4 * lc) * 4;
-      const u32x4 v0 = *reinterpret_cast<const u32x4*>(vrow);
-      const u32x4 v1 = *reinterpret_cast<const u32x4*>(vrow + 64 * 4);
-      const int vmo = ((gs * 4 + mcol) * G + 8 * lk) * 2;
-      const u32x4 vs = *reinterpret_cast<const u32x4*>(vstage + S::offVS + vmo);
-      const u32x4 vz = *reinterpret_cast<const u32x4*>(vstage + S::offVZ + vmo);
-      // p of tokens 8*lk .. 8*lk+7 (pair e: tokens 2e, 2e+1); B = p * S as
-      // fp16 hi + lo of the binary32 product (the probabilities are not exact
-      // in fp16, so the product is formed in binary32 and split).  (Handing p
-      // over as fp16 hi + lo pairs instead, for packed fp16 products here,
-      // takes 48 fewer instructions in this wave and 16 more in the key
-      // wave, and measured 3% slower: the key wave sets the pace.)
-      const float* prow = hp + (gs * GQ + hsrc) * kRowP + 8 * lk;
-      const f32x4 p0 = *reinterpret_cast<const f32x4*>(prow);
-      const f32x4 p1 = *reinterpret_cast<const f32x4*>(prow + 4);
+    // p.V of 32 tokens (one MFMA k block): p0, p1 the probabilities of this
+    // lane's 8 tokens, vs / vz their scales and zeros (channel group mcol,
+    // token t in half t & 1 of element t / 2), av the codes (entry pairs
+    // (a, a + 4), see codes8).  B = p * S as fp16 hi + lo of the binary32
+    // product (the probabilities are not exact in fp16, so the product is
+    // formed in binary32 and split).  (Handing p over as fp16 hi + lo pairs
+    // instead, for packed fp16 products here, takes 48 fewer instructions in
+    // this wave and 16 more in the key wave, and measured 3% slower: the key
+    // wave sets the pace.)
+    auto products = [&](const f32x4& p0, const f32x4& p1, const u32x4& vs, const u32x4& vz, const half8_t (&av)[8]) {
       const float p[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
       u32x4 h4, l4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
+        // pair e: tokens e and e + 4
         uint32_t hi, lo;
-        split_pair(times_half<0>(p[2 * e], vs[e]), times_half<1>(p[2 * e + 1], vs[e]), hi, lo);
+        const float b0 = (e & 1) ? times_half<1>(p[e], vs[e >> 1]) : times_half<0>(p[e], vs[e >> 1]);
+        const float b1 = (e & 1) ? times_half<1>(p[e + 4], vs[2 + (e >> 1)]) : times_half<0>(p[e + 4], vs[2 + (e >> 1)]);
+        split_pair(b0, b1, hi, lo);
         h4[e] = hi;
         l4[e] = lo;
         zcls[e] = fmaf(p[2 * e], lo_half(vz[e]), zcls[e]);
         zcls[e] = fmaf(p[2 * e + 1], hi_half(vz[e]), zcls[e]);
       }
-      const half8_t bph = as_h8(h4), bpl = as_h8(l4);
-      const uint32_t vc[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-      half8_t av[8];
-#pragma unroll
-      for (int be = 0; be < 8; ++be)
-        av[be] = (VB == 2) ? codes8<2>(vc[be], lk & 1) : codes8<4>(vc[be], false);
       if constexpr (kHiLoCols) {
         u32x4 b4;
 #pragma unroll
@@ -890,10 +892,63 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
 #pragma unroll
         for (int be = 0; be < 8; ++be) o[be] = mfma(av[be], bp, o[be]);
       } else {
+        const half8_t bph = as_h8(h4), bpl = as_h8(l4);
 #pragma unroll
         for (int be = 0; be < 8; ++be) o[be] = mfma(av[be], bph, o[be]);
 #pragma unroll
         for (int be = 0; be < 8; ++be) o[be] = mfma(av[be], bpl, o[be]);
+      }
+    };
+    // All 4 streams, also past the split's last group: the key wave hands
+    // over p = 0 there and the stage repeats the last stream's words, so
+    // those products add zeros; the unrolled streams form one schedule.
+    // Words of channels 4 lc .. 4 lc + 3 and 64 + 4 lc .. 64 + 4 lc + 3: the
+    // 16 lanes of a read cover 256 contiguous bytes.
+    if constexpr (VB == 2) {
+      // A 2-bit word holds 16 tokens (two runs of 8).  Streams go in pairs:
+      // lanes of k block lk take word lk & 1 of stream 2 pp + lk / 2, both
+      // of its runs (one product block each), so each word read serves 16
+      // codes.
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        const int gsl = 2 * pp + (lk >> 1), w = lk & 1;
+        const uint8_t* vrow = vstage + gsl * S::vGroup + (w * D + 4 * lc) * 4;
+        const u32x4 v0 = *reinterpret_cast<const u32x4*>(vrow);
+        const u32x4 v1 = *reinterpret_cast<const u32x4*>(vrow + 64 * 4);
+        const uint32_t vc[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+#pragma unroll
+        for (int run = 0; run < 2; ++run) {
+          const int t0 = 16 * w + 8 * run;  // first token of the run in its stream
+          const int vmo = ((gsl * 4 + mcol) * G + t0) * 2;
+          const u32x4 vs = *reinterpret_cast<const u32x4*>(vstage + S::offVS + vmo);
+          const u32x4 vz = *reinterpret_cast<const u32x4*>(vstage + S::offVZ + vmo);
+          const float* prow = hp + (gsl * GQ + hsrc) * kRowP + t0;
+          const f32x4 p0 = *reinterpret_cast<const f32x4*>(prow);
+          const f32x4 p1 = *reinterpret_cast<const f32x4*>(prow + 4);
+          half8_t av[8];
+#pragma unroll
+          for (int be = 0; be < 8; ++be) av[be] = run ? codes8<2, 1>(vc[be]) : codes8<2, 0>(vc[be]);
+          products(p0, p1, vs, vz, av);
+        }
+      }
+    } else {
+      // a 4-bit word holds one run of 8 tokens: k block lk takes word lk
+#pragma unroll
+      for (int gs = 0; gs < 4; ++gs) {
+        const uint8_t* vrow = vstage + gs * S::vGroup + (lk * D + 4 * lc) * 4;
+        const u32x4 v0 = *reinterpret_cast<const u32x4*>(vrow);
+        const u32x4 v1 = *reinterpret_cast<const u32x4*>(vrow + 64 * 4);
+        const uint32_t vc[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        const int vmo = ((gs * 4 + mcol) * G + 8 * lk) * 2;
+        const u32x4 vs = *reinterpret_cast<const u32x4*>(vstage + S::offVS + vmo);
+        const u32x4 vz = *reinterpret_cast<const u32x4*>(vstage + S::offVZ + vmo);
+        const float* prow = hp + (gs * GQ + hsrc) * kRowP + 8 * lk;
+        const f32x4 p0 = *reinterpret_cast<const f32x4*>(prow);
+        const f32x4 p1 = *reinterpret_cast<const f32x4*>(prow + 4);
+        half8_t av[8];
+#pragma unroll
+        for (int be = 0; be < 8; ++be) av[be] = codes8<4, 0>(vc[be]);
+        products(p0, p1, vs, vz, av);
       }
     }
   }
