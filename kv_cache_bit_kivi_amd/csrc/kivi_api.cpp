@@ -901,8 +901,11 @@ kivi_status kivi_append_decode_attn(kivi_cache* c, const void* k_new, const void
   if ((st = plan_decode(c, after_token(c), gq, plan)) != KIVI_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int R = c->cfg.residual_length;
-  // a full window is packed before the token enters it (a launch of its
-  // own, once every R steps); then the token takes the next window slot
+  // A full window is packed before the token enters it (a launch of its
+  // own, once every R steps); then the token takes the next window slot.
+  // (Packing it inside the decode launch, by the workgroup of the last split,
+  // was measured slower at every workload: that workgroup's 4 blocks in a
+  // row outlast the separate launch.)
   if (c->ragged) {
     std::vector<char> fl(c->cfg.batch, 0);
     for (int b = 0; b < c->cfg.batch; ++b) fl[b] = c->sr[b] == R;
