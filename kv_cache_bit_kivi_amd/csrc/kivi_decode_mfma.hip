@@ -129,6 +129,15 @@ __device__ __forceinline__ void mul_pair_exact(uint32_t a, uint32_t b, uint32_t&
   asm("v_pk_fma_f16 %0, %1, %2, %3 neg_lo:[0,0,1] neg_hi:[0,0,1]" : "=v"(lo) : "v"(a), "v"(b), "v"(hi));
 }
 
+// RN(a * b - RN(m * b)) for fp16 pairs: with m = a the exact remainder of
+// mul_pair_exact's hi (its lo), with m = 0 the hi itself.
+__device__ __forceinline__ uint32_t residual_pair(uint32_t a, uint32_t b, uint32_t m) {
+  uint32_t h, r;
+  asm("v_pk_mul_f16 %0, %1, %2" : "=v"(h) : "v"(m), "v"(b));
+  asm("v_pk_fma_f16 %0, %1, %2, %3 neg_lo:[0,0,1] neg_hi:[0,0,1]" : "=v"(r) : "v"(a), "v"(b), "v"(h));
+  return r;
+}
+
 // acc + a.x * b.x + a.y * b.y for fp16 pairs a, b (v_dot2_f32_f16).
 __device__ __forceinline__ float dot2_acc(uint32_t a, uint32_t b, float acc) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), acc, false);
@@ -589,8 +598,15 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
   constexpr int KL = KB;  // key words per lane (32 channels)
   const int lane = threadIdx.x & 63;
   const int lc = lane & 15, lk = lane >> 4;
-  const int hq = lc >> 2;  // head of this lane's B / C columns
+  const int hq = lc >> 2;  // head slot of this lane's B / C columns
   const int jt = lc & 3;
+  // With fewer than 3 heads per kv head, head slots hq >= NQ are free: slot
+  // NQ + h carries the lo half of head h's q'' * S, so one product per code
+  // block takes both halves (half the products); the two columns' sums are
+  // added before the softmax.  With 4 heads each column holds hi, then lo.
+  constexpr bool kHiLoCols = NQ <= 2;
+  const int hsrc = kHiLoCols ? hq % NQ : hq;  // head whose q this column takes
+  const int part = kHiLoCols ? hq / NQ : 0;   // 0: hi, 1: lo, 2 and 3 (NQ = 1): unused
 
   // The value wave waits at every step's barrier for this wave's softmax, so
   // this wave issues ahead of other workgroups' waves on its SIMD.
@@ -602,10 +618,10 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
     const int f0 = step_first(gb, 0, n_steps, rot);
     issue_kstage<KB, VB, GT, PAGED>(a, u, ubase, f0, min(4, ge - f0), smem, smem + S::offKM0);
   }
-  // q of head hq, channels 32*lk .. 32*lk+31 (head slots hq >= NQ: zeros)
+  // q of head hsrc, channels 32*lk .. 32*lk+31 (unused head slots: zeros)
   float qf[32];
-  if (hq < NQ) {
-    const uint16_t* qp = a.q + ((long long)b * a.Hq + h0 + hq) * D + 32 * lk;
+  if (kHiLoCols ? part < 2 : hq < NQ) {
+    const uint16_t* qp = a.q + ((long long)b * a.Hq + h0 + hsrc) * D + 32 * lk;
 #pragma unroll
     for (int i = 0; i < 32; i += 8) {
       const uint4 v = *reinterpret_cast<const uint4*>(qp + i);
@@ -644,6 +660,9 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
 #pragma unroll
     for (int a = 0; a < 4; ++a)
       q2[4 * c + a] = pk_rne(__builtin_amdgcn_ldexpf(qf[8 * c + a], -ek), __builtin_amdgcn_ldexpf(qf[8 * c + a + 4], -ek));
+  // lo columns (kHiLoCols): B = RN(q'' S - RN(qm S)) with qm = q'' gives the
+  // lo half and qm = 0 the hi half, two packed instructions either way
+  const uint32_t qmask = (kHiLoCols && part == 1) ? 0xffffffffu : 0u;
   // raw product -> score: products are c q S 2^(F-15-Ek)
   const float k_unscale = __builtin_amdgcn_ldexpf(a.qscale, 15 - KS::F + ek);
   const float z_unscale = __builtin_amdgcn_ldexpf(a.qscale, ek);
@@ -710,21 +729,29 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
       for (int e = 0; e < 4; ++e) {
         const uint32_t qq = q2[4 * c + e];
         uint32_t hi, lo;
-        mul_pair_exact(qq, sx[e], hi, lo);
+        if constexpr (kHiLoCols) {
+          hi = residual_pair(qq, sx[e], qq & qmask);  // this column's half
+          lo = 0u;
+        } else {
+          mul_pair_exact(qq, sx[e], hi, lo);
+        }
         h4[e] = hi;
         l4[e] = lo;
         bcls[e] = dot2_acc(qq, zx[e], bcls[e]);
       }
-      const half8_t bh = as_h8(h4), bl = as_h8(l4);
       half8_t ak[8];
 #pragma unroll
       for (int s = 0; s < 8; ++s)
         ak[s] = (KB == 4) ? codes8<4, 0>(kw[s][c & (KL - 1)])
                 : (c & 1) ? codes8<2, 1>(kw[s][c >> 1]) : codes8<2, 0>(kw[s][c >> 1]);
+      const half8_t bh = as_h8(h4);
 #pragma unroll
       for (int s = 0; s < 8; ++s) sc[s] = mfma(ak[s], bh, sc[s]);
+      if constexpr (!kHiLoCols) {
+        const half8_t bl = as_h8(l4);
 #pragma unroll
-      for (int s = 0; s < 8; ++s) sc[s] = mfma(ak[s], bl, sc[s]);
+        for (int s = 0; s < 8; ++s) sc[s] = mfma(ak[s], bl, sc[s]);
+      }
     }
     float bias = (bcls[0] + bcls[1]) + (bcls[2] + bcls[3]);
     bias = swap_sum<16>(bias);
@@ -740,7 +767,8 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
     // distinct banks.
     float* const sl = reinterpret_cast<float*>(smem + S::offP0 + (step & 1) * S::pBytes);
     // (raw products; each reader applies the scale and its stream's
-    // zero-point term to its own 8 scores)
+    // zero-point term to its own 8 scores, and with kHiLoCols adds the lo
+    // column, which the diagonal lanes of slot hq + NQ write like a head)
     if (diag) {
 #pragma unroll
       for (int s = 0; s < 8; ++s)
@@ -751,8 +779,15 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
     const int row = (lk * GQ + hq) * kRowP + 8 * jt;
     float x[8];
     {
-      const f32x4 x0 = *reinterpret_cast<const f32x4*>(sl + row);
-      const f32x4 x1 = *reinterpret_cast<const f32x4*>(sl + row + 4);
+      f32x4 x0 = *reinterpret_cast<const f32x4*>(sl + row);
+      f32x4 x1 = *reinterpret_cast<const f32x4*>(sl + row + 4);
+      if constexpr (kHiLoCols) {
+        // the lo column's sums of head hq sit in head slot hq + NQ's row
+        // (lanes of slots hq >= NQ read a row of their own and are masked)
+        const int lrow = (lk * GQ + ((hq + NQ) & (GQ - 1))) * kRowP + 8 * jt;
+        x0 += *reinterpret_cast<const f32x4*>(sl + lrow);
+        x1 += *reinterpret_cast<const f32x4*>(sl + lrow + 4);
+      }
       const float bz = sl[S::offBias / 4 + lk * GQ + hq];
       // streams past the last group hold no tokens; slots hq >= NQ no head
       const bool valid = lk < ns && hq < NQ;
