@@ -27,6 +27,7 @@ Prints one JSON line.  Inputs are resident in HBM before timing starts.
 """
 import argparse
 import ctypes
+import dataclasses
 import hashlib
 import json
 import os
@@ -58,6 +59,9 @@ def parse():
     p.add_argument("--ragged", action="store_true",
                    help="sequences of different lengths: sequence b's prefix has T_b tokens, "
                         "drawn uniformly from [T/2, T] (seed 0)")
+    p.add_argument("--q-heads", type=int, default=0,
+                   help="query heads per sequence instead of the workload's (e.g. 64 on c2: the "
+                        "64q/8kv shape of 70B-class models, 8 query heads per kv head)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run one plain 1 GiB device copy first (counter calibration "
                         "for profiler runs)")
@@ -152,6 +156,11 @@ def run(args):
     from kv_cache_bit_kivi_amd.inputs import WORKLOADS, make_layer
 
     w = WORKLOADS[args.workload]
+    if args.q_heads:
+        if args.q_heads % w.kv_heads:
+            raise SystemExit(f"--q-heads {args.q_heads} is not a multiple of {w.kv_heads} kv heads")
+        w = dataclasses.replace(w, name=f"{w.name}gq{args.q_heads // w.kv_heads}", q_heads=args.q_heads,
+                                description=f"{w.description}, with {args.q_heads} query heads")
     dev = torch.device("cuda:0")
     T, R, B = w.tokens, w.residual_length, w.batch
     scale = 1.0 / np.sqrt(w.head_dim)
