@@ -414,9 +414,16 @@ static_assert(Stage<4, 2>::bytes == mfma_wg_lds_bytes(4, 2), "lds");
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef const __attribute__((address_space(1))) void glb_void_t;
 
-__device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
+// 16 bytes per lane from global memory to LDS.  Records are read once, with
+// the streaming hint (nt), unless several head groups read them (`keep`):
+// the other workgroups of the pair then find them in the XCD's L2.
+__device__ __forceinline__ void dma16(const void* src, void* lds_dst, bool keep) {
   // address-space conversions need C-style casts
-  __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)lds_dst, 16, 0, 2);
+  if (keep) {
+    __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)lds_dst, 16, 0, 0);
+  } else {
+    __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)lds_dst, 16, 0, 2);
+  }
 }
 
 // Records of streams g0 .. g0 + 3 of unit u (unit-major, or through the
@@ -478,7 +485,7 @@ __device__ __forceinline__ void issue_kstage(const DecodeArgs& a, long long u, c
 #pragma unroll
     for (int j = 0; j < S::kGroup / 1024; ++j)  // a stream's rows: kGroup bytes from row 32 * hf
       dma16(rp[gi] + BL.k_codes + hf[gi] * S::kGroup + j * 1024 + lane * 16,
-            dst + gi * S::kGroupPad + j * 1024);
+            dst + gi * S::kGroupPad + j * 1024, a.hg > 1);
   }
   // scale and zero of the stream's block: 256 bytes per stream and field, 16
   // lanes per stream.  Stream i's 16-byte chunk j lands in LDS slot
@@ -486,8 +493,8 @@ __device__ __forceinline__ void issue_kstage(const DecodeArgs& a, long long u, c
   // 4 lk + c of four streams at once, which then fall on distinct banks.
   const uint8_t* const meta =
       lane_record<KB, VB, GT, PAGED>(rp, g0, ns, lane) + ((lane - 4 * (lane >> 4)) & 15) * 16;
-  dma16(meta + BL.k_scale, meta_dst);
-  dma16(meta + BL.k_zero, meta_dst + 4 * D * 2);
+  dma16(meta + BL.k_scale, meta_dst, a.hg > 1);
+  dma16(meta + BL.k_zero, meta_dst + 4 * D * 2, a.hg > 1);
 }
 
 // Value stage of groups [g0, g0 + ns): Stage::vLoads instructions.
@@ -504,7 +511,8 @@ __device__ __forceinline__ void issue_vstage(const DecodeArgs& a, long long u, c
   for (int gi = 0; gi < 4; ++gi) {
 #pragma unroll
     for (int j = 0; j < S::vGroup / 1024; ++j)  // the stream's words: vGroup bytes from word row hf * VB
-      dma16(rp[gi] + BL.v_codes + hf[gi] * S::vGroup + j * 1024 + lane * 16, dst + gi * S::vGroup + j * 1024);
+      dma16(rp[gi] + BL.v_codes + hf[gi] * S::vGroup + j * 1024 + lane * 16, dst + gi * S::vGroup + j * 1024,
+            a.hg > 1);
   }
   // scale and zero of the stream's 32 tokens, stage layout [stream][4 channel
   // groups of 32][32 tokens]; a block stores [D / G][G], so with G = 64 two
@@ -513,8 +521,8 @@ __device__ __forceinline__ void issue_vstage(const DecodeArgs& a, long long u, c
   const int c = lane & 15;
   const int off = ((32 * (c >> 2)) / GT * GT + kStream * lane_half(g0, ns, GT / kStream, lane) + 8 * (c & 3)) * 2;
   const uint8_t* const meta = lane_record<KB, VB, GT, PAGED>(rp, g0, ns, lane) + off;
-  dma16(meta + BL.v_scale, dst + S::offVS);
-  dma16(meta + BL.v_zero, dst + S::offVZ);
+  dma16(meta + BL.v_scale, dst + S::offVS, a.hg > 1);
+  dma16(meta + BL.v_zero, dst + S::offVZ, a.hg > 1);
 }
 
 // ---------------------------------------------------------------------------
