@@ -414,8 +414,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("f16 hi+lo matrix operands x 2/4-bit codes, f32 accumulation" if w.gq in (1, 2, 4)
-                  else "f32"),
+        "dtype": "f16 hi+lo matrix operands x 2/4-bit codes, f32 accumulation",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.description}", "batch": w.batch,
                    "kv_heads": w.kv_heads, "q_heads": w.q_heads, "head_dim": w.head_dim,

@@ -19,11 +19,12 @@
 //   q . k^_t   = sum_d (q_d S_gd) c_td + sum_d q_d Z_gd         (key group g)
 //   sum_t p_t v^_t,d = sum_t (p_t S_tm) c_td + sum_t p_t Z_tm   (value group m)
 // Codes enter v_mfma_f32_16x16x32_f16 as the normal fp16 numbers c * 2^(F-15)
-// (exact), extracted from the split-half words with one mask and one packed
-// multiply per pair.  The folded operands q*S and p*S are carried as fp16
-// hi + lo pairs (two MFMAs): q*S exactly, p*S within 2^-22 relative; the
-// zero-point term of the keys (one dot product per group and head) runs on
-// the vector ALUs.
+// (exact), extracted from the split-half words by two masks per word and one
+// fp4/fp8 conversion per pair.  The folded operands q*S and p*S are carried
+// as fp16 hi + lo pairs: q*S exactly, p*S within 2^-22 relative.  With 4 heads
+// in a workgroup the pair takes two products; with 1 or 2 the lo halves ride
+// in the spare head-slot columns of the same product.  The zero-point term of
+// the keys (one dot product per group and head) runs on the vector ALUs.
 //
 // Key side: four consecutive 32-token groups at once, block-diagonal: A rows
 // are 4 tokens of each of the 4 groups, B columns are the 4 heads x 4 groups,
