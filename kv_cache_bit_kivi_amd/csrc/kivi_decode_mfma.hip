@@ -614,8 +614,19 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
   // block takes both halves (half the products); the two columns' sums are
   // added before the softmax.  With 4 heads each column holds hi, then lo.
   constexpr bool kHiLoCols = NQ <= 2;
-  const int hsrc = kHiLoCols ? hq % NQ : hq;  // head whose q this column takes
-  const int part = kHiLoCols ? hq / NQ : 0;   // 0: hi, 1: lo, 2 and 3 (NQ = 1): unused
+  // With 4 heads the operands swap roles: A (rows) is the dense operand,
+  // row m = 8 s + 2 h + part holding half `part` of head h's q'' * S for
+  // stream s of a pair of streams, and B (columns) holds the codes of 16
+  // tokens, 8 of each stream of the pair.  One product then takes both
+  // halves, and the hi and lo sums of a score land in the same output lane
+  // (rows 4 lk .. 4 lk + 3: head 2 (lk & 1) and 2 (lk & 1) + 1, hi then lo),
+  // where they are added.  Two dense operands (stream pairs 0-1 and 2-3)
+  // serve 8 products per code block: 32 per step instead of 64.  (Not with
+  // 4-bit keys and 2-bit values: that variant runs 3 waves per SIMD, and the
+  // paired layout's registers spill there inside the step loop.)
+  constexpr bool kPairRows = NQ == 4 && !(KB == 4 && VB == 2);
+  const int hsrc = kHiLoCols ? hq % NQ : kPairRows ? (lc >> 1) & 3 : hq;  // head whose q this lane takes
+  const int part = kHiLoCols ? hq / NQ : kPairRows ? lc & 1 : 0;  // 0: hi, 1: lo, 2 and 3 (NQ = 1): unused
 
   // The value wave waits at every step's barrier for this wave's softmax, so
   // this wave issues ahead of other workgroups' waves on its SIMD.
@@ -652,11 +663,14 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
 #pragma unroll
   for (int i = 0; i < 32; ++i) qabs = fmaxf(qabs, fabsf(qf[i]));
   qabs = swap_max<16>(qabs);
-  qabs = swap_max<32>(qabs);  // the 128 channels of head hq
+  qabs = swap_max<32>(qabs);  // the 128 channels of head hsrc
   // q'' = q 2^-Ek and q'' S below 2^15 (q'' itself too, when the scales are
   // below 1); p' = p 2^-Ev <= 2^-Ev and p' S below 2^15
   const int ek = range_exp(qabs * fmaxf(sk_max, 1.0f));
   const int ev = range_exp(sv_max);
+  // the exponent of head hq, whose scores this lane reads in the softmax
+  // (lane 2 hq holds head hq's in the paired-rows layout)
+  const int ek_r = kPairRows ? __shfl(ek, 2 * hq) : ek;
   // q'' as fp16 pairs (pair p: channels 2p, 2p+1).  The power-of-two factor
   // keeps q'' exact (a bf16 q is rounded to fp16 once).
   // softmax_scale * log2(e) * 2^Ek multiplies the scores afterwards.  Head
@@ -671,10 +685,10 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
       q2[4 * c + a] = pk_rne(__builtin_amdgcn_ldexpf(qf[8 * c + a], -ek), __builtin_amdgcn_ldexpf(qf[8 * c + a + 4], -ek));
   // lo columns (kHiLoCols): B = RN(q'' S - RN(qm S)) with qm = q'' gives the
   // lo half and qm = 0 the hi half, two packed instructions either way
-  const uint32_t qmask = (kHiLoCols && part == 1) ? 0xffffffffu : 0u;
+  const uint32_t qmask = ((kHiLoCols || kPairRows) && part == 1) ? 0xffffffffu : 0u;
   // raw product -> score: products are c q S 2^(F-15-Ek)
-  const float k_unscale = __builtin_amdgcn_ldexpf(a.qscale, 15 - KS::F + ek);
-  const float z_unscale = __builtin_amdgcn_ldexpf(a.qscale, ek);
+  const float k_unscale = __builtin_amdgcn_ldexpf(a.qscale, 15 - KS::F + ek_r);
+  const float z_unscale = __builtin_amdgcn_ldexpf(a.qscale, ek);  // (the zero-point term of head hsrc)
 
   const bool diag = (lc & 3) == lk;  // lane holds scores (stream lk)
   float m_run = -INFINITY;           // running max of head hq (base 2)
@@ -688,21 +702,34 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
     wave_lds_sync();
     const uint8_t* const meta = smem + S::offKM0 + (step & 1) * S::kMetaBytes;
 
-    const int ga = lc >> 2;  // stream of this lane's A row
-    const int gc = lc & 3;   // stream of this lane's B column
-    // chunk 4 lk + c of stream gc sits in slot 4 ((lk + gc) mod 4) + c
-    const u32x4* sBp = reinterpret_cast<const u32x4*>(meta + gc * D * 2 + 64 * ((lk + gc) & 3));
-    const u32x4* zBp = reinterpret_cast<const u32x4*>(meta + 4 * D * 2 + gc * D * 2 + 64 * ((lk + gc) & 3));
-    const uint8_t* krow = smem + ga * S::kGroupPad + (lc & 3) * S::kRow + 4 * KL * lk;
+    // chunk 4 lk + c of stream st sits in slot 4 ((lk + st) mod 4) + c
+    auto meta_chunks = [&](int field, int st) {
+      return reinterpret_cast<const u32x4*>(meta + field * 4 * D * 2 + st * D * 2 + 64 * ((lk + st) & 3));
+    };
+    // scale chunks of the lane's dense operand(s) and zero chunks of its
+    // zero-point term.  Default layout: stream lc & 3 for both.  Paired
+    // rows: scales of stream lc >> 3 of each pair; the zero-point term of
+    // head hsrc and stream 2 (lc & 1) + (lc >> 3), so the 16 lanes of a k
+    // block cover the 16 (stream, head) terms.
+    const int gs0 = kPairRows ? lc >> 3 : lc & 3;
+    const u32x4* sBp = meta_chunks(0, gs0);
+    const u32x4* sBp1 = meta_chunks(0, gs0 + 2);
+    const u32x4* zBp = meta_chunks(1, kPairRows ? 2 * (lc & 1) + (lc >> 3) : lc & 3);
+    // code rows: default, tile s holds token 4 s + (lc & 3) of stream lc >> 2
+    // (A rows); paired rows, tile 4 P + j holds token 4 (lc & 7) + j of
+    // stream 2 P + (lc >> 3) (B columns)
+    const uint8_t* krow = kPairRows ? smem + (lc >> 3) * S::kGroupPad + 4 * (lc & 7) * S::kRow + 4 * KL * lk
+                                    : smem + (lc >> 2) * S::kGroupPad + (lc & 3) * S::kRow + 4 * KL * lk;
     uint32_t kw[8][KL];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
+      const int off = kPairRows ? (s >> 2) * 2 * S::kGroupPad + (s & 3) * S::kRow : 4 * s * S::kRow;
       if constexpr (KL == 2) {
-        const u32x2 v = *reinterpret_cast<const u32x2*>(krow + 4 * s * S::kRow);
+        const u32x2 v = *reinterpret_cast<const u32x2*>(krow + off);
         kw[s][0] = v[0];
         kw[s][1] = v[1];
       } else {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(krow + 4 * s * S::kRow);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(krow + off);
 #pragma unroll
         for (int i = 0; i < KL; ++i) kw[s][i] = v[i];
       }
@@ -738,8 +765,8 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
       for (int e = 0; e < 4; ++e) {
         const uint32_t qq = q2[4 * c + e];
         uint32_t hi, lo;
-        if constexpr (kHiLoCols) {
-          hi = residual_pair(qq, sx[e], qq & qmask);  // this column's half
+        if constexpr (kHiLoCols || kPairRows) {
+          hi = residual_pair(qq, sx[e], qq & qmask);  // this lane's half (pair 0 in paired rows)
           lo = 0u;
         } else {
           mul_pair_exact(qq, sx[e], hi, lo);
@@ -748,23 +775,39 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
         l4[e] = lo;
         bcls[e] = dot2_acc(qq, zx[e], bcls[e]);
       }
+      if constexpr (kPairRows) {
+        // the dense operand of streams 2 and 3 (l4)
+        const u32x4 sB1 = sBp1[c];
+        const uint32_t sx1[4] = {halves<0>(sB1[0], sB1[2]), halves<1>(sB1[0], sB1[2]), halves<0>(sB1[1], sB1[3]),
+                                 halves<1>(sB1[1], sB1[3])};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) l4[e] = residual_pair(q2[4 * c + e], sx1[e], q2[4 * c + e] & qmask);
+      }
       half8_t ak[8];
 #pragma unroll
       for (int s = 0; s < 8; ++s)
         ak[s] = (KB == 4) ? codes8<4, 0>(kw[s][c & (KL - 1)])
                 : (c & 1) ? codes8<2, 1>(kw[s][c >> 1]) : codes8<2, 0>(kw[s][c >> 1]);
       const half8_t bh = as_h8(h4);
+      if constexpr (kPairRows) {
+        const half8_t bh1 = as_h8(l4);
 #pragma unroll
-      for (int s = 0; s < 8; ++s) sc[s] = mfma(ak[s], bh, sc[s]);
-      if constexpr (!kHiLoCols) {
-        const half8_t bl = as_h8(l4);
+        for (int s = 0; s < 4; ++s) sc[s] = mfma(bh, ak[s], sc[s]);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) sc[s] = mfma(ak[s], bl, sc[s]);
+        for (int s = 4; s < 8; ++s) sc[s] = mfma(bh1, ak[s], sc[s]);
+      } else {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) sc[s] = mfma(ak[s], bh, sc[s]);
+        if constexpr (!kHiLoCols) {
+          const half8_t bl = as_h8(l4);
+#pragma unroll
+          for (int s = 0; s < 8; ++s) sc[s] = mfma(ak[s], bl, sc[s]);
+        }
       }
     }
     float bias = (bcls[0] + bcls[1]) + (bcls[2] + bcls[3]);
     bias = swap_sum<16>(bias);
-    bias = swap_sum<32>(bias) * z_unscale;  // all 128 channels: head hq, group g0 + (lc & 3)
+    bias = swap_sum<32>(bias) * z_unscale;  // all 128 channels: head hsrc, the zero-point stream
 
     // ------------------------------------------------------------- softmax
     // The 16 diagonal lanes hold the step's 512 scores (head hq, stream lk,
@@ -778,7 +821,26 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
     // (raw products; each reader applies the scale and its stream's
     // zero-point term to its own 8 scores, and with kHiLoCols adds the lo
     // column, which the diagonal lanes of slot hq + NQ write like a head)
-    if (diag) {
+    if constexpr (kPairRows) {
+      // lanes whose rows (stream lk >> 1 of the pair) and column (stream
+      // lc >> 3) agree hold heads 2 (lk & 1) and 2 (lk & 1) + 1 of tokens
+      // 4 (lc & 7) .. + 3 over the pair's 4 tiles: hi + lo
+      if ((lc >> 3) == (lk >> 1)) {
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+          f32x4 xa, xb;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            xa[j] = sc[4 * pr + j][0] + sc[4 * pr + j][1];
+            xb[j] = sc[4 * pr + j][2] + sc[4 * pr + j][3];
+          }
+          float* const dst = sl + ((2 * pr + (lc >> 3)) * GQ + 2 * (lk & 1)) * kRowP + 4 * (lc & 7);
+          *reinterpret_cast<f32x4*>(dst) = xa;
+          *reinterpret_cast<f32x4*>(dst + kRowP) = xb;
+        }
+      }
+      if (lk == 0) sl[S::offBias / 4 + (2 * (lc & 1) + (lc >> 3)) * GQ + hsrc] = bias;
+    } else if (diag) {
 #pragma unroll
       for (int s = 0; s < 8; ++s)
         *reinterpret_cast<f32x4*>(sl + (lk * GQ + hq) * kRowP + 4 * s) = sc[s];
