@@ -56,6 +56,11 @@
  *                                          adjacent
  *   + G*D*bv/8                    k_scale  fp16 [D]     {S} per channel
  *   + 2*D                         k_zero   fp16 [D]     {Z} per channel
+ *                                          (both interleaved: position i of
+ *                                          the 8 channels 8j .. 8j+7 holds
+ *                                          channel 8j + i/2 + 4 (i mod 2),
+ *                                          so word w holds channels 8j + w
+ *                                          and 8j + w + 4)
  *   + 4*D                         v_scale  fp16 [D / G][G]  {S} per (channel
  *                                          group, row)
  *   + 6*D                         v_zero   fp16 [D / G][G]

@@ -155,7 +155,9 @@ __device__ __forceinline__ float dot2_acc(uint32_t a, uint32_t b, float acc) {
 // exactly: every code becomes the normal fp16 number c * 2^(F-15) (F = 6 for
 // 2-bit, 4 for 4-bit), zero stays zero.  A conversion pairs the codes of
 // entries a and a + 4 of a run of 8 (a = 0..3), so the dense operand of
-// every product takes the same pairing.
+// every product takes the same pairing (the record stores the key scale and
+// zero interleaved in that order; the value wave picks scale halves per
+// token).
 //
 // Normal operands matter for the accuracy of the products: measured on
 // MI355X, a v_mfma_f32_16x16x32_f16 whose A operand holds fp16 subnormals
@@ -197,13 +199,6 @@ __device__ __forceinline__ half8_t codes8(uint32_t x) {
     r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(z1, kScale, true));
   }
   return as_h8(r);
-}
-
-// (lo half of a, lo half of b) or (hi half of a, hi half of b) of two fp16
-// pairs, one v_perm_b32.
-template <int SEL>
-__device__ __forceinline__ uint32_t halves(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, SEL == 0 ? 0x05040100u : 0x07060302u);
 }
 
 // Cross-lane exchanges on the vector ALUs (no LDS round trip):
@@ -592,6 +587,28 @@ __device__ __forceinline__ int step_first(int gb, int step, int n_steps, int rot
   return gb + 4 * k;
 }
 
+// Wave priority by progress.  Six workgroups share a CU and waves of equal
+// priority issue oldest first, so with fixed priorities the workgroups of
+// one launch progress at different rates by their dispatch order: measured
+// on MI355X with per-workgroup timestamps (c2 decode, 43 steps each), the
+// first and third workgroup of each CU finished after 124 us, the second and
+// fourth after 180 us, whose value waves shared a SIMD with two key waves;
+// the launch lasts as long as its slowest workgroup.  A wave in the first
+// half of its steps therefore issues ahead of waves in their second half,
+// so workgroups that run ahead yield to those behind; within a half the key
+// wave leads, since the value wave waits at every step's barrier for its
+// softmax.  (Measured: c2 decode 187 -> 184 us back to back, 172 -> 169 us
+// after idle; c1 -2%; rotating priorities or four progress bands balanced
+// the workgroups as well but gained no more.)
+template <bool KEY>
+__device__ __forceinline__ void progress_prio(int step, int n_steps) {
+  if (2 * step < n_steps) {
+    __builtin_amdgcn_s_setprio(KEY ? 3 : 2);
+  } else {
+    __builtin_amdgcn_s_setprio(KEY ? 1 : 0);
+  }
+}
+
 // Smallest E with x * 2^-E < 2^15 (x >= 0 finite), at least -30 (x = 0 and
 // tiny x take -30).
 __device__ __forceinline__ int range_exp(float x) { return max(-30, __builtin_amdgcn_frexp_expf(x) - 15); }
@@ -628,9 +645,6 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
   const int hsrc = kHiLoCols ? hq % NQ : kPairRows ? (lc >> 1) & 3 : hq;  // head whose q this lane takes
   const int part = kHiLoCols ? hq / NQ : kPairRows ? lc & 1 : 0;  // 0: hi, 1: lo, 2 and 3 (NQ = 1): unused
 
-  // The value wave waits at every step's barrier for this wave's softmax, so
-  // this wave issues ahead of other workgroups' waves on its SIMD.
-  __builtin_amdgcn_s_setprio(1);
   constexpr BlockLayout BLu = block_layout(KB, VB, GT);
   const uint8_t* const ubase = a.blocks + static_cast<size_t>(u) * a.nb * BLu.bytes;  // (unit-major)
   // the first stage's loads go out before q is read: their latencies overlap
@@ -695,6 +709,7 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
   float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // sum of p' (four partial sums)
 
   for (int step = 0; step < n_steps; ++step) {
+    progress_prio<true>(step, n_steps);
     const int g0 = step_first(gb, step, n_steps, rot);
     const int ns = min(4, ge - g0);
     // this step's codes and metadata are the only loads of this wave in flight
@@ -753,13 +768,11 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
     for (int s = 0; s < 8; ++s) sc[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      // scale and zero of channels 8c .. 8c+7 as pairs (2k, 2k+1), re-paired
-      // (a, a + 4) like q2 and the codes
+      // scale and zero of 8 channels as the pairs (a, a + 4), a = 0..3, of q2
+      // and the codes: the record stores them interleaved in that order
       const u32x4 sB = sBp[c], zB = zBp[c];
-      const uint32_t sx[4] = {halves<0>(sB[0], sB[2]), halves<1>(sB[0], sB[2]), halves<0>(sB[1], sB[3]),
-                              halves<1>(sB[1], sB[3])};
-      const uint32_t zx[4] = {halves<0>(zB[0], zB[2]), halves<1>(zB[0], zB[2]), halves<0>(zB[1], zB[3]),
-                              halves<1>(zB[1], zB[3])};
+      const uint32_t sx[4] = {sB[0], sB[1], sB[2], sB[3]};
+      const uint32_t zx[4] = {zB[0], zB[1], zB[2], zB[3]};
       u32x4 h4, l4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -778,8 +791,7 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
       if constexpr (kPairRows) {
         // the dense operand of streams 2 and 3 (l4)
         const u32x4 sB1 = sBp1[c];
-        const uint32_t sx1[4] = {halves<0>(sB1[0], sB1[2]), halves<1>(sB1[0], sB1[2]), halves<0>(sB1[1], sB1[3]),
-                                 halves<1>(sB1[1], sB1[3])};
+        const uint32_t sx1[4] = {sB1[0], sB1[1], sB1[2], sB1[3]};
 #pragma unroll
         for (int e = 0; e < 4; ++e) l4[e] = residual_pair(q2[4 * c + e], sx1[e], q2[4 * c + e] & qmask);
       }
@@ -945,6 +957,7 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
   for (int i = 0; i < 8; ++i) o[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   for (int step = 0; step < n_steps; ++step) {
+    progress_prio<false>(step, n_steps);
     const uint8_t* vstage = vbase + (step & 1) * S::vBytes;
     const bool more = step + 1 < n_steps;
     if (more) {

@@ -43,6 +43,18 @@ __device__ __forceinline__ void store_stream2(uint32_t* p, uint32_t x, uint32_t 
   __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t*>(p));
 }
 
+// Interleaving of the per-channel key scale or zero inside a quad of lanes
+// (all 4 active): lane k holds the fp16 pair of channels (2k, 2k+1) of the
+// quad's 8 channels; the result of lane k is the pair (k, k + 4), the low
+// halves of lanes 0 and 2 for k = 0, their high halves for k = 1, the low
+// halves of lanes 1 and 3 for k = 2 and their high halves for k = 3.
+__device__ __forceinline__ uint32_t quad_interleave(uint32_t x, int lane) {
+  const uint32_t a = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), 0x50, 0xF, 0xF, false));  // [0,0,1,1]
+  const uint32_t b = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), 0xFA, 0xF, 0xF, false));  // [2,2,3,3]
+  // (low of a, low of b) or (high of a, high of b)
+  return __builtin_amdgcn_perm(b, a, (lane & 1) ? 0x07060302u : 0x05040100u);
+}
+
 // fp16 bit pattern of a binary32 value, nearest-even; zero is stored as +0.
 __device__ __forceinline__ uint16_t f16_bits_canon(float f) {
   return f == 0.0f ? uint16_t(0) : __half_as_ushort(__float2half_rn(f));
@@ -463,9 +475,13 @@ __device__ __forceinline__ void pack_block(const uint16_t* __restrict__ ksrc, co
       const uint32_t sb0 = f16_bits_canon(s0), sb1 = f16_bits_canon(s1);
       const uint32_t top = wave_max(max(sb0, sb1));  // one wave: all 128 key channels
       if ((it & 63) == 0) atomicMax(&smax_k, top);
-      store_stream(reinterpret_cast<uint32_t*>(rec + BL.k_scale) + it, sb0 | (sb1 << 16));
-      store_stream(reinterpret_cast<uint32_t*>(rec + BL.k_zero) + it,
-                   f16_bits_canon(mn0) | (static_cast<uint32_t>(f16_bits_canon(mn1)) << 16));
+      // stored interleaved: word w of each 8 channels holds channels w and
+      // w + 4 (the pairing of the decode's code conversions).  Lane k of a
+      // quad holds channels 2k, 2k+1 of the quad's 8; word k takes the low
+      // (k even) or high (k odd) halves of lanes k / 2 and k / 2 + 2.
+      const uint32_t zb = f16_bits_canon(mn0) | (static_cast<uint32_t>(f16_bits_canon(mn1)) << 16);
+      store_stream(reinterpret_cast<uint32_t*>(rec + BL.k_scale) + it, quad_interleave(sb0 | (sb1 << 16), it));
+      store_stream(reinterpret_cast<uint32_t*>(rec + BL.k_zero) + it, quad_interleave(zb, it));
     } else if (it < D / 2 + D) {
       // value group: row t, channels m*G .. m*G+G-1; index i = m*G + t
       const int i = it - D / 2;

@@ -37,6 +37,13 @@ EXPORTED = (
 )
 
 
+
+# Stored order of the key scale and zero of a block record inside each group
+# of 8 channels: position i holds channel KEY_META_ORDER[i] (word w of the
+# group holds channels w and w + 4; see include/kivi.h).
+KEY_META_ORDER = (0, 4, 1, 5, 2, 6, 3, 7)
+
+
 class kivi_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "num_kv_heads", "head_dim", "max_tokens", "k_bits", "v_bits",
@@ -397,7 +404,9 @@ class KiviCache:
         """Device tensors aliasing the cache fields, shaped [B*H][...] per unit.
         The packed fields are strided views into the block records: unit u,
         block g, field f lies at blocks + (u * NB + g) * block_bytes + off_f;
-        "scale_max" holds one word per record index ([B*H][NB] unit-major)."""
+        "k_scale" and "k_zero" are in stored order (KEY_META_ORDER within each
+        8 channels); "scale_max" holds one word per record index ([B*H][NB]
+        unit-major)."""
         torch = self.torch
         v = self.view()
         c = self.cfg

@@ -8,6 +8,17 @@ from kv_cache_bit_kivi_amd.inputs import bits16
 ARRAYS = ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_resid", "v_resid")
 
 
+def natural_key_meta(a):
+    """A record's key scale or zero (uint16 [..., n*8], stored order) in
+    channel order: stored position i of each 8 channels is channel
+    kivi.KEY_META_ORDER[i]."""
+    from kv_cache_bit_kivi_amd import kivi
+    s = a.reshape(*a.shape[:-1], -1, 8)
+    out = np.empty_like(s)
+    out[..., list(kivi.KEY_META_ORDER)] = s
+    return out.reshape(a.shape)
+
+
 def gpu_arrays(cache, units=None):
     """Host copies of the GPU cache arrays, shaped per unit; optionally only
     the listed units (copied one by one to keep host memory small)."""
@@ -20,6 +31,8 @@ def gpu_arrays(cache, units=None):
             t = t[torch.as_tensor(units, device=t.device)]
         a = t.contiguous().view(t.shape[0], -1).cpu().numpy()
         out[name] = a.view(np.uint32) if ("codes" in name or name == "scale_max") else a.view(np.uint16)
+        if name in ("k_scale", "k_zero"):
+            out[name] = natural_key_meta(out[name])
     return out
 
 
@@ -45,8 +58,8 @@ def paged_arrays(cache, table, units=None):
 
     out = {
         "k_codes": field(v.off_k_codes, G * D * cfg.k_bits // 8, True),
-        "k_scale": field(v.off_k_scale, 2 * D, False),
-        "k_zero": field(v.off_k_zero, 2 * D, False),
+        "k_scale": natural_key_meta(field(v.off_k_scale, 2 * D, False)),
+        "k_zero": natural_key_meta(field(v.off_k_zero, 2 * D, False)),
         "v_codes": field(v.off_v_codes, G * D * cfg.v_bits // 8, True),
         "v_scale": field(v.off_v_scale, 2 * D, False),
         "v_zero": field(v.off_v_zero, 2 * D, False),

@@ -199,3 +199,10 @@ def test_binding_without_library_fails_loudly(tmp_path):
     assert r.returncode != 0
     assert "ImportError" in r.stderr and "libkivi.so is missing" in r.stderr
     assert "no CPU fallback" in r.stderr
+
+
+def test_key_meta_order_matches_header_formula():
+    # include/kivi.h: position i of each 8 channels 8j .. 8j+7 holds channel
+    # 8j + i/2 + 4 (i mod 2)
+    from kv_cache_bit_kivi_amd import kivi
+    assert kivi.KEY_META_ORDER == tuple(i // 2 + 4 * (i % 2) for i in range(8))
