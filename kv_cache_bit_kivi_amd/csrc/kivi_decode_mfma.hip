@@ -422,6 +422,25 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_dst, bool keep)
   }
 }
 
+// 16 bytes per lane from a unit's records to LDS through a buffer resource
+// (unit-major caches): byte offset voff (per lane) + soff (uniform) from the
+// unit's first record; the resource's size bounds every access.  Streaming
+// hint as in dma16.
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, int voff, int soff, void* lds_dst, bool keep) {
+  if (keep) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_dst, 16, voff, soff, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_dst, 16, voff, soff, 0, 2);
+  }
+}
+
+// Buffer resource over the nb records of one unit (gfx9 raw buffer: stride
+// 0, size in bytes, default data format word).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t unit_rsrc(const uint8_t* ubase, int nb, int block_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(ubase), static_cast<short>(0), nb * block_bytes,
+                                           0x00020000);
+}
+
 // Records of streams g0 .. g0 + 3 of unit u (unit-major, or through the
 // page table when PAGED).  A stream is 32 tokens: a whole block of G = 32, or
 // half `hf` of a block of G = 64.  Slots past the last valid stream
@@ -473,6 +492,26 @@ __device__ __forceinline__ void issue_kstage(const DecodeArgs& a, long long u, c
   using S = Stage<KB, VB>;
   constexpr BlockLayout BL = block_layout(KB, VB, GT);
   const int lane = threadIdx.x & 63;
+  if constexpr (!PAGED) {
+    // unit-major: record offsets from the stream index (uniform), lane
+    // offsets in the per-lane operand; no address arithmetic on the vector
+    // ALUs beyond the metadata lanes' record
+    constexpr int SPB = GT / kStream;
+    const __amdgpu_buffer_rsrc_t r = unit_rsrc(ubase, a.nb, BL.bytes);
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      const int g = min(g0 + gi, g0 + ns - 1);
+      const int rec = (g / SPB) * BL.bytes + BL.k_codes + (g % SPB) * S::kGroup;
+#pragma unroll
+      for (int j = 0; j < S::kGroup / 1024; ++j)
+        dma16_buf(r, lane * 16, rec + j * 1024, dst + gi * S::kGroupPad + j * 1024, a.hg > 1);
+    }
+    const int gm = min(g0 + (lane >> 4), g0 + ns - 1);
+    const int voff = (gm / SPB) * BL.bytes + ((lane - 4 * (lane >> 4)) & 15) * 16;
+    dma16_buf(r, voff, BL.k_scale, meta_dst, a.hg > 1);
+    dma16_buf(r, voff, BL.k_zero, meta_dst + 4 * D * 2, a.hg > 1);
+    return;
+  }
   const uint8_t* rp[4];
   int hf[4];
   step_records<KB, VB, GT, PAGED>(a, u, ubase, g0, ns, rp, hf);
@@ -500,6 +539,26 @@ __device__ __forceinline__ void issue_vstage(const DecodeArgs& a, long long u, c
   using S = Stage<KB, VB>;
   constexpr BlockLayout BL = block_layout(KB, VB, GT);
   const int lane = threadIdx.x & 63;
+  if constexpr (!PAGED) {
+    constexpr int SPB = GT / kStream;
+    const __amdgpu_buffer_rsrc_t r = unit_rsrc(ubase, a.nb, BL.bytes);
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      const int g = min(g0 + gi, g0 + ns - 1);
+      const int rec = (g / SPB) * BL.bytes + BL.v_codes + (g % SPB) * S::vGroup;
+#pragma unroll
+      for (int j = 0; j < S::vGroup / 1024; ++j)
+        dma16_buf(r, lane * 16, rec + j * 1024, dst + gi * S::vGroup + j * 1024, a.hg > 1);
+    }
+    // scale and zero: see below
+    const int c = lane & 15;
+    const int gm = min(g0 + (lane >> 4), g0 + ns - 1);
+    const int voff = (gm / SPB) * BL.bytes +
+                     ((32 * (c >> 2)) / GT * GT + kStream * (gm % SPB) + 8 * (c & 3)) * 2;
+    dma16_buf(r, voff, BL.v_scale, dst + S::offVS, a.hg > 1);
+    dma16_buf(r, voff, BL.v_zero, dst + S::offVZ, a.hg > 1);
+    return;
+  }
   const uint8_t* rp[4];
   int hf[4];
   step_records<KB, VB, GT, PAGED>(a, u, ubase, g0, ns, rp, hf);
@@ -871,13 +930,16 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
         x0 += *reinterpret_cast<const f32x4*>(sl + lrow);
         x1 += *reinterpret_cast<const f32x4*>(sl + lrow + 4);
       }
-      const float bz = sl[S::offBias / 4 + lk * GQ + hq];
-      // streams past the last group hold no tokens; slots hq >= NQ no head
+      // streams past the last group hold no tokens; slots hq >= NQ no head.
+      // Their raw sums are finite (the stage repeats the last stream's
+      // words; unused slots multiply zeros), so a zero-point term of -inf
+      // masks all 8 scores.
       const bool valid = lk < ns && hq < NQ;
+      const float bz = valid ? sl[S::offBias / 4 + lk * GQ + hq] : -INFINITY;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        x[i] = valid ? fmaf(x0[i], k_unscale, bz) : -INFINITY;
-        x[4 + i] = valid ? fmaf(x1[i], k_unscale, bz) : -INFINITY;
+        x[i] = fmaf(x0[i], k_unscale, bz);
+        x[4 + i] = fmaf(x1[i], k_unscale, bz);
       }
     }
     float mx = max_raw(max_raw(max_raw(x[0], x[1]), max_raw(x[2], x[3])),
