@@ -41,6 +41,37 @@ PEAK_GBPS = 8000.0  # MI355X HBM3E
 METRIC = "fused 2-bit dequant decode-attn effective HBM GB/s + % peak; pack GB/s"
 
 
+class TimingEvent:
+    """A HIP event for timing only, created with hipEventDisableSystemFence
+    through the HIP runtime torch has loaded: a default event performs a
+    system-scope fence when it is recorded (a write-back and invalidation of
+    the caches), which delays the launches around each marker and lengthens
+    the interval it measures."""
+    _hip = None
+
+    def __init__(self):
+        if TimingEvent._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime already in the process
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            TimingEvent._hip = hip
+        self.handle = ctypes.c_void_p()
+        if self._hip.hipEventCreateWithFlags(ctypes.byref(self.handle), 0x20000000) != 0:  # DisableSystemFence
+            raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def record(self, stream):
+        if self._hip.hipEventRecord(self.handle, ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_time(self, end):
+        """Milliseconds from this event to `end` (both completed)."""
+        ms = ctypes.c_float()
+        if self._hip.hipEventElapsedTime(ctypes.byref(ms), self.handle, end.handle) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -203,11 +234,11 @@ def run(args):
     # the library right around the decode kernel, [3] after the call
     every = max(1, args.phase_every)
     marked = list(range(0, args.steps, every))[:64]
-    events = {k: [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in layers] for k in marked}
+    events = {k: [[TimingEvent() for _ in range(4)] for _ in layers] for k in marked}
     for evs in events.values():
         for ev in evs:
             for e in ev:
-                e.record(stream)  # creates the event
+                e.record(sp)
     torch.cuda.synchronize()
     lib = kivi.lib
     new_tok = [(ctypes.c_void_p(L["kn"].data_ptr()), ctypes.c_void_p(L["vn"].data_ptr())) for L in layers]
@@ -221,8 +252,8 @@ def run(args):
                 raise kivi.KiviError(kivi.KIVI_ERR_INVALID_ARG, kivi.last_error_message())
             if evs is not None:
                 ev = evs[i]
-                lib.kivi_set_timing_events(h, ctypes.c_void_p(ev[1].cuda_event), ctypes.c_void_p(ev[2].cuda_event))
-                ev[0].record(stream)
+                lib.kivi_set_timing_events(h, ev[1].handle, ev[2].handle)
+                ev[0].record(sp)
             a = L["decode"]
             st = lib.kivi_append_decode_attn(a[0], new_tok[i][0], new_tok[i][1], ctypes.c_void_p(a[3]), a[4],
                                              a[5], ctypes.c_void_p(a[6]), a[7], ctypes.c_void_p(a[8]), a[9],
@@ -230,7 +261,7 @@ def run(args):
             if st != kivi.KIVI_OK:
                 raise kivi.KiviError(st, kivi.last_error_message())
             if evs is not None:
-                ev[3].record(stream)
+                ev[3].record(sp)
                 lib.kivi_set_timing_events(h, null, null)
 
     if args.copy_calibration:
@@ -269,10 +300,10 @@ def run(args):
     c0 = L0["cache"]
     for _ in range(args.cold_iters):
         scrub.fill_(1)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
+        e0, e1 = TimingEvent(), TimingEvent()
+        e0.record(sp)
         c0.decode_attn(L0["q"], scale, out=L0["out"])
-        e1.record(stream)
+        e1.record(sp)
         torch.cuda.synchronize()
         cold.append(e0.elapsed_time(e1) * 1e-3)
 
@@ -284,10 +315,10 @@ def run(args):
     wgs = 8 * torch.cuda.get_device_properties(dev).multi_processor_count
     sink = torch.empty(wgs * 256, dtype=torch.int32, device=dev)
     for _ in range(args.probe_iters):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
+        e0, e1 = TimingEvent(), TimingEvent()
+        e0.record(sp)
         kivi.kivi_stream_read_probe(src.data_ptr(), nbytes, sink.data_ptr(), sink.numel() * 4, wgs, sp)
-        e1.record(stream)
+        e1.record(sp)
         torch.cuda.synchronize()
         probe.append(e0.elapsed_time(e1) * 1e-3)
     del src, sink, scrub
@@ -296,15 +327,15 @@ def run(args):
     pack = []
     for _ in range(args.pack_iters):
         for L in layers:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0, e1 = TimingEvent(), TimingEvent()
             c = L["cache"]
             c.reset()
-            e0.record(stream)
+            e0.record(sp)
             if args.ragged:
                 c.append_varlen(L["kp"], L["vp"], lens)
             else:
                 kivi.kivi_append(c.handle, L["kp"].data_ptr(), L["vp"].data_ptr(), T, sp)
-            e1.record(stream)
+            e1.record(sp)
             torch.cuda.synchronize()
             pack.append(e0.elapsed_time(e1) * 1e-3)
     return w, wall, phase, cold, probe, nbytes, pack, layers, (lens if args.ragged else None)

@@ -363,7 +363,9 @@ kivi_status kivi_cache_get_view(const kivi_cache* cache, kivi_cache_view* view);
  * split_end right after it, before the merge (hipEvent_t handles passed as
  * void*, created by the caller; both or neither; NULL, NULL removes them).
  * Each record is a stream marker, so a marked launch starts a little later
- * than an unmarked one.  For caches of more than 64 sequences of different
+ * than an unmarked one; events created with hipEventDisableSystemFence skip
+ * the cache write-back and invalidation a default event's record performs,
+ * and bracket the kernel more tightly.  For caches of more than 64 sequences of different
  * lengths the events bracket the last launch pair's split kernel.
  * Errors: INVALID_ARG (null cache, only one event given). */
 kivi_status kivi_set_timing_events(kivi_cache* cache, void* split_begin, void* split_end);
