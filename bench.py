@@ -79,6 +79,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="c2", choices=["c0", "c1", "c2", "c3", "c4"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--settle-ms", type=float, default=100.0,
+                   help="untimed decode steps before the warm-up for this long (ms): from idle, the decode "
+                        "runs up to a third slower for the first ~30 ms of sustained load")
     p.add_argument("--phase-every", type=int, default=2,
                    help="bracket the launches with HIP events on every N-th timed step")
     p.add_argument("--pack-iters", type=int, default=20, help="timed prefix packs (all layers each)")
@@ -233,7 +236,7 @@ def run(args):
     # events of the marked steps: [0] before the call, [1] and [2] recorded by
     # the library right around the decode kernel, [3] after the call
     every = max(1, args.phase_every)
-    marked = list(range(0, args.steps, every))[:64]
+    marked = list(range(0, args.steps, every))[:256]
     events = {k: [[TimingEvent() for _ in range(4)] for _ in layers] for k in marked}
     for evs in events.values():
         for ev in evs:
@@ -272,13 +275,24 @@ def run(args):
         torch.cuda.synchronize()
         del src, dst
 
+    # Settle: from idle, MI355X runs the first ~30 ms of sustained load
+    # slower (a kernel trace of the c2 decode: 155-171 us at the start, 208 us
+    # after 3-7 ms, 163 us at 19 ms, 145-158 us from 40 ms on), so untimed
+    # steps run until the clocks have settled, then the W warm-up steps and
+    # the K timed ones.
+    settle_steps, t_settle = 0, time.perf_counter() + args.settle_ms * 1e-3
+    while time.perf_counter() < t_settle:
+        for _ in range(5):
+            step()
+        torch.cuda.synchronize()
+        settle_steps += 5
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
     # Each event record is a stream marker that the next launch waits for, so
     # the launches are bracketed on every `phase_every`-th timed step only (at
-    # most 64 of them); the other steps run back to back as a serving loop
+    # most 256 of them); the other steps run back to back as a serving loop
     # would.  `value` counts every timed step, marked or not.
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -338,7 +352,7 @@ def run(args):
             e1.record(sp)
             torch.cuda.synchronize()
             pack.append(e0.elapsed_time(e1) * 1e-3)
-    return w, wall, phase, cold, probe, nbytes, pack, layers, (lens if args.ragged else None)
+    return w, wall, phase, cold, probe, nbytes, pack, layers, (lens if args.ragged else None), settle_steps
 
 
 def cpu_baseline(w, layers, lens=None):
@@ -399,7 +413,7 @@ def main():
         sys.exit(2)
     import numpy as np
 
-    w, wall, phase, cold, probe, probe_bytes, pack, layers, lens = run(args)
+    w, wall, phase, cold, probe, probe_bytes, pack, layers, lens, settle_steps = run(args)
     ab = algorithmic_bytes(w, lens)
     kname, ksrc = decode_kernel(w)
     phases = {}
@@ -441,6 +455,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"ms": args.settle_ms, "steps": settle_steps},
         "ms_per_step": wall * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
