@@ -422,9 +422,9 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_dst, bool keep)
   }
 }
 
-// 16 bytes per lane from a unit's records to LDS through a buffer resource
+// 16 bytes per lane from a step's records to LDS through a buffer resource
 // (unit-major caches): byte offset voff (per lane) + soff (uniform) from the
-// unit's first record; the resource's size bounds every access.  Streaming
+// step's first record; the resource's size bounds every access.  Streaming
 // hint as in dma16.
 __device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, int voff, int soff, void* lds_dst, bool keep) {
   if (keep) {
@@ -434,11 +434,14 @@ __device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, int voff, in
   }
 }
 
-// Buffer resource over the nb records of one unit (gfx9 raw buffer: stride
-// 0, size in bytes, default data format word).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t unit_rsrc(const uint8_t* ubase, int nb, int block_bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(ubase), static_cast<short>(0), nb * block_bytes,
-                                           0x00020000);
+// Buffer resource over the records of the 4 streams of a step starting at
+// stream g0 of a unit-major unit (at most 4 records from the record of g0;
+// gfx9 raw buffer: stride 0, size in bytes, default data format word).  The
+// 64-bit base keeps the 32-bit offsets small for a unit of any size.
+template <int GT, int BYTES>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t step_rsrc(const uint8_t* ubase, int g0) {
+  const uint8_t* base = ubase + static_cast<size_t>(g0 / (GT / kStream)) * BYTES;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), static_cast<short>(0), 4 * BYTES, 0x00020000);
 }
 
 // Records of streams g0 .. g0 + 3 of unit u (unit-major, or through the
@@ -497,17 +500,17 @@ __device__ __forceinline__ void issue_kstage(const DecodeArgs& a, long long u, c
     // offsets in the per-lane operand; no address arithmetic on the vector
     // ALUs beyond the metadata lanes' record
     constexpr int SPB = GT / kStream;
-    const __amdgpu_buffer_rsrc_t r = unit_rsrc(ubase, a.nb, BL.bytes);
+    const __amdgpu_buffer_rsrc_t r = step_rsrc<GT, BL.bytes>(ubase, g0);
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi) {
       const int g = min(g0 + gi, g0 + ns - 1);
-      const int rec = (g / SPB) * BL.bytes + BL.k_codes + (g % SPB) * S::kGroup;
+      const int rec = (g / SPB - g0 / SPB) * BL.bytes + BL.k_codes + (g % SPB) * S::kGroup;
 #pragma unroll
       for (int j = 0; j < S::kGroup / 1024; ++j)
         dma16_buf(r, lane * 16, rec + j * 1024, dst + gi * S::kGroupPad + j * 1024, a.hg > 1);
     }
     const int gm = min(g0 + (lane >> 4), g0 + ns - 1);
-    const int voff = (gm / SPB) * BL.bytes + ((lane - 4 * (lane >> 4)) & 15) * 16;
+    const int voff = (gm / SPB - g0 / SPB) * BL.bytes + ((lane - 4 * (lane >> 4)) & 15) * 16;
     dma16_buf(r, voff, BL.k_scale, meta_dst, a.hg > 1);
     dma16_buf(r, voff, BL.k_zero, meta_dst + 4 * D * 2, a.hg > 1);
     return;
@@ -541,11 +544,11 @@ __device__ __forceinline__ void issue_vstage(const DecodeArgs& a, long long u, c
   const int lane = threadIdx.x & 63;
   if constexpr (!PAGED) {
     constexpr int SPB = GT / kStream;
-    const __amdgpu_buffer_rsrc_t r = unit_rsrc(ubase, a.nb, BL.bytes);
+    const __amdgpu_buffer_rsrc_t r = step_rsrc<GT, BL.bytes>(ubase, g0);
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi) {
       const int g = min(g0 + gi, g0 + ns - 1);
-      const int rec = (g / SPB) * BL.bytes + BL.v_codes + (g % SPB) * S::vGroup;
+      const int rec = (g / SPB - g0 / SPB) * BL.bytes + BL.v_codes + (g % SPB) * S::vGroup;
 #pragma unroll
       for (int j = 0; j < S::vGroup / 1024; ++j)
         dma16_buf(r, lane * 16, rec + j * 1024, dst + gi * S::vGroup + j * 1024, a.hg > 1);
@@ -553,7 +556,7 @@ __device__ __forceinline__ void issue_vstage(const DecodeArgs& a, long long u, c
     // scale and zero: see below
     const int c = lane & 15;
     const int gm = min(g0 + (lane >> 4), g0 + ns - 1);
-    const int voff = (gm / SPB) * BL.bytes +
+    const int voff = (gm / SPB - g0 / SPB) * BL.bytes +
                      ((32 * (c >> 2)) / GT * GT + kStream * (gm % SPB) + 8 * (c & 3)) * 2;
     dma16_buf(r, voff, BL.v_scale, dst + S::offVS, a.hg > 1);
     dma16_buf(r, voff, BL.v_zero, dst + S::offVZ, a.hg > 1);
