@@ -51,7 +51,16 @@ class TimingEvent:
 
     def __init__(self):
         if TimingEvent._hip is None:
-            hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime already in the process
+            # the runtime torch has already loaded (found by its soname)
+            hip = None
+            for name in ("libamdhip64.so.7", "libamdhip64.so"):
+                try:
+                    hip = ctypes.CDLL(name)
+                    break
+                except OSError:
+                    continue
+            if hip is None:
+                raise RuntimeError("HIP runtime library not found")
             hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
             hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
             hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
