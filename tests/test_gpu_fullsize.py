@@ -140,3 +140,49 @@ def _sampled_parity(w, name, paged=False):
         err = np.abs(o_got - o_ref).max()
         print(f"workload {name}: unit {u} attention max abs error {err:.2e}", flush=True)
         assert err <= TOL
+
+
+def test_unit_beyond_2gib_of_records():
+    """One (batch, kv head) unit whose block records span more than 2 GiB: 22.4M
+    tokens at 2/2 bits, 3 KiB per 32-token record, so offsets inside the unit
+    pass 2^31 bytes.  The decode over the unit-major records (stages loaded
+    through buffer resources based at each step's first record) equals, bit for
+    bit, the decode of the same records through an identity page table (global
+    loads with 64-bit addresses); sampled records (the first, one in the middle
+    and the last two, beyond 2 GiB) equal the oracle's packing of their own 32
+    tokens, since quantization is local to a block.  (The oracle over all 22.4M
+    tokens would take minutes.)"""
+    from tests.gpu_helpers import natural_key_meta
+    nblk = 700_416  # 700 416 x 3072 B > 2^31
+    T, G, D, Hq = nblk * 32, 32, 128, 4
+    print(f"unit beyond 2 GiB: T={T}, {nblk} records of 3072 B ({nblk * 3072 / 2**30:.2f} GiB)", flush=True)
+    gen = torch.Generator(device=DEV).manual_seed(11)
+    k = (torch.randn(1, 1, T + 1, D, generator=gen, device=DEV) * 1.5).to(torch.float16)
+    v = torch.randn(1, 1, T + 1, D, generator=gen, device=DEV).to(torch.float16)
+    q = torch.randn(1, Hq, D, generator=gen, device=DEV).to(torch.float16)
+    c = kivi.KiviCache(1, 1, T + 1, k_bits=2, v_bits=2, residual_length=128, dtype=torch.float16, device=DEV)
+    c.append(k[:, :, :T].contiguous(), v[:, :, :T].contiguous())
+    c.append(k[:, :, T:].contiguous(), v[:, :, T:].contiguous())
+    assert c.lengths() == ([T], [1])
+    scale = 1.0 / np.sqrt(D)
+    o_unit = c.decode_attn(q, scale).clone()
+    nb = c.view().num_blocks
+    c.set_page_table(torch.arange(nb, dtype=torch.int32, device=DEV)[None].contiguous(), nb)
+    o_paged = c.decode_attn(q, scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o_unit).all()
+    assert torch.equal(o_unit, o_paged), "unit-major and paged decodes of the same records differ"
+    a = c.arrays()
+    for g in (0, nblk // 2, nblk - 2, nblk - 1):
+        ref = oracle.OracleCache(1, 1, D, G + 1, 2, 2, G, G, oracle.F16)
+        ref.append(bits16(k[:, :, g * G:g * G + G + 1].cpu()), bits16(v[:, :, g * G:g * G + G + 1].cpu()))
+        assert (ref.n_quant, ref.n_resid) == (G, 1)
+        want = oracle_arrays(ref)
+        got = {n: a[n][0, g].contiguous().cpu().numpy().reshape(1, -1) for n in
+               ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero")}
+        got = {n: x.view(np.uint32) if "codes" in n else x.view(np.uint16) for n, x in got.items()}
+        got["k_scale"], got["k_zero"] = natural_key_meta(got["k_scale"]), natural_key_meta(got["k_zero"])
+        for n, x in got.items():
+            w = want[n][:, :x.shape[1]]
+            assert np.array_equal(x, w), f"record {g}: {n} differs from the oracle"
+    print(f"unit beyond 2 GiB: decodes bit-identical, 4 sampled records match the oracle", flush=True)
