@@ -408,30 +408,27 @@ static_assert(Stage<2, 4>::bytes == mfma_wg_lds_bytes(2, 4), "lds");
 static_assert(Stage<4, 2>::bytes == mfma_wg_lds_bytes(4, 2), "lds");
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef const __attribute__((address_space(1))) void glb_void_t;
 
 // 16 bytes per lane from global memory to LDS.  Records are read once, with
-// the streaming hint (nt), unless several head groups read them (`keep`):
-// the other workgroups of the pair then find them in the XCD's L2.
-__device__ __forceinline__ void dma16(const void* src, void* lds_dst, bool keep) {
+// the streaming hint (nt), unless several head groups read them (KEEP): the
+// other workgroups of the pair then find them in the XCD's L2.  (The hint is
+// an immediate of the instruction, hence a template argument: a run-time
+// flag costs a branch around every load.)
+template <bool KEEP>
+__device__ __forceinline__ void dma16(const void* src, lds_u8* lds_dst) {
   // address-space conversions need C-style casts
-  if (keep) {
-    __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)lds_dst, 16, 0, 0);
-  } else {
-    __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)lds_dst, 16, 0, 2);
-  }
+  __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)lds_dst, 16, 0, KEEP ? 0 : 2);
 }
 
 // 16 bytes per lane from a step's records to LDS through a buffer resource
 // (unit-major caches): byte offset voff (per lane) + soff (uniform) from the
 // step's first record; the resource's size bounds every access.  Streaming
 // hint as in dma16.
-__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, int voff, int soff, void* lds_dst, bool keep) {
-  if (keep) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_dst, 16, voff, soff, 0, 0);
-  } else {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_dst, 16, voff, soff, 0, 2);
-  }
+template <bool KEEP>
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, int voff, int soff, lds_u8* lds_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_dst, 16, voff, soff, 0, KEEP ? 0 : 2);
 }
 
 // Buffer resource over the records of the 4 streams of a step starting at
@@ -487,11 +484,28 @@ __device__ __forceinline__ int lane_half(int g0, int ns, int spb, int lane) {
   return min(g0 + (lane >> 4), g0 + ns - 1) % spb;
 }
 
+// Byte offset, from the record of stream g0, of the record holding stream
+// g0 + min(i, ns - 1) and the index of that stream inside its record
+// (unit-major records lie BYTES apart).
+template <int GT, int BYTES>
+__device__ __forceinline__ int stream_record(int g0, int i, int ns, int& half) {
+  const int c = min(i, ns - 1);
+  if constexpr (GT == kStream) {
+    half = 0;
+    return c * BYTES;
+  } else {
+    constexpr int SPB = GT / kStream;
+    const int g = g0 + c;
+    half = g % SPB;
+    return (g / SPB - g0 / SPB) * BYTES;
+  }
+}
+
 // Key stage of streams [g0, g0 + ns): codes to `dst`, scale and zero to
 // `meta`; Stage::kLoads instructions.
-template <int KB, int VB, int GT, bool PAGED>
+template <int KB, int VB, int GT, bool PAGED, bool KEEP>
 __device__ __forceinline__ void issue_kstage(const DecodeArgs& a, long long u, const uint8_t* ubase, int g0, int ns,
-                                             uint8_t* dst, uint8_t* meta_dst) {
+                                             lds_u8* dst, lds_u8* meta_dst) {
   using S = Stage<KB, VB>;
   constexpr BlockLayout BL = block_layout(KB, VB, GT);
   const int lane = threadIdx.x & 63;
@@ -499,20 +513,19 @@ __device__ __forceinline__ void issue_kstage(const DecodeArgs& a, long long u, c
     // unit-major: record offsets from the stream index (uniform), lane
     // offsets in the per-lane operand; no address arithmetic on the vector
     // ALUs beyond the metadata lanes' record
-    constexpr int SPB = GT / kStream;
     const __amdgpu_buffer_rsrc_t r = step_rsrc<GT, BL.bytes>(ubase, g0);
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi) {
-      const int g = min(g0 + gi, g0 + ns - 1);
-      const int rec = (g / SPB - g0 / SPB) * BL.bytes + BL.k_codes + (g % SPB) * S::kGroup;
+      int hf;
+      const int rec = stream_record<GT, BL.bytes>(g0, gi, ns, hf) + BL.k_codes + hf * S::kGroup;
 #pragma unroll
       for (int j = 0; j < S::kGroup / 1024; ++j)
-        dma16_buf(r, lane * 16, rec + j * 1024, dst + gi * S::kGroupPad + j * 1024, a.hg > 1);
+        dma16_buf<KEEP>(r, lane * 16, rec + j * 1024, dst + gi * S::kGroupPad + j * 1024);
     }
-    const int gm = min(g0 + (lane >> 4), g0 + ns - 1);
-    const int voff = (gm / SPB - g0 / SPB) * BL.bytes + ((lane - 4 * (lane >> 4)) & 15) * 16;
-    dma16_buf(r, voff, BL.k_scale, meta_dst, a.hg > 1);
-    dma16_buf(r, voff, BL.k_zero, meta_dst + 4 * D * 2, a.hg > 1);
+    int hm;
+    const int voff = stream_record<GT, BL.bytes>(g0, lane >> 4, ns, hm) + ((lane - 4 * (lane >> 4)) & 15) * 16;
+    dma16_buf<KEEP>(r, voff, BL.k_scale, meta_dst);
+    dma16_buf<KEEP>(r, voff, BL.k_zero, meta_dst + 4 * D * 2);
     return;
   }
   const uint8_t* rp[4];
@@ -522,8 +535,7 @@ __device__ __forceinline__ void issue_kstage(const DecodeArgs& a, long long u, c
   for (int gi = 0; gi < 4; ++gi) {
 #pragma unroll
     for (int j = 0; j < S::kGroup / 1024; ++j)  // a stream's rows: kGroup bytes from row 32 * hf
-      dma16(rp[gi] + BL.k_codes + hf[gi] * S::kGroup + j * 1024 + lane * 16,
-            dst + gi * S::kGroupPad + j * 1024, a.hg > 1);
+      dma16<KEEP>(rp[gi] + BL.k_codes + hf[gi] * S::kGroup + j * 1024 + lane * 16, dst + gi * S::kGroupPad + j * 1024);
   }
   // scale and zero of the stream's block: 256 bytes per stream and field, 16
   // lanes per stream.  Stream i's 16-byte chunk j lands in LDS slot
@@ -531,35 +543,34 @@ __device__ __forceinline__ void issue_kstage(const DecodeArgs& a, long long u, c
   // 4 lk + c of four streams at once, which then fall on distinct banks.
   const uint8_t* const meta =
       lane_record<KB, VB, GT, PAGED>(rp, g0, ns, lane) + ((lane - 4 * (lane >> 4)) & 15) * 16;
-  dma16(meta + BL.k_scale, meta_dst, a.hg > 1);
-  dma16(meta + BL.k_zero, meta_dst + 4 * D * 2, a.hg > 1);
+  dma16<KEEP>(meta + BL.k_scale, meta_dst);
+  dma16<KEEP>(meta + BL.k_zero, meta_dst + 4 * D * 2);
 }
 
 // Value stage of groups [g0, g0 + ns): Stage::vLoads instructions.
-template <int KB, int VB, int GT, bool PAGED>
+template <int KB, int VB, int GT, bool PAGED, bool KEEP>
 __device__ __forceinline__ void issue_vstage(const DecodeArgs& a, long long u, const uint8_t* ubase, int g0, int ns,
-                                             uint8_t* dst) {
+                                             lds_u8* dst) {
   using S = Stage<KB, VB>;
   constexpr BlockLayout BL = block_layout(KB, VB, GT);
   const int lane = threadIdx.x & 63;
   if constexpr (!PAGED) {
-    constexpr int SPB = GT / kStream;
     const __amdgpu_buffer_rsrc_t r = step_rsrc<GT, BL.bytes>(ubase, g0);
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi) {
-      const int g = min(g0 + gi, g0 + ns - 1);
-      const int rec = (g / SPB - g0 / SPB) * BL.bytes + BL.v_codes + (g % SPB) * S::vGroup;
+      int hf;
+      const int rec = stream_record<GT, BL.bytes>(g0, gi, ns, hf) + BL.v_codes + hf * S::vGroup;
 #pragma unroll
       for (int j = 0; j < S::vGroup / 1024; ++j)
-        dma16_buf(r, lane * 16, rec + j * 1024, dst + gi * S::vGroup + j * 1024, a.hg > 1);
+        dma16_buf<KEEP>(r, lane * 16, rec + j * 1024, dst + gi * S::vGroup + j * 1024);
     }
     // scale and zero: see below
     const int c = lane & 15;
-    const int gm = min(g0 + (lane >> 4), g0 + ns - 1);
-    const int voff = (gm / SPB - g0 / SPB) * BL.bytes +
-                     ((32 * (c >> 2)) / GT * GT + kStream * (gm % SPB) + 8 * (c & 3)) * 2;
-    dma16_buf(r, voff, BL.v_scale, dst + S::offVS, a.hg > 1);
-    dma16_buf(r, voff, BL.v_zero, dst + S::offVZ, a.hg > 1);
+    int hm;
+    const int voff = stream_record<GT, BL.bytes>(g0, lane >> 4, ns, hm) +
+                     ((32 * (c >> 2)) / GT * GT + kStream * hm + 8 * (c & 3)) * 2;
+    dma16_buf<KEEP>(r, voff, BL.v_scale, dst + S::offVS);
+    dma16_buf<KEEP>(r, voff, BL.v_zero, dst + S::offVZ);
     return;
   }
   const uint8_t* rp[4];
@@ -569,8 +580,7 @@ __device__ __forceinline__ void issue_vstage(const DecodeArgs& a, long long u, c
   for (int gi = 0; gi < 4; ++gi) {
 #pragma unroll
     for (int j = 0; j < S::vGroup / 1024; ++j)  // the stream's words: vGroup bytes from word row hf * VB
-      dma16(rp[gi] + BL.v_codes + hf[gi] * S::vGroup + j * 1024 + lane * 16, dst + gi * S::vGroup + j * 1024,
-            a.hg > 1);
+      dma16<KEEP>(rp[gi] + BL.v_codes + hf[gi] * S::vGroup + j * 1024 + lane * 16, dst + gi * S::vGroup + j * 1024);
   }
   // scale and zero of the stream's 32 tokens, stage layout [stream][4 channel
   // groups of 32][32 tokens]; a block stores [D / G][G], so with G = 64 two
@@ -579,8 +589,8 @@ __device__ __forceinline__ void issue_vstage(const DecodeArgs& a, long long u, c
   const int c = lane & 15;
   const int off = ((32 * (c >> 2)) / GT * GT + kStream * lane_half(g0, ns, GT / kStream, lane) + 8 * (c & 3)) * 2;
   const uint8_t* const meta = lane_record<KB, VB, GT, PAGED>(rp, g0, ns, lane) + off;
-  dma16(meta + BL.v_scale, dst + S::offVS, a.hg > 1);
-  dma16(meta + BL.v_zero, dst + S::offVZ, a.hg > 1);
+  dma16<KEEP>(meta + BL.v_scale, dst + S::offVS);
+  dma16<KEEP>(meta + BL.v_zero, dst + S::offVZ);
 }
 
 // ---------------------------------------------------------------------------
@@ -678,9 +688,9 @@ __device__ __forceinline__ int range_exp(float x) { return max(-30, __builtin_am
 // ---------------------------------------------------------------------------
 // Key wave: scores of each step on the matrix cores, online softmax, and the
 // probabilities handed to the value wave.  Writes m and l of the partial.
-template <int KB, int VB, bool BF16, int NQ, int GT, bool PAGED>
+template <int KB, int VB, bool BF16, int NQ, int GT, bool PAGED, bool KEEP>
 __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b, int h0, int split,
-                                         int gb, int ge, int n_steps, int rot, uint8_t* smem) {
+                                         int gb, int ge, int n_steps, int rot, uint8_t* smem, lds_u8* lsm) {
   using S = Stage<KB, VB>;
   using KS = CodeScale<KB>;
   constexpr int KL = KB;  // key words per lane (32 channels)
@@ -712,7 +722,7 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
   // the first stage's loads go out before q is read: their latencies overlap
   {
     const int f0 = step_first(gb, 0, n_steps, rot);
-    issue_kstage<KB, VB, GT, PAGED>(a, u, ubase, f0, min(4, ge - f0), smem, smem + S::offKM0);
+    issue_kstage<KB, VB, GT, PAGED, KEEP>(a, u, ubase, f0, min(4, ge - f0), lsm, lsm + S::offKM0);
   }
   // q of head hsrc, channels 32*lk .. 32*lk+31 (unused head slots: zeros)
   float qf[32];
@@ -816,8 +826,8 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
     wave_lds_sync();
     if (step + 1 < n_steps) {
       const int g1 = step_first(gb, step + 1, n_steps, rot);
-      issue_kstage<KB, VB, GT, PAGED>(a, u, ubase, g1, min(4, ge - g1), smem,
-                                      smem + S::offKM0 + ((step + 1) & 1) * S::kMetaBytes);
+      issue_kstage<KB, VB, GT, PAGED, KEEP>(a, u, ubase, g1, min(4, ge - g1), lsm,
+                                            lsm + S::offKM0 + ((step + 1) & 1) * S::kMetaBytes);
     }
     // B = q' * S (hi, lo) for head hq and group g0 + gc, built per block of
     // 32 channels right before its products (the vector work of block c+1
@@ -991,9 +1001,9 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
 // ---------------------------------------------------------------------------
 // Value wave: p.V of each step on the matrix cores, one step behind the key
 // wave.  Writes o of the partial; the last split also runs the window.
-template <int KB, int VB, bool BF16, int NQ, int GT, bool PAGED>
+template <int KB, int VB, bool BF16, int NQ, int GT, bool PAGED, bool KEEP>
 __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int b, int h0, int split,
-                                           int gb, int ge, int n_steps, int rot, uint8_t* smem) {
+                                           int gb, int ge, int n_steps, int rot, uint8_t* smem, lds_u8* lsm) {
   using S = Stage<KB, VB>;
   using VS = CodeScale<VB>;
   const int lane = threadIdx.x & 63;
@@ -1008,11 +1018,12 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
   const int hsrc = kHiLoCols ? hq % NQ : hq;  // head whose probabilities this column takes
   const int part = kHiLoCols ? hq / NQ : 0;   // 0: hi, 1: lo, 2 and 3 (NQ = 1): unused
   uint8_t* const vbase = smem + S::offV0;
+  lds_u8* const lvbase = lsm + S::offV0;
   constexpr BlockLayout BLu = block_layout(KB, VB, GT);
   const uint8_t* const ubase = a.blocks + static_cast<size_t>(u) * a.nb * BLu.bytes;  // (unit-major)
   {
     const int f0 = step_first(gb, 0, n_steps, rot);
-    issue_vstage<KB, VB, GT, PAGED>(a, u, ubase, f0, min(4, ge - f0), vbase);
+    issue_vstage<KB, VB, GT, PAGED, KEEP>(a, u, ubase, f0, min(4, ge - f0), lvbase);
   }
   constexpr float v_unscale = static_cast<float>(1 << (15 - VS::F));  // product -> output
 
@@ -1027,7 +1038,7 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
     const bool more = step + 1 < n_steps;
     if (more) {
       const int g1 = step_first(gb, step + 1, n_steps, rot);
-      issue_vstage<KB, VB, GT, PAGED>(a, u, ubase, g1, min(4, ge - g1), vbase + ((step + 1) & 1) * S::vBytes);
+      issue_vstage<KB, VB, GT, PAGED, KEEP>(a, u, ubase, g1, min(4, ge - g1), lvbase + ((step + 1) & 1) * S::vBytes);
     }
     wg_barrier();  // the key wave has written this step's probabilities
     if (more) {
@@ -1180,10 +1191,11 @@ __device__ __forceinline__ unsigned pair_of(unsigned w, int hg, int& g) {
   return (w / (8u * hg)) * 8u + (w & 7u);
 }
 
-template <int KB, int VB, bool BF16, int NQ, int GT, bool PAGED>
+template <int KB, int VB, bool BF16, int NQ, int GT, bool PAGED, bool KEEP>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma(DecodeArgs a) {
   using S = Stage<KB, VB>;
   __shared__ __align__(16) uint8_t smem[S::bytes];
+  lds_u8* const lsm = (lds_u8*)smem;  // (C-style: an address-space conversion)
   const int wave = threadIdx.x >> 6;  // 0: key wave, 1: value wave
   const int nx = a.n_split_packed > 0 ? a.n_split_packed : 1;
   int hgi;
@@ -1220,9 +1232,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
       const int rot = static_cast<int>(P % static_cast<unsigned>(n_steps));
       // Both waves run the same number of steps and meet at one barrier per step.
       if (wave == 0) {
-        key_wave<KB, VB, BF16, NQ, GT, PAGED>(a, u, b, h0, split, gb, ge, n_steps, rot, smem);
+        key_wave<KB, VB, BF16, NQ, GT, PAGED, KEEP>(a, u, b, h0, split, gb, ge, n_steps, rot, smem, lsm);
       } else {
-        value_wave<KB, VB, BF16, NQ, GT, PAGED>(a, u, b, h0, split, gb, ge, n_steps, rot, smem);
+        value_wave<KB, VB, BF16, NQ, GT, PAGED, KEEP>(a, u, b, h0, split, gb, ge, n_steps, rot, smem, lsm);
       }
     }
   }
@@ -1239,17 +1251,26 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
   }
 }
 
-template <int KB, int VB, bool BF16, int NQ, int GT, bool PAGED>
-hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
+template <int KB, int VB, bool BF16, int NQ, int GT, bool PAGED, bool KEEP>
+hipError_t launch_k(const DecodeArgs& a, hipStream_t stream) {
   // one workgroup per packed split (per head group), one split when nothing
   // is packed; the last one also runs the window.  A ragged launch covers
   // a.B sequences from a.seq0.
   const long long pairs = (long long)(a.n_split_packed > 0 ? a.n_split_packed : 1) * a.B * a.H;
   const long long grid = a.hg == 1 ? pairs : (pairs + 7) / 8 * 8 * a.hg;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((decode_mfma<KB, VB, BF16, NQ, GT, PAGED>), dim3(static_cast<unsigned>(grid)), dim3(128), 0,
+  hipLaunchKernelGGL((decode_mfma<KB, VB, BF16, NQ, GT, PAGED, KEEP>), dim3(static_cast<unsigned>(grid)), dim3(128), 0,
                      stream, a);
   return hipGetLastError();
+}
+
+template <int KB, int VB, bool BF16, int NQ, int GT, bool PAGED>
+hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
+  // head groups (only with 4 heads per workgroup) keep the records in L2
+  if constexpr (NQ == 4) {
+    if (a.hg > 1) return launch_k<KB, VB, BF16, NQ, GT, PAGED, true>(a, stream);
+  }
+  return launch_k<KB, VB, BF16, NQ, GT, PAGED, false>(a, stream);
 }
 
 template <int KB, int VB, bool BF16, int NQ>
