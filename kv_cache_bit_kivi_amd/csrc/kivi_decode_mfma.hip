@@ -1017,6 +1017,7 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
   constexpr bool kHiLoCols = NQ <= 2;
   const int hsrc = kHiLoCols ? hq % NQ : hq;  // head whose probabilities this column takes
   const int part = kHiLoCols ? hq / NQ : 0;   // 0: hi, 1: lo, 2 and 3 (NQ = 1): unused
+  const uint32_t pmask = (part & 1) ? 0xffffffffu : 0u;  // (kHiLoCols) this column's half, see products
   uint8_t* const vbase = smem + S::offV0;
   lds_u8* const lvbase = lsm + S::offV0;
   constexpr BlockLayout BLu = block_layout(KB, VB, GT);
@@ -1073,17 +1074,23 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
         uint32_t hi, lo;
         const float b0 = (e & 1) ? times_half<1>(p[e], vs[e >> 1]) : times_half<0>(p[e], vs[e >> 1]);
         const float b1 = (e & 1) ? times_half<1>(p[e + 4], vs[2 + (e >> 1)]) : times_half<0>(p[e + 4], vs[2 + (e >> 1)]);
-        split_pair(b0, b1, hi, lo);
-        h4[e] = hi;
-        l4[e] = lo;
+        if constexpr (kHiLoCols) {
+          // this lane's half only: RN(b - RN(b) & mask), the hi half with
+          // mask 0 and the lo half with mask ~0 (columns of slots past the lo
+          // ones take either; their sums are never read)
+          hi = pk_rne(b0, b1);
+          const uint32_t hm = hi & pmask;
+          h4[e] = pk_rne(minus_half<0>(hm, b0), minus_half<1>(hm, b1));
+        } else {
+          split_pair(b0, b1, hi, lo);
+          h4[e] = hi;
+          l4[e] = lo;
+        }
         zcls[e] = fmaf(p[2 * e], lo_half(vz[e]), zcls[e]);
         zcls[e] = fmaf(p[2 * e + 1], hi_half(vz[e]), zcls[e]);
       }
       if constexpr (kHiLoCols) {
-        u32x4 b4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) b4[e] = part == 0 ? h4[e] : part == 1 ? l4[e] : 0u;
-        const half8_t bp = as_h8(b4);
+        const half8_t bp = as_h8(h4);
 #pragma unroll
         for (int be = 0; be < 8; ++be) o[be] = mfma(av[be], bp, o[be]);
       } else {
