@@ -662,9 +662,9 @@ kivi_status plan_decode(const kivi_cache* c, const DecodeState& st, int gq, Deco
   const int G = kivi::kStream;
   const int units = c->cfg.batch * c->cfg.num_kv_heads;
   const int nqg = st.n_quant / G;
-  // a workgroup serves up to 4 query heads of its kv head; 8 or 16 take 2 or
-  // 4 workgroups (head groups) per split
-  const int hg = gq > 4 ? gq / 4 : 1;
+  // a workgroup serves up to 8 query heads of its kv head; 16 take 2
+  // workgroups (head groups) per split
+  const int hg = gq > 8 ? gq / 8 : 1;
   int n_split_packed = 0, gps = 0;
   // one workgroup (key wave + value wave) per split and head group; one
   // round of as many as fit in LDS on every CU, each split a multiple of 4
@@ -674,7 +674,7 @@ kivi_status plan_decode(const kivi_cache* c, const DecodeState& st, int gq, Deco
     // resident workgroups per CU: LDS, and at most 6 (3 waves per SIMD at
     // the kernel's register budget)
     const int wgs_per_cu = std::max(
-        1, std::min(6, kivi::kLdsPerCu / kivi::mfma_wg_lds_bytes(c->cfg.k_bits, c->cfg.v_bits)));
+        1, std::min(6, kivi::kLdsPerCu / kivi::mfma_wg_lds_bytes(c->cfg.k_bits, c->cfg.v_bits, gq >= 8 ? 8 : 4)));
     const long long slots = (long long)wgs_per_cu * c->cu_count;
     const int max_split = std::max(1, std::min((nqg + 3) / 4, kivi::kMaxSplits - 1));
     auto plan = [&](int want, int& g, int& np) {

@@ -1,9 +1,10 @@
 // kivi_decode_mfma.hip - decode attention with both contractions on the
 // matrix cores, for 1, 2, 4, 8 or 16 query heads per kv head (multi-head and
-// grouped-query attention).  The matrix columns hold 4 head slots; with
-// fewer heads the spare slots carry zeros and are masked out, and 8 or 16
-// heads take 2 or 4 workgroups (head groups) per split, launched side by side
-// on one XCD so that the second reads the records from its L2.
+// grouped-query attention).  A workgroup serves up to 4 query heads in 4 head
+// slots of the matrix columns (spare slots carry zeros and are masked out),
+// or 8 in the eight-head layout (key_wave8, value_wave8); 16 heads take 2
+// workgroups (head groups) per split, launched side by side on one XCD so
+// that the second reads the records from its L2.
 //
 // Method: split-K decode attention over the packed cache (dequantized value =
 // code * scale + zero, page "KIVI: Asymmetric 2-Bit KV Cache Quantization
@@ -219,6 +220,16 @@ __device__ __forceinline__ float partner(float v) {
   }
 }
 
+// Reductions over the 16 lanes of a DPP row (lanes 16 r .. 16 r + 15): the
+// quad exchanges (lane ^ 1, lane ^ 2) leave each lane its quad's result, the
+// half-row mirror (lane i <-> 7 - i of each 8) combines the two quads of a
+// half row and the row mirror (i <-> 15 - i) the two halves.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
 // max(a, b) as one v_max_f32: the operands are scores or -inf, never NaN, so
 // the NaN quieting the compiler adds to fmaxf (one more instruction per
 // operand that it cannot prove canonical, such as a cross-lane result) is
@@ -243,6 +254,18 @@ __device__ __forceinline__ float swap_sum(float v) {
   auto r = (M == 16) ? __builtin_amdgcn_permlane16_swap(x, x, false, false)
                      : __builtin_amdgcn_permlane32_swap(x, x, false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float row_max16(float v) {
+  v = max_raw(v, partner<1>(v));
+  v = max_raw(v, partner<2>(v));
+  v = max_raw(v, dpp_f<kDppHalfMirror>(v));
+  return max_raw(v, dpp_f<kDppMirror>(v));
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v = v + partner<1>(v);
+  v = v + partner<2>(v);
+  v = v + dpp_f<kDppHalfMirror>(v);
+  return v + dpp_f<kDppMirror>(v);
 }
 __device__ __forceinline__ float xor_max(float v, int m) { return fmaxf(v, __shfl_xor(v, m)); }
 __device__ __forceinline__ float xor_sum(float v, int m) { return v + __shfl_xor(v, m); }
@@ -382,7 +405,8 @@ __device__ void window_wave(const DecodeArgs& a, long long u, int b, int h0, int
 //   hand-over   x2: scores, then in place probabilities [stream][head][kRowP]
 //               fp32, and the rescale factor of each head, written by the key
 //               wave.
-template <int KB, int VB>
+// NH: query heads of a workgroup (4, or 8 in the eight-head layout).
+template <int KB, int VB, int NH = GQ>
 struct Stage {
   static constexpr int kRow = D * KB / 8;              // bytes per key row
   static constexpr int kGroup = G * kRow;              // 1 or 2 KiB
@@ -393,19 +417,23 @@ struct Stage {
   static constexpr int vGroup = (G * VB / 32) * D * 4; // 1 or 2 KiB
   static constexpr int offVS = 4 * vGroup, offVZ = offVS + 4 * D * 2;
   static constexpr int vBytes = offVZ + 4 * D * 2;
-  static constexpr int offAlpha = 4 * GQ * kRowP * 4;   // in a hand-over buffer
-  static constexpr int offBias = offAlpha + 16;          // zero-point terms [stream][head]
-  static constexpr int pBytes = offBias + 16 * 4;
+  static constexpr int offAlpha = 4 * NH * kRowP * 4;   // in a hand-over buffer
+  static constexpr int offBias = offAlpha + 4 * NH;      // zero-point terms [stream][head]
+  static constexpr int pBytes = offBias + 4 * NH * 4;
   static constexpr int offV0 = offKM0 + 2 * kMetaBytes, offP0 = offV0 + 2 * vBytes;
   static constexpr int bytes = offP0 + 2 * pBytes;     // LDS per workgroup
   static constexpr int kLoads = (4 * kGroup + 2 * 4 * D * 2) / 1024;  // DMA instructions
   static constexpr int vLoads = (4 * vGroup + 2 * 4 * D * 2) / 1024;
-  static_assert(vBytes >= (GQ * D + GQ * G) * 4, "window scratch fits in a value stage");
+  static_assert(vBytes >= (NH * D + NH * G) * 4, "window scratch fits in a value stage");
 };
-static_assert(Stage<2, 2>::bytes == mfma_wg_lds_bytes(2, 2), "lds");
-static_assert(Stage<4, 4>::bytes == mfma_wg_lds_bytes(4, 4), "lds");
-static_assert(Stage<2, 4>::bytes == mfma_wg_lds_bytes(2, 4), "lds");
-static_assert(Stage<4, 2>::bytes == mfma_wg_lds_bytes(4, 2), "lds");
+static_assert(Stage<2, 2>::bytes == mfma_wg_lds_bytes(2, 2, 4), "lds");
+static_assert(Stage<4, 4>::bytes == mfma_wg_lds_bytes(4, 4, 4), "lds");
+static_assert(Stage<2, 4>::bytes == mfma_wg_lds_bytes(2, 4, 4), "lds");
+static_assert(Stage<4, 2>::bytes == mfma_wg_lds_bytes(4, 2, 4), "lds");
+static_assert(Stage<2, 2, 8>::bytes == mfma_wg_lds_bytes(2, 2, 8), "lds");
+static_assert(Stage<4, 4, 8>::bytes == mfma_wg_lds_bytes(4, 4, 8), "lds");
+static_assert(Stage<2, 4, 8>::bytes == mfma_wg_lds_bytes(2, 4, 8), "lds");
+static_assert(Stage<4, 2, 8>::bytes == mfma_wg_lds_bytes(4, 2, 8), "lds");
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -1181,10 +1209,366 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
   }
 }
 
+// ---------------------------------------------------------------------------
+// Eight query heads per workgroup (8 or 16 per kv head).  The key products
+// put the dense operand in the rows, 8 heads x (hi, lo) = all 16, and the
+// codes of 16 tokens of one stream in the columns, so no product is wasted
+// and the codes of a record are converted once for all 8 heads (with 4 heads
+// per workgroup two workgroups converted them each).  Output lane (lk, lc)
+// then holds, for token lc of each (stream, tile of 16 tokens), the hi and
+// lo sums of heads 2 lk and 2 lk + 1: its 16 scores, no LDS round trip.  The
+// value products keep the codes as rows (16 channels, two channel groups per
+// tile) and take as columns 8 heads x the tile's 2 channel groups: half of
+// each product's sums are used (a quarter with 4 heads).
+template <int KB, int VB, bool BF16, int GT, bool PAGED, bool KEEP>
+__device__ __forceinline__ void key_wave8(const DecodeArgs& a, long long u, int b, int h0, int split,
+                                          int gb, int ge, int n_steps, int rot, uint8_t* smem, lds_u8* lsm) {
+  using S = Stage<KB, VB, 8>;
+  using KS = CodeScale<KB>;
+  constexpr int KL = KB;  // key words per lane (32 channels)
+  const int lane = threadIdx.x & 63;
+  const int lc = lane & 15, lk = lane >> 4;
+  const int hr = lc >> 1, part = lc & 1;  // A row lc: half `part` of head hr's q'' * S
+  constexpr BlockLayout BLu = block_layout(KB, VB, GT);
+  const uint8_t* const ubase = a.blocks + static_cast<size_t>(u) * a.nb * BLu.bytes;  // (unit-major)
+  {
+    const int f0 = step_first(gb, 0, n_steps, rot);
+    issue_kstage<KB, VB, GT, PAGED, KEEP>(a, u, ubase, f0, min(4, ge - f0), lsm, lsm + S::offKM0);
+  }
+  // q of head hr, channels 32 lk .. 32 lk + 31
+  float qf[32];
+  {
+    const uint16_t* qp = a.q + ((long long)b * a.Hq + h0 + hr) * D + 32 * lk;
+#pragma unroll
+    for (int i = 0; i < 32; i += 8) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qp + i);
+      const uint32_t ww[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qf[i + 2 * e] = to_f32<BF16>(static_cast<uint16_t>(ww[e]));
+        qf[i + 2 * e + 1] = to_f32<BF16>(static_cast<uint16_t>(ww[e] >> 16));
+      }
+    }
+  }
+  float sk_max, sv_max;
+  split_scale_max<GT, PAGED>(a, u, gb, ge, sk_max, sv_max);
+  float qabs = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) qabs = fmaxf(qabs, fabsf(qf[i]));
+  qabs = swap_max<16>(qabs);
+  qabs = swap_max<32>(qabs);  // the 128 channels of head hr
+  const int ek = range_exp(qabs * fmaxf(sk_max, 1.0f));
+  const int ev = range_exp(sv_max);
+  // exponents of the two heads whose scores this lane holds (lane 2 h has head h's)
+  const int ek0 = __shfl(ek, 4 * lk), ek1 = __shfl(ek, 4 * lk + 2);
+  uint32_t q2[16];  // pair 4 c + a: channels 8 c + a and 8 c + a + 4 of the lane's 32 (see codes8)
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      q2[4 * c + e] =
+          pk_rne(__builtin_amdgcn_ldexpf(qf[8 * c + e], -ek), __builtin_amdgcn_ldexpf(qf[8 * c + e + 4], -ek));
+  const uint32_t qmask = part ? 0xffffffffu : 0u;  // hi (RN(q'' S)) or lo (its exact remainder)
+  const float k_unscale0 = __builtin_amdgcn_ldexpf(a.qscale, 15 - KS::F + ek0);
+  const float k_unscale1 = __builtin_amdgcn_ldexpf(a.qscale, 15 - KS::F + ek1);
+  const float z_unscale = __builtin_amdgcn_ldexpf(a.qscale, ek);  // the zero-point terms of head hr
+
+  float m_run[2] = {-INFINITY, -INFINITY};  // running max of heads 2 lk, 2 lk + 1 (base 2)
+  float lsum[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
+
+  for (int step = 0; step < n_steps; ++step) {
+    progress_prio<true>(step, n_steps);
+    const int g0 = step_first(gb, step, n_steps, rot);
+    const int ns = min(4, ge - g0);
+    wait_vm<0>();
+    wave_lds_sync();
+    const uint8_t* const meta = smem + S::offKM0 + (step & 1) * S::kMetaBytes;
+    // chunk 4 lk + c of stream st sits in slot 4 ((lk + st) mod 4) + c
+    auto meta_chunks = [&](int field, int st) {
+      return reinterpret_cast<const u32x4*>(meta + field * 4 * D * 2 + st * D * 2 + 64 * ((lk + st) & 3));
+    };
+    // codes: B column lc of tile s = 2 g + tt is token 16 tt + lc of stream g
+    uint32_t kw[8][KL];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const uint8_t* row = smem + (s >> 1) * S::kGroupPad + (16 * (s & 1) + lc) * S::kRow + 4 * KL * lk;
+      if constexpr (KL == 2) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(row);
+        kw[s][0] = v[0];
+        kw[s][1] = v[1];
+      } else {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(row);
+#pragma unroll
+        for (int i = 0; i < KL; ++i) kw[s][i] = v[i];
+      }
+    }
+    wave_lds_sync();
+    if (step + 1 < n_steps) {
+      const int g1 = step_first(gb, step + 1, n_steps, rot);
+      issue_kstage<KB, VB, GT, PAGED, KEEP>(a, u, ubase, g1, min(4, ge - g1), lsm,
+                                            lsm + S::offKM0 + ((step + 1) & 1) * S::kMetaBytes);
+    }
+    // A (per stream and block of 32 channels) = this lane's half of q'' * S;
+    // the zero-point terms sum_d q'_d Z_d of head hr and streams 2 part,
+    // 2 part + 1 on the vector ALUs
+    float bcls[2] = {0.0f, 0.0f};
+    f32x4 sc[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) sc[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      // the codes of a tile are converted right before its products (few
+      // registers live)
+      auto codes = [&](int s) {
+        return (KB == 4) ? codes8<4, 0>(kw[s][c & (KL - 1)])
+               : (c & 1) ? codes8<2, 1>(kw[s][c >> 1]) : codes8<2, 0>(kw[s][c >> 1]);
+      };
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const u32x4 sB = meta_chunks(0, g)[c];
+        u32x4 h4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h4[e] = residual_pair(q2[4 * c + e], sB[e], q2[4 * c + e] & qmask);
+        const half8_t ah = as_h8(h4);
+        sc[2 * g] = mfma(ah, codes(2 * g), sc[2 * g]);
+        sc[2 * g + 1] = mfma(ah, codes(2 * g + 1), sc[2 * g + 1]);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const u32x4 zB = meta_chunks(1, 2 * part + j)[c];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bcls[j] = dot2_acc(q2[4 * c + e], zB[e], bcls[j]);
+      }
+    }
+    float* const sl = reinterpret_cast<float*>(smem + S::offP0 + (step & 1) * S::pBytes);
+    // zero-point terms over all 128 channels, exchanged through LDS as [stream][head]
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float bz = swap_sum<16>(bcls[j]);
+      bz = swap_sum<32>(bz) * z_unscale;
+      if (lk == 0) sl[S::offBias / 4 + (2 * part + j) * 8 + hr] = bz;
+    }
+    wave_lds_order();
+    // scores of heads 2 lk (rows 4 lk, 4 lk + 1: hi, lo) and 2 lk + 1 (rows
+    // 4 lk + 2, 4 lk + 3) at token 16 (s & 1) + lc of stream s >> 1.
+    // Streams past the last group hold no tokens: a zero-point term of -inf
+    // masks their scores (their raw sums are finite).
+    float x0[8], x1[8];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const u32x2 bzw = *reinterpret_cast<const u32x2*>(sl + S::offBias / 4 + g * 8 + 2 * lk);
+      const bool valid = g < ns;
+      const float bz0 = valid ? __uint_as_float(bzw[0]) : -INFINITY;
+      const float bz1 = valid ? __uint_as_float(bzw[1]) : -INFINITY;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const f32x4 v = sc[2 * g + tt];
+        x0[2 * g + tt] = fmaf(v[0] + v[1], k_unscale0, bz0);
+        x1[2 * g + tt] = fmaf(v[2] + v[3], k_unscale1, bz1);
+      }
+    }
+    float mx0 = max_raw(max_raw(max_raw(x0[0], x0[1]), max_raw(x0[2], x0[3])),
+                        max_raw(max_raw(x0[4], x0[5]), max_raw(x0[6], x0[7])));
+    float mx1 = max_raw(max_raw(max_raw(x1[0], x1[1]), max_raw(x1[2], x1[3])),
+                        max_raw(max_raw(x1[4], x1[5]), max_raw(x1[6], x1[7])));
+    mx0 = row_max16(mx0);  // the 16 lanes of group lk hold all 128 tokens of head 2 lk
+    mx1 = row_max16(mx1);
+    float alpha[2];
+    const float mxs[2] = {mx0, mx1};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float m_new = fmaxf(m_run[i], mxs[i]);
+      alpha[i] = !(m_new > m_run[i]) ? 1.0f : (m_run[i] == -INFINITY ? 0.0f : fast_exp2(m_run[i] - m_new));
+      m_run[i] = m_new;
+      lsum[i][0] *= alpha[i];
+      lsum[i][1] *= alpha[i];
+    }
+    const float mm0 = m_run[0] + static_cast<float>(ev), mm1 = m_run[1] + static_cast<float>(ev);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const float p0 = fast_exp2(x0[s] - mm0), p1 = fast_exp2(x1[s] - mm1);
+      lsum[0][s & 1] += p0;
+      lsum[1][s & 1] += p1;
+      float* const pr = sl + ((s >> 1) * 8 + 2 * lk) * kRowP + 16 * (s & 1) + lc;
+      pr[0] = p0;
+      pr[kRowP] = p1;
+    }
+    if (lc == 0) {
+      sl[S::offAlpha / 4 + 2 * lk] = alpha[0];
+      sl[S::offAlpha / 4 + 2 * lk + 1] = alpha[1];
+    }
+    wg_barrier();  // step's probabilities ready
+  }
+
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float l = row_sum16(lsum[i][0] + lsum[i][1]);
+    if (lc == 0) {
+      // l and the value wave's o carry 2^-Ev; m + Ev restores their weight
+      float* P = a.partial + (((long long)b * a.Hq + h0 + 2 * lk + i) * a.n_split + split) * (D + 2);
+      P[0] = m_run[i] + static_cast<float>(ev);
+      P[1] = l;
+    }
+  }
+}
+
+template <int KB, int VB, bool BF16, int GT, bool PAGED, bool KEEP>
+__device__ __forceinline__ void value_wave8(const DecodeArgs& a, long long u, int b, int h0, int split,
+                                            int gb, int ge, int n_steps, int rot, uint8_t* smem, lds_u8* lsm) {
+  using S = Stage<KB, VB, 8>;
+  using VS = CodeScale<VB>;
+  const int lane = threadIdx.x & 63;
+  const int lc = lane & 15, lk = lane >> 4;
+  // B column lc: head hsrc, channel group msel of tiles 0-3 (channels 0-63)
+  // and 2 + msel of tiles 4-7
+  const int hsrc = lc >> 1, msel = lc & 1;
+  uint8_t* const vbase = smem + S::offV0;
+  lds_u8* const lvbase = lsm + S::offV0;
+  constexpr BlockLayout BLu = block_layout(KB, VB, GT);
+  const uint8_t* const ubase = a.blocks + static_cast<size_t>(u) * a.nb * BLu.bytes;  // (unit-major)
+  {
+    const int f0 = step_first(gb, 0, n_steps, rot);
+    issue_vstage<KB, VB, GT, PAGED, KEEP>(a, u, ubase, f0, min(4, ge - f0), lvbase);
+  }
+  constexpr float v_unscale = static_cast<float>(1 << (15 - VS::F));  // product -> output
+
+  float za[4] = {0.0f, 0.0f, 0.0f, 0.0f}, zb[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // sums of p' * Z
+  f32x4 o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (int step = 0; step < n_steps; ++step) {
+    progress_prio<false>(step, n_steps);
+    const uint8_t* vstage = vbase + (step & 1) * S::vBytes;
+    const bool more = step + 1 < n_steps;
+    if (more) {
+      const int g1 = step_first(gb, step + 1, n_steps, rot);
+      issue_vstage<KB, VB, GT, PAGED, KEEP>(a, u, ubase, g1, min(4, ge - g1),
+                                            lvbase + ((step + 1) & 1) * S::vBytes);
+    }
+    wg_barrier();  // the key wave has written this step's probabilities
+    if (more) {
+      wait_vm<S::vLoads>();
+    } else {
+      wait_vm<0>();
+    }
+    wave_lds_sync();
+    const float* hp = reinterpret_cast<const float*>(smem + S::offP0 + (step & 1) * S::pBytes);
+    const float alpha = hp[S::offAlpha / 4 + hsrc];
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] *= alpha;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        za[e] *= alpha;
+        zb[e] *= alpha;
+      }
+    }
+    // p.V of one k block of 32 tokens: p0, p1 this lane's 8 tokens of head
+    // hsrc; scale and zero of channel group msel (va*) and 2 + msel (vb*);
+    // av the codes (entry pairs (a, a + 4), see codes8)
+    auto products = [&](const f32x4& p0, const f32x4& p1, const u32x4& vsa, const u32x4& vza, const u32x4& vsb,
+                        const u32x4& vzb, const uint32_t (&vc)[8], int run) {
+      const float p[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+      u32x4 ha, la, hb, lb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // pair e: tokens e and e + 4
+        uint32_t hi, lo;
+        float b0 = (e & 1) ? times_half<1>(p[e], vsa[e >> 1]) : times_half<0>(p[e], vsa[e >> 1]);
+        float b1 = (e & 1) ? times_half<1>(p[e + 4], vsa[2 + (e >> 1)]) : times_half<0>(p[e + 4], vsa[2 + (e >> 1)]);
+        split_pair(b0, b1, hi, lo);
+        ha[e] = hi;
+        la[e] = lo;
+        b0 = (e & 1) ? times_half<1>(p[e], vsb[e >> 1]) : times_half<0>(p[e], vsb[e >> 1]);
+        b1 = (e & 1) ? times_half<1>(p[e + 4], vsb[2 + (e >> 1)]) : times_half<0>(p[e + 4], vsb[2 + (e >> 1)]);
+        split_pair(b0, b1, hi, lo);
+        hb[e] = hi;
+        lb[e] = lo;
+        za[e] = fmaf(p[2 * e], lo_half(vza[e]), za[e]);
+        za[e] = fmaf(p[2 * e + 1], hi_half(vza[e]), za[e]);
+        zb[e] = fmaf(p[2 * e], lo_half(vzb[e]), zb[e]);
+        zb[e] = fmaf(p[2 * e + 1], hi_half(vzb[e]), zb[e]);
+      }
+      const half8_t bha = as_h8(ha), bla = as_h8(la), bhb = as_h8(hb), blb = as_h8(lb);
+      // each tile's codes converted right before its two products
+#pragma unroll
+      for (int be = 0; be < 8; ++be) {
+        const half8_t av = (VB == 4) ? codes8<4, 0>(vc[be]) : run ? codes8<2, 1>(vc[be]) : codes8<2, 0>(vc[be]);
+        o[be] = mfma(av, be < 4 ? bha : bhb, o[be]);
+        o[be] = mfma(av, be < 4 ? bla : blb, o[be]);
+      }
+    };
+    // All 4 streams, also past the split's last group (p = 0 there, see value_wave).
+    if constexpr (VB == 2) {
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        const int gsl = 2 * pp + (lk >> 1), w = lk & 1;
+        const uint8_t* vrow = vstage + gsl * S::vGroup + (w * D + 4 * lc) * 4;
+        const u32x4 v0 = *reinterpret_cast<const u32x4*>(vrow);
+        const u32x4 v1 = *reinterpret_cast<const u32x4*>(vrow + 64 * 4);
+        const uint32_t vc[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+#pragma unroll
+        for (int run = 0; run < 2; ++run) {
+          const int t0 = 16 * w + 8 * run;  // first token of the run in its stream
+          const int vma = ((gsl * 4 + msel) * G + t0) * 2, vmb = ((gsl * 4 + 2 + msel) * G + t0) * 2;
+          const u32x4 vsa = *reinterpret_cast<const u32x4*>(vstage + S::offVS + vma);
+          const u32x4 vza = *reinterpret_cast<const u32x4*>(vstage + S::offVZ + vma);
+          const u32x4 vsb = *reinterpret_cast<const u32x4*>(vstage + S::offVS + vmb);
+          const u32x4 vzb = *reinterpret_cast<const u32x4*>(vstage + S::offVZ + vmb);
+          const float* prow = hp + (gsl * 8 + hsrc) * kRowP + t0;
+          const f32x4 p0 = *reinterpret_cast<const f32x4*>(prow);
+          const f32x4 p1 = *reinterpret_cast<const f32x4*>(prow + 4);
+          products(p0, p1, vsa, vza, vsb, vzb, vc, run);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int gs = 0; gs < 4; ++gs) {
+        const uint8_t* vrow = vstage + gs * S::vGroup + (lk * D + 4 * lc) * 4;
+        const u32x4 v0 = *reinterpret_cast<const u32x4*>(vrow);
+        const u32x4 v1 = *reinterpret_cast<const u32x4*>(vrow + 64 * 4);
+        const uint32_t vc[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        const int vma = ((gs * 4 + msel) * G + 8 * lk) * 2, vmb = ((gs * 4 + 2 + msel) * G + 8 * lk) * 2;
+        const u32x4 vsa = *reinterpret_cast<const u32x4*>(vstage + S::offVS + vma);
+        const u32x4 vza = *reinterpret_cast<const u32x4*>(vstage + S::offVZ + vma);
+        const u32x4 vsb = *reinterpret_cast<const u32x4*>(vstage + S::offVS + vmb);
+        const u32x4 vzb = *reinterpret_cast<const u32x4*>(vstage + S::offVZ + vmb);
+        const float* prow = hp + (gs * 8 + hsrc) * kRowP + 8 * lk;
+        const f32x4 p0 = *reinterpret_cast<const f32x4*>(prow);
+        const f32x4 p1 = *reinterpret_cast<const f32x4*>(prow + 4);
+        products(p0, p1, vsa, vza, vsb, vzb, vc, 0);
+      }
+    }
+  }
+
+  float zsa = (za[0] + za[1]) + (za[2] + za[3]);
+  float zsb = (zb[0] + zb[1]) + (zb[2] + zb[3]);
+  zsa = swap_sum<32>(swap_sum<16>(zsa));  // over the 4 row chunks: head hsrc, channel group msel
+  zsb = swap_sum<32>(swap_sum<16>(zsb));  // channel group 2 + msel
+  // Row 4 lk + r of product be is channel 16 lk + 4 r + be (be < 4, group
+  // lk / 2) or 64 + 16 lk + 4 r + be - 4 (group 2 + lk / 2): the lanes whose
+  // column takes group lk / 2 and 2 + lk / 2 write both halves.
+  if (msel == (lk >> 1)) {
+    float* P = a.partial + (((long long)b * a.Hq + h0 + hsrc) * a.n_split + split) * (D + 2);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      f32x4 x, y;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = fmaf(o[i][r], v_unscale, zsa);
+        y[i] = fmaf(o[4 + i][r], v_unscale, zsb);
+      }
+      *reinterpret_cast<f32x4*>(P + 2 + 16 * lk + 4 * r) = x;
+      *reinterpret_cast<f32x4*>(P + 2 + 64 + 16 * lk + 4 * r) = y;
+    }
+  }
+}
+
 // Workgroup w of the launch (a 1-D grid) -> pair index P = split + nx * row
 // over the (split, unit row) pairs, and head group hg.  With one head group
-// P = w.  With hg > 1 head groups (8 or 16 query heads per kv head: 4 heads
-// per workgroup) the workgroups of one pair read the same records; w takes
+// P = w.  With hg > 1 head groups (16 query heads per kv head: 8 heads per
+// workgroup) the workgroups of one pair read the same records; w takes
 // them 8 apart, so they fall on the same XCD (workgroups are dealt to the 8
 // XCDs in turn) at about the same time and the second one reads the records
 // from that XCD's L2:
@@ -1200,7 +1584,8 @@ __device__ __forceinline__ unsigned pair_of(unsigned w, int hg, int& g) {
 
 template <int KB, int VB, bool BF16, int NQ, int GT, bool PAGED, bool KEEP>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma(DecodeArgs a) {
-  using S = Stage<KB, VB>;
+  constexpr int NH = NQ == 8 ? 8 : GQ;  // head slots of the stage layout
+  using S = Stage<KB, VB, NH>;
   __shared__ __align__(16) uint8_t smem[S::bytes];
   lds_u8* const lsm = (lds_u8*)smem;  // (C-style: an address-space conversion)
   const int wave = threadIdx.x >> 6;  // 0: key wave, 1: value wave
@@ -1238,10 +1623,18 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
       // groups of one pair take the same walk
       const int rot = static_cast<int>(P % static_cast<unsigned>(n_steps));
       // Both waves run the same number of steps and meet at one barrier per step.
-      if (wave == 0) {
-        key_wave<KB, VB, BF16, NQ, GT, PAGED, KEEP>(a, u, b, h0, split, gb, ge, n_steps, rot, smem, lsm);
+      if constexpr (NQ == 8) {
+        if (wave == 0) {
+          key_wave8<KB, VB, BF16, GT, PAGED, KEEP>(a, u, b, h0, split, gb, ge, n_steps, rot, smem, lsm);
+        } else {
+          value_wave8<KB, VB, BF16, GT, PAGED, KEEP>(a, u, b, h0, split, gb, ge, n_steps, rot, smem, lsm);
+        }
       } else {
-        value_wave<KB, VB, BF16, NQ, GT, PAGED, KEEP>(a, u, b, h0, split, gb, ge, n_steps, rot, smem, lsm);
+        if (wave == 0) {
+          key_wave<KB, VB, BF16, NQ, GT, PAGED, KEEP>(a, u, b, h0, split, gb, ge, n_steps, rot, smem, lsm);
+        } else {
+          value_wave<KB, VB, BF16, NQ, GT, PAGED, KEEP>(a, u, b, h0, split, gb, ge, n_steps, rot, smem, lsm);
+        }
       }
     }
   }
@@ -1254,7 +1647,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3))) void d
     wave_lds_sync();
     window_wave<BF16, NQ>(a, u, b, h0, a.n_split_packed, nr, hgi == 0,
                           reinterpret_cast<float (*)[D]>(smem + S::offV0),
-                          reinterpret_cast<float (*)[G]>(smem + S::offV0 + GQ * D * 4));
+                          reinterpret_cast<float (*)[G]>(smem + S::offV0 + NH * D * 4));
   }
 }
 
@@ -1273,8 +1666,9 @@ hipError_t launch_k(const DecodeArgs& a, hipStream_t stream) {
 
 template <int KB, int VB, bool BF16, int NQ, int GT, bool PAGED>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  // head groups (only with 4 heads per workgroup) keep the records in L2
-  if constexpr (NQ == 4) {
+  // head groups (16 query heads per kv head: two workgroups of 8) keep the
+  // records in L2
+  if constexpr (NQ == 8) {
     if (a.hg > 1) return launch_k<KB, VB, BF16, NQ, GT, PAGED, true>(a, stream);
   }
   return launch_k<KB, VB, BF16, NQ, GT, PAGED, false>(a, stream);
@@ -1289,14 +1683,14 @@ hipError_t launch_gp(const DecodeArgs& a, hipStream_t stream) {
 
 template <int KB, int VB, bool BF16>
 hipError_t launch_nq(const DecodeArgs& a, hipStream_t stream) {
-  // 8 and 16 query heads per kv head: 2 or 4 head groups of 4 (a.hg)
-  if (a.hg != (a.gq > 4 ? a.gq / 4 : 1)) return hipErrorInvalidValue;
+  // 16 query heads per kv head: 2 head groups of 8 (a.hg)
+  if (a.hg != (a.gq > 8 ? a.gq / 8 : 1)) return hipErrorInvalidValue;
   switch (a.gq) {
     case 1: return launch_gp<KB, VB, BF16, 1>(a, stream);
     case 2: return launch_gp<KB, VB, BF16, 2>(a, stream);
-    case 4:
+    case 4: return launch_gp<KB, VB, BF16, 4>(a, stream);
     case 8:
-    case 16: return launch_gp<KB, VB, BF16, 4>(a, stream);
+    case 16: return launch_gp<KB, VB, BF16, 8>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

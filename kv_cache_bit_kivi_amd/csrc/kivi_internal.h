@@ -123,12 +123,13 @@ struct DecodeArgs {
 };
 
 // LDS bytes of one workgroup (key wave + value wave) of the matrix-core
-// decode kernel: one key-code buffer, two key-metadata buffers, two value
-// stages and two hand-over buffers.  Bounds the resident workgroups per CU.
-constexpr int mfma_wg_lds_bytes(int k_bits, int v_bits) {
+// decode kernel serving `heads` query heads (4, or 8 in the eight-head
+// layout): one key-code buffer, two key-metadata buffers, two value stages
+// and two hand-over buffers.  Bounds the resident workgroups per CU.
+constexpr int mfma_wg_lds_bytes(int k_bits, int v_bits, int heads) {
   return 4 * (kGroup * kHeadDim * k_bits / 8 + 64) + 2 * (2 * 4 * kHeadDim * 2) +
          2 * (4 * kGroup * v_bits / 32 * kHeadDim * 4 + 2 * 4 * kHeadDim * 2) +
-         2 * (4 * 4 * 36 * 4 + 16 + 16 * 4);
+         2 * (4 * heads * 36 * 4 + 4 * heads + 16 * heads);
 }
 constexpr int kLdsPerCu = 160 * 1024;  // MI355X (gfx950)
 

@@ -183,8 +183,8 @@ void fused_step_plan() {
       CHECK(field(db, KIND) == 2 && field(da, NQ) == field(db, NQ) && field(da, NR) == field(db, NR));
       CHECK(field(da, NSPLIT) == field(db, NSPLIT) && field(da, NSPLIT_PACKED) == field(db, NSPLIT_PACKED));
       CHECK(field(da, FUSED) == 1 && field(db, FUSED) == 0);
-      // 2 kv heads: 8 and 16 query heads per kv head take 2 and 4 head groups
-      CHECK(field(da, HG) == (hq / 2 > 4 ? hq / 8 : 1) && field(db, HG) == field(da, HG));
+      // 2 kv heads: 16 query heads per kv head take 2 head groups of 8
+      CHECK(field(da, HG) == (hq / 2 > 8 ? hq / 16 : 1) && field(db, HG) == field(da, HG));
       (void)n0;
     }
     CHECK(kivi_cache_destroy(a) == KIVI_OK);
