@@ -282,9 +282,9 @@ kivi_status kivi_decode_attn_workspace_bytes(const kivi_cache* cache,
  * softmax states are merged exactly (log-sum-exp) in a second kernel; the
  * workspace holds those partials.
  * The products run on the matrix cores with fp16 operands (hi + lo pairs,
- * about 22 significant bits); one workgroup serves up to 4 query heads of a
- * kv head per token split, so 8 or 16 query heads per kv head take 2 or 4
- * workgroups over the same records.  Each workgroup scales its folded operands q*S and p*S by powers of two chosen
+ * about 22 significant bits); one workgroup serves up to 8 query heads of a
+ * kv head per token split, so 16 query heads per kv head take 2 workgroups
+ * over the same records.  Each workgroup scales its folded operands q*S and p*S by powers of two chosen
  * from the largest |q| of each head and the scale maxima of the records it
  * reads, so every input in the domain stated above stays in the operands'
  * range; the scaling is exact and undone in fp32.
