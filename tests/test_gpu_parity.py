@@ -39,7 +39,12 @@ CASES = [("c0",            1, 1, 1, 1024, 2, 2, torch.float16, 128),
          ("r1024_flush",   1, 1, 2, 2048, 2, 2, torch.bfloat16, 1024),
          ("r256_mha_4b",   2, 2, 2, 700, 4, 4, torch.float16, 256),
          ("r1024_gq8",     1, 1, 8, 1500, 2, 2, torch.float16, 1024),
-         # 16 query heads per kv head: 4 head groups per split
+         # 8 query heads per kv head in one workgroup (the eight-head layout),
+         # every bit pair, long caches
+         ("gq8_k2v4_bf16", 1, 2, 16, 900, 2, 4, torch.bfloat16, 128),
+         ("gq8_k4v2_long", 1, 1, 8, 3000, 4, 2, torch.float16, 128),
+         ("gq8_4b_long",   2, 1, 8, 2500, 4, 4, torch.float16, 64),
+         # 16 query heads per kv head: 2 head groups of 8 per split
          ("gq16",          2, 1, 16, 900, 2, 2, torch.float16, 128),
          ("gq16_bf16_4b",  1, 2, 32, 450, 4, 4, torch.bfloat16, 64)]
 IDS = [c[0] for c in CASES]
