@@ -44,6 +44,8 @@
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "kivi_internal.h"
 
 namespace kivi {
@@ -298,6 +300,29 @@ __device__ __forceinline__ void wg_barrier() {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Parity of a step (which half of the double buffers it uses): a constant
+// when the step loop runs in pairs, else from the step index.
+struct RuntimeParity {};
+template <int P>
+__device__ __forceinline__ constexpr int parity(int, std::integral_constant<int, P>) { return P; }
+__device__ __forceinline__ int parity(int step, RuntimeParity) { return step & 1; }
+
+// Runs steps 0 .. n_steps - 1 of a wave.  In pairs (even and odd steps use
+// fixed halves of the double buffers, so their LDS offsets are constants),
+// except for 4-bit keys with 2-bit values, whose register budget the doubled
+// loop body exceeds.
+template <bool PAIRS, typename F>
+__device__ __forceinline__ void run_steps(int n_steps, F&& one_step) {
+  if constexpr (PAIRS) {
+    for (int step = 0; step < n_steps; step += 2) {
+      one_step(step, std::integral_constant<int, 0>{});
+      if (step + 1 < n_steps) one_step(step + 1, std::integral_constant<int, 1>{});
+    }
+  } else {
+    for (int step = 0; step < n_steps; ++step) one_step(step, RuntimeParity{});
+  }
+}
 
 // ---------------------------------------------------------------------------
 // Residual window on the vector ALUs (one wave, fp32), written as its own
@@ -808,14 +833,15 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
   float m_run = -INFINITY;           // running max of head hq (base 2)
   float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // sum of p' (four partial sums)
 
-  for (int step = 0; step < n_steps; ++step) {
+  auto one_step = [&](int step, auto par) __attribute__((always_inline)) {
+    const int PAR = parity(step, par);
     progress_prio<true>(step, n_steps);
     const int g0 = step_first(gb, step, n_steps, rot);
     const int ns = min(4, ge - g0);
     // this step's codes and metadata are the only loads of this wave in flight
     wait_vm<0>();
     wave_lds_sync();
-    const uint8_t* const meta = smem + S::offKM0 + (step & 1) * S::kMetaBytes;
+    const uint8_t* const meta = smem + S::offKM0 + PAR * S::kMetaBytes;
 
     // chunk 4 lk + c of stream st sits in slot 4 ((lk + st) mod 4) + c
     auto meta_chunks = [&](int field, int st) {
@@ -855,7 +881,7 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
     if (step + 1 < n_steps) {
       const int g1 = step_first(gb, step + 1, n_steps, rot);
       issue_kstage<KB, VB, GT, PAGED, KEEP>(a, u, ubase, g1, min(4, ge - g1), lsm,
-                                            lsm + S::offKM0 + ((step + 1) & 1) * S::kMetaBytes);
+                                            lsm + S::offKM0 + (1 - PAR) * S::kMetaBytes);
     }
     // B = q' * S (hi, lo) for head hq and group g0 + gc, built per block of
     // 32 channels right before its products (the vector work of block c+1
@@ -929,7 +955,7 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
     // 8j .. 8j+7 of stream lk, and overwrites them with their probabilities.
     // Rows of 32 scores are padded to kRowP floats: the 16 rows start on
     // distinct banks.
-    float* const sl = reinterpret_cast<float*>(smem + S::offP0 + (step & 1) * S::pBytes);
+    float* const sl = reinterpret_cast<float*>(smem + S::offP0 + PAR * S::pBytes);
     // (raw products; each reader applies the scale and its stream's
     // zero-point term to its own 8 scores, and with kHiLoCols adds the lo
     // column, which the diagonal lanes of slot hq + NQ write like a head)
@@ -1011,7 +1037,8 @@ __device__ __forceinline__ void key_wave(const DecodeArgs& a, long long u, int b
     *reinterpret_cast<f32x4*>(sl + row + 4) = p1;
     if (lk == 0 && jt == 0) sl[S::offAlpha / 4 + hq] = alpha;
     wg_barrier();  // step's probabilities ready
-  }
+  };
+  run_steps<!(KB == 4 && VB == 2)>(n_steps, one_step);
 
   float l = (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
   l = l + partner<1>(l);
@@ -1061,13 +1088,14 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  for (int step = 0; step < n_steps; ++step) {
+  auto one_step = [&](int step, auto par) __attribute__((always_inline)) {
+    const int PAR = parity(step, par);
     progress_prio<false>(step, n_steps);
-    const uint8_t* vstage = vbase + (step & 1) * S::vBytes;
+    const uint8_t* vstage = vbase + PAR * S::vBytes;
     const bool more = step + 1 < n_steps;
     if (more) {
       const int g1 = step_first(gb, step + 1, n_steps, rot);
-      issue_vstage<KB, VB, GT, PAGED, KEEP>(a, u, ubase, g1, min(4, ge - g1), lvbase + ((step + 1) & 1) * S::vBytes);
+      issue_vstage<KB, VB, GT, PAGED, KEEP>(a, u, ubase, g1, min(4, ge - g1), lvbase + (1 - PAR) * S::vBytes);
     }
     wg_barrier();  // the key wave has written this step's probabilities
     if (more) {
@@ -1076,7 +1104,7 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
       wait_vm<0>();
     }
     wave_lds_sync();
-    const float* hp = reinterpret_cast<const float*>(smem + S::offP0 + (step & 1) * S::pBytes);
+    const float* hp = reinterpret_cast<const float*>(smem + S::offP0 + PAR * S::pBytes);
     const float alpha = hp[S::offAlpha / 4 + hsrc];
     if (__any(alpha != 1.0f)) {
 #pragma unroll
@@ -1181,7 +1209,8 @@ __device__ __forceinline__ void value_wave(const DecodeArgs& a, long long u, int
         products(p0, p1, vs, vz, av);
       }
     }
-  }
+  };
+  run_steps<!(KB == 4 && VB == 2)>(n_steps, one_step);
 
   float z = (zcls[0] + zcls[1]) + (zcls[2] + zcls[3]);
   z = swap_sum<16>(z);
