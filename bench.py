@@ -469,7 +469,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16 hi+lo matrix operands x 2/4-bit codes, f32 accumulation",
+        "dtype": "f16",
+        "arithmetic": "decode: f16 matrix-core operands (hi + lo halves of q*S and p*S, codes as exact f16) "
+                      "with f32 accumulation and f32 softmax; pack: binary32 quantizer",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.description}", "batch": w.batch,
                    "kv_heads": w.kv_heads, "q_heads": w.q_heads, "head_dim": w.head_dim,

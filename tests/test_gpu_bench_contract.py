@@ -37,6 +37,7 @@ def test_bench_line_contract():
     assert (j["n_gpus"], j["steps"], j["warmup"]) == (1, 6, 1)
     assert j["unit"] == "GB/s" and j["higher_is_better"] is True and j["data"] == "synthetic"
     assert j["vs_baseline"] is None and j["cpu_baseline"] is None
+    assert j["dtype"] == "f16"  # the decode's matrix-product operand type
     assert j["config"]["workload"].startswith("c2:")
     ab = bench.algorithmic_bytes(WORKLOADS["c2"])
     assert j["value"] == pytest.approx(bench.step_bytes(ab) / (j["ms_per_step"] * 1e-3) / 1e9, rel=1e-9)
