@@ -63,6 +63,80 @@ def test_grid_exact_cache_is_plain_attention(oracle_mod, kb, vb, dtype, gq, G):
     assert np.max(np.abs(out - ref)) < 1e-11
 
 
+def _unpack(words, bits, per_word):
+    # code i of a word sits at bit bits * (i // 2) + 16 * (i % 2) (the
+    # split-half order of the packed layout); returns [..., per_word]
+    i = np.arange(per_word)
+    off = (bits * (i // 2) + 16 * (i % 2)).astype(np.uint32)
+    return ((words[..., None].astype(np.uint32) >> off) & ((1 << bits) - 1)).astype(np.float64)
+
+
+def _dequantized_cache(arr, B, H, D, G, R, kb, vb, nq, nr, dtype):
+    # Keys and values the cache stands for, read out of the oracle's arrays
+    # by the layout alone: code * S + Z for packed tokens ("Asymmetric 2-Bit"
+    # guide, "Step 2"; keys grouped per channel, values per token), the
+    # stored window for the rest.
+    U, cap, nb = B * H, arr["k_codes"].size // (B * H * D * kb // 32), nq // G
+    f16 = lambda b: b.astype(np.uint16).view(np.float16).astype(np.float64)
+    kc = _unpack(arr["k_codes"].reshape(U, cap, D * kb // 32), kb, 32 // kb).reshape(U, cap, D)[:, :nq]
+    ks = f16(arr["k_scale"]).reshape(U, -1, D)[:, :nb]
+    kz = f16(arr["k_zero"]).reshape(U, -1, D)[:, :nb]
+    Kp = kc.reshape(U, nb, G, D) * ks[:, :, None, :] + kz[:, :, None, :]
+    vw = G * vb // 32
+    vc = _unpack(arr["v_codes"].reshape(U, -1, vw, D)[:, :nb], vb, 32 // vb)   # [U][nb][w][D][i]
+    vc = vc.transpose(0, 1, 2, 4, 3).reshape(U, nb, G, D)                       # row w*Pv + i
+    vs = f16(arr["v_scale"]).reshape(U, -1, D // G, G)[:, :nb].transpose(0, 1, 3, 2)  # [U][nb][row][m]
+    vz = f16(arr["v_zero"]).reshape(U, -1, D // G, G)[:, :nb].transpose(0, 1, 3, 2)
+    Vp = vc * np.repeat(vs, G, axis=3) + np.repeat(vz, G, axis=3)
+    kr = from_bits(arr["k_resid"].reshape(U, R, D)[:, :nr], dtype)
+    vr = from_bits(arr["v_resid"].reshape(U, R, D)[:, :nr], dtype)
+    K = np.concatenate([Kp.reshape(U, nq, D), kr], axis=1).reshape(B, H, nq + nr, D)
+    V = np.concatenate([Vp.reshape(U, nq, D), vr], axis=1).reshape(B, H, nq + nr, D)
+    return K, V
+
+
+@pytest.mark.parametrize("kb,vb,dtype,gq,G", [(2, 2, "f16", 4, 32), (4, 2, "bf16", 2, 32),
+                                              (2, 4, "f16", 1, 64), (4, 4, "bf16", 8, 32)])
+def test_attention_over_dequantized_records(oracle_mod, kb, vb, dtype, gq, G):
+    # General (off-grid) data: the oracle's attention equals textbook softmax
+    # attention over the keys and values its own records dequantize to, read
+    # out here from the documented layout.  A wrong group, row or channel
+    # index, a dropped zero point, a wrong window slot or a swapped key/value
+    # operand in the attention would each move the result by far more than
+    # rounding.
+    rng = np.random.default_rng(kb * 10 + vb + gq + G)
+    B, H, D, R = 2, 2, 128, 64
+    T = 3 * R + 37
+    K, V = _rand(rng, (B, H, T, D), dtype), _rand(rng, (B, H, T, D), dtype)
+    K[..., 5] *= 16.0  # an outlier channel (keys) and a spread of value rows (exact scalings)
+    V[:, :, ::7] *= 4.0
+    K, V = from_bits(to_bits(K, dtype), dtype), from_bits(to_bits(V, dtype), dtype)
+    q = _rand(rng, (B, H * gq, D), dtype)
+    c = oracle_mod.OracleCache(B, H, D, T, kb, vb, G, R, 0 if dtype == "f16" else 1)
+    c.append(to_bits(K, dtype), to_bits(V, dtype))
+    nq, nr = c.n_quant, c.n_resid
+    assert (nq, nr) == (192, 37)
+    Kd, Vd = _dequantized_cache(c.arrays(), B, H, D, G, R, kb, vb, nq, nr, dtype)
+    # the read-out is the cache's content: window tokens exact, packed ones
+    # within half a step (plus the fp16 rounding of S and Z) of the inputs
+    assert np.array_equal(Kd[:, :, nq:], K[:, :, nq:]) and np.array_equal(Vd[:, :, nq:], V[:, :, nq:])
+    nb = nq // G
+    kg = K[:, :, :nq].reshape(B, H, nb, G, D)                     # key groups: axis 3
+    vg = V[:, :, :nq].reshape(B, H, nq, D // G, G)                # value groups: axis 4
+    for x, xd, ax, bits, shape in ((kg, Kd[:, :, :nq].reshape(kg.shape), 3, kb, kg.shape),
+                                   (vg, Vd[:, :, :nq].reshape(vg.shape), 4, vb, vg.shape)):
+        lo, hi = x.min(axis=ax, keepdims=True), x.max(axis=ax, keepdims=True)
+        # half a step, plus the fp16 rounding of S (times qmax) and of Z
+        bound = 0.5 * (hi - lo) / (2 ** bits - 1) + 2.0 ** -10 * ((hi - lo) + np.abs(lo)) + 1e-12
+        assert np.all(np.abs(xd - x) <= bound)
+        assert np.max(np.abs(xd - x)) > 0
+    out = c.decode_attn(to_bits(q, dtype), SCALE)
+    ref = attention_fp64(q, Kd, Vd, SCALE, gq)
+    assert np.max(np.abs(out - ref)) < 1e-12
+    # and it is not plain attention on the inputs (the codes are lossy)
+    assert np.max(np.abs(out - attention_fp64(q, K, V, SCALE, gq))) > 1e-4
+
+
 def test_single_token_returns_its_value(oracle_mod):
     rng = np.random.default_rng(2)
     K, V = _rand(rng, (1, 1, 1, 128), "f16"), _rand(rng, (1, 1, 1, 128), "f16")
