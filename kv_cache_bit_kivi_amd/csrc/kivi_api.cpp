@@ -48,6 +48,14 @@ struct kivi_cache {
   uint32_t* scale_max;  // one entry per block record (same index)
   uint16_t* k_resid;
   uint16_t* v_resid;
+  // The last decode plan and the inputs it was made from.  The ragged plan
+  // search loops over split sizes and sequences; its inputs (the packed
+  // lengths) change once every R tokens of a sequence, so most decode steps
+  // reuse the plan.  Only plan_decode reads or writes these.
+  mutable bool memo_valid;
+  mutable int memo_key[6];
+  mutable std::vector<int> memo_sq;
+  mutable int memo_plan[4];
 };
 
 namespace {
@@ -656,7 +664,30 @@ struct DecodePlan {
 
 // Plans the decode launches over state `st` for gq query heads per kv head
 // (pure host arithmetic: no device access, no change of the cache).
+kivi_status plan_decode_uncached(const kivi_cache* c, const DecodeState& st, int gq, DecodePlan& out);
+
+// plan_decode_uncached, reused while its inputs are unchanged: the state's
+// longest packed length, whether a window exists, the packed length of each
+// sequence (ragged), the head ratio, a forced split count and the
+// compute-unit count.  The configuration is fixed per cache.
 kivi_status plan_decode(const kivi_cache* c, const DecodeState& st, int gq, DecodePlan& out) {
+  const int key[6] = {st.ragged ? 1 : 0, st.n_quant, st.n_resid > 0 ? 1 : 0, gq, c->forced_splits, c->cu_count};
+  if (c->memo_valid && std::equal(key, key + 6, c->memo_key) && (!st.ragged || st.sq == c->memo_sq)) {
+    out = DecodePlan{c->memo_plan[0], c->memo_plan[1], c->memo_plan[2], c->memo_plan[3]};
+    return KIVI_OK;
+  }
+  const kivi_status r = plan_decode_uncached(c, st, gq, out);
+  c->memo_valid = r == KIVI_OK;
+  if (r == KIVI_OK) {
+    std::copy(key, key + 6, c->memo_key);
+    c->memo_sq = st.ragged ? st.sq : std::vector<int>();
+    const int plan[4] = {out.n_split, out.n_split_packed, out.gps, out.hg};
+    std::copy(plan, plan + 4, c->memo_plan);
+  }
+  return r;
+}
+
+kivi_status plan_decode_uncached(const kivi_cache* c, const DecodeState& st, int gq, DecodePlan& out) {
   // the kernel walks the packed tokens in streams of 32 (a block of G = 32,
   // or half a block of G = 64)
   const int G = kivi::kStream;

@@ -8,7 +8,8 @@
 // (later calls return KIVI_ERR_HIP); a failed device query returns
 // KIVI_ERR_HIP before anything is enqueued and leaves the cache unchanged
 // and usable; the fused decode step plans the state after its append before
-// its first launch; launch arguments follow the window rules.
+// its first launch; launch arguments follow the window rules; a reused
+// decode plan equals a fresh one.
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -245,6 +246,43 @@ void ragged_paths() {
   }
   CHECK(kivi_cache_destroy(h) == KIVI_OK);
 }
+// The decode plan is reused while its inputs are unchanged: over fused
+// steps of sequences of different lengths (windows flushing at different
+// steps, a forced split count set and cleared, the head ratio changing), every
+// launch's split counts equal those a fresh cache plans for the same lengths.
+// With 2 compute units no ragged grid fits one round, and the plan then
+// depends on every sequence's length, not only the longest.
+void plan_reuse() {
+  for (int cus : {256, 2}) {
+  stub_reset();
+  stub_device(1, cus);
+  const kivi_config cf = config(5, 2, 6000);
+  kivi_cache* a = make(cf);
+  const int32_t n[5] = {3000, 1200, 5000, 0, 2500};
+  CHECK(kivi_append_varlen(a, kIn, kIn, n, 5000, nullptr) == KIVI_OK);
+  for (int t = 0; t < 300; ++t) {
+    const int hq = t < 150 ? 32 : (t < 220 ? 2 : 8);
+    if (t == 100) CHECK(kivi_set_decode_splits(a, 3) == KIVI_OK);
+    if (t == 120) CHECK(kivi_set_decode_splits(a, 0) == KIVI_OK);
+    CHECK(step(a, hq) == KIVI_OK);
+    const int da = stub_launches() - 1;
+    CHECK(field(da, KIND) == 2 && field(da, FUSED) == 1);
+    int32_t nq[5], nr[5];
+    CHECK(kivi_cache_get_lengths(a, nq, nr) == KIVI_OK);
+    kivi_cache* b = make(cf);
+    CHECK(kivi_cache_set_lengths(b, nq, nr) == KIVI_OK);
+    if (t >= 100 && t < 120) CHECK(kivi_set_decode_splits(b, 3) == KIVI_OK);
+    CHECK(decode(b, hq) == KIVI_OK);
+    const int db = stub_launches() - 1;
+    CHECK(field(db, KIND) == 2 && field(db, RAGGED) == field(da, RAGGED));
+    CHECK(field(da, NSPLIT) == field(db, NSPLIT) && field(da, NSPLIT_PACKED) == field(db, NSPLIT_PACKED));
+    CHECK(field(da, HG) == field(db, HG));
+    CHECK(kivi_cache_destroy(b) == KIVI_OK);
+  }
+  CHECK(kivi_cache_destroy(a) == KIVI_OK);
+  }
+}
+
 // Declared lengths (a restored snapshot): validated per sequence, no launch.
 void set_lengths_rules() {
   stub_reset();
@@ -283,6 +321,7 @@ int main() {
   fused_step_plan();
   fused_step_failures();
   ragged_paths();
+  plan_reuse();
   set_lengths_rules();
   std::printf("contract: %d checks passed\n", g_checks);
   return 0;
