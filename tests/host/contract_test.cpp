@@ -283,6 +283,22 @@ void plan_reuse() {
   }
 }
 
+// The largest forced split count: 1020 packed streams in 255 splits of one
+// step, plus the window's partial: 256, the most the merge takes.
+void most_splits() {
+  stub_reset();
+  kivi_cache* h = make(config(1, 2, 32700));
+  CHECK(kivi_append(h, kIn, kIn, 32700, nullptr) == KIVI_OK);
+  int nq, nr;
+  lengths(h, nq, nr);
+  CHECK(nq == 32640 && nr == 60);
+  CHECK(kivi_set_decode_splits(h, 1000000) == KIVI_OK);
+  CHECK(decode(h, 8) == KIVI_OK);
+  const int d = stub_launches() - 1;
+  CHECK(field(d, KIND) == 2 && field(d, NSPLIT) == 256 && field(d, NSPLIT_PACKED) == 255);
+  CHECK(kivi_cache_destroy(h) == KIVI_OK);
+}
+
 // Declared lengths (a restored snapshot): validated per sequence, no launch.
 void set_lengths_rules() {
   stub_reset();
@@ -322,6 +338,7 @@ int main() {
   fused_step_failures();
   ragged_paths();
   plan_reuse();
+  most_splits();
   set_lengths_rules();
   std::printf("contract: %d checks passed\n", g_checks);
   return 0;

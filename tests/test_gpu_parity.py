@@ -171,6 +171,33 @@ def test_split_invariance_and_determinism(case):
     assert np.array_equal(again, outs[0])
 
 
+@pytest.mark.parametrize("kb,vb,dt", [(2, 2, torch.float16), (4, 4, torch.bfloat16)], ids=["2b_f16", "4b_bf16"])
+def test_most_splits(kb, vb, dt):
+    # The largest split count the kernels take: 32640 packed tokens (1020
+    # streams) forced into 255 splits of one step each, plus the window's
+    # partial = 256 partials per query head, all merged by one workgroup
+    # (with 2 units the automatic plan is the same).  Against the oracle
+    # (2e-3) and a 3-split plan (the split-invariance bound).
+    w, x = _setup(("most_splits", 1, 2, 8, 32699, kb, vb, dt, 128), seed=6)
+    T = w.tokens + 1
+    cache = _gpu_cache(w, T)
+    cache.append(_dev(x.k, 0, T), _dev(x.v, 0, T))
+    assert (cache.n_quant, cache.n_resid) == (32640, 60)
+    q = x.q.contiguous().to(DEV)
+    scale = 1.0 / np.sqrt(w.head_dim)
+    print(f"most splits {kb}/{vb} {dt}", flush=True)
+    cache.set_splits(10 ** 6)
+    most = cache.decode_attn(q, scale).cpu().numpy().astype(np.float64)
+    cache.set_splits(3)
+    few = cache.decode_attn(q, scale).cpu().numpy().astype(np.float64)
+    ref = oracle_for(x.k, x.v, w, T)
+    o_ref = ref.decode_attn(bits16(x.q), scale)
+    print(f"most splits: vs oracle {np.max(np.abs(most - o_ref)):.2e}, vs 3 splits {np.max(np.abs(most - few)):.2e}",
+          flush=True)
+    assert np.max(np.abs(most - o_ref)) < TOL
+    assert np.max(np.abs(most - few)) < 1e-4
+
+
 def test_empty_and_errors_gpu():
     w, x = _setup(CASES[1])
     cache = _gpu_cache(w, 10)
